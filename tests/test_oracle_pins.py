@@ -1,0 +1,280 @@
+"""Pins for the float64 oracle: facts fixed by the pages and by mathematics,
+chosen so a plausible mistake in the oracle (wrong nibble order, wrong group
+index, dropped bias, swapped scale/bias, transposed operand, wrong silu sign)
+fails at least one of them. No GPU needed."""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from tests.tolerance import tol
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bf16(v):
+    return synthetic.bf16_bits_from_f64(np.asarray(v, dtype=np.float64))
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- unpacking
+
+
+def test_unpack_hand_worked_words():
+    for case in _load("unpack_words.json")["cases"]:
+        word = np.array([[int(case["word"], 16)]], dtype=np.uint32)
+        q = oracle.unpack_codes(word, 8)
+        assert q.tolist() == [case["codes"]], case
+
+
+def test_unpack_multiword_row_order():
+    # two rows, two words each: code k of row n is at word k//8, nibble k%8
+    wq = np.array([[0x76543210, 0xFEDCBA98], [0x01234567, 0x89ABCDEF]], dtype=np.uint32)
+    q = oracle.unpack_codes(wq, 16)
+    assert q[0].tolist() == list(range(16))
+    assert q[1].tolist() == [7, 6, 5, 4, 3, 2, 1, 0, 15, 14, 13, 12, 11, 10, 9, 8]
+
+
+# ------------------------------------------------------------ dequantization
+
+
+def test_dequant_hand_worked():
+    for case in _load("dequant_cases.json")["cases"]:
+        s = np.full((1, 1), int(case["scale_bits"], 16), dtype=np.uint16)
+        b = np.full((1, 1), int(case["bias_bits"], 16), dtype=np.uint16)
+        q = np.full((1, 64), case["q"], dtype=np.uint8)
+        wq = synthetic.pack_codes_low_nibble_first(q)
+        w = oracle.dequantize(wq, s, b, 64)
+        assert np.all(w == case["w"]), case
+
+
+def test_bf16_decode_known_patterns():
+    bits = np.array([0x3F80, 0xBF80, 0x4000, 0x0000, 0x8000, 0x3F00, 0x7F7F], dtype=np.uint16)
+    v = oracle.bf16_to_f64(bits)
+    assert v[:6].tolist() == [1.0, -1.0, 2.0, 0.0, -0.0, 0.5]
+    assert math.copysign(1.0, v[4]) == -1.0
+    assert v[6] == float.fromhex("0x1.fe00000000000p+127")
+
+
+# ------------------------------------------------------------- closed forms
+
+
+def _random_weight(rng, N, K, scale_sign_mix=True):
+    q = rng.integers(0, 16, (N, K), dtype=np.uint8)
+    s = np.abs(rng.normal(0, 0.02, (N, K // 64)))
+    if scale_sign_mix:
+        s *= rng.choice([-1.0, 1.0, 0.0], size=s.shape, p=[0.3, 0.6, 0.1])
+    sb = _bf16(s)
+    bb = _bf16(rng.normal(0, 0.2, (N, K // 64)))
+    return q, synthetic.pack_codes_low_nibble_first(q), sb, bb
+
+
+@pytest.mark.parametrize("k", [0, 1, 7, 8, 31, 32, 63, 64, 65, 127, 128, 255])
+def test_one_hot_activation_picks_one_weight(k):
+    """x = e_k gives y[n] = s[n][k//64] * q[n][k] + b[n][k//64]; k=32 separates
+    64-wide groups from 32-wide ones, k=63/64 sits on a group boundary."""
+    rng = np.random.default_rng(100 + k)
+    N, K = 16, 256
+    q, wq, sb, bb = _random_weight(rng, N, K)
+    x = np.zeros((1, K), dtype=np.uint16)
+    x[0, k] = 0x3F80  # 1.0
+    y = oracle.matmul_rows(wq, sb, bb, x)[0]
+    s = oracle.bf16_to_f64(sb)[:, k // 64]
+    b = oracle.bf16_to_f64(bb)[:, k // 64]
+    assert np.array_equal(y, s * q[:, k].astype(np.float64) + b)
+
+
+def _group_code_sums_bytewise(wq, K):
+    """Sum of codes per (row, group) computed bytewise from the words (an
+    independent path from the oracle's shift-per-code unpack)."""
+    words = wq.astype(np.uint64)
+    lo = words & 0x0F0F0F0F
+    hi = (words >> 4) & 0x0F0F0F0F
+    per_word = np.zeros(words.shape, dtype=np.int64)
+    for byte in range(4):
+        per_word += ((lo >> (8 * byte)) & 0xFF).astype(np.int64)
+        per_word += ((hi >> (8 * byte)) & 0xFF).astype(np.int64)
+    return per_word.reshape(wq.shape[0], K // 64, 8).sum(axis=2)
+
+
+def test_all_ones_activation_closed_form():
+    rng = np.random.default_rng(7)
+    N, K = 24, 512
+    _, wq, sb, bb = _random_weight(rng, N, K)
+    x = np.full((1, K), 0x3F80, dtype=np.uint16)
+    y = oracle.matmul_rows(wq, sb, bb, x)[0]
+    qsum = _group_code_sums_bytewise(wq, K).astype(np.float64)
+    s = oracle.bf16_to_f64(sb)
+    b = oracle.bf16_to_f64(bb)
+    terms = s * qsum + 64.0 * b  # each exact: s*qsum has <= 8+10 bits
+    expect = np.array([math.fsum(r) for r in terms])
+    A = oracle.error_weight(wq, sb, bb, x)[0]
+    assert np.all(np.abs(y - expect) <= (K + 2) * 2.0 ** -52 * A)
+
+
+def test_integer_weights_reduce_to_integer_matmul():
+    """With s=1, b=0 the weights are the codes; with small-integer x the
+    product is an exact integer matrix product (int64 matmul)."""
+    rng = np.random.default_rng(11)
+    N, K, M = 20, 192, 3
+    q, wq, _, _ = _random_weight(rng, N, K)
+    sb = np.full((N, K // 64), 0x3F80, dtype=np.uint16)
+    bb = np.zeros((N, K // 64), dtype=np.uint16)
+    xi = rng.integers(-8, 9, (M, K))
+    x = _bf16(xi.astype(np.float64))
+    y = oracle.matmul_rows(wq, sb, bb, x)
+    assert np.array_equal(y, (xi @ q.astype(np.int64).T).astype(np.float64))
+
+
+def test_rectangular_shapes_and_orientation():
+    """y is [M][N]; row m only depends on x[m] and column n only on weight row n."""
+    rng = np.random.default_rng(12)
+    N, K, M = 8, 128, 3
+    _, wq, sb, bb = _random_weight(rng, N, K)
+    x = _bf16(rng.normal(0, 1, (M, K)))
+    y = oracle.matmul_rows(wq, sb, bb, x)
+    assert y.shape == (M, N)
+    y_row1 = oracle.matmul_rows(wq, sb, bb, x[1:2])
+    y_col5 = oracle.matmul_rows(wq[5:6], sb[5:6], bb[5:6], x)
+    assert np.array_equal(y[1:2], y_row1)
+    assert np.array_equal(y[:, 5:6], y_col5)
+
+
+# ------------------------------------------------------- exact brute force
+
+
+@pytest.mark.parametrize("seed,N,K,M", [(1, 4, 64, 1), (2, 8, 128, 3), (3, 3, 256, 2)])
+def test_fsum_equals_fraction_bruteforce(seed, N, K, M):
+    rng = np.random.default_rng(seed)
+    _, wq, sb, bb = _random_weight(rng, N, K)
+    x = _bf16(rng.normal(0, 1, (M, K)) * rng.choice([1e-3, 1.0, 30.0], (M, K)))
+    exact = oracle.matmul_rows_fraction(wq, sb, bb, x)
+    fs = oracle.matmul_rows_exact(wq, sb, bb, x)
+    for i in range(M):
+        for n in range(N):
+            assert fs[i, n] == float(exact[i][n])  # fsum is correctly rounded
+
+
+def test_fraction_bruteforce_float32_activations():
+    rng = np.random.default_rng(4)
+    N, K, M = 3, 128, 2
+    _, wq, sb, bb = _random_weight(rng, N, K)
+    x = rng.normal(0, 1, (M, K)).astype(np.float32)
+    exact = oracle.matmul_rows_fraction(wq, sb, bb, x)
+    fs = oracle.matmul_rows_exact(wq, sb, bb, x)
+    for i in range(M):
+        for n in range(N):
+            assert fs[i, n] == float(exact[i][n])
+
+
+@pytest.mark.parametrize("cfg", [0, 2])
+def test_dgemm_within_float64_bound_of_exact(cfg):
+    data = synthetic.config(cfg)
+    w = data["w"] if cfg == 0 else data["wq"]
+    x = data["x"][:4]
+    cols = np.arange(0, w.N, max(1, w.N // 48))
+    y = oracle.matmul_rows(w.wq, w.scales, w.biases, x, cols=cols)
+    ye = oracle.matmul_rows_exact(w.wq, w.scales, w.biases, x, cols=cols)
+    A = oracle.error_weight(w.wq, w.scales, w.biases, x, cols=cols)
+    assert np.all(np.abs(y - ye) <= (w.K + 2) * 2.0 ** -52 * A)
+    # and the exact sums are genuinely non-trivial
+    assert np.all(np.abs(ye) > 0)
+
+
+def test_error_weight_dominates_and_is_tight_for_positive_data():
+    rng = np.random.default_rng(5)
+    N, K = 6, 128
+    q = rng.integers(0, 16, (N, K), dtype=np.uint8)
+    wq = synthetic.pack_codes_low_nibble_first(q)
+    sb = _bf16(np.abs(rng.normal(0, 0.1, (N, 2))))
+    bb = _bf16(np.abs(rng.normal(0, 0.1, (N, 2))))
+    x = _bf16(np.abs(rng.normal(0, 1, (2, K))))
+    y = oracle.matmul_rows(wq, sb, bb, x)
+    A = oracle.error_weight(wq, sb, bb, x)
+    assert np.allclose(y, A, rtol=1e-14, atol=0)  # all terms positive: A == y
+    x2 = _bf16(rng.normal(0, 1, (2, K)))
+    assert np.all(np.abs(oracle.matmul_rows(wq, sb, bb, x2)) <= oracle.error_weight(wq, sb, bb, x2))
+
+
+# ------------------------------------------------------------------ SwiGLU
+
+
+def test_silu_identities():
+    a = np.array([0.0, 0.5, -0.5, 3.0, -3.0, 12.5, -12.5])
+    s = oracle.silu(a)
+    assert s[0] == 0.0
+    # silu(-a) = silu(a) - a
+    assert np.allclose(oracle.silu(-a), s - a, rtol=0, atol=1e-15)
+    # silu(a) -> a for large a, -> -0 for very negative a
+    assert oracle.silu(np.array([40.0]))[0] == 40.0
+    big_neg = oracle.silu(np.array([-800.0]))[0]
+    assert big_neg == 0.0 and math.copysign(1.0, big_neg) == -1.0
+    # silu(1) = 1 / (1 + 1/e)
+    assert abs(oracle.silu(np.array([1.0]))[0] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-16
+    # closed form at log(3): sigmoid = 3/4
+    assert abs(oracle.silu(np.array([math.log(3.0)]))[0] - 0.75 * math.log(3.0)) < 1e-15
+
+
+def test_swiglu_is_silu_of_first_times_second():
+    a = np.array([1.0, -2.0, 0.0, 4.0])
+    c = np.array([2.0, 3.0, 5.0, -0.5])
+    z = oracle.swiglu(a, c)
+    assert z[2] == 0.0
+    assert abs(z[0] - 2.0 / (1.0 + math.exp(-1.0))) < 1e-15
+    assert abs(z[1] - 3.0 * (-2.0) / (1.0 + math.exp(2.0))) < 1e-15
+    # not symmetric: swapping the operands changes the value
+    assert not np.allclose(oracle.swiglu(c, a), z)
+
+
+# ------------------------------------------------------- planted mistakes
+
+
+def _plant(kind, wq, sb, bb, K):
+    """Oracle variants with one planted mistake each (the pages' own control
+    is the other group size; the rest are the natural slips)."""
+    q = oracle.unpack_codes(wq, K).astype(np.float64)
+    s = oracle.bf16_to_f64(sb)
+    b = oracle.bf16_to_f64(bb)
+    G = K // 64
+    g = np.arange(K) // 64
+    if kind == "group32":
+        g = np.minimum(np.arange(K) // 32, G - 1)
+        return s[:, g] * q + b[:, g]
+    if kind == "high_nibble_first":
+        k = np.arange(K)
+        words = np.asarray(wq, dtype=np.uint32)[:, k // 8]
+        qh = ((words >> (4 * (7 - k % 8)).astype(np.uint32)) & 0xF).astype(np.float64)
+        return s[:, g] * qh + b[:, g]
+    if kind == "bias_dropped":
+        return s[:, g] * q
+    if kind == "scale_bias_swapped":
+        return b[:, g] * q + s[:, g]
+    if kind == "w_rounded_bf16":
+        return oracle.bf16_to_f64(_bf16(s[:, g] * q + b[:, g]))
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["group32", "high_nibble_first", "bias_dropped", "scale_bias_swapped", "w_rounded_bf16"])
+@pytest.mark.parametrize("cfg", [0, 2])
+def test_planted_mistakes_fail_the_tolerance(kind, cfg):
+    data = synthetic.config(cfg)
+    w = data["w"] if cfg == 0 else data["wq"]
+    x = data["x"][:4]
+    cols = np.arange(0, w.N, 4)
+    wq, sb, bb = w.wq[cols], w.scales[cols], w.biases[cols]
+    y = oracle.matmul_rows(wq, sb, bb, x)
+    A = oracle.error_weight(wq, sb, bb, x)
+    W_bad = _plant(kind, wq, sb, bb, w.K)
+    y_bad = oracle.activations_f64(x) @ W_bad.T
+    ratio = np.max(np.abs(y_bad - y) / tol(A, w.K))
+    assert ratio > 1.0, (kind, cfg, ratio)
