@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the q4g64 hot path on one MI355X.
+
+One step is one decode FFN step at one activation row, with the workload's
+sizes: qmv_w13_swiglu over w1 and w3 (8192 x 2048 each, bf16 x, float32
+SwiGLU output), then qmv_rows over w2 (2048 x 8192) on that float32 output.
+Weights rotate over a pool of packed copies larger than the 256 MB MALL plus
+the L2s, so every step streams its 28 MB of weights from HBM, as a real
+decode step streams the model's weights once per token.
+
+The timed region replays a HIP graph of the K steps (host launch cost would
+otherwise dominate a 5 us step), bracketed by torch.cuda.synchronize(). Per
+kernel durations come from HIP events recorded on the library's stream
+around every launch of an eager pass over the same steps (the queue is
+pre-filled by a busy kernel so no host gap falls between an event and its
+kernel). The prompt GEMM is reported beside it (TFLOP/s against the bf16
+matrix-core peak) on the 8192-row w1/w3 + SwiGLU window.
+
+The float64 oracle is timed on the host on a bounded sample of the same
+decode step (cpu_baseline).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+METRIC = "GB/s + rows/s for qmv decode; TFLOP/s for pgemm prefill (% of roofline)"
+
+
+def qbytes(N, K):
+    return N * K * 9 // 16
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def to_dev(a, dt, dev):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(dev)
+
+
+def pack_dev(w, dev):
+    import bit_weight_only_q4g64_amd as q4
+
+    return q4.pack(to_dev(w.wq, np.int32, dev), to_dev(w.scales, np.int16, dev), to_dev(w.biases, np.int16, dev))
+
+
+def cpu_baseline(d, budget_s=12.0):
+    """The float64 oracle on the same decode step, repeated while under budget."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count() or 1
+    w1, w3, w2, x = d["w1"], d["w3"], d["w2"], d["x"]
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        a = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, x)
+        c = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, x)
+        z = oracle.swiglu(a, c)
+        oracle.matmul_rows(w2.wq, w2.scales, w2.biases, z)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 5:
+            break
+    step = float(np.median(times))
+    nbytes = decode_step_bytes(d)
+    return {
+        "value": nbytes / step / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(times)} full decode FFN steps (w1/w3 8192x2048 + SwiGLU, w2 2048x8192, 1 row) in numpy float64; "
+        f"median {step * 1e3:.1f} ms per step",
+    }
+
+
+def decode_step_bytes(d):
+    w1, w2 = d["w1"], d["w2"]
+    b13 = 2 * qbytes(w1.N, w1.K) + w1.K * 2 + w1.N * 4
+    b2 = qbytes(w2.N, w2.K) + w2.K * 4 + w2.N * 4
+    return b13 + b2
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--pool-mb", type=int, default=1200, help="size of the rotating weight pool (cold HBM reads)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pgemm", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (sharding is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_weight_only_q4g64_amd as q4
+    import synthetic
+
+    q4.lib()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log("generating the decode FFN workload")
+    d = synthetic.config(1)
+    w1, w3, w2 = d["w1"], d["w3"], d["w2"]
+    copy_bytes = q4.packed_bytes(w1.N, w1.K) * 2 + q4.packed_bytes(w2.N, w2.K)
+    ncopies = max(2, -(-args.pool_mb * (1 << 20) // copy_bytes))
+    base = [pack_dev(w1, dev), pack_dev(w3, dev), pack_dev(w2, dev)]
+    pool = [base] + [[t.clone() for t in base] for _ in range(ncopies - 1)]
+    torch.cuda.synchronize()
+    log(f"pool: {ncopies} copies of {copy_bytes / 1e6:.1f} MB = {ncopies * copy_bytes / 2**30:.2f} GiB")
+    x = to_dev(d["x"], np.int16, dev).view(torch.bfloat16)
+    z = torch.empty((1, w1.N), dtype=torch.float32, device=dev)
+    y = torch.empty((1, w2.N), dtype=torch.float32, device=dev)
+
+    def step(i, ev=None):
+        p1, p3, p2 = pool[i % ncopies]
+        if ev is not None:
+            ev[0].record()
+        q4.qmv_w13_swiglu(p1, p3, w1.N, w1.K, x, y=z)
+        if ev is not None:
+            ev[1].record()
+        q4.qmv_rows(p2, w2.N, w2.K, z, y=y)
+        if ev is not None:
+            ev[2].record()
+
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    # graph of K steps (each step on the next pool copy)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(K):
+                step(W + i)
+    torch.cuda.synchronize()
+    g.replay()  # untimed replay: first-launch costs
+    torch.cuda.synchronize()
+
+    log(f"timed region: {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    # eager pass with events around every kernel, queue pre-filled by a busy kernel
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * 0.00004 * K))  # ~40 us of GPU time per step to enqueue behind
+    for i in range(K):
+        step(W + i, evs[i])
+    torch.cuda.synchronize()
+    t13 = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3  # us
+    t2 = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+
+    b13 = 2 * qbytes(w1.N, w1.K) + w1.K * 2 + w1.N * 4
+    b2 = qbytes(w2.N, w2.K) + w2.K * 4 + w2.N * 4
+    step_bytes = b13 + b2
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    ach13 = b13 / (t13.mean() * 1e-6) / 1e9
+    ach2 = b2 / (t2.mean() * 1e-6) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode FFN step: qmv_w13_swiglu over w1/w3 8192x2048 q4g64 + SwiGLU, then qmv_rows over w2 "
+            "2048x8192 q4g64 on the float32 output; 1 bf16 activation row; seed 1",
+            "rows": 1,
+            "step_bytes": step_bytes,
+            "weight_pool_gib": round(ncopies * copy_bytes / 2**30, 3),
+            "timing": "HIP graph of K steps, wall clock between synchronizes",
+        },
+        "rows_per_s": round(1.0 / (ms_per_step * 1e-3), 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "qmv_w13_swiglu (qmv_kernel<0,2>)",
+            "achieved": round(ach13, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(ach13 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": b13,
+            "avg_launch_us": round(float(t13.mean()), 3),
+        },
+        "kernels": {
+            "qmv_w13_swiglu": {"avg_us": round(float(t13.mean()), 3), "p10_us": round(float(np.percentile(t13, 10)), 3),
+                               "p90_us": round(float(np.percentile(t13, 90)), 3), "GB/s": round(ach13, 1)},
+            "qmv_rows_w2_f32x": {"avg_us": round(float(t2.mean()), 3), "p10_us": round(float(np.percentile(t2, 10)), 3),
+                                 "p90_us": round(float(np.percentile(t2, 90)), 3), "GB/s": round(ach2, 1),
+                                 "frac": round(ach2 / HBM_PEAK_GBS, 4)},
+        },
+    }
+    del g, pool
+    torch.cuda.empty_cache()
+
+    if not args.no_pgemm:
+        result["pgemm"] = bench_pgemm(dev)
+
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(d)
+    print(json.dumps(result), flush=True)
+
+
+def bench_pgemm(dev, reps=10):
+    """w1/w3 + SwiGLU (bf16 out) over the 8192-row prompt as one window."""
+    import torch
+
+    import bit_weight_only_q4g64_amd as q4
+    import synthetic
+
+    log("prompt GEMM: 8192 x (2 x 8192) x 2048 with SwiGLU")
+    rng = np.random.default_rng(4)
+    w1 = synthetic.draw_qweight(rng, "w1", 8192, 2048)
+    w3 = synthetic.draw_qweight(rng, "w3", 8192, 2048)
+    x = to_dev(synthetic.draw_bf16_rows(rng, 8192, 2048), np.int16, dev).view(torch.bfloat16)
+    p1, p3 = pack_dev(w1, dev), pack_dev(w3, dev)
+    z = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        q4.qmm_window(p1, p3, 8192, 2048, x, y=z)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        e[0].record()
+        q4.qmm_window(p1, p3, 8192, 2048, x, y=z)
+        e[1].record()
+    torch.cuda.synchronize()
+    t = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3  # s
+    flops = 2.0 * 8192 * (2 * 8192) * 2048
+    tf = flops / t.mean() / 1e12
+    return {
+        "workload": "qmm_window w1/w3 8192x2048 + SwiGLU, M=8192 prompt rows, bf16 out (seed 4 shapes)",
+        "avg_ms": round(float(t.mean() * 1e3), 4),
+        "TFLOP/s": round(tf, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / BF16_PEAK_TFLOPS, 4)},
+    }
+
+
+if __name__ == "__main__":
+    main()

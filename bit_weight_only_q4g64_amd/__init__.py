@@ -1,0 +1,201 @@
+"""q4g64 on MI355X: Python binding of the C-ABI library ``libq4g64.so``.
+
+Argument marshalling only. Every step of the computation runs in the HIP
+kernels behind ``include/q4g64.h``; PyTorch provides device memory and the
+stream. If the library is not built, every call raises: there is no fallback.
+
+Tensors: canonical weights are ``wq`` int32/uint32 [N][K/8] (bit patterns),
+``scales``/``biases`` int16/uint16/bfloat16 [N][K/64] (bf16 bit patterns);
+activations are ``torch.bfloat16`` (or ``torch.float32`` for ``qmv_rows``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4g64.so")
+
+Q4_OK, Q4_EINVAL, Q4_EALIGN, Q4_EDEVICE, Q4_EUNSUPPORTED = 0, -1, -2, -3, -4
+Q4_BF16, Q4_F32 = 0, 1
+
+_lib = None
+
+_I64 = ctypes.c_int64
+_P = ctypes.c_void_p
+_SIGNATURES = {
+    "q4g64_abi_version": (ctypes.c_int, []),
+    "q4g64_packed_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "pack_q4g64": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P]),
+    "unpack_q4g64": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
+    "qmv_rows": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, _I64, ctypes.c_int, _P, _I64, _P]),
+    "qmv_w13_swiglu": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
+    "qmm_window": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P]),
+    "qmm_cut": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _I64, _P]),
+    "q4_last_error": (ctypes.c_char_p, []),
+}
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m bit_weight_only_q4g64_amd.build` "
+                "(the q4g64 ops have no non-HIP implementation)"
+            )
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != Q4_OK:
+        raise Q4Error(fn, status, lib().q4_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _rowmajor(t: torch.Tensor, name: str) -> int:
+    """Row stride (elements) of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    return t.stride(0)
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return int(lib().q4g64_packed_bytes(N, K))
+
+
+def pack(wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor) -> torch.Tensor:
+    """Canonical MLX q4g64 (device tensors) -> packed device layout (uint8 tensor)."""
+    for t, name in ((wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _dev(t, name)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    N, K = wq.shape[0], wq.shape[1] * 8
+    if wq.element_size() != 4 or scales.element_size() != 2 or biases.element_size() != 2:
+        raise ValueError("wq holds 32-bit words, scales/biases 16-bit bf16 patterns")
+    if tuple(scales.shape) != (N, K // 64) or tuple(biases.shape) != (N, K // 64):
+        raise ValueError("scales and biases must be [N][K/64]")
+    nbytes = packed_bytes(N, K)
+    if nbytes == 0:
+        raise Q4Error("pack_q4g64", Q4_EINVAL, f"invalid shape N={N} K={K}")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=wq.device)
+    _check("pack_q4g64", lib().pack_q4g64(wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), N, K, out.data_ptr(), _stream()))
+    return out
+
+
+def unpack(packed: torch.Tensor, N: int, K: int):
+    """Packed layout -> canonical (wq int32 [N][K/8], scales int16, biases int16 [N][K/64])."""
+    _dev(packed, "packed")
+    wq = torch.empty((N, K // 8), dtype=torch.int32, device=packed.device)
+    sc = torch.empty((N, K // 64), dtype=torch.int16, device=packed.device)
+    bi = torch.empty((N, K // 64), dtype=torch.int16, device=packed.device)
+    _check("unpack_q4g64", lib().unpack_q4g64(packed.data_ptr(), N, K, wq.data_ptr(), sc.data_ptr(), bi.data_ptr(), _stream()))
+    return wq, sc, bi
+
+
+def qmv_rows(packed: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[r] = W x[r] for the R = x.shape[0] (1..16) rows of x (bf16 or float32)."""
+    _dev(packed, "packed")
+    _dev(x, "x")
+    ldx = _rowmajor(x, "x")
+    if x.dtype == torch.bfloat16:
+        xd = Q4_BF16
+    elif x.dtype == torch.float32:
+        xd = Q4_F32
+    else:
+        raise ValueError("x must be bfloat16 or float32")
+    R = x.shape[0]
+    if y is None:
+        y = torch.empty((R, N), dtype=torch.float32, device=x.device)
+    if y.dtype != torch.float32 or y.shape[0] < R:
+        raise ValueError("y must be float32 with at least R rows")
+    _check("qmv_rows", lib().qmv_rows(packed.data_ptr(), N, K, x.data_ptr(), xd, ldx, R, y.data_ptr(), _rowmajor(y, "y"), _stream()))
+    return y
+
+
+def qmv_w13_swiglu(p1: torch.Tensor, p3: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[r] = silu(W1 x[r]) * (W3 x[r]) for the 1..16 bf16 rows of x."""
+    _dev(p1, "packed_w1")
+    _dev(p3, "packed_w3")
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    R = x.shape[0]
+    if y is None:
+        y = torch.empty((R, N), dtype=torch.float32, device=x.device)
+    _check(
+        "qmv_w13_swiglu",
+        lib().qmv_w13_swiglu(p1.data_ptr(), p3.data_ptr(), N, K, x.data_ptr(), _rowmajor(x, "x"), R, y.data_ptr(), _rowmajor(y, "y"), _stream()),
+    )
+    return y
+
+
+def _out_dtype(dtype) -> int:
+    if dtype == torch.float32:
+        return Q4_F32
+    if dtype == torch.bfloat16:
+        return Q4_BF16
+    raise ValueError("output dtype must be float32 or bfloat16")
+
+
+def qmm_window(pa: torch.Tensor, pb: torch.Tensor | None, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None,
+               out_dtype=torch.float32) -> torch.Tensor:
+    """Prompt window: y = A x (pb None) or silu(A x) * (B x), for all M rows of x."""
+    _dev(pa, "packed_a")
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _check(
+        "qmm_window",
+        lib().qmm_window(pa.data_ptr(), None if pb is None else pb.data_ptr(), N, K, x.data_ptr(), _rowmajor(x, "x"), M,
+                         y.data_ptr(), _out_dtype(y.dtype), _rowmajor(y, "y"), _stream()),
+    )
+    return y
+
+
+def qmm_cut(pa: torch.Tensor, pb: torch.Tensor | None, N: int, K: int, x: torch.Tensor, windows, y: torch.Tensor | None = None,
+            out_dtype=torch.float32) -> torch.Tensor:
+    """Run the prompt x through consecutive windows of the given row counts."""
+    _dev(pa, "packed_a")
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    windows = [int(w) for w in windows]
+    if sum(windows) != x.shape[0]:
+        raise ValueError("window row counts must add up to the prompt's rows")
+    if y is None:
+        y = torch.empty((x.shape[0], N), dtype=out_dtype, device=x.device)
+    arr = (ctypes.c_int64 * len(windows))(*windows)
+    _check(
+        "qmm_cut",
+        lib().qmm_cut(pa.data_ptr(), None if pb is None else pb.data_ptr(), N, K, x.data_ptr(), _rowmajor(x, "x"), arr,
+                      len(windows), y.data_ptr(), _out_dtype(y.dtype), _rowmajor(y, "y"), _stream()),
+    )
+    return y

@@ -1,0 +1,227 @@
+// Host side of the q4g64 C ABI: argument validation, launch configuration and
+// error reporting. Every entry point validates on the host first and enqueues
+// nothing when an argument is rejected.
+#include "../../include/q4g64.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "common.h"
+#include "pack.h"
+#include "pgemm.h"
+#include "qmv.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int kPgemmRT = 4;  // row tiles (16 rows each) per pgemm workgroup
+constexpr size_t kMaxLds = 64 * 1024;
+
+int check_nk(const char* fn, int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N % 64 != 0 || K % 64 != 0)
+    return fail(Q4_EINVAL, "%s: N=%lld and K=%lld must be positive multiples of 64", fn, (long long)N, (long long)K);
+  if (N > kMaxDim || K > kMaxDim || N * K > kMaxElems)
+    return fail(Q4_EINVAL, "%s: N=%lld x K=%lld is too large", fn, (long long)N, (long long)K);
+  return Q4_OK;
+}
+
+int check_ptr(const char* fn, const char* name, const void* p, uintptr_t align) {
+  if (p == nullptr) return fail(Q4_EALIGN, "%s: %s is NULL", fn, name);
+  if (!aligned(p, align)) return fail(Q4_EALIGN, "%s: %s is not %u-byte aligned", fn, name, (unsigned)align);
+  return Q4_OK;
+}
+
+int launched(const char* fn) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(Q4_EDEVICE, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return Q4_OK;
+}
+
+unsigned grid_for(int64_t total, int block) {
+  int64_t g = (total + block - 1) / block;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+int check_x(const char* fn, const void* x, int x_dtype, int64_t ldx, int64_t K) {
+  if (x_dtype != Q4_BF16 && x_dtype != Q4_F32) return fail(Q4_EINVAL, "%s: x_dtype %d is not Q4_BF16 or Q4_F32", fn, x_dtype);
+  if (int rc = check_ptr(fn, "x", x, 16)) return rc;
+  if (ldx < K) return fail(Q4_EINVAL, "%s: ldx=%lld < K=%lld", fn, (long long)ldx, (long long)K);
+  const int64_t es = x_dtype == Q4_BF16 ? 2 : 4;
+  if ((ldx * es) % 16 != 0) return fail(Q4_EALIGN, "%s: ldx=%lld elements does not keep rows 16-byte aligned", fn, (long long)ldx);
+  return Q4_OK;
+}
+
+int qmm_window_impl(const char* fn, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x,
+                    int64_t ldx, int64_t M, void* y, int y_dtype, int64_t ldy, hipStream_t s) {
+  using namespace q4;
+  const bool swiglu = packed_b != nullptr;
+  const bool obf16 = y_dtype == Q4_BF16;
+  const int cols_per_wg = kPgemmWaves * (swiglu ? 32 : 64);
+  dim3 grid((unsigned)((N + cols_per_wg - 1) / cols_per_wg), (unsigned)((M + kPgemmRT * 16 - 1) / (kPgemmRT * 16)));
+  dim3 block(kPgemmWaves * 64);
+  const uint8_t* a = (const uint8_t*)packed_a;
+  const uint8_t* b = (const uint8_t*)packed_b;
+  if (swiglu) {
+    if (obf16)
+      hipLaunchKernelGGL((pgemm_kernel<true, true, kPgemmRT>), grid, block, 0, s, a, b, (int)N, (int)K, x, ldx, (int)M, y, ldy);
+    else
+      hipLaunchKernelGGL((pgemm_kernel<true, false, kPgemmRT>), grid, block, 0, s, a, b, (int)N, (int)K, x, ldx, (int)M, y, ldy);
+  } else {
+    if (obf16)
+      hipLaunchKernelGGL((pgemm_kernel<false, true, kPgemmRT>), grid, block, 0, s, a, a, (int)N, (int)K, x, ldx, (int)M, y, ldy);
+    else
+      hipLaunchKernelGGL((pgemm_kernel<false, false, kPgemmRT>), grid, block, 0, s, a, a, (int)N, (int)K, x, ldx, (int)M, y, ldy);
+  }
+  return launched(fn);
+}
+
+int check_window_args(const char* fn, const void* packed_a, const void* packed_b, int64_t N, int64_t K,
+                      const uint16_t* x, int64_t ldx, const void* y, int y_dtype, int64_t ldy) {
+  if (int rc = check_nk(fn, N, K)) return rc;
+  if (int rc = check_ptr(fn, "packed_a", packed_a, 16)) return rc;
+  if (packed_b != nullptr && !aligned(packed_b, 16)) return fail(Q4_EALIGN, "%s: packed_b is not 16-byte aligned", fn);
+  if (int rc = check_x(fn, x, Q4_BF16, ldx, K)) return rc;
+  if (y_dtype != Q4_BF16 && y_dtype != Q4_F32) return fail(Q4_EINVAL, "%s: y_dtype %d is not Q4_BF16 or Q4_F32", fn, y_dtype);
+  if (int rc = check_ptr(fn, "y", y, y_dtype == Q4_F32 ? 4 : 2)) return rc;
+  if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4g64_abi_version(void) { return 1; }
+
+const char* q4_last_error(void) { return g_err; }
+
+size_t q4g64_packed_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N % 64 != 0 || K % 64 != 0 || N > kMaxDim || K > kMaxDim || N * K > kMaxElems) return 0;
+  return (size_t)q4::packed_bytes(N, K);
+}
+
+int pack_q4g64(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, int64_t N, int64_t K, void* packed,
+               void* stream) {
+  const char* fn = "pack_q4g64";
+  if (int rc = check_nk(fn, N, K)) return rc;
+  if (int rc = check_ptr(fn, "wq", wq, 16)) return rc;
+  if (int rc = check_ptr(fn, "scales", scales, 2)) return rc;
+  if (int rc = check_ptr(fn, "biases", biases, 2)) return rc;
+  if (int rc = check_ptr(fn, "packed", packed, 16)) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t words = q4::codes_bytes(N, K) / 4;
+  const int64_t sb_entries = (N / q4::kTileN) * q4::n_pairs(K) * q4::kTileN;
+  uint8_t* out = (uint8_t*)packed;
+  hipLaunchKernelGGL(q4::pack_codes_kernel, dim3(grid_for(words, 256)), dim3(256), 0, s, wq, N, K, (uint32_t*)out);
+  if (int rc = launched(fn)) return rc;
+  hipLaunchKernelGGL(q4::pack_sb_kernel, dim3(grid_for(sb_entries, 256)), dim3(256), 0, s, scales, biases, N, K,
+                     (q4::u32x2*)(out + q4::codes_bytes(N, K)));
+  return launched(fn);
+}
+
+int unpack_q4g64(const void* packed, int64_t N, int64_t K, uint32_t* wq, uint16_t* scales, uint16_t* biases,
+                 void* stream) {
+  const char* fn = "unpack_q4g64";
+  if (int rc = check_nk(fn, N, K)) return rc;
+  if (int rc = check_ptr(fn, "packed", packed, 16)) return rc;
+  if (int rc = check_ptr(fn, "wq", wq, 16)) return rc;
+  if (int rc = check_ptr(fn, "scales", scales, 2)) return rc;
+  if (int rc = check_ptr(fn, "biases", biases, 2)) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const uint8_t* in = (const uint8_t*)packed;
+  hipLaunchKernelGGL(q4::unpack_codes_kernel, dim3(grid_for(N * (K / 8), 256)), dim3(256), 0, s, (const uint32_t*)in, N, K, wq);
+  if (int rc = launched(fn)) return rc;
+  hipLaunchKernelGGL(q4::unpack_sb_kernel, dim3(grid_for(N * (K / 64), 256)), dim3(256), 0, s,
+                     (const q4::u32x2*)(in + q4::codes_bytes(N, K)), N, K, scales, biases);
+  return launched(fn);
+}
+
+int qmv_rows(const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R, float* y,
+             int64_t ldy, void* stream) {
+  const char* fn = "qmv_rows";
+  if (int rc = check_nk(fn, N, K)) return rc;
+  if (R < 1 || R > 16) return fail(Q4_EINVAL, "%s: R=%d is outside 1..16", fn, R);
+  if (int rc = check_ptr(fn, "packed", packed, 16)) return rc;
+  if (int rc = check_x(fn, x, x_dtype, ldx, K)) return rc;
+  if (int rc = check_ptr(fn, "y", y, 4)) return rc;
+  if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  const int nseg = q4::qmv_segments(K);
+  const size_t lds = (size_t)nseg * 1024;
+  if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
+  const int maxw = x_dtype == Q4_BF16 ? q4::QmvLimits<0>::kMaxWaves : q4::QmvLimits<1>::kMaxWaves;
+  const int nwaves = nseg < maxw ? nseg : maxw;
+  hipStream_t s = (hipStream_t)stream;
+  const uint8_t* pk = (const uint8_t*)packed;
+  if (x_dtype == Q4_BF16)
+    hipLaunchKernelGGL((q4::qmv_kernel<0, 1>), dim3((unsigned)(N / 16)), dim3(nwaves * 64), lds, s, pk, pk, (int)N, (int)K, x,
+                       ldx, R, y, ldy);
+  else
+    hipLaunchKernelGGL((q4::qmv_kernel<1, 1>), dim3((unsigned)(N / 16)), dim3(nwaves * 64), lds, s, pk, pk, (int)N, (int)K, x,
+                       ldx, R, y, ldy);
+  return launched(fn);
+}
+
+int qmv_w13_swiglu(const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                   int R, float* y, int64_t ldy, void* stream) {
+  const char* fn = "qmv_w13_swiglu";
+  if (int rc = check_nk(fn, N, K)) return rc;
+  if (R < 1 || R > 16) return fail(Q4_EINVAL, "%s: R=%d is outside 1..16", fn, R);
+  if (int rc = check_ptr(fn, "packed_w1", packed_w1, 16)) return rc;
+  if (int rc = check_ptr(fn, "packed_w3", packed_w3, 16)) return rc;
+  if (int rc = check_x(fn, x, Q4_BF16, ldx, K)) return rc;
+  if (int rc = check_ptr(fn, "y", y, 4)) return rc;
+  if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  const int nseg = q4::qmv_segments(K);
+  const size_t lds = (size_t)nseg * 2 * 1024;
+  if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the fused decode limit of 8192", fn, (long long)K);
+  const int nwaves = nseg < q4::QmvLimits<0>::kMaxWaves ? nseg : q4::QmvLimits<0>::kMaxWaves;
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL((q4::qmv_kernel<0, 2>), dim3((unsigned)(N / 16)), dim3(nwaves * 64), lds, s,
+                     (const uint8_t*)packed_w1, (const uint8_t*)packed_w3, (int)N, (int)K, (const void*)x, ldx, R, y, ldy);
+  return launched(fn);
+}
+
+int qmm_window(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx, int64_t M,
+               void* y, int y_dtype, int64_t ldy, void* stream) {
+  const char* fn = "qmm_window";
+  if (int rc = check_window_args(fn, packed_a, packed_b, N, K, x, ldx, y, y_dtype, ldy)) return rc;
+  if (M < 1 || M > 65535LL * kPgemmRT * 16) return fail(Q4_EINVAL, "%s: M=%lld is outside 1..%lld", fn, (long long)M, 65535LL * kPgemmRT * 16);
+  return qmm_window_impl(fn, packed_a, packed_b, N, K, x, ldx, M, y, y_dtype, ldy, (hipStream_t)stream);
+}
+
+int qmm_cut(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+            const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, void* stream) {
+  const char* fn = "qmm_cut";
+  if (int rc = check_window_args(fn, packed_a, packed_b, N, K, x, ldx, y, y_dtype, ldy)) return rc;
+  if (window_rows == nullptr || n_windows < 1) return fail(Q4_EINVAL, "%s: need at least one window", fn);
+  for (int w = 0; w < n_windows; ++w)
+    if (window_rows[w] < 1 || window_rows[w] > 65535LL * kPgemmRT * 16)
+      return fail(Q4_EINVAL, "%s: window %d has %lld rows", fn, w, (long long)window_rows[w]);
+  const int64_t es = y_dtype == Q4_F32 ? 4 : 2;
+  int64_t row0 = 0;
+  for (int w = 0; w < n_windows; ++w) {
+    const uint16_t* xw = x + row0 * ldx;
+    void* yw = (uint8_t*)y + row0 * ldy * es;
+    if (int rc = qmm_window_impl(fn, packed_a, packed_b, N, K, xw, ldx, window_rows[w], yw, y_dtype, ldy, (hipStream_t)stream))
+      return rc;
+    row0 += window_rows[w];
+  }
+  return Q4_OK;
+}
+
+}  // extern "C"

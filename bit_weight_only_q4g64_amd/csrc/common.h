@@ -1,0 +1,104 @@
+// Shared device helpers for the q4g64 kernels (gfx950 / CDNA4).
+//
+// Numerics. Every kernel forms only exact products: a 4-bit code q (0..15) is
+// turned into an exact bf16 integer, multiplied by a bf16 activation on the
+// matrix cores (8 x 4 significant bits fit in float32), and each 64-wide group
+// is reduced on the matrix cores into a float32 partial P_g = sum q*x together
+// with the activation sum S_g = sum x. The group's scale and bias enter once
+// per group in float32: acc <- fma(s_g, P_g, fma(b_g, S_g, acc)). This is the
+// affine MLX dequantization w = s*q + b applied after the in-group sum
+// (TensorFold PR #1696, later revision, "What it adds", prompt GEMM item: a
+// chain per 64-wide k block, blocks added in order).
+//
+// Determinism. The result of v_mfma_f32_16x16x32_bf16 in one output slot
+// depends only on that slot's A row, B column and C input, so a row's bits do
+// not depend on which slot it occupies or on the other rows sharing the
+// instruction. The order of operations per output is a function of K only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 64;        // k per quantization group
+constexpr int kTileN = 16;        // output columns per column tile
+constexpr int kPairCodeBytes = 1024;  // codes of one column tile x 128 k (two groups)
+constexpr int kPairSbBytes = 128;     // scale+bias of one column tile x two groups
+
+// Device layout sizes (see include/q4g64.h for the full description).
+__host__ __device__ inline int64_t n_pairs(int64_t K) { return (K / kGroup + 1) / 2; }
+__host__ __device__ inline int64_t codes_bytes(int64_t N, int64_t K) {
+  return (N / kTileN) * n_pairs(K) * kPairCodeBytes;
+}
+__host__ __device__ inline int64_t packed_bytes(int64_t N, int64_t K) {
+  return (N / kTileN) * n_pairs(K) * (kPairCodeBytes + kPairSbBytes);
+}
+
+// Position of code e (k offset e within an 8-code word) in a device word.
+// Codes 0..3 sit at even nibbles, 4..7 at odd nibbles, so masking the word
+// with 0x0F0F0F0F yields codes 0..3 one per byte and (w >> 4) yields 4..7.
+__host__ __device__ constexpr int dev_nibble(int e) { return e < 4 ? 2 * e : 2 * (e - 4) + 1; }
+
+// 8 codes of a device word -> 8 exact bf16 integers in k order.
+// A byte holding a code q (0..15) read as an OCP e4m3 value is q * 2^-9
+// (exponent field 0 or 1), so the scaled conversion by 2^9 gives q exactly.
+__device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  const bf16x2 c01 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false);
+  const bf16x2 c23 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true);
+  const bf16x2 c45 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false);
+  const bf16x2 c67 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true);
+  const auto c0123 = __builtin_shufflevector(c01, c23, 0, 1, 2, 3);
+  const auto c4567 = __builtin_shufflevector(c45, c67, 0, 1, 2, 3);
+  return __builtin_shufflevector(c0123, c4567, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16x8 ones_bf16x8() {
+  const u32x4 one = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  return __builtin_bit_cast(bf16x8, one);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// bf16 bit pattern in the low / high half of a word -> float32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// float32 x = h + m + l exactly, each a bf16 (truncation keeps the top 8
+// significant bits; each remainder is exact in float32).
+__device__ __forceinline__ void split3(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
+  const uint32_t hu = __float_as_uint(x) & 0xFFFF0000u;
+  const float r1 = x - __uint_as_float(hu);
+  const uint32_t mu = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = r1 - __uint_as_float(mu);
+  h = hu >> 16;
+  m = mu >> 16;
+  l = __float_as_uint(r2) >> 16;
+}
+
+// SwiGLU gate in float32: silu(a) = a / (1 + exp(-a)), library expf and an
+// IEEE division (no fast-math, no contraction).
+__device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + expf(-a)); }
+
+}  // namespace q4

@@ -1,0 +1,133 @@
+/*
+ * q4g64 — 4-bit group-64 weight-only quantized matmul for MI355X (gfx950).
+ *
+ * C ABI. Plain pointers and sizes; no HIP, torch or C++ types in signatures.
+ *
+ * The operation (TensorFold PR #1696, "What it adds": the LFM3 projections use
+ * MLX 4-bit group-64 weights read as stored; later revision, "What it adds":
+ * N-row decode matvecs, fused w1 + w3 + SwiGLU and fused attention matvecs,
+ * and the prompt GEMM that dequantizes weight tiles as it loads them):
+ *
+ *     q[n][k] = (wq[n][k/8] >> 4*(k%8)) & 0xF               codes, low nibble first
+ *     w[n][k] = scale[n][k/64] * q[n][k] + bias[n][k/64]    affine dequantization
+ *     y[r][n] = sum_k w[n][k] * x[r][k]                     float32 result
+ *     SwiGLU:  z = silu(w1 x) * (w3 x),  silu(a) = a / (1 + exp(-a))
+ *
+ * Canonical weight input ("MLX q4g64"):
+ *     wq      uint32 [N][K/8]    (row-major, contiguous)
+ *     scales  uint16 [N][K/64]   bf16 bit patterns
+ *     biases  uint16 [N][K/64]   bf16 bit patterns
+ *
+ * Device ("packed") layout, produced by pack_q4g64 and read by every kernel.
+ * With T = N/16 column tiles, G = K/64 groups and P = ceil(G/2) group pairs:
+ *   - codes: T*P blocks of 1024 bytes, block (t, p) at byte (t*P + p)*1024.
+ *     Lane L (0..63) of a wave reads the 16 bytes at L*16: four 32-bit words
+ *     h = 0..3 holding the 8 codes of column n = 16t + L%16 at
+ *     k = 128p + 32h + 8*(L/16) + e, e = 0..7, code e at nibble 2e (e < 4)
+ *     or 2(e-4)+1 (e >= 4). Words past K (odd G) are zero.
+ *   - scale/bias: T*P blocks of 128 bytes after the codes; block (t, p),
+ *     column c = 0..15 at byte c*8: bf16 {scale, bias} of group 2p then of
+ *     group 2p+1 (zero past G).
+ *   Size: T*P*1152 bytes = 0.5625*N*K bytes for even G.
+ *
+ * Summation order. Each 64-wide group is reduced on the matrix cores into
+ * P_g = sum q*x and S_g = sum x (exact products, float32 sums) and folded as
+ * acc = fma(s_g, P_g, fma(b_g, S_g, acc)) in ascending g. Decode calls
+ * (qmv_rows, qmv_w13_swiglu) fold each 256-wide k segment from zero and add
+ * the segments in ascending order; qmm_window folds one chain over all of K.
+ * Each order is a function of K alone: a row's bits never depend on R, on M,
+ * on the window cut, on the row's position or on the other rows.
+ *
+ * Conventions for every call below:
+ *   - All array arguments are DEVICE pointers owned by the caller; the
+ *     library allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Kernels are
+ *     enqueued asynchronously on it; execution errors surface at the caller's
+ *     next synchronization.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is enqueued and a negative status is returned, with a
+ *     message available from q4_last_error() on the calling thread.
+ *   - N and K must be positive multiples of 64. Packed buffers, x and wq must
+ *     be 16-byte aligned; x row strides (ldx, in elements) must keep every row
+ *     16-byte aligned. Outputs must not alias inputs.
+ *   - The caller passes the same (N, K) to pack_q4g64 and to every use.
+ */
+#ifndef Q4G64_H
+#define Q4G64_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4_OK 0
+#define Q4_EINVAL (-1)       /* bad shape, count, stride or dtype */
+#define Q4_EALIGN (-2)       /* null or misaligned pointer / stride */
+#define Q4_EDEVICE (-3)      /* a HIP call or kernel launch failed */
+#define Q4_EUNSUPPORTED (-4) /* valid request outside what this build implements */
+
+#define Q4_BF16 0 /* bf16 bit patterns stored as uint16 */
+#define Q4_F32 1  /* IEEE float32 */
+
+/* ABI version of this header (incremented on incompatible changes). */
+int q4g64_abi_version(void);
+
+/* Bytes of the packed device layout for an N x K matrix; 0 if (N, K) is invalid. */
+size_t q4g64_packed_bytes(int64_t N, int64_t K);
+
+/* Canonical MLX q4g64 (wq, scales, biases on the device) -> packed layout.
+ * An integer permutation of the input bits: bit-exact and invertible.
+ * `packed` must hold q4g64_packed_bytes(N, K) bytes. */
+int pack_q4g64(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, int64_t N, int64_t K,
+               void* packed, void* stream);
+
+/* Inverse of pack_q4g64: packed layout -> canonical wq [N][K/8], scales and biases [N][K/64]. */
+int unpack_q4g64(const void* packed, int64_t N, int64_t K, uint32_t* wq, uint16_t* scales, uint16_t* biases,
+                 void* stream);
+
+/* Decode matvec over R = 1..16 rows (PR #1696, later revision, "What it adds":
+ * N-row matvecs for streams that share a decode step).
+ *   x: R rows of K activations, row stride ldx elements; x_dtype Q4_BF16 or
+ *      Q4_F32 (float32 rows are split into three exact bf16 pieces).
+ *   y: float32 [R][ldy], ldy >= N.
+ * Row r of y is bit-identical to the result of the same call with R = 1 on
+ * that row alone. Limits: K <= 16384 (bf16 x) / 16384 (float32 x). */
+int qmv_rows(const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R, float* y,
+             int64_t ldy, void* stream);
+
+/* Fused decode FFN gate (PR #1696, "What it adds": w1 + w3 + SwiGLU in one
+ * pass): y[r][n] = silu(a) * c with a = (w1 x)[r][n], c = (w3 x)[r][n], each
+ * computed in qmv_rows' order; bit-equal to composing two qmv_rows results
+ * with the same float32 silu. x bf16 [R][ldx], y float32 [R][ldy], R = 1..16,
+ * K <= 8192. */
+int qmv_w13_swiglu(const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
+                   int64_t ldx, int R, float* y, int64_t ldy, void* stream);
+
+/* Prompt-window GEMM (PR #1696, later revision, "What it adds": pgemm).
+ *   x: bf16 [M][ldx], any M >= 1.
+ *   packed_b == NULL: y = A x.  packed_b != NULL: y = silu(A x) * (B x), the
+ *   paired w1/w3 projections with the SwiGLU epilogue (PR #1514, "What
+ *   changes": paired FFN projections keep their rounding boundaries).
+ *   y: [M][ldy], y_dtype Q4_F32 or Q4_BF16 (round to nearest even).
+ * A row's result does not depend on M, on its offset or on the other rows. */
+int qmm_window(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+               int64_t M, void* y, int y_dtype, int64_t ldy, void* stream);
+
+/* Window driver: runs qmm_window over consecutive windows of a prompt.
+ * window_rows is a HOST array of n_windows positive row counts; window w
+ * covers rows [sum of earlier counts, + window_rows[w]) of x and y. The
+ * result is bit-identical for every cut (PR #1696, later revision, "Checks":
+ * windows of 64, 128, 256 and a ragged cut agree bit for bit). */
+int qmm_cut(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+            const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* q4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4G64_H */

@@ -45,13 +45,13 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def activations_f64(x: np.ndarray) -> np.ndarray:
-    """bf16 patterns (uint16) or float32 activations -> float64 (exact)."""
+    """bf16 patterns (uint16), float32 or float64 activations -> float64 (exact)."""
     x = np.asarray(x)
     if x.dtype == np.uint16:
         return bf16_to_f64(x)
-    if x.dtype == np.float32:
+    if x.dtype in (np.float32, np.float64):
         return x.astype(np.float64)
-    raise TypeError("activations are bf16 bit patterns (uint16) or float32")
+    raise TypeError("activations are bf16 bit patterns (uint16), float32 or float64")
 
 
 def unpack_codes(wq: np.ndarray, K: int) -> np.ndarray:

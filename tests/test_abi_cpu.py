@@ -1,0 +1,125 @@
+"""The C-ABI library: it loads, exports every function include/q4g64.h
+declares, and rejects bad arguments on the host with the documented status
+codes before anything reaches a device (no GPU needed: these calls fail
+validation and never enqueue)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_weight_only_q4g64_amd as q4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4g64.h")
+
+FAKE = 0x10000  # aligned non-null address; only passed where validation fails first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return [n for n in names if n not in ("if", "defined")]
+
+
+def test_header_declares_the_boundary():
+    names = set(_declared())
+    for must in ("pack_q4g64", "qmv_rows", "qmv_w13_swiglu", "qmm_window", "qmm_cut", "q4g64_packed_bytes", "q4_last_error"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = q4.lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert set(_declared()) == set(q4._SIGNATURES)
+    assert lib.q4g64_abi_version() == 1
+
+
+def test_packed_bytes():
+    assert q4.packed_bytes(512, 256) == 512 * 256 * 9 // 16
+    assert q4.packed_bytes(8192, 2048) == 9437184
+    assert q4.packed_bytes(64, 192) == 4 * 2 * 1152  # odd group count pads the last pair
+    for bad in ((0, 64), (64, 0), (100, 64), (64, 100), (-64, 64), (1 << 31, 64)):
+        assert q4.packed_bytes(*bad) == 0
+
+
+def _rc(name, *args):
+    lib = q4.lib()
+    rc = getattr(lib, name)(*args)
+    return rc, lib.q4_last_error().decode()
+
+
+@pytest.mark.parametrize("N,K", [(100, 256), (512, 100), (0, 256), (512, -64), (48, 256)])
+def test_bad_shapes_rejected(N, K):
+    rc, msg = _rc("qmv_rows", FAKE, N, K, FAKE, q4.Q4_BF16, 256, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EINVAL and "multiples of 64" in msg
+    rc, _ = _rc("pack_q4g64", FAKE, FAKE, FAKE, N, K, FAKE, None)
+    assert rc == q4.Q4_EINVAL
+    rc, _ = _rc("qmm_window", FAKE, None, N, K, FAKE, 256, 4, FAKE, q4.Q4_F32, 512, None)
+    assert rc == q4.Q4_EINVAL
+
+
+@pytest.mark.parametrize("R", [0, 17, -1])
+def test_row_count_rejected(R):
+    rc, msg = _rc("qmv_rows", FAKE, 512, 256, FAKE, q4.Q4_BF16, 256, R, FAKE, 512, None)
+    assert rc == q4.Q4_EINVAL and "R=" in msg
+    rc, _ = _rc("qmv_w13_swiglu", FAKE, FAKE, 512, 256, FAKE, 256, R, FAKE, 512, None)
+    assert rc == q4.Q4_EINVAL
+
+
+def test_null_and_misaligned_pointers_rejected():
+    rc, msg = _rc("qmv_rows", None, 512, 256, FAKE, q4.Q4_BF16, 256, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EALIGN and "NULL" in msg
+    rc, msg = _rc("qmv_rows", FAKE + 8, 512, 256, FAKE, q4.Q4_BF16, 256, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EALIGN and "aligned" in msg
+    rc, _ = _rc("qmv_rows", FAKE, 512, 256, FAKE + 2, q4.Q4_BF16, 256, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EALIGN
+    rc, _ = _rc("qmm_window", FAKE, FAKE + 4, 512, 256, FAKE, 256, 4, FAKE, q4.Q4_F32, 512, None)
+    assert rc == q4.Q4_EALIGN
+
+
+def test_strides_and_dtypes_rejected():
+    # ldx < K
+    rc, _ = _rc("qmv_rows", FAKE, 512, 256, FAKE, q4.Q4_BF16, 128, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EINVAL
+    # ldx keeps rows 16-byte aligned only in multiples of 8 bf16 / 4 float32
+    rc, _ = _rc("qmv_rows", FAKE, 512, 256, FAKE, q4.Q4_BF16, 260, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EALIGN
+    rc, _ = _rc("qmv_rows", FAKE, 512, 256, FAKE, q4.Q4_F32, 258, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EALIGN
+    # ldy < N
+    rc, _ = _rc("qmv_rows", FAKE, 512, 256, FAKE, q4.Q4_BF16, 256, 1, FAKE, 500, None)
+    assert rc == q4.Q4_EINVAL
+    # unknown dtypes
+    rc, _ = _rc("qmv_rows", FAKE, 512, 256, FAKE, 7, 256, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EINVAL
+    rc, _ = _rc("qmm_window", FAKE, None, 512, 256, FAKE, 256, 4, FAKE, 9, 512, None)
+    assert rc == q4.Q4_EINVAL
+
+
+def test_window_counts_rejected():
+    rc, _ = _rc("qmm_window", FAKE, None, 512, 256, FAKE, 256, 0, FAKE, q4.Q4_F32, 512, None)
+    assert rc == q4.Q4_EINVAL
+    arr = (ctypes.c_int64 * 3)(17, 0, 5)
+    rc, msg = _rc("qmm_cut", FAKE, None, 512, 256, FAKE, 256, arr, 3, FAKE, q4.Q4_F32, 512, None)
+    assert rc == q4.Q4_EINVAL and "window 1" in msg
+    rc, _ = _rc("qmm_cut", FAKE, None, 512, 256, FAKE, 256, None, 0, FAKE, q4.Q4_F32, 512, None)
+    assert rc == q4.Q4_EINVAL
+
+
+def test_decode_k_limits():
+    rc, msg = _rc("qmv_rows", FAKE, 512, 32768, FAKE, q4.Q4_BF16, 32768, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EUNSUPPORTED and "16384" in msg
+    rc, msg = _rc("qmv_w13_swiglu", FAKE, FAKE, 512, 16384, FAKE, 16384, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EUNSUPPORTED and "8192" in msg
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    x = torch.zeros((1, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        q4.qmv_rows(torch.zeros(10, dtype=torch.uint8), 512, 256, x)

@@ -1,0 +1,136 @@
+"""Prefill window GEMM on the GPU: float64 parity on the 1000-row prompt and
+bit-identity across every cut (64, 128, 256, ragged, single rows)."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_only_q4g64_amd as q4
+import oracle
+import synthetic
+from tests.gpu_helpers import DEV, bits16, bits32, check_within, dev_bf16, dev_weight, host_f64, say
+from tests.tolerance import tol, tol_bf16_out, tol_swiglu
+
+pytestmark = pytest.mark.gpu
+
+# rows at and around every window boundary of the four cuts
+SAMPLE_ROWS = [0, 1, 15, 16, 17, 63, 64, 127, 128, 255, 256, 316, 317, 511, 512, 767, 768, 959, 960, 999]
+
+
+@pytest.fixture(scope="module")
+def c3():
+    d = synthetic.config(3)
+    d["p1"] = dev_weight(d["w1"])
+    d["p3"] = dev_weight(d["w3"])
+    d["xd"] = dev_bf16(d["x"])
+    return d
+
+
+@pytest.fixture(scope="module")
+def c3_whole(c3):
+    w1 = c3["w1"]
+    z = q4.qmm_window(c3["p1"], c3["p3"], w1.N, w1.K, c3["xd"])
+    torch.cuda.synchronize()
+    return z
+
+
+def test_c3_swiglu_parity(c3, c3_whole):
+    w1, w3 = c3["w1"], c3["w3"]
+    say("c3 pgemm SwiGLU 1000x8192 parity on boundary rows")
+    xs = c3["x"][SAMPLE_ROWS]
+    a64 = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, xs)
+    c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, xs)
+    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, xs), w1.K),
+                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, xs), w3.K))
+    z = host_f64(c3_whole)[SAMPLE_ROWS]
+    ratio = float(np.max(np.abs(z - oracle.swiglu(a64, c64)) / Tz))
+    say(f"c3 max err/Tz {ratio:.3g}")
+    assert ratio <= 1.0
+
+
+@pytest.mark.parametrize("cut", ["w64", "w128", "w256", "ragged"])
+def test_c3_cuts_bit_identical(c3, c3_whole, cut):
+    w1 = c3["w1"]
+    say(f"c3 cut {cut}")
+    z = q4.qmm_cut(c3["p1"], c3["p3"], w1.N, w1.K, c3["xd"], c3["cuts"][cut])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits32(z), bits32(c3_whole))
+
+
+def test_c3_single_row_windows(c3, c3_whole):
+    """Every row alone equals the row inside a window (sampled rows)."""
+    w1 = c3["w1"]
+    say("c3 M=1 windows")
+    ref = bits32(c3_whole)
+    for r in SAMPLE_ROWS:
+        z1 = q4.qmm_window(c3["p1"], c3["p3"], w1.N, w1.K, c3["xd"][r : r + 1])
+        assert np.array_equal(bits32(z1)[0], ref[r]), r
+
+
+def test_c3_bf16_output_is_rne_of_float32(c3, c3_whole):
+    w1, w3 = c3["w1"], c3["w3"]
+    zb = q4.qmm_window(c3["p1"], c3["p3"], w1.N, w1.K, c3["xd"], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    f = c3_whole.cpu().numpy()
+    expect = synthetic.bf16_bits_from_f64(f.astype(np.float64))  # f32 -> bf16 RNE
+    assert np.array_equal(bits16(zb).view(np.uint16), expect)
+    # and against the oracle with the bf16 half-ulp added
+    xs = c3["x"][SAMPLE_ROWS[:6]]
+    a64 = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, xs)
+    c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, xs)
+    z64 = oracle.swiglu(a64, c64)
+    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, xs), w1.K),
+                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, xs), w3.K))
+    zb64 = oracle.bf16_to_f64(bits16(zb).view(np.uint16)[SAMPLE_ROWS[:6]])
+    assert np.all(np.abs(zb64 - z64) <= tol_bf16_out(z64, Tz))
+
+
+@pytest.mark.parametrize("M", [1, 2, 17, 64, 65, 100])
+def test_plain_window_parity_and_row_permutation(M):
+    d = synthetic.config(2)
+    w = synthetic.concat_rows(d["wq"], d["wk"], d["wv"])
+    rng = np.random.default_rng(M)
+    x = synthetic.draw_bf16_rows(rng, M, w.K)
+    say(f"plain pgemm qkv M={M}")
+    pk = dev_weight(w)
+    xd = dev_bf16(x)
+    y = q4.qmm_window(pk, None, w.N, w.K, xd)
+    torch.cuda.synchronize()
+    check_within(host_f64(y), w, x, label=f"pgemm plain M={M}")
+    perm = rng.permutation(M)
+    yp = q4.qmm_window(pk, None, w.N, w.K, xd[torch.from_numpy(perm).to(DEV)])
+    assert np.array_equal(bits32(yp), bits32(y)[perm])
+    yb = q4.qmm_window(pk, None, w.N, w.K, xd, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(yb).view(np.uint16), synthetic.bf16_bits_from_f64(y.cpu().numpy().astype(np.float64)))
+
+
+@pytest.mark.parametrize("N,K,M", [(64, 64, 5), (64, 192, 33), (320, 640, 40)])
+def test_pgemm_edge_shapes(N, K, M):
+    say(f"edge pgemm N={N} K={K} M={M}")
+    rng = np.random.default_rng(N * K + M)
+    w = synthetic.draw_qweight(rng, "e", N, K)
+    w3 = synthetic.draw_qweight(rng, "e3", N, K)
+    s = (w.scales.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    w.scales = synthetic.bf16_bits_from_f64(s * rng.choice([-1.0, 1.0, 0.0], size=s.shape))
+    x = synthetic.bf16_bits_from_f64(rng.normal(0, 1, (M, K)) * rng.choice([1e-4, 1.0, 50.0], (M, K)))
+    pk, pk3, xd = dev_weight(w), dev_weight(w3), dev_bf16(x)
+    y = host_f64(q4.qmm_window(pk, None, N, K, xd))
+    check_within(y, w, x, label="edge pgemm")
+    z = host_f64(q4.qmm_window(pk, pk3, N, K, xd))
+    a64 = oracle.matmul_rows(w.wq, w.scales, w.biases, x)
+    c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, x)
+    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w.wq, w.scales, w.biases, x), K),
+                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, x), K))
+    assert np.all(np.abs(z - oracle.swiglu(a64, c64)) <= Tz)
+
+
+def test_window_and_decode_orders_differ(c3):
+    """Control for the bit tests: the prompt GEMM and the decode matvec use
+    different (each fixed) summation orders, and the bit comparisons can see
+    that difference on real data."""
+    w1 = c3["w1"]
+    xs = c3["xd"][:16]
+    a_win = bits32(q4.qmm_window(c3["p1"], None, w1.N, w1.K, xs))
+    a_dec = bits32(q4.qmv_rows(c3["p1"], w1.N, w1.K, xs))
+    assert not np.array_equal(a_win, a_dec)
