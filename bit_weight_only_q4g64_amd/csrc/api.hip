@@ -160,19 +160,12 @@ int qmv_rows(const void* packed, int64_t N, int64_t K, const void* x, int x_dtyp
   if (int rc = check_x(fn, x, x_dtype, ldx, K)) return rc;
   if (int rc = check_ptr(fn, "y", y, 4)) return rc;
   if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
-  const int nseg = q4::qmv_segments(K);
-  const size_t lds = (size_t)nseg * 1024;
+  if ((int64_t)R * ldx * (x_dtype == Q4_F32 ? 4 : 2) >= (int64_t(1) << 31))
+    return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
+  const size_t lds = q4::qmv_lds_bytes(K, x_dtype == Q4_F32, 1, R);
   if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
-  const int maxw = x_dtype == Q4_BF16 ? q4::QmvLimits<0>::kMaxWaves : q4::QmvLimits<1>::kMaxWaves;
-  const int nwaves = nseg < maxw ? nseg : maxw;
-  hipStream_t s = (hipStream_t)stream;
-  const uint8_t* pk = (const uint8_t*)packed;
-  if (x_dtype == Q4_BF16)
-    hipLaunchKernelGGL((q4::qmv_kernel<0, 1>), dim3((unsigned)(N / 16)), dim3(nwaves * 64), lds, s, pk, pk, (int)N, (int)K, x,
-                       ldx, R, y, ldy);
-  else
-    hipLaunchKernelGGL((q4::qmv_kernel<1, 1>), dim3((unsigned)(N / 16)), dim3(nwaves * 64), lds, s, pk, pk, (int)N, (int)K, x,
-                       ldx, R, y, ldy);
+  q4::qmv_launch((const uint8_t*)packed, (const uint8_t*)packed, 1, (int)N, (int)K, x, x_dtype == Q4_F32, ldx, R, y, ldy,
+                 (hipStream_t)stream);
   return launched(fn);
 }
 
@@ -186,13 +179,12 @@ int qmv_w13_swiglu(const void* packed_w1, const void* packed_w3, int64_t N, int6
   if (int rc = check_x(fn, x, Q4_BF16, ldx, K)) return rc;
   if (int rc = check_ptr(fn, "y", y, 4)) return rc;
   if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
-  const int nseg = q4::qmv_segments(K);
-  const size_t lds = (size_t)nseg * 2 * 1024;
+  if ((int64_t)R * ldx * 2 >= (int64_t(1) << 31))
+    return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
+  const size_t lds = q4::qmv_lds_bytes(K, 0, 2, R);
   if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the fused decode limit of 8192", fn, (long long)K);
-  const int nwaves = nseg < q4::QmvLimits<0>::kMaxWaves ? nseg : q4::QmvLimits<0>::kMaxWaves;
-  hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL((q4::qmv_kernel<0, 2>), dim3((unsigned)(N / 16)), dim3(nwaves * 64), lds, s,
-                     (const uint8_t*)packed_w1, (const uint8_t*)packed_w3, (int)N, (int)K, (const void*)x, ldx, R, y, ldy);
+  q4::qmv_launch((const uint8_t*)packed_w1, (const uint8_t*)packed_w3, 2, (int)N, (int)K, x, 0, ldx, R, y, ldy,
+                 (hipStream_t)stream);
   return launched(fn);
 }
 

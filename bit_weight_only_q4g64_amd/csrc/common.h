@@ -97,6 +97,20 @@ __device__ __forceinline__ void split3(float x, uint32_t& h, uint32_t& m, uint32
   l = __float_as_uint(r2) >> 16;
 }
 
+// Raw buffer access: a scalar resource (base, size in bytes) and a 32-bit
+// per-lane byte offset plus a scalar byte offset. Reads past `bytes` return 0.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
 // SwiGLU gate in float32: silu(a) = a / (1 + exp(-a)), library expf and an
 // IEEE division (no fast-math, no contraction).
 __device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + expf(-a)); }

@@ -1,12 +1,13 @@
 // Decode matvecs over 1..16 activation rows (qmv) on the matrix cores.
 //
 // One workgroup owns one 16-column tile of the weight matrix (or the same
-// tile of w1 and w3 for the fused SwiGLU variant) and all of K. Its waves
-// split K into segments of kSegGroups groups (a fixed function of K): each
-// wave streams its segment's codes with 128-bit loads, turns them into exact
-// bf16 integers in registers, and reduces them with v_mfma_f32_16x16x32_bf16
-// against the activation rows, which fill the 16 row slots (unused slots are
-// zero). Per output the order is:
+// tile of w1 and w3 for the fused SwiGLU variant) and all of K. K is cut into
+// segments of kSegGroups groups (a fixed function of K); each wave owns up to
+// SPW segments and issues every weight load of all of them before any
+// compute, so a workgroup has its whole column tile in flight at once. Codes
+// become exact bf16 integers in registers and are reduced with
+// v_mfma_f32_16x16x32_bf16 against the activation rows. Per output the order
+// is:
 //
 //   for each segment s (ascending):   part_s = 0
 //     for each group g in s:           P = mfma(x[g, 32..63], q, mfma(x[g, 0..31], q, 0))
@@ -14,175 +15,382 @@
 //                                      part_s = fma(s_g, P, fma(b_g, S, part_s))
 //   y = ((part_0 + part_1) + part_2) + ...
 //
-// Nothing in it depends on R, on the slot a row occupies or on the launch
-// shape, so every row is bit-equal to its one-row result (TensorFold PR #1696,
-// later revision, "What it adds": rows that share a decode step are summed as
-// the one-row kernels sum them).
+// bf16 activations: the 16 row slots of the instruction hold rows 0..15.
+// float32 activations: each float is split exactly into three bf16 pieces
+// h + m + l; row r of a 4-row tile uses slots 4r (h), 4r+1 (m), 4r+2 (l)
+// (slot 4r+3 is zero), and P = (P_h + P_m) + P_l, S = (S_h + S_m) + S_l are
+// combined in-lane before the fold. R > 4 uses ceil(R/4) row tiles.
+//
+// Nothing in the order depends on R, on the slot a row occupies or on the
+// launch shape, so every row is bit-equal to its one-row result (TensorFold
+// PR #1696, later revision, "What it adds": rows that share a decode step are
+// summed as the one-row kernels sum them).
 #pragma once
 
 #include "common.h"
 
 namespace q4 {
 
-constexpr int kSegGroups = 4;                 // groups per k segment (256 k)
+constexpr int kSegGroups = 4;  // groups per k segment (256 k)
 constexpr int kSegPairs = kSegGroups / 2;
-// Waves per workgroup: 16 for bf16 activations; 8 for float32 activations,
-// whose three-piece split needs more registers per wave.
-template <int XF32>
-struct QmvLimits {
-  static constexpr int kMaxWaves = XF32 ? 8 : 16;
-};
+constexpr int kQmvMaxWaves = 16;
 
 __host__ __device__ inline int qmv_segments(int64_t K) { return (int)((K / kGroup + kSegGroups - 1) / kSegGroups); }
 
-// Activation fragment of row i (lane & 15), k = k0 + 8*(lane >> 4) .. +7 as
-// bf16 pieces. bf16 input: one piece. float32 input: three exact pieces.
-template <int XF32>
-struct XFrag {
-  static constexpr int kPieces = XF32 ? 3 : 1;
-  bf16x8 p[kPieces];
-};
-
-template <int XF32>
-__device__ __forceinline__ XFrag<XF32> load_xfrag(const void* __restrict__ xv, int64_t ldx, int row, bool ok, int64_t k0,
-                                                   int kc) {
-  XFrag<XF32> f;
-  if constexpr (!XF32) {
-    if (ok) {
-      const uint16_t* p = (const uint16_t*)xv + (int64_t)row * ldx + k0 + kc * 8;
-      f.p[0] = __builtin_bit_cast(bf16x8, *(const u32x4*)p);
-    } else {
-      f.p[0] = zero_bf16x8();
-    }
-  } else {
-    if (ok) {
-      const float* p = (const float*)xv + (int64_t)row * ldx + k0 + kc * 8;
-      const f32x4 a = *(const f32x4*)p;
-      const f32x4 b = *(const f32x4*)(p + 4);
-      const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      uint32_t h[8], m[8], l[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) split3(v[e], h[e], m[e], l[e]);
-      u32x4 H, Mi, L;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        H[j] = h[2 * j] | (h[2 * j + 1] << 16);
-        Mi[j] = m[2 * j] | (m[2 * j + 1] << 16);
-        L[j] = l[2 * j] | (l[2 * j + 1] << 16);
-      }
-      f.p[0] = __builtin_bit_cast(bf16x8, H);
-      f.p[1] = __builtin_bit_cast(bf16x8, Mi);
-      f.p[2] = __builtin_bit_cast(bf16x8, L);
-    } else {
-      f.p[0] = f.p[1] = f.p[2] = zero_bf16x8();
-    }
-  }
-  return f;
+// Layout of the dynamic LDS: per-segment partials, then (XLDS) the staged
+// activations. bf16 x: [R][K + 8] bf16 (rows padded by 16 bytes against bank
+// conflicts). float32 x: three bf16 planes h, m, l of [R][K + 8] each.
+__host__ __device__ inline int64_t qmv_xs_stride(int64_t K) { return K + 8; }
+__host__ __device__ inline size_t qmv_part_bytes(int64_t K, int xf32, int nmat, int rt, int nv = 4) {
+  return (size_t)qmv_segments(K) * nmat * rt * (xf32 ? 1 : nv) * 64 * sizeof(float);
+}
+// Row slots per lane group the bf16 path keeps for R rows.
+__host__ __device__ inline int qmv_nv(int R) { return R <= 1 ? 1 : (R <= 2 ? 2 : 4); }
+__host__ __device__ inline size_t qmv_xs_bytes(int64_t K, int xf32, int R) {
+  return (size_t)(xf32 ? 3 : 1) * R * qmv_xs_stride(K) * sizeof(uint16_t);
 }
 
-// NMAT = 1: y = W x (float32 out). NMAT = 2: y = silu(W1 x) * (W3 x).
-template <int XF32, int NMAT>
-__global__ __launch_bounds__(QmvLimits<XF32>::kMaxWaves * 64) void qmv_kernel(const uint8_t* __restrict__ pk0, const uint8_t* __restrict__ pk1,
-                                                 int N, int K, const void* __restrict__ xv, int64_t ldx, int R,
-                                                 float* __restrict__ y, int64_t ldy) {
-  extern __shared__ f32x4 part[];  // [segment][matrix][lane]
-  const int64_t t = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+// XF32 = 0: bf16 x, one row tile of 16 rows.  XF32 = 1: float32 x, RTF row
+// tiles of 4 rows x 3 pieces.  NMAT = 1: y = W x.  NMAT = 2: y = silu(W1 x) * (W3 x).
+// SPW: maximum segments per wave.  XLDS: activations staged in LDS once per
+// workgroup (else each wave reads its fragments from global memory). NV:
+// row slots per lane group kept by the bf16 path. None of these changes the
+// arithmetic of a stored row.
+template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV>
+__global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* __restrict__ pk0, const uint8_t* __restrict__ pk1,
+                                                              int N, int K, const void* __restrict__ xv, int64_t ldx, int R,
+                                                              float* __restrict__ y, int64_t ldy) {
+  constexpr int kRT = XF32 ? RTF : 1;  // row tiles
+  // accumulators per lane per row tile: bf16 x keeps row slots 4*kc + v for
+  // v < NV (NV = 4 when R > 4, else the smallest of 1, 2, 4 covering R); the
+  // slots left out hold rows >= R and are never stored
+  constexpr int kPerLane = XF32 ? 1 : NV;
+  constexpr int kXElem = XF32 ? 4 : 2;  // bytes per activation element
+  extern __shared__ __align__(16) uint8_t smem[];
+  float* part = (float*)smem;  // [segment][matrix][row tile][kPerLane][lane]
+  uint16_t* xs = (uint16_t*)(smem + qmv_part_bytes(K, XF32, NMAT, kRT, NV));
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int i = lane & 15, kc = lane >> 4;
   const int G = K / kGroup;
-  const int64_t P = (G + 1) / 2;
+  const int P = (G + 1) / 2;
   const int nseg = qmv_segments(K);
   const int64_t cb = codes_bytes(N, K);
+  const int xsi = (int)qmv_xs_stride(K);
+  const uint32_t xrow = (uint32_t)(ldx * kXElem);  // bytes per activation row
   const bf16x8 ones = ones_bf16x8();
-  const bool row_ok = i < R;
-  const uint8_t* pks[2] = {pk0, pk1};
 
-  for (int seg = wave; seg < nseg; seg += nwaves) {
-    const int g0 = seg * kSegGroups;
-    // Issue every load of the segment first: codes, scale/bias, activations.
-    u32x4 cw[NMAT][kSegPairs];
-    u32x2 sbw[NMAT][kSegPairs];
+  // buffer resources: this column tile's codes and scale/bias, and x
+  rsrc_t cres[NMAT], sres[NMAT];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
+  for (int m = 0; m < NMAT; ++m) {
+    const uint8_t* pk = m ? pk1 : pk0;
+    cres[m] = make_rsrc(pk + (int64_t)t * P * kPairCodeBytes, (uint32_t)P * kPairCodeBytes);
+    sres[m] = make_rsrc(pk + cb + (int64_t)t * P * kPairSbBytes, (uint32_t)P * kPairSbBytes);
+  }
+  const rsrc_t xres = make_rsrc(xv, (uint32_t)R * xrow);
+
+  // 1) activations: the first batch of staging loads is issued before the
+  //    weight loads, so writing it to LDS waits for nothing else. Staging
+  //    slot (r, j) covers row r, 16-byte chunk threadIdx.x + j * blockDim.x;
+  //    r and j are uniform and walk the rows in order.
+  constexpr int kBatch = 4;
+  const int nthr = blockDim.x;
+  const int per_row = K * kXElem / 16;  // 16-byte chunks per row
+  const int jmax = (per_row + nthr - 1) / nthr;
+  auto xload = [&](int r, int j) -> u32x4 {
+    int c = (int)threadIdx.x + j * nthr;
+    c = c < per_row ? c : per_row - 1;
+    return buf_load16(xres, (uint32_t)c * 16u, (uint32_t)r * xrow);
+  };
+  u32x4 xv0[kBatch];
+  if constexpr (XLDS) {
+    int r = 0, j = 0;
 #pragma unroll
-      for (int pp = 0; pp < kSegPairs; ++pp) {
-        const int64_t p = g0 / 2 + pp;
-        if (p < P) {
-          cw[m][pp] = __builtin_nontemporal_load((const u32x4*)(pks[m] + (t * P + p) * kPairCodeBytes + lane * 16));
-          sbw[m][pp] = *(const u32x2*)(pks[m] + cb + (t * P + p) * kPairSbBytes + i * 8);
-        } else {
-          cw[m][pp] = u32x4{0u, 0u, 0u, 0u};
-          sbw[m][pp] = u32x2{0u, 0u};
-        }
+    for (int u = 0; u < kBatch; ++u) {
+      if (r >= R) break;
+      xv0[u] = xload(r, j);
+      if (++j == jmax) { j = 0; ++r; }
+    }
+  }
+
+  // 2) every weight load of this wave's segments (pair indices past the
+  //    matrix are clamped to its last pair; those values are never used)
+  u32x4 cw[SPW][NMAT][kSegPairs];
+  u32x2 sbw[SPW][NMAT][kSegPairs];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int seg = wave + j * nwaves;
+#pragma unroll
+    for (int pp = 0; pp < kSegPairs; ++pp) {
+      int p = seg * kSegPairs + pp;
+      p = p < P ? p : P - 1;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        cw[j][m][pp] = buf_load16(cres[m], (uint32_t)lane * 16u, (uint32_t)p * kPairCodeBytes);
+        sbw[j][m][pp] = buf_load8(sres[m], (uint32_t)i * 8u, (uint32_t)p * kPairSbBytes);
       }
     }
-    XFrag<XF32> xf[kSegGroups][2];
-#pragma unroll
-    for (int gg = 0; gg < kSegGroups; ++gg) {
-      const int g = g0 + gg;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) xf[gg][hh] = load_xfrag<XF32>(xv, ldx, i, row_ok && g < G, (int64_t)g * kGroup + hh * 32, kc);
-    }
+  }
 
-    f32x4 acc[NMAT];
+  // 3) write the staged activations (float32 rows as three exact bf16 planes)
+  if constexpr (XLDS) {
+    const int plane = R * xsi;
+    auto put = [&](int r, int j, const u32x4& v) {
+      const int c = (int)threadIdx.x + j * nthr;
+      if (c >= per_row) return;
+      if constexpr (!XF32) {
+        *(u32x4*)(xs + r * xsi + c * 8) = v;
+      } else {
+        uint32_t h[4], m[4], l[4];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < 4; ++w) split3(__uint_as_float(v[w]), h[w], m[w], l[w]);
+        uint16_t* d = xs + r * xsi + c * 4;
+        *(u32x2*)d = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        *(u32x2*)(d + plane) = u32x2{m[0] | (m[1] << 16), m[2] | (m[3] << 16)};
+        *(u32x2*)(d + 2 * plane) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+      }
+    };
+    int r = 0, j = 0;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (r >= R) break;
+      put(r, j, xv0[u]);
+      if (++j == jmax) { j = 0; ++r; }
+    }
+    // slots beyond the first batch (large R * K): kBatch loads, then their writes
+    while (r < R) {
+      u32x4 v[kBatch];
+      int r2 = r, j2 = j;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (r2 < R) v[u] = xload(r2, j2);
+        if (++j2 == jmax) { j2 = 0; ++r2; }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (r < R) put(r, j, v[u]);
+        if (++j == jmax) { j = 0; ++r; }
+      }
+    }
+    __syncthreads();
+  }
+
+  // Activation fragment of row tile rt, group g, half hh for this lane. Slots
+  // of rows >= R (and the unused fourth piece slot) read a valid row: their
+  // results are independent of the other slots and never stored.
+  const int frow = XF32 ? 0 : (i < R ? i : R - 1);
+  auto xfrag = [&](int rt, int g, int hh) -> bf16x8 {
+    const int k0 = g * kGroup + hh * 32 + kc * 8;
+    if constexpr (!XF32) {
+      if constexpr (XLDS) return __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + frow * xsi + k0));
+      else return __builtin_bit_cast(bf16x8, buf_load16(xres, (uint32_t)frow * xrow + (uint32_t)k0 * 2u, 0u));
+    } else {
+      int row = rt * 4 + (i >> 2);
+      row = row < R ? row : R - 1;
+      int piece = i & 3;
+      piece = piece < 3 ? piece : 2;
+      if constexpr (XLDS) return __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + (piece * R + row) * xsi + k0));
+      else {
+        const u32x4 a = buf_load16(xres, (uint32_t)row * xrow + (uint32_t)k0 * 4u, 0u);
+        const u32x4 b = buf_load16(xres, (uint32_t)row * xrow + (uint32_t)k0 * 4u + 16u, 0u);
+        uint32_t o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint32_t h, m, l;
+          split3(__uint_as_float(e < 4 ? a[e] : b[e - 4]), h, m, l);
+          o[e] = piece == 0 ? h : (piece == 1 ? m : l);
+        }
+        return __builtin_bit_cast(bf16x8, u32x4{o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16)});
+      }
+    }
+  };
+
+  // 4) compute, one segment after another
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int seg = wave + j * nwaves;
+    if (seg >= nseg) break;
+    float acc[NMAT][kRT][kPerLane];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+        for (int v = 0; v < kPerLane; ++v) acc[m][rt][v] = 0.f;
+    const int g0 = seg * kSegGroups;
 #pragma unroll
     for (int gg = 0; gg < kSegGroups; ++gg) {
       const int g = g0 + gg;
       if (g >= G) break;
       const int pp = gg >> 1, gh = gg & 1;
-      f32x4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int pc = 0; pc < XFrag<XF32>::kPieces; ++pc) {
-        S = mfma16(xf[gg][0].p[pc], ones, S);
-        S = mfma16(xf[gg][1].p[pc], ones, S);
-      }
+      bf16x8 q[NMAT][2];
+      float sc[NMAT], bs[NMAT];
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
-        const bf16x8 q0 = codes_to_bf16(gh ? cw[m][pp][2] : cw[m][pp][0]);
-        const bf16x8 q1 = codes_to_bf16(gh ? cw[m][pp][3] : cw[m][pp][1]);
-        f32x4 Pm = {0.f, 0.f, 0.f, 0.f};
+        q[m][0] = codes_to_bf16(gh ? cw[j][m][pp][2] : cw[j][m][pp][0]);
+        q[m][1] = codes_to_bf16(gh ? cw[j][m][pp][3] : cw[j][m][pp][1]);
+        const uint32_t w = gh ? sbw[j][m][pp][1] : sbw[j][m][pp][0];
+        sc[m] = bf16_lo(w);
+        bs[m] = bf16_hi(w);
+      }
 #pragma unroll
-        for (int pc = 0; pc < XFrag<XF32>::kPieces; ++pc) {
-          Pm = mfma16(xf[gg][0].p[pc], q0, Pm);
-          Pm = mfma16(xf[gg][1].p[pc], q1, Pm);
+      for (int rt = 0; rt < kRT; ++rt) {
+        const bf16x8 xa0 = xfrag(rt, g, 0), xa1 = xfrag(rt, g, 1);
+        f32x4 S = mfma16(xa0, ones, f32x4{0.f, 0.f, 0.f, 0.f});
+        S = mfma16(xa1, ones, S);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          f32x4 Pm = mfma16(xa0, q[m][0], f32x4{0.f, 0.f, 0.f, 0.f});
+          Pm = mfma16(xa1, q[m][1], Pm);
+          if constexpr (!XF32) {
+#pragma unroll
+            for (int v = 0; v < kPerLane; ++v) acc[m][rt][v] = __builtin_fmaf(sc[m], Pm[v], __builtin_fmaf(bs[m], S[v], acc[m][rt][v]));
+          } else {
+            const float Pr = (Pm[0] + Pm[1]) + Pm[2];
+            const float Sr = (S[0] + S[1]) + S[2];
+            acc[m][rt][0] = __builtin_fmaf(sc[m], Pr, __builtin_fmaf(bs[m], Sr, acc[m][rt][0]));
+          }
         }
-        const uint32_t sbword = gh ? sbw[m][pp][1] : sbw[m][pp][0];
-        const float s = bf16_lo(sbword), b = bf16_hi(sbword);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[m][v] = __builtin_fmaf(s, Pm[v], __builtin_fmaf(b, S[v], acc[m][v]));
       }
     }
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) part[(seg * NMAT + m) * 64 + lane] = acc[m];
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+        for (int v = 0; v < kPerLane; ++v) part[(((seg * NMAT + m) * kRT + rt) * kPerLane + v) * 64 + lane] = acc[m][rt][v];
   }
   __syncthreads();
   if (wave != 0) return;
-  f32x4 tot[NMAT];
+
+  // 5) add the segments in ascending order; epilogue
+  float tot[NMAT][kRT][kPerLane];
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m) tot[m] = part[m * 64 + lane];
-  for (int seg = 1; seg < nseg; ++seg) {
+  for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      const f32x4 ps = part[(seg * NMAT + m) * 64 + lane];
+    for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) tot[m][v] = tot[m][v] + ps[v];
-    }
-  }
-  const int64_t n = t * kTileN + i;
+      for (int v = 0; v < kPerLane; ++v) tot[m][rt][v] = part[((m * kRT + rt) * kPerLane + v) * 64 + lane];
+  for (int seg = 1; seg < nseg; ++seg)
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int r = 4 * kc + v;
-    if (r < R) {
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+        for (int v = 0; v < kPerLane; ++v)
+          tot[m][rt][v] = tot[m][rt][v] + part[(((seg * NMAT + m) * kRT + rt) * kPerLane + v) * 64 + lane];
+
+  const int64_t n = (int64_t)t * kTileN + i;
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+#pragma unroll
+    for (int v = 0; v < kPerLane; ++v) {
+      const int r = XF32 ? rt * 4 + kc : 4 * kc + v;
+      if (r >= R) continue;
       float out;
       if constexpr (NMAT == 1) {
-        out = tot[0][v];
+        out = tot[0][rt][v];
       } else {
-        out = silu_f32(tot[0][v]) * tot[1][v];
+        out = silu_f32(tot[0][rt][v]) * tot[1][rt][v];
       }
       y[(int64_t)r * ldy + n] = out;
     }
+  }
+}
+
+// Row tiles the float32 path instantiates for R rows (1, 2 or 4 tiles of 4 rows).
+inline int qmv_row_tiles(int xf32, int R) {
+  if (!xf32) return 1;
+  const int rtf = (R + 3) / 4;
+  return rtf <= 1 ? 1 : (rtf <= 2 ? 2 : 4);
+}
+
+// Largest dynamic LDS a workgroup may use on this device (queried once).
+inline size_t qmv_max_lds() {
+  static size_t cached = 0;
+  if (cached == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
+      cached = (size_t)v;
+    else
+      cached = 64 * 1024;
+  }
+  return cached;
+}
+
+// LDS needed without staging (partials only); the launch adds the staged
+// activations when they fit.
+inline size_t qmv_lds_bytes(int64_t K, int xf32, int nmat, int R) {
+  return qmv_part_bytes(K, xf32, nmat, qmv_row_tiles(xf32, R), xf32 ? 1 : qmv_nv(R));
+}
+
+template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV>
+inline void qmv_launch_t(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
+                         int64_t ldy, int nwaves, size_t lds, hipStream_t s) {
+  auto kern = qmv_kernel<XF32, NMAT, SPW, RTF, XLDS, NV>;
+  // allow dynamic LDS beyond the 64 KB default, once per instantiation
+  static const bool lds_ok =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)qmv_max_lds()) == hipSuccess;
+  (void)lds_ok;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(N / kTileN)), dim3(nwaves * 64), lds, s, pk0, pk1, N, K, x, ldx, R, y, ldy);
+}
+
+template <int XF32, int NMAT, int RTF, bool XLDS, int NV>
+inline void qmv_launch_spw(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
+                           int64_t ldy, size_t lds, hipStream_t s) {
+  const int nseg = qmv_segments(K);
+  const int nwaves = nseg < kQmvMaxWaves ? nseg : kQmvMaxWaves;
+  const int spw = (nseg + nwaves - 1) / nwaves;
+  if (spw <= 1) {
+    qmv_launch_t<XF32, NMAT, 1, RTF, XLDS, NV>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
+  } else if (spw <= 2) {
+    qmv_launch_t<XF32, NMAT, 2, RTF, XLDS, NV>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
+  } else {
+    // the fused two-matrix variant is limited to K <= 8192 (two segments per wave)
+    if constexpr (NMAT == 1) qmv_launch_t<XF32, NMAT, 4, RTF, XLDS, NV>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
+  }
+}
+
+template <int XF32, int NMAT, int RTF, int NV>
+inline void qmv_launch_lds(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
+                           int64_t ldy, hipStream_t s) {
+  const size_t part = qmv_part_bytes(K, XF32, NMAT, XF32 ? RTF : 1, NV);
+  const size_t staged = part + qmv_xs_bytes(K, XF32, R);
+  if (staged <= qmv_max_lds())
+    qmv_launch_spw<XF32, NMAT, RTF, true, NV>(pk0, pk1, N, K, x, ldx, R, y, ldy, staged, s);
+  else
+    qmv_launch_spw<XF32, NMAT, RTF, false, NV>(pk0, pk1, N, K, x, ldx, R, y, ldy, part, s);
+}
+
+template <int NMAT>
+inline void qmv_launch_bf16(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
+                            int64_t ldy, hipStream_t s) {
+  const int nv = qmv_nv(R);
+  if (nv == 1)
+    qmv_launch_lds<0, NMAT, 1, 1>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+  else if (nv == 2)
+    qmv_launch_lds<0, NMAT, 1, 2>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+  else
+    qmv_launch_lds<0, NMAT, 1, 4>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+}
+
+inline void qmv_launch(const uint8_t* pk0, const uint8_t* pk1, int nmat, int N, int K, const void* x, int xf32, int64_t ldx,
+                       int R, float* y, int64_t ldy, hipStream_t s) {
+  if (!xf32) {
+    if (nmat == 1)
+      qmv_launch_bf16<1>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    else
+      qmv_launch_bf16<2>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+  } else {
+    const int rt = qmv_row_tiles(1, R);
+    if (rt == 1)
+      qmv_launch_lds<1, 1, 1, 1>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    else if (rt == 2)
+      qmv_launch_lds<1, 1, 2, 1>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    else
+      qmv_launch_lds<1, 1, 4, 1>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
   }
 }
 
