@@ -162,6 +162,8 @@ int qmv_rows(const void* packed, int64_t N, int64_t K, const void* x, int x_dtyp
   if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
   if ((int64_t)R * ldx * (x_dtype == Q4_F32 ? 4 : 2) >= (int64_t(1) << 31))
     return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
+  // up to 4 segments per wave, 16 waves: K <= 16384
+  if (K > q4::kQmvMaxK) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
   const size_t lds = q4::qmv_lds_bytes(K, x_dtype == Q4_F32, 1, R);
   if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
   q4::qmv_launch((const uint8_t*)packed, (const uint8_t*)packed, 1, (int)N, (int)K, x, x_dtype == Q4_F32, ldx, R, y, ldy,
@@ -181,6 +183,8 @@ int qmv_w13_swiglu(const void* packed_w1, const void* packed_w3, int64_t N, int6
   if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
   if ((int64_t)R * ldx * 2 >= (int64_t(1) << 31))
     return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
+  // up to 2 segments per wave, 16 waves: K <= 8192
+  if (K > q4::kQmvMaxK / 2) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the fused decode limit of 8192", fn, (long long)K);
   const size_t lds = q4::qmv_lds_bytes(K, 0, 2, R);
   if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the fused decode limit of 8192", fn, (long long)K);
   q4::qmv_launch((const uint8_t*)packed_w1, (const uint8_t*)packed_w3, 2, (int)N, (int)K, x, 0, ldx, R, y, ldy,

@@ -34,6 +34,8 @@ namespace q4 {
 constexpr int kSegGroups = 4;  // groups per k segment (256 k)
 constexpr int kSegPairs = kSegGroups / 2;
 constexpr int kQmvMaxWaves = 16;
+constexpr int kQmvMaxSpw = 4;  // segments per wave the kernels instantiate
+constexpr int64_t kQmvMaxK = (int64_t)kQmvMaxWaves * kQmvMaxSpw * kSegGroups * kGroup;  // 16384
 
 __host__ __device__ inline int qmv_segments(int64_t K) { return (int)((K / kGroup + kSegGroups - 1) / kSegGroups); }
 
