@@ -9,11 +9,12 @@ the L2s, so every step streams its 28 MB of weights from HBM, as a real
 decode step streams the model's weights once per token.
 
 The timed region replays a HIP graph of the K steps (host launch cost would
-otherwise dominate a 5 us step), bracketed by torch.cuda.synchronize(). Per
-kernel durations come from HIP events recorded on the library's stream
-around every launch of an eager pass over the same steps (the queue is
-pre-filled by a busy kernel so no host gap falls between an event and its
-kernel). The prompt GEMM is reported beside it (TFLOP/s against the bf16
+otherwise dominate a 10 us step), bracketed by torch.cuda.synchronize(). The
+runtime cannot time events inside a graph, and an event between two decode
+kernels costs about as much as the kernel, so each kernel's average duration
+is taken over a graph of the same K launches of that kernel alone (same pool
+rotation and buffers), bracketed by two HIP events on the stream it runs on.
+The prompt GEMM is reported beside it (TFLOP/s against the bf16
 matrix-core peak) on the 8192-row w1/w3 + SwiGLU window.
 
 The float64 oracle is timed on the host on a bounded sample of the same
@@ -93,6 +94,71 @@ def cpu_baseline(d, budget_s=12.0):
     }
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["bit_weight_only_q4g64_amd/csrc/common.h", "bit_weight_only_q4g64_amd/csrc/qmv.h",
+                  "bit_weight_only_q4g64_amd/csrc/pgemm.h", "bit_weight_only_q4g64_amd/csrc/api.hip"]
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_per_launch(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter on a plain copy
+    of known size), or None when the summary is missing or was taken on
+    different kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}.md")
+    try:
+        with open(path) as f:
+            text = f.read()
+        data = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if data.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return data.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(torch):
+    """A plain device copy of a known size, for scaling the byte counters."""
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+
+
+def batch_average_us(torch, launch, first, K):
+    """Average device time per launch of K launches captured in one graph."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(K):
+                launch(first + i)
+    torch.cuda.synchronize()
+    g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / K
+
+
 def decode_step_bytes(d):
     w1, w2 = d["w1"], d["w2"]
     b13 = 2 * qbytes(w1.N, w1.K) + w1.K * 2 + w1.N * 4
@@ -108,6 +174,10 @@ def main():
     ap.add_argument("--pool-mb", type=int, default=1200, help="size of the rotating weight pool (cold HBM reads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pgemm", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the timed steps directly instead of replaying a graph (for per-dispatch counters)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (the reference for scaling HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -116,6 +186,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
 
     import bit_weight_only_q4g64_amd as q4
     import synthetic
@@ -153,34 +227,48 @@ def main():
     torch.cuda.synchronize()
 
     # graph of K steps (each step on the next pool copy)
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
+    g = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(K):
+                    step(W + i)
+        torch.cuda.synchronize()
+        g.replay()  # untimed replay: first-launch costs
+        torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+
+    def run_timed():
+        if g is not None:
+            g.replay()
+        else:
             for i in range(K):
-                step(W + i)
-    torch.cuda.synchronize()
-    g.replay()  # untimed replay: first-launch costs
-    torch.cuda.synchronize()
+                step(W + i, evs[i])
 
     log(f"timed region: {K} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    g.replay()
+    run_timed()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
-
-    # eager pass with events around every kernel, queue pre-filled by a busy kernel
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(2.4e9 * 0.00004 * K))  # ~40 us of GPU time per step to enqueue behind
-    for i in range(K):
-        step(W + i, evs[i])
-    torch.cuda.synchronize()
-    t13 = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3  # us
-    t2 = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    if g is not None:
+        # The runtime cannot time events inside a graph, and an event between
+        # two kernels costs about as much as a decode kernel. Each kernel's
+        # average duration is therefore taken over a graph of the same K
+        # launches of that kernel alone (same pool rotation, same buffers),
+        # bracketed by two events on the stream it runs on.
+        t13 = np.array([batch_average_us(torch, lambda i: q4.qmv_w13_swiglu(pool[i % ncopies][0], pool[i % ncopies][1],
+                                                                            w1.N, w1.K, x, y=z), W, K)])
+        t2 = np.array([batch_average_us(torch, lambda i: q4.qmv_rows(pool[i % ncopies][2], w2.N, w2.K, z, y=y), W, K)])
+        timing_src = "HIP events around a graph of the same K launches of each kernel alone, divided by K"
+    else:
+        t13 = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3  # us
+        t2 = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+        timing_src = "HIP events around each kernel of the timed steps (launched directly)"
 
     b13 = 2 * qbytes(w1.N, w1.K) + w1.K * 2 + w1.N * 4
     b2 = qbytes(w2.N, w2.K) + w2.K * 4 + w2.N * 4
@@ -208,7 +296,9 @@ def main():
             "rows": 1,
             "step_bytes": step_bytes,
             "weight_pool_gib": round(ncopies * copy_bytes / 2**30, 3),
-            "timing": "HIP graph of K steps, wall clock between synchronizes",
+            "kernel_source_hash": kernel_source_hash(),
+            "timing": ("HIP graph of K steps" if g is not None else "K directly launched steps") + ", wall clock between synchronizes",
+            "kernel_timing": timing_src,
         },
         "rows_per_s": round(1.0 / (ms_per_step * 1e-3), 1),
         "roofline": {
@@ -218,7 +308,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(ach13 / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic_per_launch("qmv_w13_swiglu"),
             "algorithmic_bytes_per_launch": b13,
             "avg_launch_us": round(float(t13.mean()), 3),
         },
