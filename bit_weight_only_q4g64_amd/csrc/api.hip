@@ -27,7 +27,6 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
-constexpr int kPgemmRT = 4;  // row tiles (16 rows each) per pgemm workgroup
 constexpr size_t kMaxLds = 64 * 1024;
 
 int check_nk(const char* fn, int64_t N, int64_t K) {
@@ -72,20 +71,20 @@ int qmm_window_impl(const char* fn, const void* packed_a, const void* packed_b, 
   const bool swiglu = packed_b != nullptr;
   const bool obf16 = y_dtype == Q4_BF16;
   const int cols_per_wg = kPgemmWaves * (swiglu ? 32 : 64);
-  dim3 grid((unsigned)((N + cols_per_wg - 1) / cols_per_wg), (unsigned)((M + kPgemmRT * 16 - 1) / (kPgemmRT * 16)));
+  dim3 grid((unsigned)((N + cols_per_wg - 1) / cols_per_wg), (unsigned)((M + kPgemmRows - 1) / kPgemmRows));
   dim3 block(kPgemmWaves * 64);
   const uint8_t* a = (const uint8_t*)packed_a;
   const uint8_t* b = (const uint8_t*)packed_b;
   if (swiglu) {
     if (obf16)
-      hipLaunchKernelGGL((pgemm_kernel<true, true, kPgemmRT>), grid, block, 0, s, a, b, (int)N, (int)K, x, ldx, (int)M, y, ldy);
+      hipLaunchKernelGGL((pgemm_kernel<true, true>), grid, block, 0, s, a, b, (int)N, (int)K, x, ldx, (int)M, y, ldy);
     else
-      hipLaunchKernelGGL((pgemm_kernel<true, false, kPgemmRT>), grid, block, 0, s, a, b, (int)N, (int)K, x, ldx, (int)M, y, ldy);
+      hipLaunchKernelGGL((pgemm_kernel<true, false>), grid, block, 0, s, a, b, (int)N, (int)K, x, ldx, (int)M, y, ldy);
   } else {
     if (obf16)
-      hipLaunchKernelGGL((pgemm_kernel<false, true, kPgemmRT>), grid, block, 0, s, a, a, (int)N, (int)K, x, ldx, (int)M, y, ldy);
+      hipLaunchKernelGGL((pgemm_kernel<false, true>), grid, block, 0, s, a, a, (int)N, (int)K, x, ldx, (int)M, y, ldy);
     else
-      hipLaunchKernelGGL((pgemm_kernel<false, false, kPgemmRT>), grid, block, 0, s, a, a, (int)N, (int)K, x, ldx, (int)M, y, ldy);
+      hipLaunchKernelGGL((pgemm_kernel<false, false>), grid, block, 0, s, a, a, (int)N, (int)K, x, ldx, (int)M, y, ldy);
   }
   return launched(fn);
 }
@@ -99,6 +98,8 @@ int check_window_args(const char* fn, const void* packed_a, const void* packed_b
   if (y_dtype != Q4_BF16 && y_dtype != Q4_F32) return fail(Q4_EINVAL, "%s: y_dtype %d is not Q4_BF16 or Q4_F32", fn, y_dtype);
   if (int rc = check_ptr(fn, "y", y, y_dtype == Q4_F32 ? 4 : 2)) return rc;
   if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  if ((int64_t)q4::kPgemmRows * ldx * 2 >= (int64_t(1) << 31))
+    return fail(Q4_EUNSUPPORTED, "%s: ldx=%lld is too large for a 128-row window tile", fn, (long long)ldx);
   return Q4_OK;
 }
 
@@ -196,7 +197,7 @@ int qmm_window(const void* packed_a, const void* packed_b, int64_t N, int64_t K,
                void* y, int y_dtype, int64_t ldy, void* stream) {
   const char* fn = "qmm_window";
   if (int rc = check_window_args(fn, packed_a, packed_b, N, K, x, ldx, y, y_dtype, ldy)) return rc;
-  if (M < 1 || M > 65535LL * kPgemmRT * 16) return fail(Q4_EINVAL, "%s: M=%lld is outside 1..%lld", fn, (long long)M, 65535LL * kPgemmRT * 16);
+  if (M < 1 || M > 65535LL * q4::kPgemmRows) return fail(Q4_EINVAL, "%s: M=%lld is outside 1..%lld", fn, (long long)M, 65535LL * q4::kPgemmRows);
   return qmm_window_impl(fn, packed_a, packed_b, N, K, x, ldx, M, y, y_dtype, ldy, (hipStream_t)stream);
 }
 
@@ -206,7 +207,7 @@ int qmm_cut(const void* packed_a, const void* packed_b, int64_t N, int64_t K, co
   if (int rc = check_window_args(fn, packed_a, packed_b, N, K, x, ldx, y, y_dtype, ldy)) return rc;
   if (window_rows == nullptr || n_windows < 1) return fail(Q4_EINVAL, "%s: need at least one window", fn);
   for (int w = 0; w < n_windows; ++w)
-    if (window_rows[w] < 1 || window_rows[w] > 65535LL * kPgemmRT * 16)
+    if (window_rows[w] < 1 || window_rows[w] > 65535LL * q4::kPgemmRows)
       return fail(Q4_EINVAL, "%s: window %d has %lld rows", fn, w, (long long)window_rows[w]);
   const int64_t es = y_dtype == Q4_F32 ? 4 : 2;
   int64_t row0 = 0;

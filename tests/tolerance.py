@@ -6,14 +6,16 @@ Rounding happens only in additions, so the error of a fixed summation order
 with n roundings is at most gamma_n * A, where A = sum of |products| (the
 oracle's ``error_weight``) and gamma_n <= n * u, with u = 2^-23 (twice the
 float32 unit roundoff, which also covers truncating rather than nearest
-rounding inside a matrix core). The count n for the kernels' order is:
+rounding inside a matrix core). The count n covers both kernel orders:
 
 * up to 64 (bf16 x) or 192 (float32 x split into three exact bf16 pieces)
   roundings inside one 64-wide group's matrix-core dot product, and as many
   for that group's activation sum;
-* 2 roundings per group in the fold acc <- fma(s, P, fma(b, S, acc)),
-  i.e. 2*K/64; up to 4*K/64 allowed so a bias term done on matrix cores fits;
-* one addition per 512-wide k segment when segments are combined;
+* per group: up to 2 roundings in the decode fold
+  acc <- fma(s, P, fma(b, S, acc)), or 1 in the prompt GEMM's fold
+  acc <- fma(s, P, acc) plus up to 4 inside the matrix-core bias product
+  sum_g b_g * S_g (4 slots per group) and its chaining: 6 * K/64 allowed;
+* one addition per 256-wide k segment when segments are combined;
 * 16 of slack.
 
 Denormal flushing adds at most a tiny absolute floor.
@@ -28,8 +30,8 @@ FLOOR = 2.0 ** -100
 def units(K: int, x_dtype: str = "bf16") -> int:
     G = K // 64
     piece = 1 if x_dtype == "bf16" else 3
-    segments = -(-G // 8)
-    return 64 * piece + 4 * G + segments + 16
+    segments = -(-G // 4)
+    return 128 * piece + 6 * G + segments + 16
 
 
 def tol(A: np.ndarray, K: int, x_dtype: str = "bf16") -> np.ndarray:
