@@ -28,6 +28,10 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 constexpr size_t kMaxLds = 64 * 1024;
+// Window GEMM: one column tile's codes (K / 128 pairs of 1 KiB) are addressed
+// with 32-bit offsets.
+constexpr int64_t kPgemmMaxK = int64_t(1) << 20;
+constexpr int64_t kPgemmMaxM = int64_t(1) << 24;
 
 int check_nk(const char* fn, int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || N % 64 != 0 || K % 64 != 0)
@@ -65,26 +69,37 @@ int check_x(const char* fn, const void* x, int x_dtype, int64_t ldx, int64_t K) 
   return Q4_OK;
 }
 
+// Workgroup grid of a window: column blocks x row blocks, as one dimension.
+int64_t pgemm_blocks(int64_t N, int64_t M, bool swiglu, int* nblk, int* mblk) {
+  const int cols = q4::pgemm_cols(swiglu);
+  const int64_t nb = (N + cols - 1) / cols, mb = (M + q4::kPgemmRows - 1) / q4::kPgemmRows;
+  *nblk = (int)nb;
+  *mblk = (int)mb;
+  return nb * mb;
+}
+
 int qmm_window_impl(const char* fn, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x,
                     int64_t ldx, int64_t M, void* y, int y_dtype, int64_t ldy, hipStream_t s) {
   using namespace q4;
   const bool swiglu = packed_b != nullptr;
   const bool obf16 = y_dtype == Q4_BF16;
-  const int cols_per_wg = kPgemmWaves * (swiglu ? 32 : 64);
-  dim3 grid((unsigned)((N + cols_per_wg - 1) / cols_per_wg), (unsigned)((M + kPgemmRows - 1) / kPgemmRows));
-  dim3 block(kPgemmWaves * 64);
+  int nblk, mblk;
+  const int64_t blocks = pgemm_blocks(N, M, swiglu, &nblk, &mblk);
+  if (blocks > INT32_MAX) return fail(Q4_EUNSUPPORTED, "%s: N=%lld x M=%lld needs too many workgroups", fn, (long long)N, (long long)M);
+  dim3 grid((unsigned)blocks), block(kPgemmThreads);
   const uint8_t* a = (const uint8_t*)packed_a;
-  const uint8_t* b = (const uint8_t*)packed_b;
+  const uint8_t* b = swiglu ? (const uint8_t*)packed_b : a;
+  const int n = (int)N, k = (int)K, m = (int)M;
   if (swiglu) {
     if (obf16)
-      hipLaunchKernelGGL((pgemm_kernel<true, true>), grid, block, 0, s, a, b, (int)N, (int)K, x, ldx, (int)M, y, ldy);
+      hipLaunchKernelGGL((pgemm_kernel<true, true>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
     else
-      hipLaunchKernelGGL((pgemm_kernel<true, false>), grid, block, 0, s, a, b, (int)N, (int)K, x, ldx, (int)M, y, ldy);
+      hipLaunchKernelGGL((pgemm_kernel<true, false>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
   } else {
     if (obf16)
-      hipLaunchKernelGGL((pgemm_kernel<false, true>), grid, block, 0, s, a, a, (int)N, (int)K, x, ldx, (int)M, y, ldy);
+      hipLaunchKernelGGL((pgemm_kernel<false, true>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
     else
-      hipLaunchKernelGGL((pgemm_kernel<false, false>), grid, block, 0, s, a, a, (int)N, (int)K, x, ldx, (int)M, y, ldy);
+      hipLaunchKernelGGL((pgemm_kernel<false, false>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
   }
   return launched(fn);
 }
@@ -99,7 +114,8 @@ int check_window_args(const char* fn, const void* packed_a, const void* packed_b
   if (int rc = check_ptr(fn, "y", y, y_dtype == Q4_F32 ? 4 : 2)) return rc;
   if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
   if ((int64_t)q4::kPgemmRows * ldx * 2 >= (int64_t(1) << 31))
-    return fail(Q4_EUNSUPPORTED, "%s: ldx=%lld is too large for a 128-row window tile", fn, (long long)ldx);
+    return fail(Q4_EUNSUPPORTED, "%s: ldx=%lld is too large for a %d-row window tile", fn, (long long)ldx, q4::kPgemmRows);
+  if (K > kPgemmMaxK) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the window GEMM limit of %lld", fn, (long long)K, (long long)kPgemmMaxK);
   return Q4_OK;
 }
 
@@ -197,7 +213,7 @@ int qmm_window(const void* packed_a, const void* packed_b, int64_t N, int64_t K,
                void* y, int y_dtype, int64_t ldy, void* stream) {
   const char* fn = "qmm_window";
   if (int rc = check_window_args(fn, packed_a, packed_b, N, K, x, ldx, y, y_dtype, ldy)) return rc;
-  if (M < 1 || M > 65535LL * q4::kPgemmRows) return fail(Q4_EINVAL, "%s: M=%lld is outside 1..%lld", fn, (long long)M, 65535LL * q4::kPgemmRows);
+  if (M < 1 || M > kPgemmMaxM) return fail(Q4_EINVAL, "%s: M=%lld is outside 1..%lld", fn, (long long)M, (long long)kPgemmMaxM);
   return qmm_window_impl(fn, packed_a, packed_b, N, K, x, ldx, M, y, y_dtype, ldy, (hipStream_t)stream);
 }
 
@@ -207,7 +223,7 @@ int qmm_cut(const void* packed_a, const void* packed_b, int64_t N, int64_t K, co
   if (int rc = check_window_args(fn, packed_a, packed_b, N, K, x, ldx, y, y_dtype, ldy)) return rc;
   if (window_rows == nullptr || n_windows < 1) return fail(Q4_EINVAL, "%s: need at least one window", fn);
   for (int w = 0; w < n_windows; ++w)
-    if (window_rows[w] < 1 || window_rows[w] > 65535LL * q4::kPgemmRows)
+    if (window_rows[w] < 1 || window_rows[w] > kPgemmMaxM)
       return fail(Q4_EINVAL, "%s: window %d has %lld rows", fn, w, (long long)window_rows[w]);
   const int64_t es = y_dtype == Q4_F32 ? 4 : 2;
   int64_t row0 = 0;

@@ -31,10 +31,13 @@
  *   Size: T*P*1152 bytes = 0.5625*N*K bytes for even G.
  *
  * Summation order. Each 64-wide group is reduced on the matrix cores into
- * P_g = sum q*x and S_g = sum x (exact products, float32 sums) and folded as
- * acc = fma(s_g, P_g, fma(b_g, S_g, acc)) in ascending g. Decode calls
- * (qmv_rows, qmv_w13_swiglu) fold each 256-wide k segment from zero and add
- * the segments in ascending order; qmm_window folds one chain over all of K.
+ * P_g = sum q*x and S_g = sum x (exact products, float32 sums). Decode calls
+ * (qmv_rows, qmv_w13_swiglu) fold acc = fma(s_g, P_g, fma(b_g, S_g, acc)) in
+ * ascending g within each 256-wide k segment, from zero, and add the
+ * segments in ascending order. qmm_window folds one chain over all of K:
+ * acc = fma(s_g, P_g, acc) in ascending g, and after every 8 groups (and
+ * after the last) acc = acc + sum over those groups of b_g * S_g, formed on
+ * the matrix cores from the exact bf16 pieces h + m + l = S_g.
  * Each order is a function of K alone: a row's bits never depend on R, on M,
  * on the window cut, on the row's position or on the other rows.
  *
@@ -111,7 +114,8 @@ int qmv_w13_swiglu(const void* packed_w1, const void* packed_w3, int64_t N, int6
  *   paired w1/w3 projections with the SwiGLU epilogue (PR #1514, "What
  *   changes": paired FFN projections keep their rounding boundaries).
  *   y: [M][ldy], y_dtype Q4_F32 or Q4_BF16 (round to nearest even).
- * A row's result does not depend on M, on its offset or on the other rows. */
+ * A row's result does not depend on M, on its offset or on the other rows.
+ * Limits: M <= 2^24, K <= 2^20, 512 * ldx < 2^31 (Q4_EINVAL / Q4_EUNSUPPORTED). */
 int qmm_window(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                int64_t M, void* y, int y_dtype, int64_t ldy, void* stream);
 
