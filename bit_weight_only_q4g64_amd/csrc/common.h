@@ -111,8 +111,28 @@ __device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t voff, uint32_t sof
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
-// SwiGLU gate in float32: silu(a) = a / (1 + exp(-a)), library expf and an
-// IEEE division (no fast-math, no contraction).
-__device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + expf(-a)); }
+// SwiGLU gate in float32: silu(a) = a / (1 + exp(-a)), within 7 * 2^-24
+// relative of the exact value wherever |silu(a)| > 2^-100:
+//   exp(-a) = 2^(t + t_lo) with t + t_lo = -a * log2(e) carried in two
+//   floats (the product's rounding error recovered by an fma, plus the
+//   constant's tail), 2^t on the hardware exp2 (1 ulp), and the tail applied
+//   as e * (1 + t_lo * ln 2) in one fma (|t_lo| <= 2^-17, so the dropped
+//   second-order term is below 2^-35): 3 units;
+//   1 + e: 1 unit; the hardware reciprocal (1 ulp): 2 units; a * r: 1 unit.
+// The exponent argument is clamped to [-80, 88] so nothing overflows: above
+// 88, exp(-a) < 2^-126 and the result is a; below -80 the result is -0,
+// within |a| exp(a) <= 80 exp(-80) < 2^-100 of the exact value.
+__device__ __forceinline__ float silu_f32(float a) {
+  constexpr float kLog2e = 0x1.715476p+0f;      // log2(e) rounded to float
+  constexpr float kLog2eTail = 0x1.4ae0c0p-26f; // log2(e) - kLog2e
+  constexpr float kLn2 = 0x1.62e430p-1f;        // ln(2) rounded to float
+  const float ac = __builtin_amdgcn_fmed3f(a, -80.0f, 88.0f);
+  const float t = -ac * kLog2e;
+  const float t_lo = __builtin_fmaf(-ac, kLog2e, -t) + (-ac) * kLog2eTail;
+  const float e = __builtin_amdgcn_exp2f(t);
+  const float e2 = __builtin_fmaf(e, t_lo * kLn2, e);
+  const float r = a * __builtin_amdgcn_rcpf(1.0f + e2);
+  return a < -80.0f ? -0.0f : r;
+}
 
 }  // namespace q4

