@@ -1,31 +1,37 @@
 // Prefill window GEMM (pgemm) on the matrix cores.
 //
-// A workgroup of 8 waves owns 256 window rows and 16 weight column tiles of
+// A workgroup of 4 waves owns 128 window rows and 16 weight column tiles of
 // 16 columns (256 output columns; SwiGLU: 128 output columns, 8 tiles of w1
-// and the same 8 tiles of w3). Wave w covers rows 128 * (w / 4) .. + 127 and
-// four of the tiles (w % 4 picks which), so each wave holds 8 x 4 output
-// tiles of 16 x 16 in registers.
+// and the same 8 tiles of w3). Wave w covers all 128 rows and 64 weight
+// columns (SwiGLU: 32 columns of w1 and the same 32 of w3), held as 4 x 2
+// output tiles of 32 x 32 for v_mfma_f32_32x32x16_bf16. A workgroup uses
+// 76 KiB of LDS, so two run on each CU: each SIMD then holds one wave of
+// each, and the two drift independently, one issuing matrix work while the
+// other waits at its barrier or converts codes.
 //
 // Operands move from HBM to LDS by buffer-to-LDS DMA, which costs no
-// registers while in flight: the 256 x 64 activation tile of a group in
-// three stages (two groups of lookahead), the codes and scale/bias words of
-// a pair of groups in two stages. One barrier per group. Each wave turns the
-// codes of its four tiles into exact bf16 integers once per group and reuses
-// them for its eight row tiles. The activation sum S_g of a row is formed
-// once per workgroup (each of the four waves sharing a row half forms it for
-// two of the eight row tiles) and shared through LDS.
+// registers while in flight: the 128 x 64 activation tile of a group in two
+// stages (one group of lookahead), the codes and scale/bias words of a pair
+// of groups in two stages. One barrier per group. Each wave turns the codes
+// of its columns into exact bf16 integers once per group and reuses them for
+// its four row tiles. The activation sum S_g of a row is formed once per
+// workgroup (each wave forms it for 32 of the 128 rows) and shared through
+// LDS.
 //
-// Per output (r, n) the order is, with chunks of 8 consecutive groups:
+// Per output (r, n) the order is, with chunks c of 8 consecutive groups:
 //
 //   acc = 0
-//   for each chunk (ascending):
-//     for each group g of the chunk (ascending):
-//       P_g = mfma(x[g, 32..63], q, mfma(x[g, 0..31], q, 0))     exact products
-//       acc = fma(s_g, P_g, acc)                                  one VALU op per output
-//       S_g = sum of x[g, :] on the matrix cores (A = ones)
-//     acc = mfma(A = exact bf16 pieces h, m, l of S_g for the chunk's groups,
-//                B = b_g repeated over the pieces, C = acc)        the bias term
+//   for each group g (ascending):
+//     P_g = four chained 16-wide k steps on the matrix cores       exact products
+//     acc = fma(s_g, P_g, acc)                                    one VALU op per output
+//     S_g = sum of x[g, :] on the matrix cores (A = ones)
+//     if g = 8 (c + 1) for a chunk c:  acc = B_c(acc)
+//   acc = B_c(acc) for the last chunk
 //   y = acc
+//
+// where B_c(acc) = mfma(A = exact bf16 pieces h, m, l of S_g for groups
+// 4..7 of chunk c, B = b_g repeated over the pieces, C = mfma(the same for
+// groups 0..3, C = acc)) adds the chunk's bias term.
 //
 // Nothing in it depends on M, on the row's offset in the window or on the
 // other rows, so a row's bits are the same for every cut of the prompt
@@ -40,22 +46,31 @@
 
 namespace q4 {
 
-constexpr int kPgemmWaves = 8;                  // 2 row halves x 4 column quarters
+constexpr int kPgemmWaves = 4;                  // 4 column quarters
 constexpr int kPgemmThreads = kPgemmWaves * 64;
-constexpr int kPgemmRT = 8;                     // 16-row tiles per wave
-constexpr int kPgemmNT = 4;                     // 16-column weight tiles per wave
-constexpr int kPgemmRows = 256;                 // window rows per workgroup
+constexpr int kPgemmRT = 4;                     // 32-row tiles per wave
+constexpr int kPgemmNT = 2;                     // 32-column tiles per wave (2 weight tiles each)
+constexpr int kPgemmRows = 128;                 // window rows per workgroup
 constexpr int kPgemmSlots = 16;                 // 16-column weight tiles per workgroup
 constexpr int kPgemmChunk = 8;                  // groups per bias chunk
-constexpr int kXStages = 3;
+constexpr int kXStages = 2;
 constexpr int kXRowBytes = kGroup * 2;          // one staged activation row of a group
-constexpr int kXStageBytes = kPgemmRows * kXRowBytes;       // 32 KiB
+constexpr int kXStageBytes = kPgemmRows * kXRowBytes;       // 16 KiB
 constexpr int kCStageBytes = kPgemmSlots * kPairCodeBytes;  // 16 KiB
 constexpr int kSbStageBytes = kPgemmSlots * kPairSbBytes;   // 2 KiB
 constexpr int kSumFloats = 2 * kPgemmRows * kPgemmChunk;    // activation sums, 2 chunks
-static_assert(kPgemmRows == 2 * kPgemmRT * 16, "two row halves of kPgemmRT tiles");
-static_assert(kPgemmSlots == 4 * kPgemmNT, "four column quarters");
+static_assert(kPgemmRows == kPgemmRT * 32, "kPgemmRT row tiles of 32");
+static_assert(kPgemmSlots == 4 * 2 * kPgemmNT, "four column quarters");
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+// D = A B + C on 32 x 32 x 16 bf16: A[i][k] in lane i + 32 (k / 8), element
+// k % 8; B[k][j] in lane j + 32 (k / 8), element k % 8; D[i][j] in lane
+// j + 32 ((i / 4) % 2), element 4 (i / 8) + i % 4.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 static_assert(kPgemmRows * kXRowBytes == kPgemmWaves * 4 * 1024, "each wave stages 4 KiB of a group");
+static_assert(kPgemmSlots == 4 * kPgemmWaves, "each wave stages 4 weight slots");
 
 // Output columns covered by one workgroup.
 __host__ __device__ constexpr int pgemm_cols(bool swiglu) { return swiglu ? 8 * kTileN : kPgemmSlots * kTileN; }
@@ -90,9 +105,8 @@ __device__ __forceinline__ uint32_t lds_addr(T* p) {
 // LDS accesses, then meet the workgroup barrier.
 template <int n>
 __device__ __forceinline__ void dma_wait_barrier() {
-  static_assert(n == 0 || n == 4 || n == 7, "wait depths used by the pipeline");
-  if constexpr (n == 7) asm volatile("s_waitcnt vmcnt(7)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (n == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  static_assert(n == 0 || n == 6, "wait depths used by the pipeline");
+  if constexpr (n == 6) asm volatile("s_waitcnt vmcnt(6)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
@@ -115,7 +129,7 @@ __host__ __device__ inline void pgemm_tile(int b, int nblk, int mblk, int& mb, i
 }
 
 template <bool SWIGLU, bool OUT_BF16>
-__global__ __launch_bounds__(kPgemmThreads, 1) void pgemm_kernel(const uint8_t* __restrict__ pa, const uint8_t* __restrict__ pb,
+__global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_kernel(const uint8_t* __restrict__ pa, const uint8_t* __restrict__ pb,
                                                                   int N, int K, const uint16_t* __restrict__ x, int64_t ldx, int M,
                                                                   void* __restrict__ yv, int64_t ldy, int nblk, int mblk) {
   __shared__ __align__(16) uint8_t xs[kXStages * kXStageBytes];
@@ -125,8 +139,7 @@ __global__ __launch_bounds__(kPgemmThreads, 1) void pgemm_kernel(const uint8_t* 
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int cw = wave & 3, hh = wave >> 2;
-  const int i = lane & 15, kc = lane >> 4;
+  const int cw = wave;
   int mb, nb;
   pgemm_tile(blockIdx.x, nblk, mblk, mb, nb);
   const int m0 = mb * kPgemmRows;
@@ -154,16 +167,22 @@ __global__ __launch_bounds__(kPgemmThreads, 1) void pgemm_kernel(const uint8_t* 
     xvo[u] = (uint32_t)(rc * ldx * 2) + (uint32_t)(xs_slot(r, lane & 7) << 4);
   }
   const uint32_t xs_lds = lds_addr(xs) + wave * 4096;
-  // codes and scale/bias words: wave w stages slots 2w and 2w + 1 (one matrix)
-  const uint8_t* mat = (SWIGLU && wave >= 4) ? pb : pa;
-  const int t0 = clamp_tile(slot_tile(2 * wave)), t1 = clamp_tile(slot_tile(2 * wave + 1));
-  const i32x4 cr0 = make_srsrc(mat + (int64_t)t0 * P * kPairCodeBytes, (uint32_t)P * kPairCodeBytes);
-  const i32x4 cr1 = make_srsrc(mat + (int64_t)t1 * P * kPairCodeBytes, (uint32_t)P * kPairCodeBytes);
-  const i32x4 sr = make_srsrc(mat + cb + (int64_t)t0 * P * kPairSbBytes, (uint32_t)((t1 - t0 + 1) * P * kPairSbBytes));
+  // codes and scale/bias words: wave w stages slots 4w .. 4w + 3, all of one
+  // matrix and (up to the clamp at N) consecutive tiles
+  const uint8_t* mat = (SWIGLU && wave >= 2) ? pb : pa;
+  int tsl[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) tsl[u] = clamp_tile(slot_tile(4 * wave + u));
+  const int t0 = tsl[0];
+  const i32x4 cr = make_srsrc(mat + (int64_t)t0 * P * kPairCodeBytes, (uint32_t)((tsl[3] - t0 + 1) * P * kPairCodeBytes));
+  const i32x4 sr = make_srsrc(mat + cb + (int64_t)t0 * P * kPairSbBytes, (uint32_t)((tsl[3] - t0 + 1) * P * kPairSbBytes));
   const uint32_t cvo = (uint32_t)lane * 16u;
-  const uint32_t svo = (uint32_t)((lane >> 5) * (t1 - t0) * P * kPairSbBytes) + (uint32_t)(lane & 31) * 4u;
-  const uint32_t cs_lds = lds_addr(cs) + 2 * wave * kPairCodeBytes;
-  const uint32_t sb_lds = lds_addr(sbs) + 2 * wave * kPairSbBytes;
+  uint32_t svo[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    svo[u] = (uint32_t)((lane >> 5) * (tsl[2 * u + 1] - tsl[2 * u]) * P * kPairSbBytes) + (uint32_t)(lane & 31) * 4u;
+  const uint32_t cs_lds = lds_addr(cs) + 4 * wave * kPairCodeBytes;
+  const uint32_t sb_lds = lds_addr(sbs) + 4 * wave * kPairSbBytes;
 
   auto issue_x = [&](int g) {
     const uint32_t dst = xs_lds + (uint32_t)(g % kXStages) * kXStageBytes;
@@ -172,53 +191,66 @@ __global__ __launch_bounds__(kPgemmThreads, 1) void pgemm_kernel(const uint8_t* 
   };
   auto issue_c = [&](int p) {
     const uint32_t st = (uint32_t)(p & 1);
-    dma_b128(cr0, cvo, (uint32_t)p * kPairCodeBytes, cs_lds + st * kCStageBytes);
-    dma_b128(cr1, cvo, (uint32_t)p * kPairCodeBytes, cs_lds + st * kCStageBytes + kPairCodeBytes);
-    dma_b32(sr, svo, (uint32_t)p * kPairSbBytes, sb_lds + st * kSbStageBytes);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      dma_b128(cr, cvo, (uint32_t)((tsl[u] - t0) * P + p) * kPairCodeBytes, cs_lds + st * kCStageBytes + u * kPairCodeBytes);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      dma_b32(sr, svo[u], (uint32_t)((tsl[2 * u] - t0) * P + p) * kPairSbBytes, sb_lds + st * kSbStageBytes + 2 * u * kPairSbBytes);
   };
 
   // ---- consumer set-up ---------------------------------------------------
-  int cslot[kPgemmNT];
+  // 32 x 32 fragments: lane = j + 32 hl; j is the row (A) or column (B, D)
+  // of the tile, hl the 8-wide k half of a 16-wide step
+  const int j = lane & 31, hl = lane >> 5, jj = j & 15;
+  // column tile s: weight slot of this lane's column (two 16-column slots)
+  int lslot[kPgemmNT];
 #pragma unroll
-  for (int s = 0; s < kPgemmNT; ++s) cslot[s] = SWIGLU ? (s < 2 ? 2 * cw + s : 8 + 2 * cw + (s - 2)) : kPgemmNT * cw + s;
-  const int rbase = hh * (kPgemmRows / 2);
-  // a wave computes only where its row half meets the window; every wave of
-  // a live half forms its share of the activation sums
-  const bool live = rbase < mt;
+  for (int s = 0; s < kPgemmNT; ++s) lslot[s] = (SWIGLU ? (s == 0 ? 2 * cw : 8 + 2 * cw) : 4 * cw + 2 * s) + (j >> 4);
+  constexpr int rbase = 0;
 
-  f32x4 acc[kPgemmRT][kPgemmNT];
+  f32x16 acc[kPgemmRT][kPgemmNT];
 #pragma unroll
   for (int rt = 0; rt < kPgemmRT; ++rt)
 #pragma unroll
-    for (int s = 0; s < kPgemmNT; ++s) acc[rt][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // raw scale/bias words of groups 2*kc, 2*kc+1 of the current chunk
-  uint32_t bsel[kPgemmNT][2];
+    for (int s = 0; s < kPgemmNT; ++s)
 #pragma unroll
-  for (int s = 0; s < kPgemmNT; ++s) bsel[s][0] = bsel[s][1] = 0u;
+      for (int r = 0; r < 16; ++r) acc[rt][s][r] = 0.f;
+  // raw scale/bias words of this lane's column for the groups its bias
+  // operand carries: 4 m + 2 hl + e (e = 0, 1) of the current chunk, m = 0, 1
+  uint32_t bsel[kPgemmNT][2][2];
+#pragma unroll
+  for (int s = 0; s < kPgemmNT; ++s) bsel[s][0][0] = bsel[s][0][1] = bsel[s][1][0] = bsel[s][1][1] = 0u;
 
   // the bias term of chunk c on the matrix cores, added into acc
   auto bias_chunk = [&](int c) {
     const float* sp = ssum + (c & 1) * kPgemmRows * kPgemmChunk;
-    const bool v0 = kPgemmChunk * c + 2 * kc < G, v1 = kPgemmChunk * c + 2 * kc + 1 < G;
-    bf16x8 bfr[kPgemmNT];
+    bf16x8 bfr[kPgemmNT][2];
 #pragma unroll
-    for (int s = 0; s < kPgemmNT; ++s) {
-      const uint32_t b0 = bsel[s][0] >> 16, b1 = bsel[s][1] >> 16;
-      bfr[s] = __builtin_bit_cast(bf16x8, u32x4{b0 | (b0 << 16), b0, b1 | (b1 << 16), b1});
-      bsel[s][0] = bsel[s][1] = 0u;
-    }
+    for (int s = 0; s < kPgemmNT; ++s)
 #pragma unroll
-    for (int rt = 0; rt < kPgemmRT; ++rt) {
-      const int row = rbase + rt * 16 + i;
-      const float2 S2 = *(const float2*)(sp + row * kPgemmChunk + 2 * kc);
-      // groups past K hold no sum in this chunk; their slots must be zero
-      const float s0 = v0 ? S2.x : 0.f, s1 = v1 ? S2.y : 0.f;
-      uint32_t h0, mm0, l0, h1, mm1, l1;
-      split3(s0, h0, mm0, l0);
-      split3(s1, h1, mm1, l1);
-      const bf16x8 afr = __builtin_bit_cast(bf16x8, u32x4{h0 | (mm0 << 16), l0, h1 | (mm1 << 16), l1});
+      for (int m = 0; m < 2; ++m) {
+        const uint32_t b0 = bsel[s][m][0] >> 16, b1 = bsel[s][m][1] >> 16;
+        bfr[s][m] = __builtin_bit_cast(bf16x8, u32x4{b0 | (b0 << 16), b0, b1 | (b1 << 16), b1});
+        bsel[s][m][0] = bsel[s][m][1] = 0u;
+      }
 #pragma unroll
-      for (int s = 0; s < kPgemmNT; ++s) acc[rt][s] = mfma16(afr, bfr[s], acc[rt][s]);
+    for (int m = 0; m < 2; ++m) {
+      const int g0 = kPgemmChunk * c + 4 * m + 2 * hl;
+      const bool v0 = g0 < G, v1 = g0 + 1 < G;
+#pragma unroll
+      for (int rt = 0; rt < kPgemmRT; ++rt) {
+        const int row = rbase + rt * 32 + j;
+        const float2 S2 = *(const float2*)(sp + row * kPgemmChunk + 4 * m + 2 * hl);
+        // groups past K hold no sum in this chunk; their slots must be zero
+        const float s0 = v0 ? S2.x : 0.f, s1 = v1 ? S2.y : 0.f;
+        uint32_t h0, mm0, l0, h1, mm1, l1;
+        split3(s0, h0, mm0, l0);
+        split3(s1, h1, mm1, l1);
+        const bf16x8 afr = __builtin_bit_cast(bf16x8, u32x4{h0 | (mm0 << 16), l0, h1 | (mm1 << 16), l1});
+#pragma unroll
+        for (int s = 0; s < kPgemmNT; ++s) acc[rt][s] = mfma32(afr, bfr[s][m], acc[rt][s]);
+      }
     }
   };
 
@@ -230,104 +262,122 @@ __global__ __launch_bounds__(kPgemmThreads, 1) void pgemm_kernel(const uint8_t* 
     const uint8_t* cb0 = cs + (p & 1) * kCStageBytes;
     const uint8_t* sb0 = sbs + (p & 1) * kSbStageBytes;
 
-    if constexpr (gh == 0) {
-      if (gg == 0 && g > 0) bias_chunk(g / kPgemmChunk - 1);
-    }
-
-    bf16x8 q[kPgemmNT][2];
+    // codes of this lane's column: k steps 0 and 2 at word 2 gh and 2 gh + 1
+    // of lane jj + 16 hl of the pair block, steps 1 and 3 at lane jj + 32 + 16 hl
+    u32x2 c02[kPgemmNT], c13[kPgemmNT];
+    uint32_t w[kPgemmNT];
     float sc[kPgemmNT];
 #pragma unroll
     for (int s = 0; s < kPgemmNT; ++s) {
-      const uint32_t w = *(const uint32_t*)(sb0 + cslot[s] * kPairSbBytes + i * 8 + gh * 4);
-      sc[s] = bf16_lo(w);
-      if (kc == (gg >> 1)) bsel[s][gh] = w;
-      const u32x2 cwd = *(const u32x2*)(cb0 + cslot[s] * kPairCodeBytes + lane * 16 + gh * 8);
-      q[s][0] = codes_to_bf16(cwd[0]);
-      q[s][1] = codes_to_bf16(cwd[1]);
+      w[s] = *(const uint32_t*)(sb0 + lslot[s] * kPairSbBytes + jj * 8 + gh * 4);
+      sc[s] = bf16_lo(w[s]);
+      const uint8_t* cl = cb0 + lslot[s] * kPairCodeBytes + (jj + 16 * hl) * 16 + gh * 8;
+      c02[s] = *(const u32x2*)cl;
+      c13[s] = *(const u32x2*)(cl + 512);
     }
 
-    // activation sums of this wave's share of the row tiles
-    float* sw = ssum + ((g / kPgemmChunk) & 1) * kPgemmRows * kPgemmChunk + gg;
+    // activation sums of this wave's 32 of the 128 rows (16 x 16 tiles)
+    {
+      const int i = lane & 15, kc = lane >> 4;
+      float* sw = ssum + ((g / kPgemmChunk) & 1) * kPgemmRows * kPgemmChunk + gg;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int row = rbase + (2 * cw + u) * 16 + i;
-      const bf16x8 xa0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc)));
-      const bf16x8 xa1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc + 4)));
-      f32x4 S = mfma16(ones, xa0, f32x4{0.f, 0.f, 0.f, 0.f});
-      S = mfma16(ones, xa1, S);
-      if (kc == 0) sw[row * kPgemmChunk] = S[0];
+      for (int u = 0; u < 2; ++u) {
+        const int row = rbase + 32 * cw + 16 * u + i;
+        const bf16x8 xa0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc)));
+        const bf16x8 xa1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc + 4)));
+        f32x4 S = mfma16(ones, xa0, f32x4{0.f, 0.f, 0.f, 0.f});
+        S = mfma16(ones, xa1, S);
+        if (kc == 0) sw[row * kPgemmChunk] = S[0];
+      }
     }
 
+    bf16x8 q[kPgemmNT][4];
+#pragma unroll
+    for (int s = 0; s < kPgemmNT; ++s) {
+      q[s][0] = codes_to_bf16(c02[s][0]);
+      q[s][2] = codes_to_bf16(c02[s][1]);
+      q[s][1] = codes_to_bf16(c13[s][0]);
+      q[s][3] = codes_to_bf16(c13[s][1]);
+    }
 #pragma unroll
     for (int rt = 0; rt < kPgemmRT; ++rt) {
-      const int row = rbase + rt * 16 + i;
-      const bf16x8 xa0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc)));
-      const bf16x8 xa1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc + 4)));
+      const int row = rbase + rt * 32 + j;
+      bf16x8 xa[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) xa[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, 2 * ks + hl)));
 #pragma unroll
       for (int s = 0; s < kPgemmNT; ++s) {
-        f32x4 Pm = mfma16(xa0, q[s][0], f32x4{0.f, 0.f, 0.f, 0.f});
-        Pm = mfma16(xa1, q[s][1], Pm);
+        f32x16 Pm = mfma32(xa[0], q[s][0], f32x16{});
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[rt][s][v] = __builtin_fmaf(sc[s], Pm[v], acc[rt][s][v]);
+        for (int ks = 1; ks < 4; ++ks) Pm = mfma32(xa[ks], q[s][ks], Pm);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[rt][s][r] = __builtin_fmaf(sc[s], Pm[r], acc[rt][s][r]);
       }
+    }
+
+    // the previous chunk's bias term follows the fold of its next chunk's
+    // first group (its sums are visible since this group's barrier); only
+    // then does this group's bias word join the new chunk's operand
+    if constexpr (gh == 0) {
+      if (gg == 0 && g > 0) bias_chunk(g / kPgemmChunk - 1);
+    }
+    const bool take = ((gg >> 1) & 1) == hl;
+#pragma unroll
+    for (int s = 0; s < kPgemmNT; ++s) {
+      if (take && gg < 4) bsel[s][0][gh] = w[s];
+      if (take && gg >= 4) bsel[s][1][gh] = w[s];
     }
   };
 
   // ---- pipeline ------------------------------------------------------------
-  // In flight at the top of group g is what was issued during group g - 1:
-  // the activations of group g + 1 (4 loads) and, when g is odd, the weights
-  // of the next pair (3 loads). Everything older has landed once the wave's
-  // vmcnt is that low; the barrier then makes every wave's stage visible and
-  // frees the stage the next DMA overwrites (read during group g - 1).
+  // During group g the wave issues the activations of group g + 1 (4 loads)
+  // and, when g is even, then the weights of the next pair (6 loads). At the
+  // top of group g everything but those weights must have landed: vmcnt(6)
+  // after an even group that issued them, vmcnt(0) otherwise; the barrier
+  // then makes every wave's stage visible and frees the stages the next DMA
+  // overwrites (read during group g - 1).
   issue_x(0);
   issue_c(0);
-  if (G > 1) issue_x(1);
   for (int p = 0; p < P; ++p) {
     const int g = 2 * p;
-    if (g + 1 < G) dma_wait_barrier<4>();
-    else dma_wait_barrier<0>();
-    if (g + 2 < G) issue_x(g + 2);
+    dma_wait_barrier<0>();
+    if (g + 1 < G) issue_x(g + 1);
     if (p + 1 < P) issue_c(p + 1);
-    if (live) group(g, std::integral_constant<int, 0>{});
+    group(g, std::integral_constant<int, 0>{});
     if (g + 1 < G) {
-      // p + 1 < P implies g + 2 < G
-      if (p + 1 < P) dma_wait_barrier<7>();
-      else if (g + 2 < G) dma_wait_barrier<4>();
+      if (p + 1 < P) dma_wait_barrier<6>();
       else dma_wait_barrier<0>();
-      if (g + 3 < G) issue_x(g + 3);
-      if (live) group(g + 1, std::integral_constant<int, 1>{});
+      if (g + 2 < G) issue_x(g + 2);
+      group(g + 1, std::integral_constant<int, 1>{});
     }
   }
   dma_wait_barrier<0>();  // the last group's sums from every wave
-  if (!live) return;
   bias_chunk((G - 1) / kPgemmChunk);
 
-  // ---- epilogue: lane holds rows m0 + rbase + rt*16 + 4*kc + v of column i of each tile
+  // ---- epilogue: element r of tile (rt, s) is row rbase + 32 rt + 8 (r / 4)
+  // + 4 hl + r % 4, column jj of the lane's weight slot
 #pragma unroll
   for (int rt = 0; rt < kPgemmRT; ++rt) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = rbase + rt * 16 + 4 * kc + v;
+    for (int r = 0; r < 16; ++r) {
+      const int row = rbase + rt * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
       if (row >= mt) continue;
       const int64_t yrow = (int64_t)(m0 + row) * ldy;
       if constexpr (SWIGLU) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int t = slot_tile(cslot[s]);
-          if (t >= ntiles) continue;
-          const float z = silu_f32(acc[rt][s][v]) * acc[rt][s + 2][v];
-          const int64_t at = yrow + (int64_t)t * kTileN + i;
-          if constexpr (OUT_BF16) ((uint16_t*)yv)[at] = f32_to_bf16_rne(z);
-          else ((float*)yv)[at] = z;
-        }
+        const int t = slot_tile(lslot[0]);
+        if (t >= ntiles) continue;
+        const float z = silu_f32(acc[rt][0][r]) * acc[rt][1][r];
+        const int64_t at = yrow + (int64_t)t * kTileN + jj;
+        if constexpr (OUT_BF16) ((uint16_t*)yv)[at] = f32_to_bf16_rne(z);
+        else ((float*)yv)[at] = z;
       } else {
 #pragma unroll
         for (int s = 0; s < kPgemmNT; ++s) {
-          const int t = slot_tile(cslot[s]);
+          const int t = slot_tile(lslot[s]);
           if (t >= ntiles) continue;
-          const int64_t at = yrow + (int64_t)t * kTileN + i;
-          if constexpr (OUT_BF16) ((uint16_t*)yv)[at] = f32_to_bf16_rne(acc[rt][s][v]);
-          else ((float*)yv)[at] = acc[rt][s][v];
+          const int64_t at = yrow + (int64_t)t * kTileN + jj;
+          if constexpr (OUT_BF16) ((uint16_t*)yv)[at] = f32_to_bf16_rne(acc[rt][s][r]);
+          else ((float*)yv)[at] = acc[rt][s][r];
         }
       }
     }
