@@ -275,14 +275,32 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
     for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
       for (int v = 0; v < kPerLane; ++v) tot[m][rt][v] = part[((m * kRT + rt) * kPerLane + v) * 64 + lane];
-  for (int seg = 1; seg < nseg; ++seg)
+  // partials are read eight segments at a time (all reads in flight
+  // together), then added one segment after another
+  constexpr int kSumBatch = 8;
+  for (int seg0 = 1; seg0 < nseg; seg0 += kSumBatch) {
+    float pv[kSumBatch][NMAT][kRT][kPerLane];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+    for (int b = 0; b < kSumBatch; ++b) {
+      const int seg = seg0 + b < nseg ? seg0 + b : nseg - 1;
 #pragma unroll
-      for (int rt = 0; rt < kRT; ++rt)
+      for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int v = 0; v < kPerLane; ++v)
-          tot[m][rt][v] = tot[m][rt][v] + part[(((seg * NMAT + m) * kRT + rt) * kPerLane + v) * 64 + lane];
+        for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+          for (int v = 0; v < kPerLane; ++v) pv[b][m][rt][v] = part[(((seg * NMAT + m) * kRT + rt) * kPerLane + v) * 64 + lane];
+    }
+#pragma unroll
+    for (int b = 0; b < kSumBatch; ++b) {
+      if (seg0 + b >= nseg) break;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+          for (int v = 0; v < kPerLane; ++v) tot[m][rt][v] = tot[m][rt][v] + pv[b][m][rt][v];
+    }
+  }
 
   const int64_t n = (int64_t)t * kTileN + i;
 #pragma unroll
