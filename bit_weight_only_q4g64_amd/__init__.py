@@ -35,6 +35,8 @@ _SIGNATURES = {
     "qmv_w13_swiglu": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
     "qmm_window": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P]),
     "qmm_cut": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _I64, _P]),
+    "q4g64_ffn_work_bytes": (ctypes.c_size_t, [_I64, ctypes.c_int]),
+    "qmv_ffn": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P, _I64, _P, _P]),
     "q4_last_error": (ctypes.c_char_p, []),
 }
 
@@ -199,3 +201,42 @@ def qmm_cut(pa: torch.Tensor, pb: torch.Tensor | None, N: int, K: int, x: torch.
                       len(windows), y.data_ptr(), _out_dtype(y.dtype), _rowmajor(y, "y"), _stream()),
     )
     return y
+
+
+def ffn_work_bytes(N1: int, R: int) -> int:
+    return int(lib().q4g64_ffn_work_bytes(N1, R))
+
+
+def ffn_workspace(N1: int, R: int, device="cuda") -> torch.Tensor:
+    """A zeroed workspace for qmv_ffn (reusable across calls with N1' <= N1, R' <= R)."""
+    nbytes = ffn_work_bytes(N1, R)
+    if nbytes == 0:
+        raise Q4Error("q4g64_ffn_work_bytes", Q4_EINVAL, f"invalid N1={N1} R={R}")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def ffn_error(work: torch.Tensor) -> int:
+    """The workspace's barrier error word (1 if a workgroup gave up waiting)."""
+    return int(work[8:12].view(torch.int32).item())
+
+
+def qmv_ffn(p1: torch.Tensor, p3: torch.Tensor, p2: torch.Tensor, N1: int, K1: int, N2: int, x: torch.Tensor, work: torch.Tensor,
+            z: torch.Tensor | None = None, y: torch.Tensor | None = None):
+    """Decode FFN step in one launch: z = silu(W1 x) * (W3 x), y = W2 z (float32), for the 1..16 bf16 rows of x."""
+    for t, name in ((p1, "packed_w1"), (p3, "packed_w3"), (p2, "packed_w2"), (x, "x"), (work, "work")):
+        _dev(t, name)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    R = x.shape[0]
+    if work.numel() < ffn_work_bytes(N1, R):
+        raise ValueError("work is smaller than ffn_work_bytes(N1, R)")
+    if z is None:
+        z = torch.empty((R, N1), dtype=torch.float32, device=x.device)
+    if y is None:
+        y = torch.empty((R, N2), dtype=torch.float32, device=x.device)
+    _check(
+        "qmv_ffn",
+        lib().qmv_ffn(p1.data_ptr(), p3.data_ptr(), p2.data_ptr(), N1, K1, N2, x.data_ptr(), _rowmajor(x, "x"), R, z.data_ptr(),
+                      _rowmajor(z, "z"), y.data_ptr(), _rowmajor(y, "y"), work.data_ptr(), _stream()),
+    )
+    return z, y

@@ -7,6 +7,7 @@
 #include <stdio.h>
 
 #include "common.h"
+#include "ffn.h"
 #include "pack.h"
 #include "pgemm.h"
 #include "qmv.h"
@@ -117,6 +118,46 @@ int check_window_args(const char* fn, const void* packed_a, const void* packed_b
     return fail(Q4_EUNSUPPORTED, "%s: ldx=%lld is too large for a %d-row window tile", fn, (long long)ldx, q4::kPgemmRows);
   if (K > kPgemmMaxK) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the window GEMM limit of %lld", fn, (long long)K, (long long)kPgemmMaxK);
   return Q4_OK;
+}
+
+template <int NV, int RTF, int SPW1, int SPW2>
+int ffn_launch_t(const uint8_t* p1, const uint8_t* p3, const uint8_t* p2, int N1, int K1, int N2, const uint16_t* x,
+                 int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, uint8_t* work, size_t lds, hipStream_t s) {
+  const int xl2 = q4::ffn_lds_bytes(K1, N1, R, true) <= q4::qmv_max_lds();
+  lds = q4::ffn_lds_bytes(K1, N1, R, xl2 != 0);
+  auto kern = q4::ffn_kernel<NV, RTF, SPW1, SPW2>;
+  static const bool lds_ok =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)q4::qmv_max_lds()) == hipSuccess;
+  (void)lds_ok;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, q4::kFfnThreads, lds) != hipSuccess)
+    return fail(Q4_EDEVICE, "qmv_ffn: device query failed");
+  if (per_cu < 1) return fail(Q4_EUNSUPPORTED, "qmv_ffn: a %zu-byte workgroup does not fit on a CU", lds);
+  // every workgroup must be resident at once (the grid barrier waits for all)
+  const int pairs1 = (N1 / q4::kTileN + 1) / 2, items2 = 2 * (N2 / q4::kTileN);
+  int nwg = cus;
+  if (nwg > (pairs1 > items2 ? pairs1 : items2)) nwg = pairs1 > items2 ? pairs1 : items2;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(q4::kFfnThreads), lds, s, p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work,
+                     xl2);
+  return launched("qmv_ffn");
+}
+
+template <int NV, int RTF, int SPW1>
+int ffn_launch_s2(int spw2, const uint8_t* p1, const uint8_t* p3, const uint8_t* p2, int N1, int K1, int N2, const uint16_t* x,
+                  int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, uint8_t* work, size_t lds, hipStream_t s) {
+  if (spw2 <= 1) return ffn_launch_t<NV, RTF, SPW1, 1>(p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
+  if (spw2 <= 2) return ffn_launch_t<NV, RTF, SPW1, 2>(p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
+  return ffn_launch_t<NV, RTF, SPW1, 4>(p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
+}
+
+template <int NV, int RTF>
+int ffn_launch_s1(int spw1, int spw2, const uint8_t* p1, const uint8_t* p3, const uint8_t* p2, int N1, int K1, int N2,
+                  const uint16_t* x, int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, uint8_t* work, size_t lds,
+                  hipStream_t s) {
+  if (spw1 <= 1) return ffn_launch_s2<NV, RTF, 1>(spw2, p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
+  if (spw1 <= 2) return ffn_launch_s2<NV, RTF, 2>(spw2, p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
+  return ffn_launch_s2<NV, RTF, 4>(spw2, p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
 }
 
 }  // namespace
@@ -235,6 +276,47 @@ int qmm_cut(const void* packed_a, const void* packed_b, int64_t N, int64_t K, co
     row0 += window_rows[w];
   }
   return Q4_OK;
+}
+
+size_t q4g64_ffn_work_bytes(int64_t N1, int R) {
+  if (N1 <= 0 || N1 % 64 != 0 || N1 > q4::kQmvMaxK || R < 1 || R > 16) return 0;
+  return q4::ffn_work_bytes(N1, R);
+}
+
+int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2, int64_t N1, int64_t K1, int64_t N2,
+            const uint16_t* x, int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, void* work, void* stream) {
+  const char* fn = "qmv_ffn";
+  if (int rc = check_nk(fn, N1, K1)) return rc;
+  if (int rc = check_nk(fn, N2, N1)) return rc;
+  if (R < 1 || R > 16) return fail(Q4_EINVAL, "%s: R=%d is outside 1..16", fn, R);
+  if (int rc = check_ptr(fn, "packed_w1", packed_w1, 16)) return rc;
+  if (int rc = check_ptr(fn, "packed_w3", packed_w3, 16)) return rc;
+  if (int rc = check_ptr(fn, "packed_w2", packed_w2, 16)) return rc;
+  if (int rc = check_x(fn, x, Q4_BF16, ldx, K1)) return rc;
+  if (int rc = check_ptr(fn, "z", z, 4)) return rc;
+  if (int rc = check_ptr(fn, "y", y, 4)) return rc;
+  if (int rc = check_ptr(fn, "work", work, 256)) return rc;
+  if (ldz < N1) return fail(Q4_EINVAL, "%s: ldz=%lld < N1=%lld", fn, (long long)ldz, (long long)N1);
+  if (ldy < N2) return fail(Q4_EINVAL, "%s: ldy=%lld < N2=%lld", fn, (long long)ldy, (long long)N2);
+  if ((int64_t)R * ldx * 2 >= (int64_t(1) << 31))
+    return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
+  // 8 waves per w1/w3 tile and 16 per w2 half-tile, up to 4 segments each
+  if (K1 > q4::kQmvMaxK / 2) return fail(Q4_EUNSUPPORTED, "%s: K1=%lld exceeds the fused decode limit of 8192", fn, (long long)K1);
+  if (N1 > q4::kQmvMaxK) return fail(Q4_EUNSUPPORTED, "%s: N1=%lld exceeds the decode limit of 16384", fn, (long long)N1);
+  const size_t lds = q4::ffn_lds_bytes(K1, N1, R, false);
+  if (lds > q4::qmv_max_lds()) return fail(Q4_EUNSUPPORTED, "%s: K1=%lld with R=%d needs %zu bytes of LDS", fn, (long long)K1, R, lds);
+  const int nseg1 = q4::qmv_segments(K1), nseg2 = q4::qmv_segments(N1);
+  const int spw1 = (nseg1 + q4::kFfnP1Waves - 1) / q4::kFfnP1Waves, spw2 = (nseg2 + q4::kFfnWaves - 1) / q4::kFfnWaves;
+  const uint8_t *a = (const uint8_t*)packed_w1, *c = (const uint8_t*)packed_w3, *d = (const uint8_t*)packed_w2;
+  uint8_t* w = (uint8_t*)work;
+  hipStream_t s = (hipStream_t)stream;
+  const int n1 = (int)N1, k1 = (int)K1, n2 = (int)N2;
+  const int nv = q4::qmv_nv(R), rtf = q4::qmv_row_tiles(1, R);
+  if (nv == 1) return ffn_launch_s1<1, 1>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
+  if (nv == 2) return ffn_launch_s1<2, 1>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
+  if (rtf == 1) return ffn_launch_s1<4, 1>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
+  if (rtf == 2) return ffn_launch_s1<4, 2>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
+  return ffn_launch_s1<4, 4>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
 }
 
 }  // extern "C"

@@ -52,6 +52,138 @@ __host__ __device__ inline size_t qmv_xs_bytes(int64_t K, int xf32, int R) {
   return (size_t)(xf32 ? 3 : 1) * R * qmv_xs_stride(K) * sizeof(uint16_t);
 }
 
+// Weight registers of one wave's segments of one column tile (codes: one
+// 128-bit word per lane per pair; scale/bias: one 64-bit word per pair).
+template <int NMAT, int SPW>
+struct QmvWeights {
+  u32x4 cw[SPW][NMAT][kSegPairs];
+  u32x2 sbw[SPW][NMAT][kSegPairs];
+};
+
+// Issue every weight load of segments seg0 + j * step (j < SPW). Pair indices
+// past the matrix are clamped to its last pair (those values are never
+// used). Lanes with on == false load nothing and hold zero codes.
+template <int NMAT, int SPW>
+__device__ __forceinline__ void qmv_issue_weights(QmvWeights<NMAT, SPW>& w, const rsrc_t (&cres)[NMAT], const rsrc_t (&sres)[NMAT],
+                                                  int seg0, int step, int P, int lane, bool on) {
+  const int i = lane & 15;
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int seg = seg0 + j * step;
+#pragma unroll
+    for (int pp = 0; pp < kSegPairs; ++pp) {
+      int p = seg * kSegPairs + pp;
+      p = p < P ? p : P - 1;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        if (on) {
+          w.cw[j][m][pp] = buf_load16(cres[m], (uint32_t)lane * 16u, (uint32_t)p * kPairCodeBytes);
+          w.sbw[j][m][pp] = buf_load8(sres[m], (uint32_t)i * 8u, (uint32_t)p * kPairSbBytes);
+        } else {
+          w.cw[j][m][pp] = u32x4{0u, 0u, 0u, 0u};
+          w.sbw[j][m][pp] = u32x2{0u, 0u};
+        }
+      }
+    }
+  }
+}
+
+// Fold the groups of one segment (g0 .. g0 + kSegGroups - 1, those below G)
+// into acc, from zero. xfrag(rt, g, hh) returns this lane's activation
+// fragment of row tile rt, group g, half hh. This is the decode order:
+//   P = mfma(x[g, 32..63], q, mfma(x[g, 0..31], q, 0))
+//   S = the same with q replaced by ones
+//   acc = fma(s_g, P, fma(b_g, S, acc))
+// with float32 rows combining their three pieces in-lane first.
+template <int XF32, int NMAT, int kRT, int kPerLane, typename XF>
+__device__ __forceinline__ void qmv_fold_segment(float (&acc)[NMAT][kRT][kPerLane], const u32x4 (&cw)[NMAT][kSegPairs],
+                                                 const u32x2 (&sbw)[NMAT][kSegPairs], int g0, int G, const XF& xfrag) {
+  const bf16x8 ones = ones_bf16x8();
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+      for (int v = 0; v < kPerLane; ++v) acc[m][rt][v] = 0.f;
+#pragma unroll
+  for (int gg = 0; gg < kSegGroups; ++gg) {
+    const int g = g0 + gg;
+    if (g >= G) break;
+    const int pp = gg >> 1, gh = gg & 1;
+    bf16x8 q[NMAT][2];
+    float sc[NMAT], bs[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      q[m][0] = codes_to_bf16(gh ? cw[m][pp][2] : cw[m][pp][0]);
+      q[m][1] = codes_to_bf16(gh ? cw[m][pp][3] : cw[m][pp][1]);
+      const uint32_t w = gh ? sbw[m][pp][1] : sbw[m][pp][0];
+      sc[m] = bf16_lo(w);
+      bs[m] = bf16_hi(w);
+    }
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      const bf16x8 xa0 = xfrag(rt, g, 0), xa1 = xfrag(rt, g, 1);
+      f32x4 S = mfma16(xa0, ones, f32x4{0.f, 0.f, 0.f, 0.f});
+      S = mfma16(xa1, ones, S);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        f32x4 Pm = mfma16(xa0, q[m][0], f32x4{0.f, 0.f, 0.f, 0.f});
+        Pm = mfma16(xa1, q[m][1], Pm);
+        if constexpr (!XF32) {
+#pragma unroll
+          for (int v = 0; v < kPerLane; ++v) acc[m][rt][v] = __builtin_fmaf(sc[m], Pm[v], __builtin_fmaf(bs[m], S[v], acc[m][rt][v]));
+        } else {
+          const float Pr = (Pm[0] + Pm[1]) + Pm[2];
+          const float Sr = (S[0] + S[1]) + S[2];
+          acc[m][rt][0] = __builtin_fmaf(sc[m], Pr, __builtin_fmaf(bs[m], Sr, acc[m][rt][0]));
+        }
+      }
+    }
+  }
+}
+
+// Segment partials in LDS: [segment][matrix][row tile][per lane][lane].
+template <int NMAT, int kRT, int kPerLane>
+__device__ __forceinline__ int qmv_part_index(int seg, int m, int rt, int v, int lane) {
+  return (((seg * NMAT + m) * kRT + rt) * kPerLane + v) * 64 + lane;
+}
+
+// The segments' partials added in ascending order (read eight segments at a
+// time so the reads are in flight together).
+template <int NMAT, int kRT, int kPerLane>
+__device__ __forceinline__ void qmv_ordered_sum(float (&tot)[NMAT][kRT][kPerLane], const float* part, int nseg, int lane) {
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+      for (int v = 0; v < kPerLane; ++v) tot[m][rt][v] = part[qmv_part_index<NMAT, kRT, kPerLane>(0, m, rt, v, lane)];
+  constexpr int kSumBatch = 8;
+  for (int seg0 = 1; seg0 < nseg; seg0 += kSumBatch) {
+    float pv[kSumBatch][NMAT][kRT][kPerLane];
+#pragma unroll
+    for (int b = 0; b < kSumBatch; ++b) {
+      const int seg = seg0 + b < nseg ? seg0 + b : nseg - 1;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+          for (int v = 0; v < kPerLane; ++v) pv[b][m][rt][v] = part[qmv_part_index<NMAT, kRT, kPerLane>(seg, m, rt, v, lane)];
+    }
+#pragma unroll
+    for (int b = 0; b < kSumBatch; ++b) {
+      if (seg0 + b >= nseg) break;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+          for (int v = 0; v < kPerLane; ++v) tot[m][rt][v] = tot[m][rt][v] + pv[b][m][rt][v];
+    }
+  }
+}
+
 // XF32 = 0: bf16 x, one row tile of 16 rows.  XF32 = 1: float32 x, RTF row
 // tiles of 4 rows x 3 pieces.  NMAT = 1: y = W x.  NMAT = 2: y = silu(W1 x) * (W3 x).
 // SPW: maximum segments per wave.  XLDS: activations staged in LDS once per
@@ -81,7 +213,6 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   const int64_t cb = codes_bytes(N, K);
   const int xsi = (int)qmv_xs_stride(K);
   const uint32_t xrow = (uint32_t)(ldx * kXElem);  // bytes per activation row
-  const bf16x8 ones = ones_bf16x8();
 
   // buffer resources: this column tile's codes and scale/bias, and x
   rsrc_t cres[NMAT], sres[NMAT];
@@ -117,24 +248,9 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
     }
   }
 
-  // 2) every weight load of this wave's segments (pair indices past the
-  //    matrix are clamped to its last pair; those values are never used)
-  u32x4 cw[SPW][NMAT][kSegPairs];
-  u32x2 sbw[SPW][NMAT][kSegPairs];
-#pragma unroll
-  for (int j = 0; j < SPW; ++j) {
-    const int seg = wave + j * nwaves;
-#pragma unroll
-    for (int pp = 0; pp < kSegPairs; ++pp) {
-      int p = seg * kSegPairs + pp;
-      p = p < P ? p : P - 1;
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m) {
-        cw[j][m][pp] = buf_load16(cres[m], (uint32_t)lane * 16u, (uint32_t)p * kPairCodeBytes);
-        sbw[j][m][pp] = buf_load8(sres[m], (uint32_t)i * 8u, (uint32_t)p * kPairSbBytes);
-      }
-    }
-  }
+  // 2) every weight load of this wave's segments
+  QmvWeights<NMAT, SPW> wts;
+  qmv_issue_weights<NMAT, SPW>(wts, cres, sres, wave, nwaves, P, lane, true);
 
   // 3) write the staged activations (float32 rows as three exact bf16 planes)
   if constexpr (XLDS) {
@@ -215,92 +331,20 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
     const int seg = wave + j * nwaves;
     if (seg >= nseg) break;
     float acc[NMAT][kRT][kPerLane];
+    qmv_fold_segment<XF32, NMAT, kRT, kPerLane>(acc, wts.cw[j], wts.sbw[j], seg * kSegGroups, G, xfrag);
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
-        for (int v = 0; v < kPerLane; ++v) acc[m][rt][v] = 0.f;
-    const int g0 = seg * kSegGroups;
-#pragma unroll
-    for (int gg = 0; gg < kSegGroups; ++gg) {
-      const int g = g0 + gg;
-      if (g >= G) break;
-      const int pp = gg >> 1, gh = gg & 1;
-      bf16x8 q[NMAT][2];
-      float sc[NMAT], bs[NMAT];
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m) {
-        q[m][0] = codes_to_bf16(gh ? cw[j][m][pp][2] : cw[j][m][pp][0]);
-        q[m][1] = codes_to_bf16(gh ? cw[j][m][pp][3] : cw[j][m][pp][1]);
-        const uint32_t w = gh ? sbw[j][m][pp][1] : sbw[j][m][pp][0];
-        sc[m] = bf16_lo(w);
-        bs[m] = bf16_hi(w);
-      }
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) {
-        const bf16x8 xa0 = xfrag(rt, g, 0), xa1 = xfrag(rt, g, 1);
-        f32x4 S = mfma16(xa0, ones, f32x4{0.f, 0.f, 0.f, 0.f});
-        S = mfma16(xa1, ones, S);
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-          f32x4 Pm = mfma16(xa0, q[m][0], f32x4{0.f, 0.f, 0.f, 0.f});
-          Pm = mfma16(xa1, q[m][1], Pm);
-          if constexpr (!XF32) {
-#pragma unroll
-            for (int v = 0; v < kPerLane; ++v) acc[m][rt][v] = __builtin_fmaf(sc[m], Pm[v], __builtin_fmaf(bs[m], S[v], acc[m][rt][v]));
-          } else {
-            const float Pr = (Pm[0] + Pm[1]) + Pm[2];
-            const float Sr = (S[0] + S[1]) + S[2];
-            acc[m][rt][0] = __builtin_fmaf(sc[m], Pr, __builtin_fmaf(bs[m], Sr, acc[m][rt][0]));
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-        for (int v = 0; v < kPerLane; ++v) part[(((seg * NMAT + m) * kRT + rt) * kPerLane + v) * 64 + lane] = acc[m][rt][v];
+        for (int v = 0; v < kPerLane; ++v) part[qmv_part_index<NMAT, kRT, kPerLane>(seg, m, rt, v, lane)] = acc[m][rt][v];
   }
   __syncthreads();
   if (wave != 0) return;
 
   // 5) add the segments in ascending order; epilogue
   float tot[NMAT][kRT][kPerLane];
-#pragma unroll
-  for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-      for (int v = 0; v < kPerLane; ++v) tot[m][rt][v] = part[((m * kRT + rt) * kPerLane + v) * 64 + lane];
-  // partials are read eight segments at a time (all reads in flight
-  // together), then added one segment after another
-  constexpr int kSumBatch = 8;
-  for (int seg0 = 1; seg0 < nseg; seg0 += kSumBatch) {
-    float pv[kSumBatch][NMAT][kRT][kPerLane];
-#pragma unroll
-    for (int b = 0; b < kSumBatch; ++b) {
-      const int seg = seg0 + b < nseg ? seg0 + b : nseg - 1;
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-          for (int v = 0; v < kPerLane; ++v) pv[b][m][rt][v] = part[(((seg * NMAT + m) * kRT + rt) * kPerLane + v) * 64 + lane];
-    }
-#pragma unroll
-    for (int b = 0; b < kSumBatch; ++b) {
-      if (seg0 + b >= nseg) break;
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-          for (int v = 0; v < kPerLane; ++v) tot[m][rt][v] = tot[m][rt][v] + pv[b][m][rt][v];
-    }
-  }
+  qmv_ordered_sum<NMAT, kRT, kPerLane>(tot, part, nseg, lane);
 
   const int64_t n = (int64_t)t * kTileN + i;
 #pragma unroll

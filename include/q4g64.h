@@ -127,6 +127,28 @@ int qmm_window(const void* packed_a, const void* packed_b, int64_t N, int64_t K,
 int qmm_cut(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
             const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, void* stream);
 
+/* Decode FFN step in one launch (PR #1696, "What it adds": w1 + w3 + SwiGLU
+ * in one pass; PR #1514, "What changes": the fusion keeps every rounding
+ * boundary):
+ *   z = silu(W1 x) * (W3 x)   float32 [R][ldz], bit-identical to qmv_w13_swiglu;
+ *   y = W2 z                  float32 [R][ldy], bit-identical to qmv_rows on z
+ *                             with x_dtype = Q4_F32.
+ * W1, W3: N1 x K1 packed; W2: N2 x N1 packed. x bf16 [R][ldx], R = 1..16.
+ * work: a DEVICE buffer of at least q4g64_ffn_work_bytes(N1, R) bytes,
+ * 256-byte aligned, zero-filled by the caller before its first use. Its
+ * first 256 bytes hold a grid-barrier state that every call leaves as it
+ * found it; the rest holds z's three exact bf16 pieces. One workspace serves
+ * any later call whose N1 and R fit in it (not concurrent calls). The call
+ * runs one workgroup per CU and needs the whole device: all of them wait at
+ * one grid barrier. A workgroup that waits more than about 20 ms gives up,
+ * sets the 32-bit word at byte 8 of work to 1 and leaves y undefined; the
+ * workspace must then be zero-filled again. Limits: K1 <= 8192,
+ * N1 <= 16384, and the staged activations must fit in LDS
+ * (Q4_EUNSUPPORTED otherwise). */
+size_t q4g64_ffn_work_bytes(int64_t N1, int R);
+int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2, int64_t N1, int64_t K1, int64_t N2,
+            const uint16_t* x, int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, void* work, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* q4_last_error(void);
 

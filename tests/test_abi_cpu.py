@@ -123,3 +123,36 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros((1, 256), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         q4.qmv_rows(torch.zeros(10, dtype=torch.uint8), 512, 256, x)
+
+
+def test_ffn_work_bytes():
+    # 256 bytes of barrier state, then three bf16 planes of R x N1
+    assert q4.ffn_work_bytes(8192, 1) == 256 + 3 * 8192 * 2
+    assert q4.ffn_work_bytes(64, 3) == 256 + 3 * 3 * 64 * 2
+    for bad in ((0, 1), (100, 1), (8192, 0), (8192, 17), (32768, 1)):
+        assert q4.ffn_work_bytes(*bad) == 0
+
+
+def _ffn(N1=8192, K1=2048, N2=2048, ldx=2048, R=1, ldz=8192, ldy=2048, work=FAKE, p=FAKE):
+    return _rc("qmv_ffn", p, FAKE, FAKE, N1, K1, N2, FAKE, ldx, R, FAKE, ldz, FAKE, ldy, work, None)
+
+
+def test_ffn_rejects_bad_arguments():
+    assert _ffn(N1=8100)[0] == q4.Q4_EINVAL
+    assert _ffn(N2=100)[0] == q4.Q4_EINVAL
+    assert _ffn(K1=0)[0] == q4.Q4_EINVAL
+    for R in (0, 17):
+        rc, msg = _ffn(R=R)
+        assert rc == q4.Q4_EINVAL and "R=" in msg
+    assert _ffn(p=None)[0] == q4.Q4_EALIGN
+    rc, msg = _ffn(work=None)
+    assert rc == q4.Q4_EALIGN and "work" in msg
+    rc, msg = _ffn(work=FAKE + 16)
+    assert rc == q4.Q4_EALIGN and "work" in msg
+    assert _ffn(ldx=1024)[0] == q4.Q4_EINVAL
+    assert _ffn(ldz=4096)[0] == q4.Q4_EINVAL
+    assert _ffn(ldy=1024)[0] == q4.Q4_EINVAL
+    rc, msg = _ffn(K1=16384, ldx=16384)
+    assert rc == q4.Q4_EUNSUPPORTED and "8192" in msg
+    rc, msg = _ffn(N1=32768, ldz=32768)
+    assert rc == q4.Q4_EUNSUPPORTED

@@ -1,0 +1,156 @@
+"""The one-launch decode FFN step (qmv_ffn) on the GPU.
+
+It must return exactly the bits of the two-call composition
+qmv_w13_swiglu -> qmv_rows (float32 input), whose parity with the float64
+oracle the decode tests establish; every row must equal its one-row result;
+the workspace's barrier state must survive repeated calls and graph replays;
+and its error word must stay 0."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_only_q4g64_amd as q4
+import oracle
+import synthetic
+from tests.gpu_helpers import DEV, bits32, dev_bf16, dev_weight, host_f64, say
+from tests.tolerance import tol, tol_swiglu
+
+pytestmark = pytest.mark.gpu
+
+
+def _composed(p1, p3, p2, N1, K1, N2, x):
+    z = q4.qmv_w13_swiglu(p1, p3, N1, K1, x)
+    y = q4.qmv_rows(p2, N2, N1, z)
+    return z, y
+
+
+def _weights(seed, N1, K1, N2):
+    rng = np.random.default_rng(seed)
+    w1 = synthetic.draw_qweight(rng, "w1", N1, K1)
+    w3 = synthetic.draw_qweight(rng, "w3", N1, K1)
+    w2 = synthetic.draw_qweight(rng, "w2", N2, N1)
+    return rng, w1, w3, w2
+
+
+@pytest.fixture(scope="module")
+def c1():
+    d = synthetic.config(1)
+    d["p1"], d["p3"], d["p2"] = dev_weight(d["w1"]), dev_weight(d["w3"]), dev_weight(d["w2"])
+    return d
+
+
+def test_c1_step_equals_composition_and_oracle(c1):
+    w1, w2 = c1["w1"], c1["w2"]
+    N1, K1, N2 = w1.N, w1.K, w2.N
+    say(f"qmv_ffn c1 N1={N1} K1={K1} N2={N2} R=1")
+    x = dev_bf16(c1["x"])
+    work = q4.ffn_workspace(N1, 1, DEV)
+    z, y = q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x, work)
+    zc, yc = _composed(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x)
+    torch.cuda.synchronize()
+    assert q4.ffn_error(work) == 0
+    assert np.array_equal(bits32(z), bits32(zc))
+    assert np.array_equal(bits32(y), bits32(yc))
+    # and the chain against the oracle's float64 chain, with the propagated bound
+    w3 = c1["w3"]
+    a64 = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, c1["x"])
+    c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, c1["x"])
+    z64 = oracle.swiglu(a64, c64)
+    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, c1["x"]), K1),
+                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, c1["x"]), K1))
+    assert np.all(np.abs(host_f64(z) - z64) <= Tz)
+    y64 = oracle.matmul_rows(w2.wq, w2.scales, w2.biases, z64)
+    bound = tol(oracle.error_weight(w2.wq, w2.scales, w2.biases, np.abs(z64) + Tz), w2.K, "f32") + \
+        oracle.error_weight(w2.wq, w2.scales, w2.biases, Tz)
+    ratio = float(np.max(np.abs(host_f64(y) - y64) / bound))
+    say(f"qmv_ffn c1 y max err/bound {ratio:.3g}")
+    assert ratio <= 1.0
+
+
+@pytest.mark.parametrize("R", [2, 3, 5, 16])
+def test_rows_equal_composition_and_one_row(c1, R):
+    w1, w2 = c1["w1"], c1["w2"]
+    N1, K1, N2 = w1.N, w1.K, w2.N
+    say(f"qmv_ffn c1 shapes R={R}")
+    rng = np.random.default_rng(100 + R)
+    xb = synthetic.draw_bf16_rows(rng, R, K1)
+    x = dev_bf16(xb)
+    work = q4.ffn_workspace(N1, R, DEV)
+    z, y = q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x, work)
+    zc, yc = _composed(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x)
+    torch.cuda.synchronize()
+    assert q4.ffn_error(work) == 0
+    assert np.array_equal(bits32(z), bits32(zc))
+    assert np.array_equal(bits32(y), bits32(yc))
+    for r in (0, R - 1):
+        z1, y1 = q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x[r : r + 1], work)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits32(z1)[0], bits32(z)[r])
+        assert np.array_equal(bits32(y1)[0], bits32(y)[r])
+
+
+def test_repeated_calls_reuse_the_workspace(c1):
+    w1, w2 = c1["w1"], c1["w2"]
+    N1, K1, N2 = w1.N, w1.K, w2.N
+    say("qmv_ffn c1 five calls on one workspace")
+    x = dev_bf16(c1["x"])
+    work = q4.ffn_workspace(N1, 1, DEV)
+    ref = None
+    for _ in range(5):
+        z, y = q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x, work)
+        torch.cuda.synchronize()
+        cur = (bits32(z), bits32(y))
+        if ref is None:
+            ref = cur
+        assert np.array_equal(cur[0], ref[0]) and np.array_equal(cur[1], ref[1])
+    state = work[0:12].view(torch.int32).cpu().numpy()
+    assert state[0] == 0 and state[2] == 0  # arrival count back at 0, no error
+    assert state[1] == 5  # one barrier generation per call
+
+
+@pytest.mark.parametrize("N1,K1,N2,R", [(64, 64, 64, 1), (192, 128, 128, 3), (16384, 2048, 4096, 1), (8192, 4096, 2048, 2)])
+def test_shapes_equal_composition(N1, K1, N2, R):
+    say(f"qmv_ffn N1={N1} K1={K1} N2={N2} R={R}")
+    rng, w1, w3, w2 = _weights(7 + N1 + K1, N1, K1, N2)
+    p1, p3, p2 = dev_weight(w1), dev_weight(w3), dev_weight(w2)
+    x = dev_bf16(synthetic.draw_bf16_rows(rng, R, K1))
+    work = q4.ffn_workspace(N1, R, DEV)
+    z, y = q4.qmv_ffn(p1, p3, p2, N1, K1, N2, x, work)
+    zc, yc = _composed(p1, p3, p2, N1, K1, N2, x)
+    torch.cuda.synchronize()
+    assert q4.ffn_error(work) == 0
+    assert np.array_equal(bits32(z), bits32(zc))
+    assert np.array_equal(bits32(y), bits32(yc))
+
+
+def test_graph_replays_equal_eager(c1):
+    w1, w2 = c1["w1"], c1["w2"]
+    N1, K1, N2 = w1.N, w1.K, w2.N
+    say("qmv_ffn c1 in a HIP graph, four replays")
+    x = dev_bf16(c1["x"])
+    work = q4.ffn_workspace(N1, 1, DEV)
+    z = torch.empty((1, N1), dtype=torch.float32, device=DEV)
+    y = torch.empty((1, N2), dtype=torch.float32, device=DEV)
+    z_ref, y_ref = q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x, work)
+    torch.cuda.synchronize()
+    zr, yr = bits32(z_ref), bits32(y_ref)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x, work, z=z, y=y)
+    torch.cuda.synchronize()
+    for k in range(4):
+        z.zero_()
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits32(z), zr), k
+        assert np.array_equal(bits32(y), yr), k
+        # eager work between replays
+        q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x, work)
+        torch.cuda.synchronize()
+    assert q4.ffn_error(work) == 0
