@@ -203,12 +203,20 @@ def qmm_cut(pa: torch.Tensor, pb: torch.Tensor | None, N: int, K: int, x: torch.
     return y
 
 
+# Barrier state in the qmv_ffn workspace (byte offsets of 32-bit words):
+# 16 arrival counters 128 bytes apart, a top counter, a generation, an error.
+FFN_COUNTER_STRIDE = 128
+FFN_TOP_OFFSET = 16 * 128
+FFN_GEN_OFFSET = 17 * 128
+FFN_ERR_OFFSET = 18 * 128
+
+
 def ffn_work_bytes(N1: int, R: int) -> int:
     return int(lib().q4g64_ffn_work_bytes(N1, R))
 
 
 def ffn_workspace(N1: int, R: int, device="cuda") -> torch.Tensor:
-    """A zeroed workspace for qmv_ffn (reusable across calls with N1' <= N1, R' <= R)."""
+    """A zeroed workspace for qmv_ffn (reusable by later calls on the same stream)."""
     nbytes = ffn_work_bytes(N1, R)
     if nbytes == 0:
         raise Q4Error("q4g64_ffn_work_bytes", Q4_EINVAL, f"invalid N1={N1} R={R}")
@@ -217,7 +225,7 @@ def ffn_workspace(N1: int, R: int, device="cuda") -> torch.Tensor:
 
 def ffn_error(work: torch.Tensor) -> int:
     """The workspace's barrier error word (1 if a workgroup gave up waiting)."""
-    return int(work[8:12].view(torch.int32).item())
+    return int(work[FFN_ERR_OFFSET : FFN_ERR_OFFSET + 4].view(torch.int32).item())
 
 
 def qmv_ffn(p1: torch.Tensor, p3: torch.Tensor, p2: torch.Tensor, N1: int, K1: int, N2: int, x: torch.Tensor, work: torch.Tensor,

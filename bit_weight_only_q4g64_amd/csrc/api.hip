@@ -280,7 +280,7 @@ int qmm_cut(const void* packed_a, const void* packed_b, int64_t N, int64_t K, co
 
 size_t q4g64_ffn_work_bytes(int64_t N1, int R) {
   if (N1 <= 0 || N1 % 64 != 0 || N1 > q4::kQmvMaxK || R < 1 || R > 16) return 0;
-  return q4::ffn_work_bytes(N1, R);
+  return q4::kFfnWorkBytes;
 }
 
 int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2, int64_t N1, int64_t K1, int64_t N2,

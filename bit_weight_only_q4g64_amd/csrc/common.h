@@ -104,6 +104,9 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
+// A per-lane offset past every buffer this library builds (all are < 2 GiB):
+// a load there returns zeros without touching memory.
+constexpr uint32_t kOffBuffer = 0x80000000u;
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }

@@ -2,23 +2,25 @@
 //
 // It computes exactly what qmv_w13_swiglu followed by qmv_rows (float32 x)
 // compute, with the same per-tile arithmetic (qmv_fold_segment and
-// qmv_ordered_sum), so z and y are bit-identical to the two calls (TensorFold
-// PR #1696, "What it adds": w1 + w3 + SwiGLU in one pass; PR #1514, "What
-// changes": the fusion keeps every rounding boundary). What changes is the
-// schedule:
+// qmv_ordered_sum) and the same exact three-piece split of z, so z and y are
+// bit-identical to the two calls (TensorFold PR #1696, "What it adds":
+// w1 + w3 + SwiGLU in one pass; PR #1514, "What changes": the fusion keeps
+// every rounding boundary). What changes is the schedule:
 //
 //   * one persistent workgroup per CU (16 waves);
 //   * at the start each workgroup issues the loads of its w1/w3 tiles AND of
 //     its first w2 work item, so the whole step's weights stream from HBM
-//     together instead of w2 waiting for the first kernel to finish;
-//   * phase 1: w1/w3 tiles two at a time (8 waves each), z written as float32
-//     and as its three exact bf16 pieces h + m + l (the split qmv_rows makes
-//     of a float32 input), so phase 2 reads MFMA fragments directly;
-//   * a grid barrier (sense-reversing counter in the caller's workspace,
-//     agent-scope release/acquire, bounded spin that records an error and
-//     lets every wave finish);
-//   * phase 2: w2 over 8-column half-tiles (two per 16-column tile), so a
-//     2048-row w2 still covers every CU; the lanes of the other half load
+//     together instead of w2 waiting for a second launch;
+//   * phase 1: w1/w3 tiles two at a time (8 waves each); z is written with
+//     device-scope (write-through) stores;
+//   * a grid barrier: workgroups arrive at one of 16 counters (each on its
+//     own 128-byte line), the last of each counter at a top counter, the last
+//     of all bumps a generation word; one release and one acquire per
+//     workgroup; the wait polls with relaxed loads and gives up after a
+//     bounded time, recording an error, so every wave finishes;
+//   * phase 2: z staged in LDS as its three bf16 planes (the staging
+//     qmv_rows does), w2 over 8-column half-tiles (two per 16-column tile) so
+//     a 2048-row w2 still covers every CU; the lanes of the other half load
 //     nothing and store nothing.
 #pragma once
 
@@ -29,43 +31,53 @@ namespace q4 {
 
 constexpr int kFfnWaves = 16;
 constexpr int kFfnThreads = kFfnWaves * 64;
-constexpr int kFfnP1Waves = 8;             // waves per w1/w3 tile in phase 1
+constexpr int kFfnP1Waves = 8;               // waves per w1/w3 tile in phase 1
+constexpr int kFfnGroups = 16;               // first-level barrier counters
+constexpr int kFfnLine = 128;                // bytes between barrier words
 constexpr uint64_t kFfnSpinTicks = 2000000;  // barrier give-up: 20 ms of the 100 MHz real-time clock
 
-// Workspace: 256 bytes of barrier state (at a fixed place, so a workspace
-// sized for the largest R serves every smaller call), then the three bf16
-// planes of z ([3][R][N1]).
-constexpr size_t kFfnStateBytes = 256;
-__host__ __device__ inline size_t ffn_planes_bytes(int64_t N1, int R) { return (size_t)3 * R * N1 * 2; }
-__host__ __device__ inline size_t ffn_work_bytes(int64_t N1, int R) { return kFfnStateBytes + ffn_planes_bytes(N1, R); }
+// Workspace: the barrier state only. Byte offsets: counter c at c * 128
+// (c < 16), the top counter at 16 * 128, the generation at 17 * 128, the
+// error word at 18 * 128.
+constexpr size_t kFfnWorkBytes = 4096;
+constexpr size_t kFfnTopOff = kFfnGroups * kFfnLine;
+constexpr size_t kFfnGenOff = (kFfnGroups + 1) * kFfnLine;
+constexpr size_t kFfnErrOff = (kFfnGroups + 2) * kFfnLine;
+static_assert(kFfnErrOff + 4 <= kFfnWorkBytes, "barrier words fit the workspace");
 
-struct FfnSync {
-  uint32_t count;  // workgroups arrived at the current barrier (0 between calls)
-  uint32_t gen;    // barrier generation (any value)
-  uint32_t err;    // set to 1 when a workgroup gave up waiting
-};
+__device__ __forceinline__ uint32_t* ffn_word(uint8_t* work, size_t off) { return (uint32_t*)(work + off); }
 
 // Grid barrier over nwg co-resident workgroups. g0 is the generation thread
-// 0 read (with acquire) at kernel start: it cannot change before this
-// workgroup arrives, because the barrier needs every arrival. One release
-// and one acquire per workgroup; the wait polls with relaxed loads, so no
-// poll invalidates a cache. Returns false if this workgroup gave up waiting
-// (then err is set and the results are invalid).
-__device__ __forceinline__ bool ffn_grid_barrier(FfnSync* sy, uint32_t nwg, uint32_t g0, uint32_t* flag) {
+// 0 read at kernel start: it cannot change before this
+// workgroup arrives, because the barrier needs every arrival. Returns false
+// if this workgroup gave up waiting (then the error word is set, the
+// counters are left mid-count and the results are invalid).
+__device__ __forceinline__ bool ffn_grid_barrier(uint8_t* work, int b, int nwg, uint32_t g0, uint32_t* flag) {
   __syncthreads();  // every wave's stores of this workgroup are done
   if (threadIdx.x == 0) {
     uint32_t ok = 1;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t arrived = __hip_atomic_fetch_add(&sy->count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (arrived == nwg - 1) {
-      __hip_atomic_store(&sy->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(&sy->gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
+    const int c = b % kFfnGroups;
+    const uint32_t nc = (uint32_t)((nwg - c + kFfnGroups - 1) / kFfnGroups);  // workgroups on counter c
+    const uint32_t ncount = (uint32_t)(nwg < kFfnGroups ? nwg : kFfnGroups);   // counters in use
+    uint32_t* cnt = ffn_word(work, (size_t)c * kFfnLine);
+    uint32_t* top = ffn_word(work, kFfnTopOff);
+    uint32_t* gen = ffn_word(work, kFfnGenOff);
+    bool last = false;
+    if (__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nc - 1) {
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ncount - 1) {
+        __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        last = true;
+      }
+    }
+    if (!last) {
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (__hip_atomic_load(&sy->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
+      while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
         if (__builtin_amdgcn_s_memrealtime() - t0 > kFfnSpinTicks) {
           ok = 0;
-          __hip_atomic_store(&sy->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(ffn_word(work, kFfnErrOff), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
         __builtin_amdgcn_s_sleep(2);
@@ -79,11 +91,11 @@ __device__ __forceinline__ bool ffn_grid_barrier(FfnSync* sy, uint32_t nwg, uint
 }
 
 // LDS of the fused kernel (bytes): phase 1 stages x and holds the partials of
-// two tiles; phase 2 reuses the space for its partials and, when xl2, the
-// three bf16 planes of z ([3][R][K2 + 8], the layout qmv_rows stages).
+// two tiles; phase 2 reuses the space for its partials and, when xl2, z's
+// three bf16 planes ([3][R][K2 + 8], the layout qmv_rows stages).
+__host__ __device__ inline int ffn_rtf(int R) { return (R + 3) / 4 <= 1 ? 1 : ((R + 3) / 4 <= 2 ? 2 : 4); }
 __host__ __device__ inline size_t ffn_part2_bytes(int64_t K2, int R) {
-  const int rtf = (R + 3) / 4 <= 1 ? 1 : ((R + 3) / 4 <= 2 ? 2 : 4);
-  return (size_t)qmv_segments(K2) * rtf * 64 * sizeof(float);
+  return (size_t)qmv_segments(K2) * ffn_rtf(R) * 64 * sizeof(float);
 }
 __host__ __device__ inline size_t ffn_lds_bytes(int64_t K1, int64_t K2, int R, bool xl2) {
   const int nv = qmv_nv(R);
@@ -92,12 +104,10 @@ __host__ __device__ inline size_t ffn_lds_bytes(int64_t K1, int64_t K2, int R, b
   return (p1 > p2 ? p1 : p2) + 16;
 }
 
-// Device-scope cache policy (sc1) for the data the two phases exchange: z's
-// stores write through the XCD's L2 and phase 2's loads of it read past it.
-constexpr int kCpolDevice = 16;
-
 // NV: row slots per lane group of phase 1 (as qmv_w13_swiglu); RTF: row tiles
 // of phase 2 (as qmv_rows with float32 x); SPW1 / SPW2: segments per wave.
+// xl2: z fits in LDS as three bf16 planes (else fragments are read from z
+// and split in registers, as qmv_rows does when its staging does not fit).
 template <int NV, int RTF, int SPW1, int SPW2>
 __global__ __launch_bounds__(kFfnThreads) void ffn_kernel(const uint8_t* __restrict__ p1, const uint8_t* __restrict__ p3,
                                                         const uint8_t* __restrict__ p2, int N1, int K1, int N2,
@@ -115,11 +125,11 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_kernel(const uint8_t* __restr
   const int64_t cb1 = codes_bytes(N1, K1), cb2 = codes_bytes(N2, K2);
   const int T1 = N1 / kTileN, pairs1 = (T1 + 1) / 2;
   const int items2 = 2 * (N2 / kTileN);
-  FfnSync* sy = (FfnSync*)work;
-  uint16_t* planes = (uint16_t*)(work + kFfnStateBytes);
-  // the barrier generation of this call (only thread 0 uses it)
+  // the barrier generation of this call (only thread 0 uses it). Relaxed:
+  // the previous call's last update precedes this launch, and a relaxed load
+  // does not hold back the weight loads issued after it.
   uint32_t g0 = 0;
-  if (threadIdx.x == 0) g0 = __hip_atomic_load(&sy->gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) g0 = __hip_atomic_load(ffn_word(work, kFfnGenOff), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- phase 1 set-up: x staged in LDS, the first tile pair's weights -----
   const int grp = wave / kFfnP1Waves, wg = wave % kFfnP1Waves;
@@ -162,19 +172,21 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_kernel(const uint8_t* __restr
     tile_rsrc(p1, cb1, t, P1, cr[0], sr[0]);
     tile_rsrc(p3, cb1, t, P1, cr[1], sr[1]);
   };
+  // (issued on every path, with a workgroup past the last tile loading
+  // nothing, so that staging x below waits for x alone)
   QmvWeights<2, SPW1> w13;
-  if (b < pairs1) {
+  {
     rsrc_t cr[2], sr[2];
-    p1_rsrc(b, cr, sr);
-    qmv_issue_weights<2, SPW1>(w13, cr, sr, wg, kFfnP1Waves, P1, lane, true);
+    p1_rsrc(b < pairs1 ? b : pairs1 - 1, cr, sr);
+    qmv_issue_weights<2, SPW1>(w13, cr, sr, wg, kFfnP1Waves, P1, lane, b < pairs1);
   }
   // the first w2 item: tile it / 2, columns 8 (it % 2) .. + 7 of that tile
   auto p2_rsrc = [&](int it, rsrc_t (&cr)[1], rsrc_t (&sr)[1]) { tile_rsrc(p2, cb2, it / 2, P2, cr[0], sr[0]); };
   QmvWeights<1, SPW2> w2w;
-  if (b < items2) {
+  {
     rsrc_t cr[1], sr[1];
-    p2_rsrc(b, cr, sr);
-    qmv_issue_weights<1, SPW2>(w2w, cr, sr, wave, kFfnWaves, P2, lane, (i >> 3) == (b & 1));
+    p2_rsrc(b < items2 ? b : items2 - 1, cr, sr);
+    qmv_issue_weights<1, SPW2>(w2w, cr, sr, wave, kFfnWaves, P2, lane, b < items2 && (i >> 3) == (b & 1));
   }
   {
     int r = 0, j = 0;
@@ -197,8 +209,7 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_kernel(const uint8_t* __restr
   auto xfrag1 = [&](int, int g, int hh) -> bf16x8 {
     return __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + frow * xsi + g * kGroup + hh * 32 + kc * 8));
   };
-  const int planes_row = N1;  // bf16 elements per plane row
-  const rsrc_t pres = make_rsrc(planes, (uint32_t)((size_t)3 * R * N1 * 2));
+  const rsrc_t zres = make_rsrc(z, (uint32_t)(R * ldz * 4));
   for (int pr = b; pr < pairs1; pr += nwg) {
     if (pr != b) {
       rsrc_t cr[2], sr[2];
@@ -227,55 +238,21 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_kernel(const uint8_t* __restr
         const int r = 4 * kc + v;
         if (r >= R) continue;
         const float zz = silu_f32(tot[0][0][v]) * tot[1][0][v];
-        z[(int64_t)r * ldz + n] = zz;
-        uint32_t h, m, l;
-        split3(zz, h, m, l);
-        const uint32_t o = (uint32_t)((r * planes_row + n) * 2), plane = (uint32_t)(R * planes_row * 2);
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)h, pres, (int)o, 0, kCpolDevice);
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)m, pres, (int)(o + plane), 0, kCpolDevice);
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)l, pres, (int)(o + 2 * plane), 0, kCpolDevice);
+        // device scope (sc1): written through the XCD's L2
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(zz), zres, (int)((r * ldz + n) * 4), 0, 16);
       }
     }
     __syncthreads();  // the partials are reused by the next pass
   }
 
-  // ---- grid barrier: every z plane written and visible ---------------------
-  const bool ok = ffn_grid_barrier(sy, (uint32_t)nwg, g0, flag);
-  if (!ok) return;
+  // ---- grid barrier: every row of z written and visible --------------------
+  if (!ffn_grid_barrier(work, b, nwg, g0, flag)) return;
 
-  // ---- phase 2: w2 on the bf16 pieces of z, half-tiles ---------------------
+  // ---- phase 2: w2 on the three bf16 pieces of z, half-tiles ---------------
   float* part2 = (float*)smem;
-  uint16_t* xs2 = (uint16_t*)(smem + ffn_part2_bytes(K2, R));
-  const int xsi2 = (int)qmv_xs_stride(K2);
-  if (xl2) {
-    // z's planes into LDS: every 16-byte chunk once, loads batched four deep
-    const int per_prow = K2 / 8, total = 3 * R * per_prow;
-    for (int c0 = (int)threadIdx.x; c0 < total; c0 += 4 * kFfnThreads) {
-      u32x4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        int c = c0 + u * kFfnThreads;
-        c = c < total ? c : total - 1;
-        v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pres, c * 16, 0, kCpolDevice));
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = c0 + u * kFfnThreads;
-        if (c < total) *(u32x4*)(xs2 + (c / per_prow) * xsi2 + (c % per_prow) * 8) = v[u];
-      }
-    }
-    __syncthreads();
-  }
-  auto xfrag2 = [&](int rt, int g, int hh) -> bf16x8 {
-    const int k0 = g * kGroup + hh * 32 + kc * 8;
-    int row = rt * 4 + (i >> 2);
-    row = row < R ? row : R - 1;
-    int piece = i & 3;
-    piece = piece < 3 ? piece : 2;
-    if (xl2) return __builtin_bit_cast(bf16x8, *(const u32x4*)(xs2 + (piece * R + row) * xsi2 + k0));
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(pres, ((piece * R + row) * planes_row + k0) * 2, 0, kCpolDevice));
-  };
-  for (int it = b; it < items2; it += nwg) {
+  const uint32_t zrow = (uint32_t)(ldz * 4);
+  // one phase-2 work item with fragment source xf: compute, reduce, store
+  auto item = [&](int it, const auto& xf) {
     const bool on = (i >> 3) == (it & 1);
     if (it != b) {
       rsrc_t cr[1], sr[1];
@@ -287,7 +264,7 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_kernel(const uint8_t* __restr
       const int seg = wave + j * kFfnWaves;
       if (seg >= nseg2) break;
       float acc[1][RTF][1];
-      qmv_fold_segment<1, 1, RTF, 1>(acc, w2w.cw[j], w2w.sbw[j], seg * kSegGroups, G2, xfrag2);
+      qmv_fold_segment<1, 1, RTF, 1>(acc, w2w.cw[j], w2w.sbw[j], seg * kSegGroups, G2, xf);
 #pragma unroll
       for (int rt = 0; rt < RTF; ++rt) part2[qmv_part_index<1, RTF, 1>(seg, 0, rt, 0, lane)] = acc[0][rt][0];
     }
@@ -303,6 +280,65 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_kernel(const uint8_t* __restr
       }
     }
     __syncthreads();
+  };
+  if (xl2) {
+    // z into LDS as three exact bf16 planes h, m, l of [R][K2 + 8] (the
+    // staging qmv_rows does for a float32 input), loads four deep per thread
+    uint16_t* xs2 = (uint16_t*)(smem + ffn_part2_bytes(K2, R));
+    const int xsi2 = (int)qmv_xs_stride(K2), plane = R * xsi2;
+    const uint32_t per_zrow = (uint32_t)K2 / 4, total = (uint32_t)R * per_zrow;  // 16-byte chunks of z
+    for (uint32_t c0 = threadIdx.x; c0 < total; c0 += 4 * kFfnThreads) {
+      u32x4 v[4];
+#pragma unroll
+      for (uint32_t u = 0; u < 4; ++u) {
+        uint32_t c = c0 + u * kFfnThreads;
+        c = c < total ? c : total - 1;
+        v[u] = buf_load16(zres, (c / per_zrow) * zrow + (c % per_zrow) * 16u, 0u);
+      }
+#pragma unroll
+      for (uint32_t u = 0; u < 4; ++u) {
+        const uint32_t c = c0 + u * kFfnThreads;
+        if (c >= total) continue;
+        uint32_t h[4], m[4], l[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) split3(__uint_as_float(v[u][w]), h[w], m[w], l[w]);
+        uint16_t* d = xs2 + (c / per_zrow) * xsi2 + (c % per_zrow) * 4;
+        *(u32x2*)d = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        *(u32x2*)(d + plane) = u32x2{m[0] | (m[1] << 16), m[2] | (m[3] << 16)};
+        *(u32x2*)(d + 2 * plane) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+      }
+    }
+    __syncthreads();
+    auto xf = [&](int rt, int g, int hh) -> bf16x8 {
+      const int k0 = g * kGroup + hh * 32 + kc * 8;
+      int row = rt * 4 + (i >> 2);
+      row = row < R ? row : R - 1;
+      int piece = i & 3;
+      piece = piece < 3 ? piece : 2;
+      return __builtin_bit_cast(bf16x8, *(const u32x4*)(xs2 + (piece * R + row) * xsi2 + k0));
+    };
+    for (int it = b; it < items2; it += nwg) item(it, xf);
+  } else {
+    // fragments straight from z, split in registers (as qmv_rows does when
+    // its input does not fit in LDS)
+    auto xf = [&](int rt, int g, int hh) -> bf16x8 {
+      const int k0 = g * kGroup + hh * 32 + kc * 8;
+      int row = rt * 4 + (i >> 2);
+      row = row < R ? row : R - 1;
+      int piece = i & 3;
+      piece = piece < 3 ? piece : 2;
+      const u32x4 a = buf_load16(zres, (uint32_t)row * zrow + (uint32_t)k0 * 4u, 0u);
+      const u32x4 c = buf_load16(zres, (uint32_t)row * zrow + (uint32_t)k0 * 4u + 16u, 0u);
+      uint32_t o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t h, m, l;
+        split3(__uint_as_float(e < 4 ? a[e] : c[e - 4]), h, m, l);
+        o[e] = piece == 0 ? h : (piece == 1 ? m : l);
+      }
+      return __builtin_bit_cast(bf16x8, u32x4{o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16)});
+    };
+    for (int it = b; it < items2; it += nwg) item(it, xf);
   }
 }
 

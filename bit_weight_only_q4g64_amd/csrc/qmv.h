@@ -62,11 +62,14 @@ struct QmvWeights {
 
 // Issue every weight load of segments seg0 + j * step (j < SPW). Pair indices
 // past the matrix are clamped to its last pair (those values are never
-// used). Lanes with on == false load nothing and hold zero codes.
+// used). Lanes with on == false read past the buffer's end, which the
+// hardware answers with zeros and no memory access: the loads stay
+// unconditional, so the count of loads in flight is the same on every path.
 template <int NMAT, int SPW>
 __device__ __forceinline__ void qmv_issue_weights(QmvWeights<NMAT, SPW>& w, const rsrc_t (&cres)[NMAT], const rsrc_t (&sres)[NMAT],
                                                   int seg0, int step, int P, int lane, bool on) {
   const int i = lane & 15;
+  const uint32_t cv = on ? (uint32_t)lane * 16u : kOffBuffer, sv = on ? (uint32_t)i * 8u : kOffBuffer;
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int seg = seg0 + j * step;
@@ -76,13 +79,8 @@ __device__ __forceinline__ void qmv_issue_weights(QmvWeights<NMAT, SPW>& w, cons
       p = p < P ? p : P - 1;
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
-        if (on) {
-          w.cw[j][m][pp] = buf_load16(cres[m], (uint32_t)lane * 16u, (uint32_t)p * kPairCodeBytes);
-          w.sbw[j][m][pp] = buf_load8(sres[m], (uint32_t)i * 8u, (uint32_t)p * kPairSbBytes);
-        } else {
-          w.cw[j][m][pp] = u32x4{0u, 0u, 0u, 0u};
-          w.sbw[j][m][pp] = u32x2{0u, 0u};
-        }
+        w.cw[j][m][pp] = buf_load16(cres[m], cv, (uint32_t)p * kPairCodeBytes);
+        w.sbw[j][m][pp] = buf_load8(sres[m], sv, (uint32_t)p * kPairSbBytes);
       }
     }
   }

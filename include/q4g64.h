@@ -134,15 +134,16 @@ int qmm_cut(const void* packed_a, const void* packed_b, int64_t N, int64_t K, co
  *   y = W2 z                  float32 [R][ldy], bit-identical to qmv_rows on z
  *                             with x_dtype = Q4_F32.
  * W1, W3: N1 x K1 packed; W2: N2 x N1 packed. x bf16 [R][ldx], R = 1..16.
- * work: a DEVICE buffer of at least q4g64_ffn_work_bytes(N1, R) bytes,
- * 256-byte aligned, zero-filled by the caller before its first use. Its
- * first 256 bytes hold a grid-barrier state that every call leaves as it
- * found it; the rest holds z's three exact bf16 pieces. One workspace serves
- * any later call whose N1 and R fit in it (not concurrent calls). The call
- * runs one workgroup per CU and needs the whole device: all of them wait at
- * one grid barrier. A workgroup that waits more than about 20 ms gives up,
- * sets the 32-bit word at byte 8 of work to 1 and leaves y undefined; the
- * workspace must then be zero-filled again. Limits: K1 <= 8192,
+ * work: a DEVICE buffer of q4g64_ffn_work_bytes(N1, R) bytes (4096 for
+ * every valid N1 and R; 0 means the arguments are invalid), 256-byte
+ * aligned, zero-filled by the caller before its first use. It holds only a
+ * grid-barrier state, which every completed call leaves ready for the next:
+ * one workspace serves any later call on the same stream (not concurrent
+ * calls). z is the exchange buffer between the two halves of the step. The
+ * call runs one workgroup per CU and needs the whole device: all of them
+ * wait at one grid barrier. A workgroup that waits more than about 20 ms
+ * gives up, sets the 32-bit word at byte 2304 of work to 1 and leaves y
+ * undefined; the workspace must then be zero-filled again. Limits: K1 <= 8192,
  * N1 <= 16384, and the staged activations must fit in LDS
  * (Q4_EUNSUPPORTED otherwise). */
 size_t q4g64_ffn_work_bytes(int64_t N1, int R);

@@ -126,9 +126,9 @@ def test_binding_refuses_host_tensors():
 
 
 def test_ffn_work_bytes():
-    # 256 bytes of barrier state, then three bf16 planes of R x N1
-    assert q4.ffn_work_bytes(8192, 1) == 256 + 3 * 8192 * 2
-    assert q4.ffn_work_bytes(64, 3) == 256 + 3 * 3 * 64 * 2
+    # the barrier state only: a fixed 4 KiB
+    assert q4.ffn_work_bytes(8192, 1) == 4096
+    assert q4.ffn_work_bytes(64, 16) == 4096
     for bad in ((0, 1), (100, 1), (8192, 0), (8192, 17), (32768, 1)):
         assert q4.ffn_work_bytes(*bad) == 0
 

@@ -104,9 +104,11 @@ def test_repeated_calls_reuse_the_workspace(c1):
         if ref is None:
             ref = cur
         assert np.array_equal(cur[0], ref[0]) and np.array_equal(cur[1], ref[1])
-    state = work[0:12].view(torch.int32).cpu().numpy()
-    assert state[0] == 0 and state[2] == 0  # arrival count back at 0, no error
-    assert state[1] == 5  # one barrier generation per call
+    state = work.view(torch.int32).cpu().numpy()
+    counters = state[[c * q4.FFN_COUNTER_STRIDE // 4 for c in range(16)]]
+    assert np.all(counters == 0) and state[q4.FFN_TOP_OFFSET // 4] == 0  # arrival counts back at 0
+    assert state[q4.FFN_ERR_OFFSET // 4] == 0
+    assert state[q4.FFN_GEN_OFFSET // 4] == 5  # one barrier generation per call
 
 
 @pytest.mark.parametrize("N1,K1,N2,R", [(64, 64, 64, 1), (192, 128, 128, 3), (16384, 2048, 4096, 1), (8192, 4096, 2048, 2)])
