@@ -6,6 +6,7 @@ its Python binding) never does, and this package imports nothing from it.
 """
 
 from .q4g64 import (  # noqa: F401
+    BITS,
     activations_f64,
     bf16_to_f64,
     dequantize,
@@ -16,4 +17,5 @@ from .q4g64 import (  # noqa: F401
     silu,
     swiglu,
     unpack_codes,
+    words_per_row,
 )

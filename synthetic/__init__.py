@@ -15,6 +15,7 @@ from .workloads import (  # noqa: F401
     draw_bf16_rows,
     draw_f32_rows,
     draw_qweight,
+    pack_codes_bits,
     pack_codes_low_nibble_first,
     sha256_of,
 )

@@ -20,6 +20,19 @@ order the workload names its tensors, weights first, then activations):
   already rounded scale, so codes are centred near 8);
 * activations ``X = bf16(rng.normal(0, 1, (rows, K)))``.
 
+Wider codes (bits = 6 or 8; PR #1514, "What changes", serves the MLX 4-, 6-
+and 8-bit checkpoints as stored; the pages give no layout or statistics):
+
+* ``wq`` uint32 ``[N][K*bits/32]``: the words of a row are one little-endian
+  bit stream and code k occupies bits ``bits*k .. bits*k+bits-1`` (8-bit codes
+  are the bytes of each word in order; 6-bit codes straddle words);
+* codes ``q = rng.integers(0, 2**bits, (N, K))``;
+* scales ``S = bf16(|rng.normal(0, 0.02)| * 15 / (2**bits - 1))`` so that the
+  weight range matches the 4-bit recipe;
+* biases ``B = bf16(-2**(bits-1) * S + rng.normal(0, 0.002))``.
+
+For bits = 4 these are exactly the draws above.
+
 ``bf16(v)`` rounds float64 -> float32 (round to nearest even) -> bf16 (round
 to nearest even on the bit pattern). Nothing here unpacks, dequantizes or
 multiplies: those steps belong to the oracle and to the kernels.
@@ -64,6 +77,28 @@ def pack_codes_low_nibble_first(q: np.ndarray) -> np.ndarray:
     return words
 
 
+def pack_codes_bits(q: np.ndarray, bits: int) -> np.ndarray:
+    """Store codes [N][K] (values < 2**bits) as uint32 [N][K*bits/32], code k
+    at bits bits*k .. of the row's little-endian bit stream."""
+    if bits == 4:
+        return pack_codes_low_nibble_first(q)
+    q = np.asarray(q, dtype=np.uint64)
+    n, k = q.shape
+    per = 32 // np.gcd(bits, 32)  # codes per whole number of words
+    wper = per * bits // 32
+    if k % per:
+        raise ValueError(f"K must be a multiple of {per} for {bits}-bit codes")
+    q = q.reshape(n, k // per, per)
+    words = np.zeros((n, k // per, wper), dtype=np.uint64)
+    for j in range(per):
+        p = bits * j
+        w, sh = p // 32, p % 32
+        words[:, :, w] |= (q[:, :, j] << np.uint64(sh)) & np.uint64(0xFFFFFFFF)
+        if sh + bits > 32:
+            words[:, :, w + 1] |= q[:, :, j] >> np.uint64(32 - sh)
+    return words.reshape(n, k // per * wper).astype(np.uint32)
+
+
 @dataclass
 class QWeight:
     """One q4g64 matrix in the canonical format."""
@@ -74,16 +109,22 @@ class QWeight:
     wq: np.ndarray  # uint32 [N][K/8]
     scales: np.ndarray  # uint16 bf16 bits [N][K/64]
     biases: np.ndarray  # uint16 bf16 bits [N][K/64]
+    bits: int = 4
 
 
-def draw_qweight(rng: np.random.Generator, name: str, N: int, K: int) -> QWeight:
+def draw_qweight(rng: np.random.Generator, name: str, N: int, K: int, bits: int = 4) -> QWeight:
     if K % GROUP or N <= 0 or K <= 0:
         raise ValueError("K must be a positive multiple of 64 and N positive")
-    q = rng.integers(0, 16, (N, K), dtype=np.uint8)
-    s_bits = bf16_bits_from_f64(np.abs(rng.normal(0.0, 0.02, (N, K // GROUP))))
+    if bits not in (4, 6, 8):
+        raise ValueError("bits must be 4, 6 or 8")
+    q = rng.integers(0, 1 << bits, (N, K), dtype=np.uint8)
+    if bits == 4:
+        s_bits = bf16_bits_from_f64(np.abs(rng.normal(0.0, 0.02, (N, K // GROUP))))
+    else:
+        s_bits = bf16_bits_from_f64(np.abs(rng.normal(0.0, 0.02, (N, K // GROUP))) * (15.0 / ((1 << bits) - 1)))
     s_val = (s_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    b_bits = bf16_bits_from_f64(-8.0 * s_val + rng.normal(0.0, 0.002, (N, K // GROUP)))
-    return QWeight(name, N, K, pack_codes_low_nibble_first(q), s_bits, b_bits)
+    b_bits = bf16_bits_from_f64(-float(1 << (bits - 1)) * s_val + rng.normal(0.0, 0.002, (N, K // GROUP)))
+    return QWeight(name, N, K, pack_codes_bits(q, bits), s_bits, b_bits, bits)
 
 
 def draw_bf16_rows(rng: np.random.Generator, rows: int, K: int, sigma: float = 1.0) -> np.ndarray:
@@ -157,6 +198,8 @@ def concat_rows(*ws: QWeight, name: str = "cat") -> QWeight:
     K = ws[0].K
     if any(w.K != K for w in ws):
         raise ValueError("all matrices must share K")
+    if any(w.bits != ws[0].bits for w in ws):
+        raise ValueError("all matrices must share bits")
     return QWeight(
         name,
         sum(w.N for w in ws),
@@ -164,4 +207,5 @@ def concat_rows(*ws: QWeight, name: str = "cat") -> QWeight:
         np.concatenate([w.wq for w in ws]),
         np.concatenate([w.scales for w in ws]),
         np.concatenate([w.biases for w in ws]),
+        ws[0].bits,
     )

@@ -278,3 +278,130 @@ def test_planted_mistakes_fail_the_tolerance(kind, cfg):
     y_bad = oracle.activations_f64(x) @ W_bad.T
     ratio = np.max(np.abs(y_bad - y) / tol(A, w.K))
     assert ratio > 1.0, (kind, cfg, ratio)
+
+
+# ------------------------------------------------- 6- and 8-bit codes (MLX)
+# The pages name the 6- and 8-bit checkpoints (PR #1514, "What changes") but
+# give no layout; the reading is a little-endian bit stream per row, code k
+# at bits bits*k .. bits*k + bits - 1.
+
+
+def _stream_words(codes, bits):
+    """Words of a row built with Python integers: an independent derivation
+    of the bit-stream layout (no numpy shifts, no per-word loop)."""
+    v = 0
+    for k, c in enumerate(codes):
+        v |= int(c) << (bits * k)
+    nwords = len(codes) * bits // 32
+    return np.array([[(v >> (32 * j)) & 0xFFFFFFFF for j in range(nwords)]], dtype=np.uint32)
+
+
+def test_unpack_6bit_straddling_hand_worked():
+    # code 5 of a row: bits 30..35, so 0b111111 is the top two bits of word 0
+    # (0xC0000000) and the low four of word 1 (0x0000000F)
+    q = oracle.unpack_codes(np.array([[0xC0000000, 0x0000000F, 0]], dtype=np.uint32), 16, 6)
+    assert q[0].tolist() == [0] * 5 + [63] + [0] * 10
+    # code 10: bits 60..65; 42 = 0b101010 puts 0b1010 at the top of word 1
+    # and 0b10 at the bottom of word 2
+    q = oracle.unpack_codes(np.array([[0, 0xA0000000, 0x2]], dtype=np.uint32), 16, 6)
+    assert q[0].tolist() == [0] * 10 + [42] + [0] * 5
+    # all bits set: every code is 63
+    q = oracle.unpack_codes(np.full((1, 3), 0xFFFFFFFF, dtype=np.uint32), 16, 6)
+    assert q[0].tolist() == [63] * 16
+
+
+@pytest.mark.parametrize("bits", [6, 8])
+def test_unpack_single_code_walk(bits):
+    """Each code position alone at its maximum, then a value pattern; the
+    words come from Python integer arithmetic."""
+    K = 64
+    top = (1 << bits) - 1
+    for k in range(K):
+        codes = [0] * K
+        codes[k] = top
+        assert oracle.unpack_codes(_stream_words(codes, bits), K, bits)[0].tolist() == codes, k
+    codes = [(7 * k + 3) % (1 << bits) for k in range(K)]
+    assert oracle.unpack_codes(_stream_words(codes, bits), K, bits)[0].tolist() == codes
+
+
+def test_unpack_8bit_is_bytes_in_order():
+    q = oracle.unpack_codes(np.array([[0x04030201, 0xFFEE8000]], dtype=np.uint32), 8, 8)
+    assert q[0].tolist() == [1, 2, 3, 4, 0x00, 0x80, 0xEE, 0xFF]
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_generator_packer_and_oracle_unpack_agree(bits):
+    """The generator's chunked packer and the oracle's bit-position unpack are
+    written independently; they must invert each other."""
+    rng = np.random.default_rng(40 + bits)
+    q = rng.integers(0, 1 << bits, (5, 320), dtype=np.uint8)
+    assert np.array_equal(oracle.unpack_codes(synthetic.pack_codes_bits(q, bits), 320, bits), q)
+
+
+def _random_weight_bits(rng, N, K, bits):
+    q = rng.integers(0, 1 << bits, (N, K), dtype=np.uint8)
+    s = np.abs(rng.normal(0, 0.02, (N, K // 64))) * rng.choice([-1.0, 1.0, 0.0], size=(N, K // 64), p=[0.3, 0.6, 0.1])
+    return q, synthetic.pack_codes_bits(q, bits), _bf16(s), _bf16(rng.normal(0, 0.2, (N, K // 64)))
+
+
+@pytest.mark.parametrize("bits", [6, 8])
+@pytest.mark.parametrize("k", [0, 5, 31, 63, 64, 127])
+def test_one_hot_activation_picks_one_weight_bits(bits, k):
+    rng = np.random.default_rng(200 + 10 * bits + k)
+    N, K = 8, 128
+    q, wq, sb, bb = _random_weight_bits(rng, N, K, bits)
+    x = np.zeros((1, K), dtype=np.uint16)
+    x[0, k] = 0x3F80
+    y = oracle.matmul_rows(wq, sb, bb, x, bits=bits)[0]
+    s = oracle.bf16_to_f64(sb)[:, k // 64]
+    b = oracle.bf16_to_f64(bb)[:, k // 64]
+    assert np.array_equal(y, s * q[:, k].astype(np.float64) + b)
+
+
+@pytest.mark.parametrize("bits", [6, 8])
+def test_integer_weights_reduce_to_integer_matmul_bits(bits):
+    rng = np.random.default_rng(300 + bits)
+    N, K, M = 12, 192, 3
+    q, wq, _, _ = _random_weight_bits(rng, N, K, bits)
+    sb = np.full((N, K // 64), 0x3F80, dtype=np.uint16)
+    bb = np.zeros((N, K // 64), dtype=np.uint16)
+    xi = rng.integers(-8, 9, (M, K))
+    y = oracle.matmul_rows(wq, sb, bb, _bf16(xi.astype(np.float64)), bits=bits)
+    assert np.array_equal(y, (xi @ q.astype(np.int64).T).astype(np.float64))
+
+
+@pytest.mark.parametrize("bits", [6, 8])
+def test_fsum_equals_fraction_bruteforce_bits(bits):
+    """Exact products summed by fsum against Fraction sums whose codes are read
+    one bit at a time from the words."""
+    rng = np.random.default_rng(400 + bits)
+    N, K, M = 3, 128, 2
+    _, wq, sb, bb = _random_weight_bits(rng, N, K, bits)
+    x = _bf16(rng.normal(0, 1, (M, K)))
+    exact = oracle.matmul_rows_exact(wq, sb, bb, x, bits=bits)
+    frac = oracle.matmul_rows_fraction(wq, sb, bb, x, bits=bits)
+    for m in range(M):
+        for n in range(N):
+            assert exact[m, n] == float(frac[m][n])
+    y = oracle.matmul_rows(wq, sb, bb, x, bits=bits)
+    A = oracle.error_weight(wq, sb, bb, x, bits=bits)
+    assert np.all(np.abs(y - exact) <= (K + 2) * 2.0 ** -52 * A)
+
+
+def test_6bit_read_without_straddling_fails():
+    """A plausible mistake, planted in a copy of the decode: 6-bit codes read
+    as five per word (never straddling) disagree with the exact sums by far
+    more than the fp32 tolerance."""
+    rng = np.random.default_rng(500)
+    N, K = 4, 64
+    q, wq, sb, bb = _random_weight_bits(rng, N, K, 6)
+    wrong = np.zeros_like(q)
+    for k in range(K):
+        word = wq[:, k // 5] if k // 5 < wq.shape[1] else np.zeros(N, dtype=np.uint32)
+        wrong[:, k] = (word >> np.uint32(6 * (k % 5))) & 0x3F
+    x = _bf16(rng.normal(0, 1, (1, K)))
+    exact = oracle.matmul_rows_exact(wq, sb, bb, x, bits=6)
+    wrong_wq = synthetic.pack_codes_bits(wrong, 6)
+    y_wrong = oracle.matmul_rows(wrong_wq, sb, bb, x, bits=6)
+    T = tol(oracle.error_weight(wq, sb, bb, x, bits=6), K)
+    assert np.any(np.abs(y_wrong - exact) > T)
