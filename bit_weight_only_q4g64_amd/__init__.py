@@ -35,6 +35,11 @@ _SIGNATURES = {
     "qmv_w13_swiglu": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
     "qmm_window": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P]),
     "qmm_cut": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _I64, _P]),
+    "qg64_packed_bytes": (ctypes.c_size_t, [ctypes.c_int, _I64, _I64]),
+    "pack_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _I64, _I64, _P, _P]),
+    "unpack_qg64": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, _P, _P, _P]),
+    "qmv_rows_qg64": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, ctypes.c_int, _I64, ctypes.c_int, _P, _I64, _P]),
+    "qmv_w13_swiglu_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
     "q4g64_ffn_work_bytes": (ctypes.c_size_t, [_I64, ctypes.c_int]),
     "qmv_ffn": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P, _I64, _P, _P]),
     "q4_last_error": (ctypes.c_char_p, []),
@@ -86,41 +91,52 @@ def _rowmajor(t: torch.Tensor, name: str) -> int:
     return t.stride(0)
 
 
-def packed_bytes(N: int, K: int) -> int:
-    return int(lib().q4g64_packed_bytes(N, K))
+def packed_bytes(N: int, K: int, bits: int = 4) -> int:
+    if bits == 4:
+        return int(lib().q4g64_packed_bytes(N, K))
+    return int(lib().qg64_packed_bytes(bits, N, K))
 
 
-def pack(wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor) -> torch.Tensor:
-    """Canonical MLX q4g64 (device tensors) -> packed device layout (uint8 tensor)."""
+def pack(wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bits: int = 4) -> torch.Tensor:
+    """Canonical MLX group-64 weights of 4, 6 or 8 bits (device tensors) ->
+    packed device layout (uint8 tensor). wq is [N][K*bits/32] words."""
     for t, name in ((wq, "wq"), (scales, "scales"), (biases, "biases")):
         _dev(t, name)
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    N, K = wq.shape[0], wq.shape[1] * 8
+    N, K = wq.shape[0], wq.shape[1] * 32 // bits
     if wq.element_size() != 4 or scales.element_size() != 2 or biases.element_size() != 2:
         raise ValueError("wq holds 32-bit words, scales/biases 16-bit bf16 patterns")
     if tuple(scales.shape) != (N, K // 64) or tuple(biases.shape) != (N, K // 64):
         raise ValueError("scales and biases must be [N][K/64]")
-    nbytes = packed_bytes(N, K)
+    nbytes = packed_bytes(N, K, bits)
     if nbytes == 0:
-        raise Q4Error("pack_q4g64", Q4_EINVAL, f"invalid shape N={N} K={K}")
+        raise Q4Error("pack_qg64", Q4_EINVAL, f"invalid shape N={N} K={K} bits={bits}")
     out = torch.empty(nbytes, dtype=torch.uint8, device=wq.device)
-    _check("pack_q4g64", lib().pack_q4g64(wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), N, K, out.data_ptr(), _stream()))
+    if bits == 4:
+        _check("pack_q4g64", lib().pack_q4g64(wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), N, K, out.data_ptr(), _stream()))
+    else:
+        _check("pack_qg64",
+               lib().pack_qg64(bits, wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), N, K, out.data_ptr(), _stream()))
     return out
 
 
-def unpack(packed: torch.Tensor, N: int, K: int):
-    """Packed layout -> canonical (wq int32 [N][K/8], scales int16, biases int16 [N][K/64])."""
+def unpack(packed: torch.Tensor, N: int, K: int, bits: int = 4):
+    """Packed layout -> canonical (wq int32 [N][K*bits/32], scales int16, biases int16 [N][K/64])."""
     _dev(packed, "packed")
-    wq = torch.empty((N, K // 8), dtype=torch.int32, device=packed.device)
+    wq = torch.empty((N, K * bits // 32), dtype=torch.int32, device=packed.device)
     sc = torch.empty((N, K // 64), dtype=torch.int16, device=packed.device)
     bi = torch.empty((N, K // 64), dtype=torch.int16, device=packed.device)
-    _check("unpack_q4g64", lib().unpack_q4g64(packed.data_ptr(), N, K, wq.data_ptr(), sc.data_ptr(), bi.data_ptr(), _stream()))
+    if bits == 4:
+        _check("unpack_q4g64", lib().unpack_q4g64(packed.data_ptr(), N, K, wq.data_ptr(), sc.data_ptr(), bi.data_ptr(), _stream()))
+    else:
+        _check("unpack_qg64",
+               lib().unpack_qg64(bits, packed.data_ptr(), N, K, wq.data_ptr(), sc.data_ptr(), bi.data_ptr(), _stream()))
     return wq, sc, bi
 
 
-def qmv_rows(packed: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
-    """y[r] = W x[r] for the R = x.shape[0] (1..16) rows of x (bf16 or float32)."""
+def qmv_rows(packed: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None, bits: int = 4) -> torch.Tensor:
+    """y[r] = W x[r] for the R = x.shape[0] (1..16) rows of x (bf16 or float32); W has 4-, 6- or 8-bit codes."""
     _dev(packed, "packed")
     _dev(x, "x")
     ldx = _rowmajor(x, "x")
@@ -135,12 +151,17 @@ def qmv_rows(packed: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Ten
         y = torch.empty((R, N), dtype=torch.float32, device=x.device)
     if y.dtype != torch.float32 or y.shape[0] < R:
         raise ValueError("y must be float32 with at least R rows")
-    _check("qmv_rows", lib().qmv_rows(packed.data_ptr(), N, K, x.data_ptr(), xd, ldx, R, y.data_ptr(), _rowmajor(y, "y"), _stream()))
+    if bits == 4:
+        _check("qmv_rows", lib().qmv_rows(packed.data_ptr(), N, K, x.data_ptr(), xd, ldx, R, y.data_ptr(), _rowmajor(y, "y"), _stream()))
+    else:
+        _check("qmv_rows_qg64",
+               lib().qmv_rows_qg64(bits, packed.data_ptr(), N, K, x.data_ptr(), xd, ldx, R, y.data_ptr(), _rowmajor(y, "y"), _stream()))
     return y
 
 
-def qmv_w13_swiglu(p1: torch.Tensor, p3: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
-    """y[r] = silu(W1 x[r]) * (W3 x[r]) for the 1..16 bf16 rows of x."""
+def qmv_w13_swiglu(p1: torch.Tensor, p3: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None,
+                   bits: int = 4) -> torch.Tensor:
+    """y[r] = silu(W1 x[r]) * (W3 x[r]) for the 1..16 bf16 rows of x; W1, W3 have 4-, 6- or 8-bit codes."""
     _dev(p1, "packed_w1")
     _dev(p3, "packed_w3")
     _dev(x, "x")
@@ -149,10 +170,18 @@ def qmv_w13_swiglu(p1: torch.Tensor, p3: torch.Tensor, N: int, K: int, x: torch.
     R = x.shape[0]
     if y is None:
         y = torch.empty((R, N), dtype=torch.float32, device=x.device)
-    _check(
-        "qmv_w13_swiglu",
-        lib().qmv_w13_swiglu(p1.data_ptr(), p3.data_ptr(), N, K, x.data_ptr(), _rowmajor(x, "x"), R, y.data_ptr(), _rowmajor(y, "y"), _stream()),
-    )
+    if bits == 4:
+        _check(
+            "qmv_w13_swiglu",
+            lib().qmv_w13_swiglu(p1.data_ptr(), p3.data_ptr(), N, K, x.data_ptr(), _rowmajor(x, "x"), R, y.data_ptr(), _rowmajor(y, "y"),
+                                 _stream()),
+        )
+    else:
+        _check(
+            "qmv_w13_swiglu_qg64",
+            lib().qmv_w13_swiglu_qg64(bits, p1.data_ptr(), p3.data_ptr(), N, K, x.data_ptr(), _rowmajor(x, "x"), R, y.data_ptr(),
+                                      _rowmajor(y, "y"), _stream()),
+        )
     return y
 
 

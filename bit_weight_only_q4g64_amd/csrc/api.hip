@@ -33,6 +33,9 @@ constexpr size_t kMaxLds = 64 * 1024;
 // with 32-bit offsets.
 constexpr int64_t kPgemmMaxK = int64_t(1) << 20;
 constexpr int64_t kPgemmMaxM = int64_t(1) << 24;
+// One-launch FFN step: at most two segments per wave in each phase.
+constexpr int64_t kFfnMaxK1 = 4096;
+constexpr int64_t kFfnMaxN1 = 8192;
 
 int check_nk(const char* fn, int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || N % 64 != 0 || K % 64 != 0)
@@ -68,6 +71,101 @@ int check_x(const char* fn, const void* x, int x_dtype, int64_t ldx, int64_t K) 
   const int64_t es = x_dtype == Q4_BF16 ? 2 : 4;
   if ((ldx * es) % 16 != 0) return fail(Q4_EALIGN, "%s: ldx=%lld elements does not keep rows 16-byte aligned", fn, (long long)ldx);
   return Q4_OK;
+}
+
+int check_bits(const char* fn, int bits) {
+  if (bits != 4 && bits != 6 && bits != 8) return fail(Q4_EINVAL, "%s: bits=%d is not 4, 6 or 8", fn, bits);
+  return Q4_OK;
+}
+
+size_t packed_bytes_impl(int bits, int64_t N, int64_t K) {
+  if (bits != 4 && bits != 6 && bits != 8) return 0;
+  if (N <= 0 || K <= 0 || N % 64 != 0 || K % 64 != 0 || N > kMaxDim || K > kMaxDim || N * K > kMaxElems) return 0;
+  return (size_t)q4::packed_bytes(N, K, bits);
+}
+
+int pack_impl(const char* fn, int bits, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, int64_t N, int64_t K,
+              void* packed, hipStream_t s) {
+  if (int rc = check_bits(fn, bits)) return rc;
+  if (int rc = check_nk(fn, N, K)) return rc;
+  if (int rc = check_ptr(fn, "wq", wq, 16)) return rc;
+  if (int rc = check_ptr(fn, "scales", scales, 2)) return rc;
+  if (int rc = check_ptr(fn, "biases", biases, 2)) return rc;
+  if (int rc = check_ptr(fn, "packed", packed, 16)) return rc;
+  const int64_t words = q4::codes_bytes(N, K, bits) / 4;
+  const int64_t sb_entries = (N / q4::kTileN) * q4::n_pairs(K) * q4::kTileN;
+  uint8_t* out = (uint8_t*)packed;
+  if (bits == 4)
+    hipLaunchKernelGGL(q4::pack_codes_kernel, dim3(grid_for(words, 256)), dim3(256), 0, s, wq, N, K, (uint32_t*)out);
+  else if (bits == 6)
+    hipLaunchKernelGGL(q4::pack_codes_wide_kernel<6>, dim3(grid_for(words, 256)), dim3(256), 0, s, wq, N, K, (uint32_t*)out);
+  else
+    hipLaunchKernelGGL(q4::pack_codes_wide_kernel<8>, dim3(grid_for(words, 256)), dim3(256), 0, s, wq, N, K, (uint32_t*)out);
+  if (int rc = launched(fn)) return rc;
+  hipLaunchKernelGGL(q4::pack_sb_kernel, dim3(grid_for(sb_entries, 256)), dim3(256), 0, s, scales, biases, N, K,
+                     (q4::u32x2*)(out + q4::codes_bytes(N, K, bits)));
+  return launched(fn);
+}
+
+int unpack_impl(const char* fn, int bits, const void* packed, int64_t N, int64_t K, uint32_t* wq, uint16_t* scales,
+                uint16_t* biases, hipStream_t s) {
+  if (int rc = check_bits(fn, bits)) return rc;
+  if (int rc = check_nk(fn, N, K)) return rc;
+  if (int rc = check_ptr(fn, "packed", packed, 16)) return rc;
+  if (int rc = check_ptr(fn, "wq", wq, 16)) return rc;
+  if (int rc = check_ptr(fn, "scales", scales, 2)) return rc;
+  if (int rc = check_ptr(fn, "biases", biases, 2)) return rc;
+  const uint8_t* in = (const uint8_t*)packed;
+  const int64_t cwords = N * (K * bits / 32);
+  if (bits == 4)
+    hipLaunchKernelGGL(q4::unpack_codes_kernel, dim3(grid_for(cwords, 256)), dim3(256), 0, s, (const uint32_t*)in, N, K, wq);
+  else if (bits == 6)
+    hipLaunchKernelGGL(q4::unpack_codes_wide_kernel<6>, dim3(grid_for(cwords, 256)), dim3(256), 0, s, (const uint32_t*)in, N, K, wq);
+  else
+    hipLaunchKernelGGL(q4::unpack_codes_wide_kernel<8>, dim3(grid_for(cwords, 256)), dim3(256), 0, s, (const uint32_t*)in, N, K, wq);
+  if (int rc = launched(fn)) return rc;
+  hipLaunchKernelGGL(q4::unpack_sb_kernel, dim3(grid_for(N * (K / 64), 256)), dim3(256), 0, s,
+                     (const q4::u32x2*)(in + q4::codes_bytes(N, K, bits)), N, K, scales, biases);
+  return launched(fn);
+}
+
+int qmv_rows_impl(const char* fn, int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx,
+                  int R, float* y, int64_t ldy, hipStream_t s) {
+  if (int rc = check_bits(fn, bits)) return rc;
+  if (int rc = check_nk(fn, N, K)) return rc;
+  if (R < 1 || R > 16) return fail(Q4_EINVAL, "%s: R=%d is outside 1..16", fn, R);
+  if (int rc = check_ptr(fn, "packed", packed, 16)) return rc;
+  if (int rc = check_x(fn, x, x_dtype, ldx, K)) return rc;
+  if (int rc = check_ptr(fn, "y", y, 4)) return rc;
+  if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  if ((int64_t)R * ldx * (x_dtype == Q4_F32 ? 4 : 2) >= (int64_t(1) << 31))
+    return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
+  // up to 4 segments per wave, 16 waves: K <= 16384
+  if (K > q4::kQmvMaxK) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
+  const size_t lds = q4::qmv_lds_bytes(K, x_dtype == Q4_F32, 1, R);
+  if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
+  q4::qmv_launch((const uint8_t*)packed, (const uint8_t*)packed, 1, (int)N, (int)K, x, x_dtype == Q4_F32, ldx, R, y, ldy, s, bits);
+  return launched(fn);
+}
+
+int qmv_w13_impl(const char* fn, int bits, const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
+                 int64_t ldx, int R, float* y, int64_t ldy, hipStream_t s) {
+  if (int rc = check_bits(fn, bits)) return rc;
+  if (int rc = check_nk(fn, N, K)) return rc;
+  if (R < 1 || R > 16) return fail(Q4_EINVAL, "%s: R=%d is outside 1..16", fn, R);
+  if (int rc = check_ptr(fn, "packed_w1", packed_w1, 16)) return rc;
+  if (int rc = check_ptr(fn, "packed_w3", packed_w3, 16)) return rc;
+  if (int rc = check_x(fn, x, Q4_BF16, ldx, K)) return rc;
+  if (int rc = check_ptr(fn, "y", y, 4)) return rc;
+  if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  if ((int64_t)R * ldx * 2 >= (int64_t(1) << 31))
+    return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
+  // up to 2 segments per wave, 16 waves: K <= 8192
+  if (K > q4::kQmvMaxK / 2) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the fused decode limit of 8192", fn, (long long)K);
+  const size_t lds = q4::qmv_lds_bytes(K, 0, 2, R);
+  if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the fused decode limit of 8192", fn, (long long)K);
+  q4::qmv_launch((const uint8_t*)packed_w1, (const uint8_t*)packed_w3, 2, (int)N, (int)K, x, 0, ldx, R, y, ldy, s, bits);
+  return launched(fn);
 }
 
 // Workgroup grid of a window: column blocks x row blocks, as one dimension.
@@ -147,8 +245,7 @@ template <int NV, int RTF, int SPW1>
 int ffn_launch_s2(int spw2, const uint8_t* p1, const uint8_t* p3, const uint8_t* p2, int N1, int K1, int N2, const uint16_t* x,
                   int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, uint8_t* work, size_t lds, hipStream_t s) {
   if (spw2 <= 1) return ffn_launch_t<NV, RTF, SPW1, 1>(p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
-  if (spw2 <= 2) return ffn_launch_t<NV, RTF, SPW1, 2>(p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
-  return ffn_launch_t<NV, RTF, SPW1, 4>(p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
+  return ffn_launch_t<NV, RTF, SPW1, 2>(p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
 }
 
 template <int NV, int RTF>
@@ -156,8 +253,7 @@ int ffn_launch_s1(int spw1, int spw2, const uint8_t* p1, const uint8_t* p3, cons
                   const uint16_t* x, int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, uint8_t* work, size_t lds,
                   hipStream_t s) {
   if (spw1 <= 1) return ffn_launch_s2<NV, RTF, 1>(spw2, p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
-  if (spw1 <= 2) return ffn_launch_s2<NV, RTF, 2>(spw2, p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
-  return ffn_launch_s2<NV, RTF, 4>(spw2, p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
+  return ffn_launch_s2<NV, RTF, 2>(spw2, p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
 }
 
 }  // namespace
@@ -168,86 +264,48 @@ int q4g64_abi_version(void) { return 1; }
 
 const char* q4_last_error(void) { return g_err; }
 
-size_t q4g64_packed_bytes(int64_t N, int64_t K) {
-  if (N <= 0 || K <= 0 || N % 64 != 0 || K % 64 != 0 || N > kMaxDim || K > kMaxDim || N * K > kMaxElems) return 0;
-  return (size_t)q4::packed_bytes(N, K);
-}
+size_t q4g64_packed_bytes(int64_t N, int64_t K) { return packed_bytes_impl(4, N, K); }
+
+size_t qg64_packed_bytes(int bits, int64_t N, int64_t K) { return packed_bytes_impl(bits, N, K); }
 
 int pack_q4g64(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, int64_t N, int64_t K, void* packed,
                void* stream) {
-  const char* fn = "pack_q4g64";
-  if (int rc = check_nk(fn, N, K)) return rc;
-  if (int rc = check_ptr(fn, "wq", wq, 16)) return rc;
-  if (int rc = check_ptr(fn, "scales", scales, 2)) return rc;
-  if (int rc = check_ptr(fn, "biases", biases, 2)) return rc;
-  if (int rc = check_ptr(fn, "packed", packed, 16)) return rc;
-  hipStream_t s = (hipStream_t)stream;
-  const int64_t words = q4::codes_bytes(N, K) / 4;
-  const int64_t sb_entries = (N / q4::kTileN) * q4::n_pairs(K) * q4::kTileN;
-  uint8_t* out = (uint8_t*)packed;
-  hipLaunchKernelGGL(q4::pack_codes_kernel, dim3(grid_for(words, 256)), dim3(256), 0, s, wq, N, K, (uint32_t*)out);
-  if (int rc = launched(fn)) return rc;
-  hipLaunchKernelGGL(q4::pack_sb_kernel, dim3(grid_for(sb_entries, 256)), dim3(256), 0, s, scales, biases, N, K,
-                     (q4::u32x2*)(out + q4::codes_bytes(N, K)));
-  return launched(fn);
+  return pack_impl("pack_q4g64", 4, wq, scales, biases, N, K, packed, (hipStream_t)stream);
+}
+
+int pack_qg64(int bits, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, int64_t N, int64_t K, void* packed,
+              void* stream) {
+  return pack_impl("pack_qg64", bits, wq, scales, biases, N, K, packed, (hipStream_t)stream);
 }
 
 int unpack_q4g64(const void* packed, int64_t N, int64_t K, uint32_t* wq, uint16_t* scales, uint16_t* biases,
                  void* stream) {
-  const char* fn = "unpack_q4g64";
-  if (int rc = check_nk(fn, N, K)) return rc;
-  if (int rc = check_ptr(fn, "packed", packed, 16)) return rc;
-  if (int rc = check_ptr(fn, "wq", wq, 16)) return rc;
-  if (int rc = check_ptr(fn, "scales", scales, 2)) return rc;
-  if (int rc = check_ptr(fn, "biases", biases, 2)) return rc;
-  hipStream_t s = (hipStream_t)stream;
-  const uint8_t* in = (const uint8_t*)packed;
-  hipLaunchKernelGGL(q4::unpack_codes_kernel, dim3(grid_for(N * (K / 8), 256)), dim3(256), 0, s, (const uint32_t*)in, N, K, wq);
-  if (int rc = launched(fn)) return rc;
-  hipLaunchKernelGGL(q4::unpack_sb_kernel, dim3(grid_for(N * (K / 64), 256)), dim3(256), 0, s,
-                     (const q4::u32x2*)(in + q4::codes_bytes(N, K)), N, K, scales, biases);
-  return launched(fn);
+  return unpack_impl("unpack_q4g64", 4, packed, N, K, wq, scales, biases, (hipStream_t)stream);
+}
+
+int unpack_qg64(int bits, const void* packed, int64_t N, int64_t K, uint32_t* wq, uint16_t* scales, uint16_t* biases,
+                void* stream) {
+  return unpack_impl("unpack_qg64", bits, packed, N, K, wq, scales, biases, (hipStream_t)stream);
 }
 
 int qmv_rows(const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R, float* y,
              int64_t ldy, void* stream) {
-  const char* fn = "qmv_rows";
-  if (int rc = check_nk(fn, N, K)) return rc;
-  if (R < 1 || R > 16) return fail(Q4_EINVAL, "%s: R=%d is outside 1..16", fn, R);
-  if (int rc = check_ptr(fn, "packed", packed, 16)) return rc;
-  if (int rc = check_x(fn, x, x_dtype, ldx, K)) return rc;
-  if (int rc = check_ptr(fn, "y", y, 4)) return rc;
-  if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
-  if ((int64_t)R * ldx * (x_dtype == Q4_F32 ? 4 : 2) >= (int64_t(1) << 31))
-    return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
-  // up to 4 segments per wave, 16 waves: K <= 16384
-  if (K > q4::kQmvMaxK) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
-  const size_t lds = q4::qmv_lds_bytes(K, x_dtype == Q4_F32, 1, R);
-  if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
-  q4::qmv_launch((const uint8_t*)packed, (const uint8_t*)packed, 1, (int)N, (int)K, x, x_dtype == Q4_F32, ldx, R, y, ldy,
-                 (hipStream_t)stream);
-  return launched(fn);
+  return qmv_rows_impl("qmv_rows", 4, packed, N, K, x, x_dtype, ldx, R, y, ldy, (hipStream_t)stream);
+}
+
+int qmv_rows_qg64(int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R, float* y,
+                  int64_t ldy, void* stream) {
+  return qmv_rows_impl("qmv_rows_qg64", bits, packed, N, K, x, x_dtype, ldx, R, y, ldy, (hipStream_t)stream);
 }
 
 int qmv_w13_swiglu(const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                    int R, float* y, int64_t ldy, void* stream) {
-  const char* fn = "qmv_w13_swiglu";
-  if (int rc = check_nk(fn, N, K)) return rc;
-  if (R < 1 || R > 16) return fail(Q4_EINVAL, "%s: R=%d is outside 1..16", fn, R);
-  if (int rc = check_ptr(fn, "packed_w1", packed_w1, 16)) return rc;
-  if (int rc = check_ptr(fn, "packed_w3", packed_w3, 16)) return rc;
-  if (int rc = check_x(fn, x, Q4_BF16, ldx, K)) return rc;
-  if (int rc = check_ptr(fn, "y", y, 4)) return rc;
-  if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
-  if ((int64_t)R * ldx * 2 >= (int64_t(1) << 31))
-    return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
-  // up to 2 segments per wave, 16 waves: K <= 8192
-  if (K > q4::kQmvMaxK / 2) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the fused decode limit of 8192", fn, (long long)K);
-  const size_t lds = q4::qmv_lds_bytes(K, 0, 2, R);
-  if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the fused decode limit of 8192", fn, (long long)K);
-  q4::qmv_launch((const uint8_t*)packed_w1, (const uint8_t*)packed_w3, 2, (int)N, (int)K, x, 0, ldx, R, y, ldy,
-                 (hipStream_t)stream);
-  return launched(fn);
+  return qmv_w13_impl("qmv_w13_swiglu", 4, packed_w1, packed_w3, N, K, x, ldx, R, y, ldy, (hipStream_t)stream);
+}
+
+int qmv_w13_swiglu_qg64(int bits, const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
+                        int64_t ldx, int R, float* y, int64_t ldy, void* stream) {
+  return qmv_w13_impl("qmv_w13_swiglu_qg64", bits, packed_w1, packed_w3, N, K, x, ldx, R, y, ldy, (hipStream_t)stream);
 }
 
 int qmm_window(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx, int64_t M,
@@ -300,9 +358,10 @@ int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2,
   if (ldy < N2) return fail(Q4_EINVAL, "%s: ldy=%lld < N2=%lld", fn, (long long)ldy, (long long)N2);
   if ((int64_t)R * ldx * 2 >= (int64_t(1) << 31))
     return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
-  // 8 waves per w1/w3 tile and 16 per w2 half-tile, up to 4 segments each
-  if (K1 > q4::kQmvMaxK / 2) return fail(Q4_EUNSUPPORTED, "%s: K1=%lld exceeds the fused decode limit of 8192", fn, (long long)K1);
-  if (N1 > q4::kQmvMaxK) return fail(Q4_EUNSUPPORTED, "%s: N1=%lld exceeds the decode limit of 16384", fn, (long long)N1);
+  // 8 waves per w1/w3 tile and 16 per w2 half-tile, up to 2 segments each
+  // (a 1024-thread workgroup leaves 128 registers per lane; more segments spill)
+  if (K1 > kFfnMaxK1) return fail(Q4_EUNSUPPORTED, "%s: K1=%lld exceeds the one-launch step limit of 4096", fn, (long long)K1);
+  if (N1 > kFfnMaxN1) return fail(Q4_EUNSUPPORTED, "%s: N1=%lld exceeds the one-launch step limit of 8192", fn, (long long)N1);
   const size_t lds = q4::ffn_lds_bytes(K1, N1, R, false);
   if (lds > q4::qmv_max_lds()) return fail(Q4_EUNSUPPORTED, "%s: K1=%lld with R=%d needs %zu bytes of LDS", fn, (long long)K1, R, lds);
   const int nseg1 = q4::qmv_segments(K1), nseg2 = q4::qmv_segments(N1);

@@ -32,13 +32,16 @@ constexpr int kTileN = 16;        // output columns per column tile
 constexpr int kPairCodeBytes = 1024;  // codes of one column tile x 128 k (two groups)
 constexpr int kPairSbBytes = 128;     // scale+bias of one column tile x two groups
 
-// Device layout sizes (see include/q4g64.h for the full description).
+// Device layout sizes (see include/q4g64.h for the full description). Codes
+// of b bits take 256 * b bytes per column tile and group pair; the scale/bias
+// block is the same for every width.
+__host__ __device__ constexpr int pair_code_bytes(int bits) { return 256 * bits; }
 __host__ __device__ inline int64_t n_pairs(int64_t K) { return (K / kGroup + 1) / 2; }
-__host__ __device__ inline int64_t codes_bytes(int64_t N, int64_t K) {
-  return (N / kTileN) * n_pairs(K) * kPairCodeBytes;
+__host__ __device__ inline int64_t codes_bytes(int64_t N, int64_t K, int bits = 4) {
+  return (N / kTileN) * n_pairs(K) * pair_code_bytes(bits);
 }
-__host__ __device__ inline int64_t packed_bytes(int64_t N, int64_t K) {
-  return (N / kTileN) * n_pairs(K) * (kPairCodeBytes + kPairSbBytes);
+__host__ __device__ inline int64_t packed_bytes(int64_t N, int64_t K, int bits = 4) {
+  return (N / kTileN) * n_pairs(K) * (pair_code_bytes(bits) + kPairSbBytes);
 }
 
 // Position of code e (k offset e within an 8-code word) in a device word.
@@ -59,6 +62,68 @@ __device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t w) {
   const auto c0123 = __builtin_shufflevector(c01, c23, 0, 1, 2, 3);
   const auto c4567 = __builtin_shufflevector(c45, c67, 0, 1, 2, 3);
   return __builtin_shufflevector(c0123, c4567, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// 8 codes given as bytes (codes 0..3 in w0, 4..7 in w1, byte e = code e) ->
+// 8 exact bf16 integers in k order. A byte converts exactly to float32 and
+// an integer below 256 has at most 8 significant bits, so its float32 bits
+// end in 16 zeros and the top half is the exact bf16.
+__device__ __forceinline__ bf16x8 bytes_to_bf16(uint32_t w0, uint32_t w1) {
+  auto pair = [](uint32_t w, int sh) -> uint32_t {
+    const float f0 = (float)((w >> sh) & 0xFFu), f1 = (float)((w >> (sh + 8)) & 0xFFu);
+    return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  };
+  const u32x4 v = {pair(w0, 0), pair(w0, 16), pair(w1, 0), pair(w1, 16)};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// 8 six-bit codes: the low nibbles in a 4-bit device word (nib) and the high
+// bit pairs in byte lanes of H (half 0 of a group: bits 0-1 codes 0..3, bits
+// 2-3 codes 4..7; half 1: bits 4-5 and 6-7) -> codes as bytes -> exact bf16.
+template <int HALF>
+__device__ __forceinline__ bf16x8 six_to_bf16(uint32_t nib, uint32_t H) {
+  uint32_t lo = nib & 0x0F0F0F0Fu, hi = (nib >> 4) & 0x0F0F0F0Fu;
+  if constexpr (HALF == 0) {
+    lo |= (H & 0x03030303u) << 4;
+    hi |= (H & 0x0C0C0C0Cu) << 2;
+  } else {
+    lo |= H & 0x30303030u;
+    hi |= (H >> 2) & 0x30303030u;
+  }
+  return bytes_to_bf16(lo, hi);
+}
+
+// One lane's codes of one group pair (halves h = 0..3: group h >> 1, half
+// h & 1). 4-bit: a[h]. 6-bit: low nibbles a[h], high pairs b[h >> 1].
+// 8-bit: a = group 0 (half hh in a[2hh], a[2hh + 1]), b = group 1.
+template <int BITS>
+struct CodeWords;
+template <>
+struct CodeWords<4> {
+  u32x4 a;
+};
+template <>
+struct CodeWords<6> {
+  u32x4 a;
+  u32x2 b;
+};
+template <>
+struct CodeWords<8> {
+  u32x4 a;
+  u32x4 b;
+};
+
+// The bf16 B-operand fragment of group gh (0/1 within the pair), half hh.
+template <int BITS, int GH, int HH>
+__device__ __forceinline__ bf16x8 code_frag(const CodeWords<BITS>& c) {
+  if constexpr (BITS == 4) {
+    return codes_to_bf16(c.a[2 * GH + HH]);
+  } else if constexpr (BITS == 6) {
+    return six_to_bf16<HH>(c.a[2 * GH + HH], c.b[GH]);
+  } else {
+    if constexpr (GH == 0) return bytes_to_bf16(c.a[2 * HH], c.a[2 * HH + 1]);
+    else return bytes_to_bf16(c.b[2 * HH], c.b[2 * HH + 1]);
+  }
 }
 
 __device__ __forceinline__ bf16x8 ones_bf16x8() {

@@ -54,9 +54,9 @@ __host__ __device__ inline size_t qmv_xs_bytes(int64_t K, int xf32, int R) {
 
 // Weight registers of one wave's segments of one column tile (codes: one
 // 128-bit word per lane per pair; scale/bias: one 64-bit word per pair).
-template <int NMAT, int SPW>
+template <int NMAT, int SPW, int BITS = 4>
 struct QmvWeights {
-  u32x4 cw[SPW][NMAT][kSegPairs];
+  CodeWords<BITS> cw[SPW][NMAT][kSegPairs];
   u32x2 sbw[SPW][NMAT][kSegPairs];
 };
 
@@ -65,11 +65,13 @@ struct QmvWeights {
 // used). Lanes with on == false read past the buffer's end, which the
 // hardware answers with zeros and no memory access: the loads stay
 // unconditional, so the count of loads in flight is the same on every path.
-template <int NMAT, int SPW>
-__device__ __forceinline__ void qmv_issue_weights(QmvWeights<NMAT, SPW>& w, const rsrc_t (&cres)[NMAT], const rsrc_t (&sres)[NMAT],
+template <int NMAT, int SPW, int BITS = 4>
+__device__ __forceinline__ void qmv_issue_weights(QmvWeights<NMAT, SPW, BITS>& w, const rsrc_t (&cres)[NMAT], const rsrc_t (&sres)[NMAT],
                                                   int seg0, int step, int P, int lane, bool on) {
   const int i = lane & 15;
+  constexpr uint32_t kPcb = pair_code_bytes(BITS);
   const uint32_t cv = on ? (uint32_t)lane * 16u : kOffBuffer, sv = on ? (uint32_t)i * 8u : kOffBuffer;
+  const uint32_t cv8 = on ? (uint32_t)lane * 8u : kOffBuffer;
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int seg = seg0 + j * step;
@@ -79,7 +81,9 @@ __device__ __forceinline__ void qmv_issue_weights(QmvWeights<NMAT, SPW>& w, cons
       p = p < P ? p : P - 1;
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
-        w.cw[j][m][pp] = buf_load16(cres[m], cv, (uint32_t)p * kPairCodeBytes);
+        w.cw[j][m][pp].a = buf_load16(cres[m], cv, (uint32_t)p * kPcb);
+        if constexpr (BITS == 6) w.cw[j][m][pp].b = buf_load8(cres[m], cv8, (uint32_t)p * kPcb + 1024u);
+        if constexpr (BITS == 8) w.cw[j][m][pp].b = buf_load16(cres[m], cv, (uint32_t)p * kPcb + 1024u);
         w.sbw[j][m][pp] = buf_load8(sres[m], sv, (uint32_t)p * kPairSbBytes);
       }
     }
@@ -93,8 +97,8 @@ __device__ __forceinline__ void qmv_issue_weights(QmvWeights<NMAT, SPW>& w, cons
 //   S = the same with q replaced by ones
 //   acc = fma(s_g, P, fma(b_g, S, acc))
 // with float32 rows combining their three pieces in-lane first.
-template <int XF32, int NMAT, int kRT, int kPerLane, typename XF>
-__device__ __forceinline__ void qmv_fold_segment(float (&acc)[NMAT][kRT][kPerLane], const u32x4 (&cw)[NMAT][kSegPairs],
+template <int XF32, int NMAT, int kRT, int kPerLane, int BITS, typename XF>
+__device__ __forceinline__ void qmv_fold_segment(float (&acc)[NMAT][kRT][kPerLane], const CodeWords<BITS> (&cw)[NMAT][kSegPairs],
                                                  const u32x2 (&sbw)[NMAT][kSegPairs], int g0, int G, const XF& xfrag) {
   const bf16x8 ones = ones_bf16x8();
 #pragma unroll
@@ -112,8 +116,8 @@ __device__ __forceinline__ void qmv_fold_segment(float (&acc)[NMAT][kRT][kPerLan
     float sc[NMAT], bs[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
-      q[m][0] = codes_to_bf16(gh ? cw[m][pp][2] : cw[m][pp][0]);
-      q[m][1] = codes_to_bf16(gh ? cw[m][pp][3] : cw[m][pp][1]);
+      q[m][0] = gh ? code_frag<BITS, 1, 0>(cw[m][pp]) : code_frag<BITS, 0, 0>(cw[m][pp]);
+      q[m][1] = gh ? code_frag<BITS, 1, 1>(cw[m][pp]) : code_frag<BITS, 0, 1>(cw[m][pp]);
       const uint32_t w = gh ? sbw[m][pp][1] : sbw[m][pp][0];
       sc[m] = bf16_lo(w);
       bs[m] = bf16_hi(w);
@@ -188,7 +192,7 @@ __device__ __forceinline__ void qmv_ordered_sum(float (&tot)[NMAT][kRT][kPerLane
 // workgroup (else each wave reads its fragments from global memory). NV:
 // row slots per lane group kept by the bf16 path. None of these changes the
 // arithmetic of a stored row.
-template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV>
+template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS>
 __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* __restrict__ pk0, const uint8_t* __restrict__ pk1,
                                                               int N, int K, const void* __restrict__ xv, int64_t ldx, int R,
                                                               float* __restrict__ y, int64_t ldy) {
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   const int G = K / kGroup;
   const int P = (G + 1) / 2;
   const int nseg = qmv_segments(K);
-  const int64_t cb = codes_bytes(N, K);
+  const int64_t cb = codes_bytes(N, K, BITS);
   const int xsi = (int)qmv_xs_stride(K);
   const uint32_t xrow = (uint32_t)(ldx * kXElem);  // bytes per activation row
 
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
 #pragma unroll
   for (int m = 0; m < NMAT; ++m) {
     const uint8_t* pk = m ? pk1 : pk0;
-    cres[m] = make_rsrc(pk + (int64_t)t * P * kPairCodeBytes, (uint32_t)P * kPairCodeBytes);
+    cres[m] = make_rsrc(pk + (int64_t)t * P * pair_code_bytes(BITS), (uint32_t)P * pair_code_bytes(BITS));
     sres[m] = make_rsrc(pk + cb + (int64_t)t * P * kPairSbBytes, (uint32_t)P * kPairSbBytes);
   }
   const rsrc_t xres = make_rsrc(xv, (uint32_t)R * xrow);
@@ -247,8 +251,8 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   }
 
   // 2) every weight load of this wave's segments
-  QmvWeights<NMAT, SPW> wts;
-  qmv_issue_weights<NMAT, SPW>(wts, cres, sres, wave, nwaves, P, lane, true);
+  QmvWeights<NMAT, SPW, BITS> wts;
+  qmv_issue_weights<NMAT, SPW, BITS>(wts, cres, sres, wave, nwaves, P, lane, true);
 
   // 3) write the staged activations (float32 rows as three exact bf16 planes)
   if constexpr (XLDS) {
@@ -388,10 +392,10 @@ inline size_t qmv_lds_bytes(int64_t K, int xf32, int nmat, int R) {
   return qmv_part_bytes(K, xf32, nmat, qmv_row_tiles(xf32, R), xf32 ? 1 : qmv_nv(R));
 }
 
-template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV>
+template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS>
 inline void qmv_launch_t(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
                          int64_t ldy, int nwaves, size_t lds, hipStream_t s) {
-  auto kern = qmv_kernel<XF32, NMAT, SPW, RTF, XLDS, NV>;
+  auto kern = qmv_kernel<XF32, NMAT, SPW, RTF, XLDS, NV, BITS>;
   // allow dynamic LDS beyond the 64 KB default, once per instantiation
   static const bool lds_ok =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)qmv_max_lds()) == hipSuccess;
@@ -399,61 +403,73 @@ inline void qmv_launch_t(const uint8_t* pk0, const uint8_t* pk1, int N, int K, c
   hipLaunchKernelGGL(kern, dim3((unsigned)(N / kTileN)), dim3(nwaves * 64), lds, s, pk0, pk1, N, K, x, ldx, R, y, ldy);
 }
 
-template <int XF32, int NMAT, int RTF, bool XLDS, int NV>
+template <int XF32, int NMAT, int RTF, bool XLDS, int NV, int BITS>
 inline void qmv_launch_spw(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
                            int64_t ldy, size_t lds, hipStream_t s) {
   const int nseg = qmv_segments(K);
   const int nwaves = nseg < kQmvMaxWaves ? nseg : kQmvMaxWaves;
   const int spw = (nseg + nwaves - 1) / nwaves;
   if (spw <= 1) {
-    qmv_launch_t<XF32, NMAT, 1, RTF, XLDS, NV>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
+    qmv_launch_t<XF32, NMAT, 1, RTF, XLDS, NV, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
   } else if (spw <= 2) {
-    qmv_launch_t<XF32, NMAT, 2, RTF, XLDS, NV>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
+    qmv_launch_t<XF32, NMAT, 2, RTF, XLDS, NV, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
   } else {
     // the fused two-matrix variant is limited to K <= 8192 (two segments per wave)
-    if constexpr (NMAT == 1) qmv_launch_t<XF32, NMAT, 4, RTF, XLDS, NV>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
+    if constexpr (NMAT == 1) qmv_launch_t<XF32, NMAT, 4, RTF, XLDS, NV, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
   }
 }
 
-template <int XF32, int NMAT, int RTF, int NV>
+template <int XF32, int NMAT, int RTF, int NV, int BITS>
 inline void qmv_launch_lds(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
                            int64_t ldy, hipStream_t s) {
   const size_t part = qmv_part_bytes(K, XF32, NMAT, XF32 ? RTF : 1, NV);
   const size_t staged = part + qmv_xs_bytes(K, XF32, R);
   if (staged <= qmv_max_lds())
-    qmv_launch_spw<XF32, NMAT, RTF, true, NV>(pk0, pk1, N, K, x, ldx, R, y, ldy, staged, s);
+    qmv_launch_spw<XF32, NMAT, RTF, true, NV, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, staged, s);
   else
-    qmv_launch_spw<XF32, NMAT, RTF, false, NV>(pk0, pk1, N, K, x, ldx, R, y, ldy, part, s);
+    qmv_launch_spw<XF32, NMAT, RTF, false, NV, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, part, s);
 }
 
-template <int NMAT>
+template <int NMAT, int BITS>
 inline void qmv_launch_bf16(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
                             int64_t ldy, hipStream_t s) {
   const int nv = qmv_nv(R);
   if (nv == 1)
-    qmv_launch_lds<0, NMAT, 1, 1>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<0, NMAT, 1, 1, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
   else if (nv == 2)
-    qmv_launch_lds<0, NMAT, 1, 2>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<0, NMAT, 1, 2, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
   else
-    qmv_launch_lds<0, NMAT, 1, 4>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<0, NMAT, 1, 4, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
 }
 
-inline void qmv_launch(const uint8_t* pk0, const uint8_t* pk1, int nmat, int N, int K, const void* x, int xf32, int64_t ldx,
-                       int R, float* y, int64_t ldy, hipStream_t s) {
+template <int BITS>
+inline void qmv_launch_bits(const uint8_t* pk0, const uint8_t* pk1, int nmat, int N, int K, const void* x, int xf32, int64_t ldx,
+                            int R, float* y, int64_t ldy, hipStream_t s) {
   if (!xf32) {
     if (nmat == 1)
-      qmv_launch_bf16<1>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+      qmv_launch_bf16<1, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
     else
-      qmv_launch_bf16<2>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+      qmv_launch_bf16<2, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
   } else {
     const int rt = qmv_row_tiles(1, R);
     if (rt == 1)
-      qmv_launch_lds<1, 1, 1, 1>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+      qmv_launch_lds<1, 1, 1, 1, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
     else if (rt == 2)
-      qmv_launch_lds<1, 1, 2, 1>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+      qmv_launch_lds<1, 1, 2, 1, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
     else
-      qmv_launch_lds<1, 1, 4, 1>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+      qmv_launch_lds<1, 1, 4, 1, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
   }
+}
+
+// bits: 4, 6 or 8 (checked by the caller).
+inline void qmv_launch(const uint8_t* pk0, const uint8_t* pk1, int nmat, int N, int K, const void* x, int xf32, int64_t ldx,
+                       int R, float* y, int64_t ldy, hipStream_t s, int bits = 4) {
+  if (bits == 6)
+    qmv_launch_bits<6>(pk0, pk1, nmat, N, K, x, xf32, ldx, R, y, ldy, s);
+  else if (bits == 8)
+    qmv_launch_bits<8>(pk0, pk1, nmat, N, K, x, xf32, ldx, R, y, ldy, s);
+  else
+    qmv_launch_bits<4>(pk0, pk1, nmat, N, K, x, xf32, ldx, R, y, ldy, s);
 }
 
 }  // namespace q4

@@ -30,6 +30,27 @@
  *     group 2p+1 (zero past G).
  *   Size: T*P*1152 bytes = 0.5625*N*K bytes for even G.
  *
+ * Wider codes (the *_qg64 calls with bits = 6 or 8; PR #1514, "What
+ * changes": the MLX 4-, 6- and 8-bit checkpoints are served as stored; the
+ * pages give no bit layout, so this reading is the plain generalisation of
+ * the 4-bit one):
+ *   - canonical wq is uint32 [N][K*bits/32]; the words of a row form one
+ *     little-endian bit stream and code k occupies bits bits*k .. bits*k +
+ *     bits - 1 (8-bit: the bytes of each word in order; 6-bit: codes
+ *     straddle words). Scales, biases and the dequantization are unchanged.
+ *   - packed codes: T*P blocks of 256*bits bytes. 8-bit: two 1024-byte
+ *     sub-blocks, one per group of the pair; lane L's 16 bytes in sub-block
+ *     j hold, for half hh = 0, 1 (k = 128p + 64j + 32hh + 8*(L/16) + e), two
+ *     words with codes e = 0..3 and 4..7, one per byte in order. 6-bit: a
+ *     1024-byte sub-block of the low four bits laid out exactly as the
+ *     4-bit codes above, then a 512-byte sub-block where lane L's two words
+ *     j = 0, 1 hold the top two bits of halves h = 2j and 2j+1: byte b
+ *     carries, from bit 0, those of codes b and 4+b of half 2j, then of
+ *     codes b and 4+b of half 2j+1.
+ *   - scale/bias blocks follow the codes as for 4 bits.
+ *   The matrix cores take every code as an exact bf16 integer, so the
+ *   summation orders below are the same for every width.
+ *
  * Summation order. Each 64-wide group is reduced on the matrix cores into
  * P_g = sum q*x and S_g = sum x (exact products, float32 sums). Decode calls
  * (qmv_rows, qmv_w13_swiglu) fold acc = fma(s_g, P_g, fma(b_g, S_g, acc)) in
@@ -90,6 +111,15 @@ int pack_q4g64(const uint32_t* wq, const uint16_t* scales, const uint16_t* biase
 int unpack_q4g64(const void* packed, int64_t N, int64_t K, uint32_t* wq, uint16_t* scales, uint16_t* biases,
                  void* stream);
 
+/* The same three calls for bits = 4, 6 or 8 (Q4_EINVAL otherwise; 0 bytes
+ * from qg64_packed_bytes). wq is [N][K*bits/32]; bits = 4 is identical to
+ * the q4g64 calls. The caller passes the same bits, N and K to every use. */
+size_t qg64_packed_bytes(int bits, int64_t N, int64_t K);
+int pack_qg64(int bits, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, int64_t N, int64_t K,
+              void* packed, void* stream);
+int unpack_qg64(int bits, const void* packed, int64_t N, int64_t K, uint32_t* wq, uint16_t* scales, uint16_t* biases,
+                void* stream);
+
 /* Decode matvec over R = 1..16 rows (PR #1696, later revision, "What it adds":
  * N-row matvecs for streams that share a decode step).
  *   x: R rows of K activations, row stride ldx elements; x_dtype Q4_BF16 or
@@ -100,6 +130,10 @@ int unpack_q4g64(const void* packed, int64_t N, int64_t K, uint32_t* wq, uint16_
 int qmv_rows(const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R, float* y,
              int64_t ldy, void* stream);
 
+/* qmv_rows for bits = 4, 6 or 8 (`packed` from pack_qg64 with the same bits). */
+int qmv_rows_qg64(int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R,
+                  float* y, int64_t ldy, void* stream);
+
 /* Fused decode FFN gate (PR #1696, "What it adds": w1 + w3 + SwiGLU in one
  * pass): y[r][n] = silu(a) * c with a = (w1 x)[r][n], c = (w3 x)[r][n], each
  * computed in qmv_rows' order; bit-equal to composing two qmv_rows results
@@ -107,6 +141,10 @@ int qmv_rows(const void* packed, int64_t N, int64_t K, const void* x, int x_dtyp
  * K <= 8192. */
 int qmv_w13_swiglu(const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
                    int64_t ldx, int R, float* y, int64_t ldy, void* stream);
+
+/* qmv_w13_swiglu for bits = 4, 6 or 8 (both matrices packed with that bits). */
+int qmv_w13_swiglu_qg64(int bits, const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
+                        int64_t ldx, int R, float* y, int64_t ldy, void* stream);
 
 /* Prompt-window GEMM (PR #1696, later revision, "What it adds": pgemm).
  *   x: bf16 [M][ldx], any M >= 1.
@@ -143,8 +181,8 @@ int qmm_cut(const void* packed_a, const void* packed_b, int64_t N, int64_t K, co
  * call runs one workgroup per CU and needs the whole device: all of them
  * wait at one grid barrier. A workgroup that waits more than about 20 ms
  * gives up, sets the 32-bit word at byte 2304 of work to 1 and leaves y
- * undefined; the workspace must then be zero-filled again. Limits: K1 <= 8192,
- * N1 <= 16384, and the staged activations must fit in LDS
+ * undefined; the workspace must then be zero-filled again. Limits: K1 <= 4096,
+ * N1 <= 8192, and the staged activations must fit in LDS
  * (Q4_EUNSUPPORTED otherwise). */
 size_t q4g64_ffn_work_bytes(int64_t N1, int R);
 int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2, int64_t N1, int64_t K1, int64_t N2,

@@ -23,7 +23,7 @@ def dev_weight(w):
     wq = torch.from_numpy(np.ascontiguousarray(w.wq).view(np.int32)).to(DEV)
     sc = torch.from_numpy(np.ascontiguousarray(w.scales).view(np.int16)).to(DEV)
     bi = torch.from_numpy(np.ascontiguousarray(w.biases).view(np.int16)).to(DEV)
-    return q4.pack(wq, sc, bi)
+    return q4.pack(wq, sc, bi, bits=getattr(w, "bits", 4))
 
 
 def dev_bf16(x_bits):
@@ -49,8 +49,9 @@ def bits16(t):
 def check_within(y_gpu, w, x, cols=None, x_dtype="bf16", rows=None, label=""):
     """|y_gpu - y64| <= T elementwise; returns (max err/T, max err/A)."""
     xs = x if rows is None else x[rows]
-    y64 = oracle.matmul_rows(w.wq, w.scales, w.biases, xs, cols=cols)
-    A = oracle.error_weight(w.wq, w.scales, w.biases, xs, cols=cols)
+    bits = getattr(w, "bits", 4)
+    y64 = oracle.matmul_rows(w.wq, w.scales, w.biases, xs, cols=cols, bits=bits)
+    A = oracle.error_weight(w.wq, w.scales, w.biases, xs, cols=cols, bits=bits)
     T = tol(A, w.K, x_dtype)
     err = np.abs(y_gpu - y64)
     ratio = float(np.max(err / T))

@@ -152,7 +152,44 @@ def test_ffn_rejects_bad_arguments():
     assert _ffn(ldx=1024)[0] == q4.Q4_EINVAL
     assert _ffn(ldz=4096)[0] == q4.Q4_EINVAL
     assert _ffn(ldy=1024)[0] == q4.Q4_EINVAL
-    rc, msg = _ffn(K1=16384, ldx=16384)
+    rc, msg = _ffn(K1=8192, ldx=8192)
+    assert rc == q4.Q4_EUNSUPPORTED and "4096" in msg
+    rc, msg = _ffn(N1=16384, ldz=16384)
     assert rc == q4.Q4_EUNSUPPORTED and "8192" in msg
-    rc, msg = _ffn(N1=32768, ldz=32768)
+
+
+def test_wide_packed_bytes():
+    # 256 * bits bytes of codes plus 128 of scale/bias per column tile and group pair
+    assert q4.packed_bytes(512, 256, bits=4) == q4.packed_bytes(512, 256)
+    assert q4.packed_bytes(512, 256, bits=8) == 32 * 2 * (2048 + 128)
+    assert q4.packed_bytes(512, 256, bits=6) == 32 * 2 * (1536 + 128)
+    assert q4.packed_bytes(8192, 2048, bits=8) == 8192 * 2048 + 8192 * 32 * 4
+    assert q4.packed_bytes(64, 192, bits=6) == 4 * 2 * (1536 + 128)
+    for bits in (0, 3, 5, 7, 16):
+        assert q4.packed_bytes(512, 256, bits=bits) == 0
+
+
+@pytest.mark.parametrize("bits", [0, 5, 7, 16])
+def test_wide_calls_reject_bad_bits(bits):
+    rc, msg = _rc("pack_qg64", bits, FAKE, FAKE, FAKE, 512, 256, FAKE, None)
+    assert rc == q4.Q4_EINVAL and "bits" in msg
+    rc, msg = _rc("unpack_qg64", bits, FAKE, 512, 256, FAKE, FAKE, FAKE, None)
+    assert rc == q4.Q4_EINVAL and "bits" in msg
+    rc, msg = _rc("qmv_rows_qg64", bits, FAKE, 512, 256, FAKE, q4.Q4_BF16, 256, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EINVAL and "bits" in msg
+    rc, msg = _rc("qmv_w13_swiglu_qg64", bits, FAKE, FAKE, 512, 256, FAKE, 256, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EINVAL and "bits" in msg
+
+
+@pytest.mark.parametrize("bits", [6, 8])
+def test_wide_calls_validate_like_q4(bits):
+    rc, msg = _rc("qmv_rows_qg64", bits, FAKE, 100, 256, FAKE, q4.Q4_BF16, 256, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EINVAL and "multiples of 64" in msg
+    rc, _ = _rc("qmv_rows_qg64", bits, FAKE, 512, 256, FAKE, q4.Q4_BF16, 256, 17, FAKE, 512, None)
+    assert rc == q4.Q4_EINVAL
+    rc, _ = _rc("qmv_rows_qg64", bits, None, 512, 256, FAKE, q4.Q4_BF16, 256, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EALIGN
+    rc, _ = _rc("qmv_w13_swiglu_qg64", bits, FAKE, FAKE, 512, 16384, FAKE, 16384, 1, FAKE, 512, None)
     assert rc == q4.Q4_EUNSUPPORTED
+    rc, _ = _rc("pack_qg64", bits, FAKE + 8, FAKE, FAKE, 512, 256, FAKE, None)
+    assert rc == q4.Q4_EALIGN

@@ -111,7 +111,8 @@ def test_repeated_calls_reuse_the_workspace(c1):
     assert state[q4.FFN_GEN_OFFSET // 4] == 5  # one barrier generation per call
 
 
-@pytest.mark.parametrize("N1,K1,N2,R", [(64, 64, 64, 1), (192, 128, 128, 3), (16384, 2048, 4096, 1), (8192, 4096, 2048, 2)])
+@pytest.mark.parametrize("N1,K1,N2,R", [(64, 64, 64, 1), (192, 128, 128, 3), (8192, 2048, 4096, 1), (8192, 4096, 2048, 2),
+                                        (4096, 2048, 1024, 16)])
 def test_shapes_equal_composition(N1, K1, N2, R):
     say(f"qmv_ffn N1={N1} K1={K1} N2={N2} R={R}")
     rng, w1, w3, w2 = _weights(7 + N1 + K1, N1, K1, N2)
