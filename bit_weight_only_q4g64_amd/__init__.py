@@ -40,6 +40,8 @@ _SIGNATURES = {
     "unpack_qg64": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, _P, _P, _P]),
     "qmv_rows_qg64": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, ctypes.c_int, _I64, ctypes.c_int, _P, _I64, _P]),
     "qmv_w13_swiglu_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
+    "qmm_window_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P]),
+    "qmm_cut_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _I64, _P]),
     "q4g64_ffn_work_bytes": (ctypes.c_size_t, [_I64, ctypes.c_int]),
     "qmv_ffn": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P, _I64, _P, _P]),
     "q4_last_error": (ctypes.c_char_p, []),
@@ -194,8 +196,8 @@ def _out_dtype(dtype) -> int:
 
 
 def qmm_window(pa: torch.Tensor, pb: torch.Tensor | None, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None,
-               out_dtype=torch.float32) -> torch.Tensor:
-    """Prompt window: y = A x (pb None) or silu(A x) * (B x), for all M rows of x."""
+               out_dtype=torch.float32, bits: int = 4) -> torch.Tensor:
+    """Prompt window: y = A x (pb None) or silu(A x) * (B x), for all M rows of x; 4-, 6- or 8-bit codes."""
     _dev(pa, "packed_a")
     _dev(x, "x")
     if x.dtype != torch.bfloat16:
@@ -203,16 +205,18 @@ def qmm_window(pa: torch.Tensor, pb: torch.Tensor | None, N: int, K: int, x: tor
     M = x.shape[0]
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    _check(
-        "qmm_window",
-        lib().qmm_window(pa.data_ptr(), None if pb is None else pb.data_ptr(), N, K, x.data_ptr(), _rowmajor(x, "x"), M,
-                         y.data_ptr(), _out_dtype(y.dtype), _rowmajor(y, "y"), _stream()),
-    )
+    pbp = None if pb is None else pb.data_ptr()
+    if bits == 4:
+        _check("qmm_window", lib().qmm_window(pa.data_ptr(), pbp, N, K, x.data_ptr(), _rowmajor(x, "x"), M, y.data_ptr(),
+                                              _out_dtype(y.dtype), _rowmajor(y, "y"), _stream()))
+    else:
+        _check("qmm_window_qg64", lib().qmm_window_qg64(bits, pa.data_ptr(), pbp, N, K, x.data_ptr(), _rowmajor(x, "x"), M,
+                                                        y.data_ptr(), _out_dtype(y.dtype), _rowmajor(y, "y"), _stream()))
     return y
 
 
 def qmm_cut(pa: torch.Tensor, pb: torch.Tensor | None, N: int, K: int, x: torch.Tensor, windows, y: torch.Tensor | None = None,
-            out_dtype=torch.float32) -> torch.Tensor:
+            out_dtype=torch.float32, bits: int = 4) -> torch.Tensor:
     """Run the prompt x through consecutive windows of the given row counts."""
     _dev(pa, "packed_a")
     _dev(x, "x")
@@ -224,11 +228,13 @@ def qmm_cut(pa: torch.Tensor, pb: torch.Tensor | None, N: int, K: int, x: torch.
     if y is None:
         y = torch.empty((x.shape[0], N), dtype=out_dtype, device=x.device)
     arr = (ctypes.c_int64 * len(windows))(*windows)
-    _check(
-        "qmm_cut",
-        lib().qmm_cut(pa.data_ptr(), None if pb is None else pb.data_ptr(), N, K, x.data_ptr(), _rowmajor(x, "x"), arr,
-                      len(windows), y.data_ptr(), _out_dtype(y.dtype), _rowmajor(y, "y"), _stream()),
-    )
+    pbp = None if pb is None else pb.data_ptr()
+    if bits == 4:
+        _check("qmm_cut", lib().qmm_cut(pa.data_ptr(), pbp, N, K, x.data_ptr(), _rowmajor(x, "x"), arr, len(windows), y.data_ptr(),
+                                        _out_dtype(y.dtype), _rowmajor(y, "y"), _stream()))
+    else:
+        _check("qmm_cut_qg64", lib().qmm_cut_qg64(bits, pa.data_ptr(), pbp, N, K, x.data_ptr(), _rowmajor(x, "x"), arr,
+                                                  len(windows), y.data_ptr(), _out_dtype(y.dtype), _rowmajor(y, "y"), _stream()))
     return y
 
 

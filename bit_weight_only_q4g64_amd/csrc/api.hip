@@ -177,7 +177,24 @@ int64_t pgemm_blocks(int64_t N, int64_t M, bool swiglu, int* nblk, int* mblk) {
   return nb * mb;
 }
 
-int qmm_window_impl(const char* fn, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x,
+template <int BITS>
+void pgemm_launch_bits(bool swiglu, bool obf16, dim3 grid, dim3 block, hipStream_t s, const uint8_t* a, const uint8_t* b, int n,
+                       int k, const uint16_t* x, int64_t ldx, int m, void* y, int64_t ldy, int nblk, int mblk) {
+  using namespace q4;
+  if (swiglu) {
+    if (obf16)
+      hipLaunchKernelGGL((pgemm_kernel<true, true, BITS>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
+    else
+      hipLaunchKernelGGL((pgemm_kernel<true, false, BITS>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
+  } else {
+    if (obf16)
+      hipLaunchKernelGGL((pgemm_kernel<false, true, BITS>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
+    else
+      hipLaunchKernelGGL((pgemm_kernel<false, false, BITS>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
+  }
+}
+
+int qmm_window_impl(const char* fn, int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x,
                     int64_t ldx, int64_t M, void* y, int y_dtype, int64_t ldy, hipStream_t s) {
   using namespace q4;
   const bool swiglu = packed_b != nullptr;
@@ -189,17 +206,12 @@ int qmm_window_impl(const char* fn, const void* packed_a, const void* packed_b, 
   const uint8_t* a = (const uint8_t*)packed_a;
   const uint8_t* b = swiglu ? (const uint8_t*)packed_b : a;
   const int n = (int)N, k = (int)K, m = (int)M;
-  if (swiglu) {
-    if (obf16)
-      hipLaunchKernelGGL((pgemm_kernel<true, true>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
-    else
-      hipLaunchKernelGGL((pgemm_kernel<true, false>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
-  } else {
-    if (obf16)
-      hipLaunchKernelGGL((pgemm_kernel<false, true>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
-    else
-      hipLaunchKernelGGL((pgemm_kernel<false, false>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
-  }
+  if (bits == 6)
+    pgemm_launch_bits<6>(swiglu, obf16, grid, block, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
+  else if (bits == 8)
+    pgemm_launch_bits<8>(swiglu, obf16, grid, block, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
+  else
+    pgemm_launch_bits<4>(swiglu, obf16, grid, block, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
   return launched(fn);
 }
 
@@ -258,6 +270,33 @@ int ffn_launch_s1(int spw1, int spw2, const uint8_t* p1, const uint8_t* p3, cons
 
 }  // namespace
 
+int qmm_window_checked(const char* fn, int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K,
+                       const uint16_t* x, int64_t ldx, int64_t M, void* y, int y_dtype, int64_t ldy, hipStream_t s) {
+  if (int rc = check_bits(fn, bits)) return rc;
+  if (int rc = check_window_args(fn, packed_a, packed_b, N, K, x, ldx, y, y_dtype, ldy)) return rc;
+  if (M < 1 || M > kPgemmMaxM) return fail(Q4_EINVAL, "%s: M=%lld is outside 1..%lld", fn, (long long)M, (long long)kPgemmMaxM);
+  return qmm_window_impl(fn, bits, packed_a, packed_b, N, K, x, ldx, M, y, y_dtype, ldy, s);
+}
+
+int qmm_cut_impl(const char* fn, int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x,
+                 int64_t ldx, const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, hipStream_t s) {
+  if (int rc = check_bits(fn, bits)) return rc;
+  if (int rc = check_window_args(fn, packed_a, packed_b, N, K, x, ldx, y, y_dtype, ldy)) return rc;
+  if (window_rows == nullptr || n_windows < 1) return fail(Q4_EINVAL, "%s: need at least one window", fn);
+  for (int w = 0; w < n_windows; ++w)
+    if (window_rows[w] < 1 || window_rows[w] > kPgemmMaxM)
+      return fail(Q4_EINVAL, "%s: window %d has %lld rows", fn, w, (long long)window_rows[w]);
+  const int64_t es = y_dtype == Q4_F32 ? 4 : 2;
+  int64_t row0 = 0;
+  for (int w = 0; w < n_windows; ++w) {
+    const uint16_t* xw = x + row0 * ldx;
+    void* yw = (uint8_t*)y + row0 * ldy * es;
+    if (int rc = qmm_window_impl(fn, bits, packed_a, packed_b, N, K, xw, ldx, window_rows[w], yw, y_dtype, ldy, s)) return rc;
+    row0 += window_rows[w];
+  }
+  return Q4_OK;
+}
+
 extern "C" {
 
 int q4g64_abi_version(void) { return 1; }
@@ -310,30 +349,23 @@ int qmv_w13_swiglu_qg64(int bits, const void* packed_w1, const void* packed_w3, 
 
 int qmm_window(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx, int64_t M,
                void* y, int y_dtype, int64_t ldy, void* stream) {
-  const char* fn = "qmm_window";
-  if (int rc = check_window_args(fn, packed_a, packed_b, N, K, x, ldx, y, y_dtype, ldy)) return rc;
-  if (M < 1 || M > kPgemmMaxM) return fail(Q4_EINVAL, "%s: M=%lld is outside 1..%lld", fn, (long long)M, (long long)kPgemmMaxM);
-  return qmm_window_impl(fn, packed_a, packed_b, N, K, x, ldx, M, y, y_dtype, ldy, (hipStream_t)stream);
+  return qmm_window_checked("qmm_window", 4, packed_a, packed_b, N, K, x, ldx, M, y, y_dtype, ldy, (hipStream_t)stream);
+}
+
+int qmm_window_qg64(int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                    int64_t M, void* y, int y_dtype, int64_t ldy, void* stream) {
+  return qmm_window_checked("qmm_window_qg64", bits, packed_a, packed_b, N, K, x, ldx, M, y, y_dtype, ldy, (hipStream_t)stream);
 }
 
 int qmm_cut(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
             const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, void* stream) {
-  const char* fn = "qmm_cut";
-  if (int rc = check_window_args(fn, packed_a, packed_b, N, K, x, ldx, y, y_dtype, ldy)) return rc;
-  if (window_rows == nullptr || n_windows < 1) return fail(Q4_EINVAL, "%s: need at least one window", fn);
-  for (int w = 0; w < n_windows; ++w)
-    if (window_rows[w] < 1 || window_rows[w] > kPgemmMaxM)
-      return fail(Q4_EINVAL, "%s: window %d has %lld rows", fn, w, (long long)window_rows[w]);
-  const int64_t es = y_dtype == Q4_F32 ? 4 : 2;
-  int64_t row0 = 0;
-  for (int w = 0; w < n_windows; ++w) {
-    const uint16_t* xw = x + row0 * ldx;
-    void* yw = (uint8_t*)y + row0 * ldy * es;
-    if (int rc = qmm_window_impl(fn, packed_a, packed_b, N, K, xw, ldx, window_rows[w], yw, y_dtype, ldy, (hipStream_t)stream))
-      return rc;
-    row0 += window_rows[w];
-  }
-  return Q4_OK;
+  return qmm_cut_impl("qmm_cut", 4, packed_a, packed_b, N, K, x, ldx, window_rows, n_windows, y, y_dtype, ldy, (hipStream_t)stream);
+}
+
+int qmm_cut_qg64(int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                 const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, void* stream) {
+  return qmm_cut_impl("qmm_cut_qg64", bits, packed_a, packed_b, N, K, x, ldx, window_rows, n_windows, y, y_dtype, ldy,
+                      (hipStream_t)stream);
 }
 
 size_t q4g64_ffn_work_bytes(int64_t N1, int R) {

@@ -57,6 +57,14 @@ constexpr int kXStages = 2;
 constexpr int kXRowBytes = kGroup * 2;          // one staged activation row of a group
 constexpr int kXStageBytes = kPgemmRows * kXRowBytes;       // 16 KiB
 constexpr int kCStageBytes = kPgemmSlots * kPairCodeBytes;  // 16 KiB
+// Wider codes are staged one group at a time (a pair would not fit two
+// workgroups per CU): per slot, 8-bit is the group's 1 KiB sub-block as is;
+// 6-bit is the group's two nibble words of every lane then its high-pair
+// word of every lane, each as a 256-byte row (three dword copies).
+__host__ __device__ constexpr int pgemm_group_code_bytes(int bits) { return bits == 8 ? 1024 : 768; }
+__host__ __device__ constexpr int pgemm_cstage_bytes(int bits) {
+  return bits == 4 ? kCStageBytes : kPgemmSlots * pgemm_group_code_bytes(bits);
+}
 constexpr int kSbStageBytes = kPgemmSlots * kPairSbBytes;   // 2 KiB
 constexpr int kSumFloats = 2 * kPgemmRows * kPgemmChunk;    // activation sums, 2 chunks
 static_assert(kPgemmRows == kPgemmRT * 32, "kPgemmRT row tiles of 32");
@@ -128,12 +136,14 @@ __host__ __device__ inline void pgemm_tile(int b, int nblk, int mblk, int& mb, i
   nb = in / h;
 }
 
-template <bool SWIGLU, bool OUT_BF16>
+template <bool SWIGLU, bool OUT_BF16, int BITS>
 __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_kernel(const uint8_t* __restrict__ pa, const uint8_t* __restrict__ pb,
                                                                   int N, int K, const uint16_t* __restrict__ x, int64_t ldx, int M,
                                                                   void* __restrict__ yv, int64_t ldy, int nblk, int mblk) {
   __shared__ __align__(16) uint8_t xs[kXStages * kXStageBytes];
-  __shared__ __align__(16) uint8_t cs[2 * kCStageBytes];
+  constexpr int kCSt = pgemm_cstage_bytes(BITS);
+  constexpr int kPcb = pair_code_bytes(BITS);
+  __shared__ __align__(16) uint8_t cs[2 * kCSt];
   __shared__ __align__(16) uint8_t sbs[2 * kSbStageBytes];
   __shared__ __align__(16) float ssum[kSumFloats];
 
@@ -147,7 +157,7 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_kernel(const uint8_t* 
   const int G = K / kGroup;
   const int P = (G + 1) / 2;
   const int ntiles = N / kTileN;
-  const int64_t cb = codes_bytes(N, K);
+  const int64_t cb = codes_bytes(N, K, BITS);
   const bf16x8 ones = ones_bf16x8();
 
   // slot (0..15) -> weight tile (unclamped)
@@ -174,14 +184,15 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_kernel(const uint8_t* 
 #pragma unroll
   for (int u = 0; u < 4; ++u) tsl[u] = clamp_tile(slot_tile(4 * wave + u));
   const int t0 = tsl[0];
-  const i32x4 cr = make_srsrc(mat + (int64_t)t0 * P * kPairCodeBytes, (uint32_t)((tsl[3] - t0 + 1) * P * kPairCodeBytes));
+  const i32x4 cr = make_srsrc(mat + (int64_t)t0 * P * kPcb, (uint32_t)((tsl[3] - t0 + 1) * P * kPcb));
   const i32x4 sr = make_srsrc(mat + cb + (int64_t)t0 * P * kPairSbBytes, (uint32_t)((tsl[3] - t0 + 1) * P * kPairSbBytes));
   const uint32_t cvo = (uint32_t)lane * 16u;
   uint32_t svo[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
     svo[u] = (uint32_t)((lane >> 5) * (tsl[2 * u + 1] - tsl[2 * u]) * P * kPairSbBytes) + (uint32_t)(lane & 31) * 4u;
-  const uint32_t cs_lds = lds_addr(cs) + 4 * wave * kPairCodeBytes;
+  constexpr int kSlotStage = BITS == 4 ? kPairCodeBytes : pgemm_group_code_bytes(BITS);  // bytes per slot per stage
+  const uint32_t cs_lds = lds_addr(cs) + 4 * wave * kSlotStage;
   const uint32_t sb_lds = lds_addr(sbs) + 4 * wave * kPairSbBytes;
 
   auto issue_x = [&](int g) {
@@ -189,14 +200,35 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_kernel(const uint8_t* 
 #pragma unroll
     for (int u = 0; u < 4; ++u) dma_b128(xr, xvo[u], (uint32_t)g * kXRowBytes, dst + u * 1024);
   };
+  auto issue_sb = [&](int p) {
+    const uint32_t st = (uint32_t)(p & 1);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      dma_b32(sr, svo[u], (uint32_t)((tsl[2 * u] - t0) * P + p) * kPairSbBytes, sb_lds + st * kSbStageBytes + 2 * u * kPairSbBytes);
+  };
+  // 4-bit: the codes of pair p (both groups) into stage p & 1
   auto issue_c = [&](int p) {
     const uint32_t st = (uint32_t)(p & 1);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       dma_b128(cr, cvo, (uint32_t)((tsl[u] - t0) * P + p) * kPairCodeBytes, cs_lds + st * kCStageBytes + u * kPairCodeBytes);
+    issue_sb(p);
+  };
+  // 6- and 8-bit: the codes of group g into stage g & 1
+  auto issue_cg = [&](int g) {
+    const uint32_t dst = cs_lds + (uint32_t)(g & 1) * kCSt;
+    const int p = g >> 1, gh = g & 1;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      dma_b32(sr, svo[u], (uint32_t)((tsl[2 * u] - t0) * P + p) * kPairSbBytes, sb_lds + st * kSbStageBytes + 2 * u * kPairSbBytes);
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t blk = (uint32_t)((tsl[u] - t0) * P + p) * kPcb;
+      if constexpr (BITS == 8) {
+        dma_b128(cr, cvo, blk + (uint32_t)gh * 1024u, dst + u * kSlotStage);
+      } else {
+        dma_b32(cr, (uint32_t)lane * 16u + (uint32_t)gh * 8u, blk, dst + u * kSlotStage);
+        dma_b32(cr, (uint32_t)lane * 16u + (uint32_t)gh * 8u + 4u, blk, dst + u * kSlotStage + 256);
+        dma_b32(cr, 1024u + (uint32_t)lane * 8u + (uint32_t)gh * 4u, blk, dst + u * kSlotStage + 512);
+      }
+    }
   };
 
   // ---- consumer set-up ---------------------------------------------------
@@ -259,21 +291,17 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_kernel(const uint8_t* 
     constexpr int gh = decltype(ghc)::value;
     const int p = g >> 1, gg = g & (kPgemmChunk - 1);
     const uint8_t* xb = xs + (g % kXStages) * kXStageBytes;
-    const uint8_t* cb0 = cs + (p & 1) * kCStageBytes;
+    const uint8_t* cb0 = cs + (BITS == 4 ? (p & 1) : (g & 1)) * kCSt;
     const uint8_t* sb0 = sbs + (p & 1) * kSbStageBytes;
 
-    // codes of this lane's column: k steps 0 and 2 at word 2 gh and 2 gh + 1
-    // of lane jj + 16 hl of the pair block, steps 1 and 3 at lane jj + 32 + 16 hl
-    u32x2 c02[kPgemmNT], c13[kPgemmNT];
+    // codes of this lane's column: k steps 0 and 2 are halves 0 and 1 of the
+    // group in lane jj + 16 hl of the block, steps 1 and 3 in lane jj + 32 + 16 hl
     uint32_t w[kPgemmNT];
     float sc[kPgemmNT];
 #pragma unroll
     for (int s = 0; s < kPgemmNT; ++s) {
       w[s] = *(const uint32_t*)(sb0 + lslot[s] * kPairSbBytes + jj * 8 + gh * 4);
       sc[s] = bf16_lo(w[s]);
-      const uint8_t* cl = cb0 + lslot[s] * kPairCodeBytes + (jj + 16 * hl) * 16 + gh * 8;
-      c02[s] = *(const u32x2*)cl;
-      c13[s] = *(const u32x2*)(cl + 512);
     }
 
     // activation sums of this wave's 32 of the 128 rows (16 x 16 tiles)
@@ -294,10 +322,28 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_kernel(const uint8_t* 
     bf16x8 q[kPgemmNT][4];
 #pragma unroll
     for (int s = 0; s < kPgemmNT; ++s) {
-      q[s][0] = codes_to_bf16(c02[s][0]);
-      q[s][2] = codes_to_bf16(c02[s][1]);
-      q[s][1] = codes_to_bf16(c13[s][0]);
-      q[s][3] = codes_to_bf16(c13[s][1]);
+      const int L = jj + 16 * hl;
+      if constexpr (BITS == 4) {
+        const uint8_t* cl = cb0 + lslot[s] * kPairCodeBytes + L * 16 + gh * 8;
+        const u32x2 c02 = *(const u32x2*)cl, c13 = *(const u32x2*)(cl + 512);
+        q[s][0] = codes_to_bf16(c02[0]);
+        q[s][2] = codes_to_bf16(c02[1]);
+        q[s][1] = codes_to_bf16(c13[0]);
+        q[s][3] = codes_to_bf16(c13[1]);
+      } else if constexpr (BITS == 8) {
+        const uint8_t* cl = cb0 + lslot[s] * kSlotStage + L * 16;
+        const u32x4 c02 = *(const u32x4*)cl, c13 = *(const u32x4*)(cl + 512);
+        q[s][0] = bytes_to_bf16(c02[0], c02[1]);
+        q[s][2] = bytes_to_bf16(c02[2], c02[3]);
+        q[s][1] = bytes_to_bf16(c13[0], c13[1]);
+        q[s][3] = bytes_to_bf16(c13[2], c13[3]);
+      } else {
+        const uint32_t* cl = (const uint32_t*)(cb0 + lslot[s] * kSlotStage);
+        q[s][0] = six_to_bf16<0>(cl[L], cl[128 + L]);
+        q[s][2] = six_to_bf16<1>(cl[64 + L], cl[128 + L]);
+        q[s][1] = six_to_bf16<0>(cl[L + 32], cl[128 + L + 32]);
+        q[s][3] = six_to_bf16<1>(cl[64 + L + 32], cl[128 + L + 32]);
+      }
     }
 #pragma unroll
     for (int rt = 0; rt < kPgemmRT; ++rt) {
@@ -336,19 +382,45 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_kernel(const uint8_t* 
   // after an even group that issued them, vmcnt(0) otherwise; the barrier
   // then makes every wave's stage visible and frees the stages the next DMA
   // overwrites (read during group g - 1).
-  issue_x(0);
-  issue_c(0);
-  for (int p = 0; p < P; ++p) {
-    const int g = 2 * p;
-    dma_wait_barrier<0>();
-    if (g + 1 < G) issue_x(g + 1);
-    if (p + 1 < P) issue_c(p + 1);
-    group(g, std::integral_constant<int, 0>{});
-    if (g + 1 < G) {
-      if (p + 1 < P) dma_wait_barrier<6>();
-      else dma_wait_barrier<0>();
-      if (g + 2 < G) issue_x(g + 2);
-      group(g + 1, std::integral_constant<int, 1>{});
+  if constexpr (BITS == 4) {
+    issue_x(0);
+    issue_c(0);
+    for (int p = 0; p < P; ++p) {
+      const int g = 2 * p;
+      dma_wait_barrier<0>();
+      if (g + 1 < G) issue_x(g + 1);
+      if (p + 1 < P) issue_c(p + 1);
+      group(g, std::integral_constant<int, 0>{});
+      if (g + 1 < G) {
+        if (p + 1 < P) dma_wait_barrier<6>();
+        else dma_wait_barrier<0>();
+        if (g + 2 < G) issue_x(g + 2);
+        group(g + 1, std::integral_constant<int, 1>{});
+      }
+    }
+  } else {
+    // one group of activations and codes in flight; the scale/bias words of
+    // a pair are issued with its first group's codes
+    issue_x(0);
+    issue_cg(0);
+    issue_sb(0);
+    for (int p = 0; p < P; ++p) {
+      const int g = 2 * p;
+      dma_wait_barrier<0>();
+      if (g + 1 < G) {
+        issue_x(g + 1);
+        issue_cg(g + 1);
+      }
+      group(g, std::integral_constant<int, 0>{});
+      if (g + 1 < G) {
+        dma_wait_barrier<0>();
+        if (g + 2 < G) {
+          issue_x(g + 2);
+          issue_cg(g + 2);
+          issue_sb(p + 1);
+        }
+        group(g + 1, std::integral_constant<int, 1>{});
+      }
     }
   }
   dma_wait_barrier<0>();  // the last group's sums from every wave

@@ -157,6 +157,10 @@ int qmv_w13_swiglu_qg64(int bits, const void* packed_w1, const void* packed_w3, 
 int qmm_window(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                int64_t M, void* y, int y_dtype, int64_t ldy, void* stream);
 
+/* qmm_window for bits = 4, 6 or 8 (both matrices packed with that bits). */
+int qmm_window_qg64(int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x,
+                    int64_t ldx, int64_t M, void* y, int y_dtype, int64_t ldy, void* stream);
+
 /* Window driver: runs qmm_window over consecutive windows of a prompt.
  * window_rows is a HOST array of n_windows positive row counts; window w
  * covers rows [sum of earlier counts, + window_rows[w]) of x and y. The
@@ -164,6 +168,10 @@ int qmm_window(const void* packed_a, const void* packed_b, int64_t N, int64_t K,
  * windows of 64, 128, 256 and a ragged cut agree bit for bit). */
 int qmm_cut(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
             const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, void* stream);
+
+/* qmm_cut for bits = 4, 6 or 8. */
+int qmm_cut_qg64(int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                 const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, void* stream);
 
 /* Decode FFN step in one launch (PR #1696, "What it adds": w1 + w3 + SwiGLU
  * in one pass; PR #1514, "What changes": the fusion keeps every rounding

@@ -112,3 +112,60 @@ def test_wide_w13_swiglu(wide, R):
     assert np.all(np.abs(host_f64(c) - c64) <= Tc)
     Tz = tol_swiglu(a64, c64, Ta, Tc)
     assert np.all(np.abs(host_f64(z) - oracle.swiglu(a64, c64)) <= Tz)
+
+
+# --------------------------------------------------------- prompt windows
+
+WIN_ROWS = [0, 1, 63, 64, 127, 128, 255, 256, 299, 300, 449]
+
+
+@pytest.fixture(scope="module", params=BITS)
+def wide_win(request):
+    bits = request.param
+    rng = np.random.default_rng(80 + bits)
+    d = {"bits": bits}
+    # K = 2112 = 33 groups: an odd group count leaves a half-filled last pair
+    d["a"] = synthetic.draw_qweight(rng, "a", 1024, 2112, bits=bits)
+    d["b"] = synthetic.draw_qweight(rng, "b", 1024, 2112, bits=bits)
+    d["x"] = synthetic.draw_bf16_rows(rng, 450, 2112)
+    d["pa"], d["pb"], d["xd"] = dev_weight(d["a"]), dev_weight(d["b"]), dev_bf16(d["x"])
+    d["plain"] = q4.qmm_window(d["pa"], None, 1024, 2112, d["xd"], bits=bits)
+    d["swiglu"] = q4.qmm_window(d["pa"], d["pb"], 1024, 2112, d["xd"], bits=bits)
+    torch.cuda.synchronize()
+    return d
+
+
+def test_wide_window_plain_parity(wide_win):
+    bits, a = wide_win["bits"], wide_win["a"]
+    say(f"qmm_window bits={bits} {a.N}x{a.K} M=450 plain")
+    check_within(host_f64(wide_win["plain"])[WIN_ROWS], a, wide_win["x"], rows=WIN_ROWS, label=f"window bits={bits}")
+
+
+def test_wide_window_swiglu_parity(wide_win):
+    bits, a, b = wide_win["bits"], wide_win["a"], wide_win["b"]
+    say(f"qmm_window bits={bits} SwiGLU parity")
+    xs = wide_win["x"][WIN_ROWS]
+    a64 = oracle.matmul_rows(a.wq, a.scales, a.biases, xs, bits=bits)
+    c64 = oracle.matmul_rows(b.wq, b.scales, b.biases, xs, bits=bits)
+    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(a.wq, a.scales, a.biases, xs, bits=bits), a.K),
+                    tol(oracle.error_weight(b.wq, b.scales, b.biases, xs, bits=bits), b.K))
+    z = host_f64(wide_win["swiglu"])[WIN_ROWS]
+    assert np.all(np.abs(z - oracle.swiglu(a64, c64)) <= Tz)
+
+
+@pytest.mark.parametrize("cut", [[64] * 7 + [2], [128] * 3 + [66], [17, 300, 133]])
+def test_wide_window_cuts_bit_identical(wide_win, cut):
+    bits = wide_win["bits"]
+    say(f"qmm_cut bits={bits} cut={cut[:3]}...")
+    for pb, ref in ((None, "plain"), (wide_win["pb"], "swiglu")):
+        z = q4.qmm_cut(wide_win["pa"], pb, 1024, 2112, wide_win["xd"], cut, bits=bits)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits32(z), bits32(wide_win[ref])), ref
+
+
+def test_wide_window_single_rows(wide_win):
+    bits = wide_win["bits"]
+    ref = bits32(wide_win["swiglu"])
+    for r in WIN_ROWS:
+        z1 = q4.qmm_window(wide_win["pa"], wide_win["pb"], 1024, 2112, wide_win["xd"][r : r + 1], bits=bits)
+        assert np.array_equal(bits32(z1)[0], ref[r]), r
