@@ -40,8 +40,10 @@ BF16_PEAK_TFLOPS = 2516.6
 METRIC = "GB/s + rows/s for qmv decode; TFLOP/s for pgemm prefill (% of roofline)"
 
 
-def qbytes(N, K):
-    return N * K * 9 // 16
+def qbytes(N, K, bits=4):
+    """Algorithmic bytes of one packed matrix: bits/8 per code plus a bf16
+    scale and bias (4 bytes) per 64 codes."""
+    return N * K * (2 * bits + 1) // 16
 
 
 def log(msg):
@@ -57,7 +59,8 @@ def to_dev(a, dt, dev):
 def pack_dev(w, dev):
     import bit_weight_only_q4g64_amd as q4
 
-    return q4.pack(to_dev(w.wq, np.int32, dev), to_dev(w.scales, np.int16, dev), to_dev(w.biases, np.int16, dev))
+    return q4.pack(to_dev(w.wq, np.int32, dev), to_dev(w.scales, np.int16, dev), to_dev(w.biases, np.int16, dev),
+                   bits=getattr(w, "bits", 4))
 
 
 def cpu_baseline(d, budget_s=12.0):
@@ -174,6 +177,7 @@ def main():
     ap.add_argument("--pool-mb", type=int, default=1200, help="size of the rotating weight pool (cold HBM reads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pgemm", action="store_true")
+    ap.add_argument("--no-wide", action="store_true", help="skip the 6- and 8-bit measurements")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps directly instead of replaying a graph (for per-dispatch counters)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -320,16 +324,107 @@ def main():
                                  "frac": round(ach2 / HBM_PEAK_GBS, 4)},
         },
     }
+    g_used = g is not None
     del g, pool
     torch.cuda.empty_cache()
 
     if not args.no_pgemm:
         result["pgemm"] = bench_pgemm(dev)
+    if not args.no_wide:
+        result["wide_codes"] = {str(b): bench_wide(dev, b, K, W, args.pool_mb, graph=g_used) for b in (6, 8)}
 
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(d)
     print(json.dumps(result), flush=True)
+
+
+def bench_wide(dev, bits, K, W, pool_mb, graph=True, reps=5):
+    """The same decode FFN step and prompt window with MLX 6- or 8-bit codes
+    (same shapes, same cold weight pool, same timing method)."""
+    import torch
+
+    import bit_weight_only_q4g64_amd as q4
+    import synthetic
+
+    log(f"{bits}-bit codes: decode FFN step and prompt window")
+    rng = np.random.default_rng(100 + bits)
+    w1 = synthetic.draw_qweight(rng, "w1", 8192, 2048, bits=bits)
+    w3 = synthetic.draw_qweight(rng, "w3", 8192, 2048, bits=bits)
+    w2 = synthetic.draw_qweight(rng, "w2", 2048, 8192, bits=bits)
+    xb = synthetic.draw_bf16_rows(rng, 1, 2048)
+    copy_bytes = q4.packed_bytes(8192, 2048, bits) * 2 + q4.packed_bytes(2048, 8192, bits)
+    ncopies = max(2, -(-pool_mb * (1 << 20) // copy_bytes))
+    base = [pack_dev(w1, dev), pack_dev(w3, dev), pack_dev(w2, dev)]
+    pool = [base] + [[t.clone() for t in base] for _ in range(ncopies - 1)]
+    x = to_dev(xb, np.int16, dev).view(torch.bfloat16)
+    z = torch.empty((1, 8192), dtype=torch.float32, device=dev)
+    y = torch.empty((1, 2048), dtype=torch.float32, device=dev)
+
+    def step(i):
+        p1, p3, p2 = pool[i % ncopies]
+        q4.qmv_w13_swiglu(p1, p3, 8192, 2048, x, y=z, bits=bits)
+        q4.qmv_rows(p2, 2048, 8192, z, y=y, bits=bits)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(K):
+                    step(W + i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        del g
+    else:
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(W + i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / K
+    t13 = batch_average_us(torch, lambda i: q4.qmv_w13_swiglu(pool[i % ncopies][0], pool[i % ncopies][1], 8192, 2048, x, y=z,
+                                                               bits=bits), W, K)
+    t2 = batch_average_us(torch, lambda i: q4.qmv_rows(pool[i % ncopies][2], 2048, 8192, z, y=y, bits=bits), W, K)
+    b13 = 2 * qbytes(8192, 2048, bits) + 2048 * 2 + 8192 * 4
+    b2 = qbytes(2048, 8192, bits) + 8192 * 4 + 2048 * 4
+    del pool, base
+    torch.cuda.empty_cache()
+
+    # prompt window: w1/w3 + SwiGLU over 8192 rows, bf16 out
+    xw = to_dev(synthetic.draw_bf16_rows(rng, 8192, 2048), np.int16, dev).view(torch.bfloat16)
+    p1, p3 = pack_dev(w1, dev), pack_dev(w3, dev)
+    zw = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        q4.qmm_window(p1, p3, 8192, 2048, xw, y=zw, bits=bits)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        e[0].record()
+        q4.qmm_window(p1, p3, 8192, 2048, xw, y=zw, bits=bits)
+        e[1].record()
+    torch.cuda.synchronize()
+    tw = np.array([e[0].elapsed_time(e[1]) for e in evs]).mean() * 1e-3
+    tf = 2.0 * 8192 * (2 * 8192) * 2048 / tw / 1e12
+    del p1, p3, zw, xw
+    torch.cuda.empty_cache()
+    return {
+        "decode_step": {"ms_per_step": round(ms, 6), "GB/s": round((b13 + b2) / (ms * 1e-3) / 1e9, 2), "step_bytes": b13 + b2},
+        "qmv_w13_swiglu": {"avg_us": round(t13, 3), "GB/s": round(b13 / (t13 * 1e-6) / 1e9, 1),
+                           "frac": round(b13 / (t13 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "qmv_rows_w2_f32x": {"avg_us": round(t2, 3), "GB/s": round(b2 / (t2 * 1e-6) / 1e9, 1),
+                             "frac": round(b2 / (t2 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "pgemm_swiglu_8192": {"avg_ms": round(tw * 1e3, 4), "TFLOP/s": round(tf, 2), "frac": round(tf / BF16_PEAK_TFLOPS, 4)},
+    }
 
 
 def bench_pgemm(dev, reps=10):
