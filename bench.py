@@ -321,7 +321,8 @@ def main():
                                "p90_us": round(float(np.percentile(t13, 90)), 3), "GB/s": round(ach13, 1)},
             "qmv_rows_w2_f32x": {"avg_us": round(float(t2.mean()), 3), "p10_us": round(float(np.percentile(t2, 10)), 3),
                                  "p90_us": round(float(np.percentile(t2, 90)), 3), "GB/s": round(ach2, 1),
-                                 "frac": round(ach2 / HBM_PEAK_GBS, 4)},
+                                 "frac": round(ach2 / HBM_PEAK_GBS, 4), "traffic": traffic_per_launch("qmv_rows_w2"),
+                                 "algorithmic_bytes_per_launch": b2},
         },
     }
     g_used = g is not None
