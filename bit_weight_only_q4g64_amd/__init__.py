@@ -42,6 +42,8 @@ _SIGNATURES = {
     "qmv_w13_swiglu_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
     "qmm_window_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P]),
     "qmm_cut_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _I64, _P]),
+    "qmv_window_costs": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P, _I64, ctypes.c_int, _P, _P]),
+    "qmv_window_cost": (ctypes.c_float, [_P, ctypes.c_int]),
     "q4g64_ffn_work_bytes": (ctypes.c_size_t, [_I64, ctypes.c_int]),
     "qmv_ffn": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P, _I64, _P, _P]),
     "q4_last_error": (ctypes.c_char_p, []),
@@ -283,3 +285,30 @@ def qmv_ffn(p1: torch.Tensor, p3: torch.Tensor, p2: torch.Tensor, N1: int, K1: i
                       _rowmajor(z, "z"), y.data_ptr(), _rowmajor(y, "y"), work.data_ptr(), _stream()),
     )
     return z, y
+
+
+WINDOW_COST_ROWS = (1, 2, 4, 8, 16)
+
+
+def window_costs(packed: torch.Tensor, N: int, K: int, x: torch.Tensor, bits: int = 4, reps: int = 20,
+                 y: torch.Tensor | None = None) -> list:
+    """Average qmv_rows time (us) at R = 1, 2, 4, 8, 16, measured on the 16 rows of x (a load-time call)."""
+    _dev(packed, "packed")
+    _dev(x, "x")
+    if x.shape[0] < 16:
+        raise ValueError("x must hold 16 rows")
+    xd = Q4_BF16 if x.dtype == torch.bfloat16 else Q4_F32 if x.dtype == torch.float32 else None
+    if xd is None:
+        raise ValueError("x must be bfloat16 or float32")
+    if y is None:
+        y = torch.empty((16, N), dtype=torch.float32, device=x.device)
+    out = (ctypes.c_float * 5)()
+    _check("qmv_window_costs", lib().qmv_window_costs(bits, packed.data_ptr(), N, K, x.data_ptr(), xd, _rowmajor(x, "x"), y.data_ptr(),
+                                                      _rowmajor(y, "y"), reps, ctypes.addressof(out), _stream()))
+    return list(out)
+
+
+def window_cost(costs, R: int) -> float:
+    """Interpolated cost of R rows (1..16) from a window_costs table."""
+    arr = (ctypes.c_float * 5)(*[float(c) for c in costs])
+    return float(lib().qmv_window_cost(ctypes.addressof(arr), R))

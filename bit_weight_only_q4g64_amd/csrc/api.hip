@@ -3,6 +3,7 @@
 // nothing when an argument is rejected.
 #include "../../include/q4g64.h"
 
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -408,6 +409,49 @@ int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2,
   if (rtf == 1) return ffn_launch_s1<4, 1>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
   if (rtf == 2) return ffn_launch_s1<4, 2>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
   return ffn_launch_s1<4, 4>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
+}
+
+static const int kCostRows[5] = {1, 2, 4, 8, 16};
+
+int qmv_window_costs(int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, float* y,
+                     int64_t ldy, int reps, float* us_out, void* stream) {
+  const char* fn = "qmv_window_costs";
+  if (us_out == nullptr) return fail(Q4_EINVAL, "%s: us_out is NULL", fn);
+  if (reps < 1 || reps > 10000) return fail(Q4_EINVAL, "%s: reps=%d is outside 1..10000", fn, reps);
+  hipStream_t s = (hipStream_t)stream;
+  // validates every argument at the largest row count (and warms the kernels up)
+  for (int i = 4; i >= 0; --i)
+    if (int rc = qmv_rows_impl(fn, bits, packed, N, K, x, x_dtype, ldx, kCostRows[i], y, ldy, s)) return rc;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return fail(Q4_EDEVICE, "%s: could not create timing events", fn);
+  }
+  int rc = Q4_OK;
+  for (int i = 0; i < 5 && rc == Q4_OK; ++i) {
+    if (hipEventRecord(e0, s) != hipSuccess) { rc = fail(Q4_EDEVICE, "%s: event record failed", fn); break; }
+    for (int r = 0; r < reps && rc == Q4_OK; ++r) rc = qmv_rows_impl(fn, bits, packed, N, K, x, x_dtype, ldx, kCostRows[i], y, ldy, s);
+    if (rc != Q4_OK) break;
+    float ms = 0.f;
+    if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
+      rc = fail(Q4_EDEVICE, "%s: event timing failed", fn);
+    else
+      us_out[i] = ms * 1000.f / (float)reps;
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return rc;
+}
+
+float qmv_window_cost(const float* us, int R) {
+  if (us == nullptr || R < 1 || R > 16) return NAN;
+  for (int i = 0; i < 4; ++i) {
+    if (R <= kCostRows[i + 1]) {
+      const float t = (float)(R - kCostRows[i]) / (float)(kCostRows[i + 1] - kCostRows[i]);
+      return us[i] + t * (us[i + 1] - us[i]);
+    }
+  }
+  return us[4];
 }
 
 }  // extern "C"

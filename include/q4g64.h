@@ -199,6 +199,25 @@ int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2,
 /* Message of the last failed call on this thread ("" if none). */
 const char* q4_last_error(void);
 
+/* Window-cost table (PR #1514, "What changes": window costs are timed at
+ * load for 1, 2, 4, 8 and 16 rows and interpolated between them, for the
+ * planner that picks how many streams' rows share a decode step).
+ *
+ * qmv_window_costs times qmv_rows_qg64 on `packed` at R = 1, 2, 4, 8, 16
+ * (x and y must hold 16 rows), each as the average of `reps` (1..10000)
+ * back-to-back launches between two HIP events on `stream`, and writes the
+ * five averages in microseconds to the HOST array us_out[5]. It blocks until
+ * the timing is done (a load-time call) and creates and destroys its two
+ * events; it allocates no device memory. Arguments are validated as for
+ * qmv_rows_qg64 at R = 16; timing failures return Q4_EDEVICE.
+ *
+ * qmv_window_cost returns the cost of R rows (1..16) read off the table by
+ * linear interpolation between the two timed row counts around R (exact at
+ * 1, 2, 4, 8, 16); NaN for R outside 1..16 or a NULL table. Host only. */
+int qmv_window_costs(int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, float* y,
+                     int64_t ldy, int reps, float* us_out, void* stream);
+float qmv_window_cost(const float* us, int R);
+
 #ifdef __cplusplus
 }
 #endif

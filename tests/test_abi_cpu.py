@@ -4,6 +4,7 @@ codes before anything reaches a device (no GPU needed: these calls fail
 validation and never enqueue)."""
 
 import ctypes
+import math
 import os
 import re
 
@@ -193,3 +194,32 @@ def test_wide_calls_validate_like_q4(bits):
     assert rc == q4.Q4_EUNSUPPORTED
     rc, _ = _rc("pack_qg64", bits, FAKE + 8, FAKE, FAKE, 512, 256, FAKE, None)
     assert rc == q4.Q4_EALIGN
+
+
+def test_window_cost_interpolation():
+    us = [5.0, 6.0, 8.0, 9.0, 13.0]
+    for R, c in zip((1, 2, 4, 8, 16), us):
+        assert q4.window_cost(us, R) == c
+    assert q4.window_cost(us, 3) == 7.0
+    assert q4.window_cost(us, 6) == 8.5
+    assert q4.window_cost(us, 12) == 11.0
+    assert abs(q4.window_cost(us, 5) - 8.25) < 1e-6
+    for R in (0, -1, 17, 100):
+        assert math.isnan(q4.window_cost(us, R))
+    assert math.isnan(q4.lib().qmv_window_cost(None, 4))
+
+
+def test_window_costs_rejects_bad_arguments():
+    out = (ctypes.c_float * 5)()
+    args = (4, FAKE, 512, 256, FAKE, q4.Q4_BF16, 256, FAKE, 512)
+    rc, msg = _rc("qmv_window_costs", *args, 10, None, None)
+    assert rc == q4.Q4_EINVAL and "us_out" in msg
+    for reps in (0, 10001):
+        rc, msg = _rc("qmv_window_costs", *args, reps, ctypes.addressof(out), None)
+        assert rc == q4.Q4_EINVAL and "reps" in msg
+    rc, msg = _rc("qmv_window_costs", 5, *args[1:], 10, ctypes.addressof(out), None)
+    assert rc == q4.Q4_EINVAL and "bits" in msg
+    rc, _ = _rc("qmv_window_costs", 4, FAKE, 100, 256, FAKE, q4.Q4_BF16, 256, FAKE, 512, 10, ctypes.addressof(out), None)
+    assert rc == q4.Q4_EINVAL
+    rc, _ = _rc("qmv_window_costs", 4, FAKE, 512, 256, FAKE, q4.Q4_BF16, 256, FAKE, 100, 10, ctypes.addressof(out), None)
+    assert rc == q4.Q4_EINVAL  # ldy < N
