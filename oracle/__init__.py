@@ -19,3 +19,11 @@ from .q4g64 import (  # noqa: F401
     unpack_codes,
     words_per_row,
 )
+from .fp8block import (  # noqa: F401
+    dequantize_fp8,
+    e4m3_to_f64,
+    error_weight_fp8,
+    matmul_rows_fp8,
+    matmul_rows_fp8_exact,
+    matmul_rows_fp8_fraction,
+)

@@ -8,12 +8,14 @@ dequantization, no dot products).
 
 from .workloads import (  # noqa: F401
     CONFIG_NAMES,
+    FP8Weight,
     QWeight,
     bf16_bits_from_f64,
     concat_rows,
     config,
     draw_bf16_rows,
     draw_f32_rows,
+    draw_fp8_weight,
     draw_qweight,
     pack_codes_bits,
     pack_codes_low_nibble_first,

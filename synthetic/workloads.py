@@ -127,6 +127,33 @@ def draw_qweight(rng: np.random.Generator, name: str, N: int, K: int, bits: int 
     return QWeight(name, N, K, pack_codes_bits(q, bits), s_bits, b_bits, bits)
 
 
+@dataclass
+class FP8Weight:
+    """One block-FP8 matrix: OCP E4M3 bytes and a float32 scale per 128 x 128 block."""
+
+    name: str
+    N: int
+    K: int
+    w8: np.ndarray  # uint8 [N][K]
+    scales: np.ndarray  # float32 [ceil(N/128)][ceil(K/128)]
+
+
+def draw_fp8_weight(rng: np.random.Generator, name: str, N: int, K: int) -> FP8Weight:
+    """Block-FP8 weights drawn in the code domain (no quantizer): a random
+    sign, an exponent field round(normal(7, 2)) clipped to 0..15 and a
+    uniform mantissa, the NaN pattern replaced by the largest finite value;
+    block scales float32(0.02 * 2**normal(0, 0.5))."""
+    if K % GROUP or N % GROUP or N <= 0 or K <= 0:
+        raise ValueError("N and K must be positive multiples of 64")
+    sign = rng.integers(0, 2, (N, K), dtype=np.uint8)
+    e = np.clip(np.rint(rng.normal(7.0, 2.0, (N, K))), 0, 15).astype(np.uint8)
+    m = rng.integers(0, 8, (N, K), dtype=np.uint8)
+    m = np.where((e == 15) & (m == 7), 6, m).astype(np.uint8)
+    w8 = ((sign << 7) | (e << 3) | m).astype(np.uint8)
+    sc = (0.02 * np.exp2(rng.normal(0.0, 0.5, (-(-N // 128), -(-K // 128))))).astype(np.float32)
+    return FP8Weight(name, N, K, w8, sc)
+
+
 def draw_bf16_rows(rng: np.random.Generator, rows: int, K: int, sigma: float = 1.0) -> np.ndarray:
     return bf16_bits_from_f64(rng.normal(0.0, sigma, (rows, K)))
 

@@ -405,3 +405,87 @@ def test_6bit_read_without_straddling_fails():
     y_wrong = oracle.matmul_rows(wrong_wq, sb, bb, x, bits=6)
     T = tol(oracle.error_weight(wq, sb, bb, x, bits=6), K)
     assert np.any(np.abs(y_wrong - exact) > T)
+
+
+# ------------------------------------------------ block FP8 (weight-only)
+# PR #1696 serves "the block FP8 export weight-only"; the reading is OCP E4M3
+# bytes with a float32 scale per 128 x 128 block.
+
+
+def test_e4m3_hand_worked_values():
+    table = {0x00: 0.0, 0x38: 1.0, 0x40: 2.0, 0x3C: 1.5, 0x7E: 448.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+             0x08: 2.0 ** -6, 0x77: 240.0, 0xB8: -1.0, 0xFE: -448.0, 0x30: 0.5}
+    codes = np.array(list(table), dtype=np.uint8)
+    assert oracle.e4m3_to_f64(codes).tolist() == list(table.values())
+    assert math.copysign(1.0, float(oracle.e4m3_to_f64(np.array([0x80], dtype=np.uint8))[0])) == -1.0
+    assert np.all(np.isnan(oracle.e4m3_to_f64(np.array([0x7F, 0xFF], dtype=np.uint8))))
+
+
+def test_e4m3_all_codes_by_accumulated_steps():
+    """Positive codes in order differ by 2^-9 below 0x08 and by 2^(e-10)
+    within exponent field e: the whole table rebuilt from its increments."""
+    expect = [0.0]
+    for c in range(1, 0x7F):
+        e = c >> 3
+        step = 2.0 ** -9 if c <= 8 else 2.0 ** ((c - 1 >> 3) - 10)
+        expect.append(expect[-1] + step)
+    v = oracle.e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    assert v.tolist() == expect
+    neg = oracle.e4m3_to_f64(np.arange(0x80, 0xFF, dtype=np.uint8))
+    assert (-neg[1:]).tolist() == expect[1:]
+
+
+def _fp8(rng, N, K):
+    return synthetic.draw_fp8_weight(rng, "f", N, K)
+
+
+@pytest.mark.parametrize("k", [0, 63, 64, 127, 128, 255])
+def test_fp8_one_hot_activation_and_block_scales(k):
+    rng = np.random.default_rng(600 + k)
+    w = _fp8(rng, 256, 256)
+    x = np.zeros((1, 256), dtype=np.uint16)
+    x[0, k] = 0x3F80
+    y = oracle.matmul_rows_fp8(w.w8, w.scales, x)[0]
+    vals = oracle.e4m3_to_f64(w.w8[:, k])
+    s = w.scales.astype(np.float64)[np.arange(256) // 128, k // 128]
+    assert np.array_equal(y, vals * s)
+    # rows 127 and 128 sit in different scale blocks
+    assert w.scales[0, k // 128] != w.scales[1, k // 128]
+
+
+def test_fp8_fsum_equals_fraction_bruteforce():
+    rng = np.random.default_rng(610)
+    w = _fp8(rng, 64, 192)
+    w8 = w.w8[:3]
+    x = _bf16(rng.normal(0, 1, (2, 192)))
+    exact = oracle.matmul_rows_fp8_exact(w8, w.scales[:1], x)
+    frac = oracle.matmul_rows_fp8_fraction(w8, w.scales[:1], x)
+    for m in range(2):
+        for n in range(3):
+            assert exact[m, n] == float(frac[m][n])
+    y = oracle.matmul_rows_fp8(w8, w.scales[:1], x)
+    A = oracle.error_weight_fp8(w8, w.scales[:1], x)
+    assert np.all(np.abs(y - exact) <= (192 + 2) * 2.0 ** -52 * A)
+
+
+@pytest.mark.parametrize("kind", ["bias8", "block64", "e5m2"])
+def test_fp8_planted_mistakes_fail(kind):
+    """Plausible misreadings of the format, planted in a copy of the decode,
+    land far outside the fp32 tolerance."""
+    rng = np.random.default_rng(620)
+    w = _fp8(rng, 256, 256)
+    x = _bf16(rng.normal(0, 1, (2, 256)))
+    exact = oracle.matmul_rows_fp8_exact(w.w8, w.scales, x)
+    c = w.w8.astype(np.int64)
+    if kind == "bias8":
+        W = oracle.e4m3_to_f64(w.w8) / 2.0 * w.scales.astype(np.float64)[np.arange(256) // 128][:, np.arange(256) // 128]
+    elif kind == "block64":
+        W = oracle.e4m3_to_f64(w.w8) * w.scales.astype(np.float64)[np.arange(256) // 64 % 2][:, np.arange(256) // 64 % 2]
+    else:
+        sign = np.where(c & 0x80, -1.0, 1.0)
+        e, m = (c >> 2) & 0x1F, (c & 3).astype(np.float64)
+        vals = sign * np.where(e == 0, m / 4 * 2.0 ** -14, (1 + m / 4) * np.exp2(e - 15.0))
+        W = vals * w.scales.astype(np.float64)[np.arange(256) // 128][:, np.arange(256) // 128]
+    y = oracle.activations_f64(x) @ W.T
+    T = tol(oracle.error_weight_fp8(w.w8, w.scales, x), 256)
+    assert np.any(np.abs(y - exact) > T)
