@@ -332,7 +332,7 @@ def main():
     if not args.no_pgemm:
         result["pgemm"] = bench_pgemm(dev)
     if not args.no_wide:
-        result["wide_codes"] = {str(b): bench_wide(dev, b, K, W, args.pool_mb, graph=g_used) for b in (6, 8)}
+        result["wide_codes"] = {str(b): bench_wide(dev, b, K, W, args.pool_mb, graph=g_used) for b in (6, 8, "fp8")}
 
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host")
@@ -341,22 +341,40 @@ def main():
 
 
 def bench_wide(dev, bits, K, W, pool_mb, graph=True, reps=5):
-    """The same decode FFN step and prompt window with MLX 6- or 8-bit codes
-    (same shapes, same cold weight pool, same timing method)."""
+    """The same decode FFN step and prompt window with MLX 6- or 8-bit codes,
+    or block-FP8 weights (bits == "fp8"): same shapes, same cold weight pool,
+    same timing method."""
     import torch
 
     import bit_weight_only_q4g64_amd as q4
     import synthetic
 
-    log(f"{bits}-bit codes: decode FFN step and prompt window")
-    rng = np.random.default_rng(100 + bits)
-    w1 = synthetic.draw_qweight(rng, "w1", 8192, 2048, bits=bits)
-    w3 = synthetic.draw_qweight(rng, "w3", 8192, 2048, bits=bits)
-    w2 = synthetic.draw_qweight(rng, "w2", 2048, 8192, bits=bits)
+    fp8 = bits == "fp8"
+    log(f"{bits} weights: decode FFN step and prompt window")
+    rng = np.random.default_rng(100 + (9 if fp8 else bits))
+    if fp8:
+        draw = lambda name, N, Kk: synthetic.draw_fp8_weight(rng, name, N, Kk)  # noqa: E731
+        pack = lambda w: q4.pack_fp8b(to_dev(w.w8, np.uint8, dev), to_dev(w.scales, np.float32, dev))  # noqa: E731
+        nbytes = q4.fp8b_packed_bytes
+        w13_call = lambda p1, p3, x, z: q4.qmv_w13_swiglu_fp8b(p1, p3, 8192, 2048, x, y=z)  # noqa: E731
+        rows_call = lambda p2, z, y: q4.qmv_rows_fp8b(p2, 2048, 8192, z, y=y)  # noqa: E731
+        win_call = lambda p1, p3, xw, zw: q4.qmm_window_fp8b(p1, p3, 8192, 2048, xw, y=zw)  # noqa: E731
+        algo = lambda N, Kk: N * Kk + 4 * N * Kk // 64  # noqa: E731  (one byte per weight + the 32-bit scale words)
+    else:
+        draw = lambda name, N, Kk: synthetic.draw_qweight(rng, name, N, Kk, bits=bits)  # noqa: E731
+        pack = lambda w: pack_dev(w, dev)  # noqa: E731
+        nbytes = lambda N, Kk: q4.packed_bytes(N, Kk, bits)  # noqa: E731
+        w13_call = lambda p1, p3, x, z: q4.qmv_w13_swiglu(p1, p3, 8192, 2048, x, y=z, bits=bits)  # noqa: E731
+        rows_call = lambda p2, z, y: q4.qmv_rows(p2, 2048, 8192, z, y=y, bits=bits)  # noqa: E731
+        win_call = lambda p1, p3, xw, zw: q4.qmm_window(p1, p3, 8192, 2048, xw, y=zw, bits=bits)  # noqa: E731
+        algo = lambda N, Kk: qbytes(N, Kk, bits)  # noqa: E731
+    w1 = draw("w1", 8192, 2048)
+    w3 = draw("w3", 8192, 2048)
+    w2 = draw("w2", 2048, 8192)
     xb = synthetic.draw_bf16_rows(rng, 1, 2048)
-    copy_bytes = q4.packed_bytes(8192, 2048, bits) * 2 + q4.packed_bytes(2048, 8192, bits)
+    copy_bytes = nbytes(8192, 2048) * 2 + nbytes(2048, 8192)
     ncopies = max(2, -(-pool_mb * (1 << 20) // copy_bytes))
-    base = [pack_dev(w1, dev), pack_dev(w3, dev), pack_dev(w2, dev)]
+    base = [pack(w1), pack(w3), pack(w2)]
     pool = [base] + [[t.clone() for t in base] for _ in range(ncopies - 1)]
     x = to_dev(xb, np.int16, dev).view(torch.bfloat16)
     z = torch.empty((1, 8192), dtype=torch.float32, device=dev)
@@ -364,8 +382,8 @@ def bench_wide(dev, bits, K, W, pool_mb, graph=True, reps=5):
 
     def step(i):
         p1, p3, p2 = pool[i % ncopies]
-        q4.qmv_w13_swiglu(p1, p3, 8192, 2048, x, y=z, bits=bits)
-        q4.qmv_rows(p2, 2048, 8192, z, y=y, bits=bits)
+        w13_call(p1, p3, x, z)
+        rows_call(p2, z, y)
 
     for i in range(W):
         step(i)
@@ -393,25 +411,24 @@ def bench_wide(dev, bits, K, W, pool_mb, graph=True, reps=5):
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / K
-    t13 = batch_average_us(torch, lambda i: q4.qmv_w13_swiglu(pool[i % ncopies][0], pool[i % ncopies][1], 8192, 2048, x, y=z,
-                                                               bits=bits), W, K)
-    t2 = batch_average_us(torch, lambda i: q4.qmv_rows(pool[i % ncopies][2], 2048, 8192, z, y=y, bits=bits), W, K)
-    b13 = 2 * qbytes(8192, 2048, bits) + 2048 * 2 + 8192 * 4
-    b2 = qbytes(2048, 8192, bits) + 8192 * 4 + 2048 * 4
+    t13 = batch_average_us(torch, lambda i: w13_call(pool[i % ncopies][0], pool[i % ncopies][1], x, z), W, K)
+    t2 = batch_average_us(torch, lambda i: rows_call(pool[i % ncopies][2], z, y), W, K)
+    b13 = 2 * algo(8192, 2048) + 2048 * 2 + 8192 * 4
+    b2 = algo(2048, 8192) + 8192 * 4 + 2048 * 4
     del pool, base
     torch.cuda.empty_cache()
 
     # prompt window: w1/w3 + SwiGLU over 8192 rows, bf16 out
     xw = to_dev(synthetic.draw_bf16_rows(rng, 8192, 2048), np.int16, dev).view(torch.bfloat16)
-    p1, p3 = pack_dev(w1, dev), pack_dev(w3, dev)
+    p1, p3 = pack(w1), pack(w3)
     zw = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
     for _ in range(2):
-        q4.qmm_window(p1, p3, 8192, 2048, xw, y=zw, bits=bits)
+        win_call(p1, p3, xw, zw)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
     torch.cuda.synchronize()
     for e in evs:
         e[0].record()
-        q4.qmm_window(p1, p3, 8192, 2048, xw, y=zw, bits=bits)
+        win_call(p1, p3, xw, zw)
         e[1].record()
     torch.cuda.synchronize()
     tw = np.array([e[0].elapsed_time(e[1]) for e in evs]).mean() * 1e-3

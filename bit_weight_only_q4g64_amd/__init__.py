@@ -42,6 +42,13 @@ _SIGNATURES = {
     "qmv_w13_swiglu_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
     "qmm_window_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P]),
     "qmm_cut_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _I64, _P]),
+    "fp8b_packed_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "pack_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
+    "unpack_fp8b": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "qmv_rows_fp8b": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, _I64, ctypes.c_int, _P, _I64, _P]),
+    "qmv_w13_swiglu_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
+    "qmm_window_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P]),
+    "qmm_cut_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _I64, _P]),
     "qmv_window_costs": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P, _I64, ctypes.c_int, _P, _P]),
     "qmv_window_cost": (ctypes.c_float, [_P, ctypes.c_int]),
     "q4g64_ffn_work_bytes": (ctypes.c_size_t, [_I64, ctypes.c_int]),
@@ -312,3 +319,102 @@ def window_cost(costs, R: int) -> float:
     """Interpolated cost of R rows (1..16) from a window_costs table."""
     arr = (ctypes.c_float * 5)(*[float(c) for c in costs])
     return float(lib().qmv_window_cost(ctypes.addressof(arr), R))
+
+
+# ---- block FP8 (E4M3 bytes, float32 scale per 128 x 128 block) -------------
+
+
+def fp8b_packed_bytes(N: int, K: int) -> int:
+    return int(lib().fp8b_packed_bytes(N, K))
+
+
+def pack_fp8b(w8: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    """E4M3 bytes [N][K] (uint8) and float32 block scales [ceil(N/128)][ceil(K/128)] -> packed layout."""
+    for t, name in ((w8, "w8"), (scales, "scales")):
+        _dev(t, name)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if w8.dtype != torch.uint8 or scales.dtype != torch.float32:
+        raise ValueError("w8 is uint8 and scales float32")
+    N, K = w8.shape
+    if tuple(scales.shape) != (-(-N // 128), -(-K // 128)):
+        raise ValueError("scales must be [ceil(N/128)][ceil(K/128)]")
+    nbytes = fp8b_packed_bytes(N, K)
+    if nbytes == 0:
+        raise Q4Error("pack_fp8b", Q4_EINVAL, f"invalid shape N={N} K={K}")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w8.device)
+    _check("pack_fp8b", lib().pack_fp8b(w8.data_ptr(), scales.data_ptr(), N, K, out.data_ptr(), _stream()))
+    return out
+
+
+def unpack_fp8b(packed: torch.Tensor, N: int, K: int):
+    """Packed layout -> (w8 uint8 [N][K], scales float32 [ceil(N/128)][ceil(K/128)])."""
+    _dev(packed, "packed")
+    w8 = torch.empty((N, K), dtype=torch.uint8, device=packed.device)
+    sc = torch.empty((-(-N // 128), -(-K // 128)), dtype=torch.float32, device=packed.device)
+    _check("unpack_fp8b", lib().unpack_fp8b(packed.data_ptr(), N, K, w8.data_ptr(), sc.data_ptr(), _stream()))
+    return w8, sc
+
+
+def qmv_rows_fp8b(packed: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[r] = W x[r] for the 1..16 rows of x (bf16 or float32), W block FP8."""
+    _dev(packed, "packed")
+    _dev(x, "x")
+    xd = Q4_BF16 if x.dtype == torch.bfloat16 else Q4_F32 if x.dtype == torch.float32 else None
+    if xd is None:
+        raise ValueError("x must be bfloat16 or float32")
+    R = x.shape[0]
+    if y is None:
+        y = torch.empty((R, N), dtype=torch.float32, device=x.device)
+    _check("qmv_rows_fp8b", lib().qmv_rows_fp8b(packed.data_ptr(), N, K, x.data_ptr(), xd, _rowmajor(x, "x"), R, y.data_ptr(),
+                                                _rowmajor(y, "y"), _stream()))
+    return y
+
+
+def qmv_w13_swiglu_fp8b(p1: torch.Tensor, p3: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[r] = silu(W1 x[r]) * (W3 x[r]) for the 1..16 bf16 rows of x, W1 and W3 block FP8."""
+    _dev(p1, "packed_w1")
+    _dev(p3, "packed_w3")
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    R = x.shape[0]
+    if y is None:
+        y = torch.empty((R, N), dtype=torch.float32, device=x.device)
+    _check("qmv_w13_swiglu_fp8b", lib().qmv_w13_swiglu_fp8b(p1.data_ptr(), p3.data_ptr(), N, K, x.data_ptr(), _rowmajor(x, "x"), R,
+                                                            y.data_ptr(), _rowmajor(y, "y"), _stream()))
+    return y
+
+
+def qmm_window_fp8b(pa: torch.Tensor, pb: torch.Tensor | None, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None,
+                    out_dtype=torch.float32) -> torch.Tensor:
+    """Prompt window with block-FP8 weights: y = A x or silu(A x) * (B x)."""
+    _dev(pa, "packed_a")
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _check("qmm_window_fp8b", lib().qmm_window_fp8b(pa.data_ptr(), None if pb is None else pb.data_ptr(), N, K, x.data_ptr(),
+                                                    _rowmajor(x, "x"), M, y.data_ptr(), _out_dtype(y.dtype), _rowmajor(y, "y"), _stream()))
+    return y
+
+
+def qmm_cut_fp8b(pa: torch.Tensor, pb: torch.Tensor | None, N: int, K: int, x: torch.Tensor, windows, y: torch.Tensor | None = None,
+                 out_dtype=torch.float32) -> torch.Tensor:
+    """The prompt x through consecutive windows, block-FP8 weights."""
+    _dev(pa, "packed_a")
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    windows = [int(w) for w in windows]
+    if sum(windows) != x.shape[0]:
+        raise ValueError("window row counts must add up to the prompt's rows")
+    if y is None:
+        y = torch.empty((x.shape[0], N), dtype=out_dtype, device=x.device)
+    arr = (ctypes.c_int64 * len(windows))(*windows)
+    _check("qmm_cut_fp8b", lib().qmm_cut_fp8b(pa.data_ptr(), None if pb is None else pb.data_ptr(), N, K, x.data_ptr(),
+                                              _rowmajor(x, "x"), arr, len(windows), y.data_ptr(), _out_dtype(y.dtype), _rowmajor(y, "y"),
+                                              _stream()))
+    return y

@@ -79,6 +79,12 @@ int check_bits(const char* fn, int bits) {
   return Q4_OK;
 }
 
+// Internal: the MLX widths or block FP8.
+int check_fmt(const char* fn, int fmt) {
+  if (fmt == q4::kFmtFp8) return Q4_OK;
+  return check_bits(fn, fmt);
+}
+
 size_t packed_bytes_impl(int bits, int64_t N, int64_t K) {
   if (bits != 4 && bits != 6 && bits != 8) return 0;
   if (N <= 0 || K <= 0 || N % 64 != 0 || K % 64 != 0 || N > kMaxDim || K > kMaxDim || N * K > kMaxElems) return 0;
@@ -132,7 +138,7 @@ int unpack_impl(const char* fn, int bits, const void* packed, int64_t N, int64_t
 
 int qmv_rows_impl(const char* fn, int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx,
                   int R, float* y, int64_t ldy, hipStream_t s) {
-  if (int rc = check_bits(fn, bits)) return rc;
+  if (int rc = check_fmt(fn, bits)) return rc;
   if (int rc = check_nk(fn, N, K)) return rc;
   if (R < 1 || R > 16) return fail(Q4_EINVAL, "%s: R=%d is outside 1..16", fn, R);
   if (int rc = check_ptr(fn, "packed", packed, 16)) return rc;
@@ -151,7 +157,7 @@ int qmv_rows_impl(const char* fn, int bits, const void* packed, int64_t N, int64
 
 int qmv_w13_impl(const char* fn, int bits, const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
                  int64_t ldx, int R, float* y, int64_t ldy, hipStream_t s) {
-  if (int rc = check_bits(fn, bits)) return rc;
+  if (int rc = check_fmt(fn, bits)) return rc;
   if (int rc = check_nk(fn, N, K)) return rc;
   if (R < 1 || R > 16) return fail(Q4_EINVAL, "%s: R=%d is outside 1..16", fn, R);
   if (int rc = check_ptr(fn, "packed_w1", packed_w1, 16)) return rc;
@@ -211,6 +217,8 @@ int qmm_window_impl(const char* fn, int bits, const void* packed_a, const void* 
     pgemm_launch_bits<6>(swiglu, obf16, grid, block, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
   else if (bits == 8)
     pgemm_launch_bits<8>(swiglu, obf16, grid, block, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
+  else if (bits == kFmtFp8)
+    pgemm_launch_bits<kFmtFp8>(swiglu, obf16, grid, block, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
   else
     pgemm_launch_bits<4>(swiglu, obf16, grid, block, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
   return launched(fn);
@@ -273,7 +281,7 @@ int ffn_launch_s1(int spw1, int spw2, const uint8_t* p1, const uint8_t* p3, cons
 
 int qmm_window_checked(const char* fn, int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K,
                        const uint16_t* x, int64_t ldx, int64_t M, void* y, int y_dtype, int64_t ldy, hipStream_t s) {
-  if (int rc = check_bits(fn, bits)) return rc;
+  if (int rc = check_fmt(fn, bits)) return rc;
   if (int rc = check_window_args(fn, packed_a, packed_b, N, K, x, ldx, y, y_dtype, ldy)) return rc;
   if (M < 1 || M > kPgemmMaxM) return fail(Q4_EINVAL, "%s: M=%lld is outside 1..%lld", fn, (long long)M, (long long)kPgemmMaxM);
   return qmm_window_impl(fn, bits, packed_a, packed_b, N, K, x, ldx, M, y, y_dtype, ldy, s);
@@ -281,7 +289,7 @@ int qmm_window_checked(const char* fn, int bits, const void* packed_a, const voi
 
 int qmm_cut_impl(const char* fn, int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x,
                  int64_t ldx, const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, hipStream_t s) {
-  if (int rc = check_bits(fn, bits)) return rc;
+  if (int rc = check_fmt(fn, bits)) return rc;
   if (int rc = check_window_args(fn, packed_a, packed_b, N, K, x, ldx, y, y_dtype, ldy)) return rc;
   if (window_rows == nullptr || n_windows < 1) return fail(Q4_EINVAL, "%s: need at least one window", fn);
   for (int w = 0; w < n_windows; ++w)
@@ -335,6 +343,7 @@ int qmv_rows(const void* packed, int64_t N, int64_t K, const void* x, int x_dtyp
 
 int qmv_rows_qg64(int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R, float* y,
                   int64_t ldy, void* stream) {
+  if (int rc = check_bits("qmv_rows_qg64", bits)) return rc;
   return qmv_rows_impl("qmv_rows_qg64", bits, packed, N, K, x, x_dtype, ldx, R, y, ldy, (hipStream_t)stream);
 }
 
@@ -345,6 +354,7 @@ int qmv_w13_swiglu(const void* packed_w1, const void* packed_w3, int64_t N, int6
 
 int qmv_w13_swiglu_qg64(int bits, const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
                         int64_t ldx, int R, float* y, int64_t ldy, void* stream) {
+  if (int rc = check_bits("qmv_w13_swiglu_qg64", bits)) return rc;
   return qmv_w13_impl("qmv_w13_swiglu_qg64", bits, packed_w1, packed_w3, N, K, x, ldx, R, y, ldy, (hipStream_t)stream);
 }
 
@@ -355,6 +365,7 @@ int qmm_window(const void* packed_a, const void* packed_b, int64_t N, int64_t K,
 
 int qmm_window_qg64(int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                     int64_t M, void* y, int y_dtype, int64_t ldy, void* stream) {
+  if (int rc = check_bits("qmm_window_qg64", bits)) return rc;
   return qmm_window_checked("qmm_window_qg64", bits, packed_a, packed_b, N, K, x, ldx, M, y, y_dtype, ldy, (hipStream_t)stream);
 }
 
@@ -365,6 +376,7 @@ int qmm_cut(const void* packed_a, const void* packed_b, int64_t N, int64_t K, co
 
 int qmm_cut_qg64(int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                  const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, void* stream) {
+  if (int rc = check_bits("qmm_cut_qg64", bits)) return rc;
   return qmm_cut_impl("qmm_cut_qg64", bits, packed_a, packed_b, N, K, x, ldx, window_rows, n_windows, y, y_dtype, ldy,
                       (hipStream_t)stream);
 }
@@ -411,11 +423,71 @@ int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2,
   return ffn_launch_s1<4, 4>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
 }
 
+size_t fp8b_packed_bytes(int64_t N, int64_t K) { return packed_bytes_impl(8, N, K); }
+
+int pack_fp8b(const uint8_t* w8, const float* scales, int64_t N, int64_t K, void* packed, void* stream) {
+  const char* fn = "pack_fp8b";
+  if (int rc = check_nk(fn, N, K)) return rc;
+  if (int rc = check_ptr(fn, "w8", w8, 16)) return rc;
+  if (int rc = check_ptr(fn, "scales", scales, 4)) return rc;
+  if (int rc = check_ptr(fn, "packed", packed, 16)) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t words = q4::codes_bytes(N, K, 8) / 4;
+  const int64_t sb_entries = (N / q4::kTileN) * q4::n_pairs(K) * q4::kTileN;
+  uint8_t* out = (uint8_t*)packed;
+  hipLaunchKernelGGL(q4::pack_codes_wide_kernel<8>, dim3(grid_for(words, 256)), dim3(256), 0, s, (const uint32_t*)w8, N, K,
+                     (uint32_t*)out);
+  if (int rc = launched(fn)) return rc;
+  hipLaunchKernelGGL(q4::pack_scale_fp8_kernel, dim3(grid_for(sb_entries, 256)), dim3(256), 0, s, scales, N, K,
+                     (q4::u32x2*)(out + q4::codes_bytes(N, K, 8)));
+  return launched(fn);
+}
+
+int unpack_fp8b(const void* packed, int64_t N, int64_t K, uint8_t* w8, float* scales, void* stream) {
+  const char* fn = "unpack_fp8b";
+  if (int rc = check_nk(fn, N, K)) return rc;
+  if (int rc = check_ptr(fn, "packed", packed, 16)) return rc;
+  if (int rc = check_ptr(fn, "w8", w8, 16)) return rc;
+  if (int rc = check_ptr(fn, "scales", scales, 4)) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const uint8_t* in = (const uint8_t*)packed;
+  hipLaunchKernelGGL(q4::unpack_codes_wide_kernel<8>, dim3(grid_for(N * (K / 4), 256)), dim3(256), 0, s, (const uint32_t*)in, N, K,
+                     (uint32_t*)w8);
+  if (int rc = launched(fn)) return rc;
+  const int64_t blocks = ((N + 127) / 128) * q4::n_pairs(K);
+  hipLaunchKernelGGL(q4::unpack_scale_fp8_kernel, dim3(grid_for(blocks, 256)), dim3(256), 0, s,
+                     (const q4::u32x2*)(in + q4::codes_bytes(N, K, 8)), N, K, scales);
+  return launched(fn);
+}
+
+int qmv_rows_fp8b(const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R, float* y, int64_t ldy,
+                  void* stream) {
+  return qmv_rows_impl("qmv_rows_fp8b", q4::kFmtFp8, packed, N, K, x, x_dtype, ldx, R, y, ldy, (hipStream_t)stream);
+}
+
+int qmv_w13_swiglu_fp8b(const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x, int64_t ldx, int R,
+                        float* y, int64_t ldy, void* stream) {
+  return qmv_w13_impl("qmv_w13_swiglu_fp8b", q4::kFmtFp8, packed_w1, packed_w3, N, K, x, ldx, R, y, ldy, (hipStream_t)stream);
+}
+
+int qmm_window_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx, int64_t M,
+                    void* y, int y_dtype, int64_t ldy, void* stream) {
+  return qmm_window_checked("qmm_window_fp8b", q4::kFmtFp8, packed_a, packed_b, N, K, x, ldx, M, y, y_dtype, ldy,
+                            (hipStream_t)stream);
+}
+
+int qmm_cut_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                 const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, void* stream) {
+  return qmm_cut_impl("qmm_cut_fp8b", q4::kFmtFp8, packed_a, packed_b, N, K, x, ldx, window_rows, n_windows, y, y_dtype, ldy,
+                      (hipStream_t)stream);
+}
+
 static const int kCostRows[5] = {1, 2, 4, 8, 16};
 
 int qmv_window_costs(int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, float* y,
                      int64_t ldy, int reps, float* us_out, void* stream) {
   const char* fn = "qmv_window_costs";
+  if (int rc = check_bits(fn, bits)) return rc;
   if (us_out == nullptr) return fail(Q4_EINVAL, "%s: us_out is NULL", fn);
   if (reps < 1 || reps > 10000) return fail(Q4_EINVAL, "%s: reps=%d is outside 1..10000", fn, reps);
   hipStream_t s = (hipStream_t)stream;

@@ -35,7 +35,12 @@ constexpr int kPairSbBytes = 128;     // scale+bias of one column tile x two gro
 // Device layout sizes (see include/q4g64.h for the full description). Codes
 // of b bits take 256 * b bytes per column tile and group pair; the scale/bias
 // block is the same for every width.
-__host__ __device__ constexpr int pair_code_bytes(int bits) { return 256 * bits; }
+// Code formats: 4, 6 and 8 are MLX affine codes of that width; kFmtFp8 is
+// block FP8 (OCP E4M3 bytes in the 8-bit layout, a float32 block scale in
+// place of each group's scale/bias word, no bias term).
+constexpr int kFmtFp8 = 9;
+__host__ __device__ constexpr int code_bits(int fmt) { return fmt == kFmtFp8 ? 8 : fmt; }
+__host__ __device__ constexpr int pair_code_bytes(int fmt) { return 256 * code_bits(fmt); }
 __host__ __device__ inline int64_t n_pairs(int64_t K) { return (K / kGroup + 1) / 2; }
 __host__ __device__ inline int64_t codes_bytes(int64_t N, int64_t K, int bits = 4) {
   return (N / kTileN) * n_pairs(K) * pair_code_bytes(bits);
@@ -112,6 +117,24 @@ struct CodeWords<8> {
   u32x4 a;
   u32x4 b;
 };
+template <>
+struct CodeWords<kFmtFp8> {
+  u32x4 a;
+  u32x4 b;
+};
+
+// 8 OCP E4M3 bytes (codes 0..3 in w0, 4..7 in w1) -> 8 bf16 in k order.
+// Every finite E4M3 value (4 significant bits, exponents 2^-9 .. 2^8) is a
+// bf16 value, so the conversion with scale 1 is exact.
+__device__ __forceinline__ bf16x8 fp8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2 c01 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 c23 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 c45 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 c67 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  const auto c0123 = __builtin_shufflevector(c01, c23, 0, 1, 2, 3);
+  const auto c4567 = __builtin_shufflevector(c45, c67, 0, 1, 2, 3);
+  return __builtin_shufflevector(c0123, c4567, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // The bf16 B-operand fragment of group gh (0/1 within the pair), half hh.
 template <int BITS, int GH, int HH>
@@ -120,6 +143,9 @@ __device__ __forceinline__ bf16x8 code_frag(const CodeWords<BITS>& c) {
     return codes_to_bf16(c.a[2 * GH + HH]);
   } else if constexpr (BITS == 6) {
     return six_to_bf16<HH>(c.a[2 * GH + HH], c.b[GH]);
+  } else if constexpr (BITS == kFmtFp8) {
+    if constexpr (GH == 0) return fp8_to_bf16(c.a[2 * HH], c.a[2 * HH + 1]);
+    else return fp8_to_bf16(c.b[2 * HH], c.b[2 * HH + 1]);
   } else {
     if constexpr (GH == 0) return bytes_to_bf16(c.a[2 * HH], c.a[2 * HH + 1]);
     else return bytes_to_bf16(c.b[2 * HH], c.b[2 * HH + 1]);

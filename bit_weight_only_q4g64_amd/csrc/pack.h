@@ -185,4 +185,33 @@ __global__ void unpack_codes_wide_kernel(const uint32_t* __restrict__ dev, int64
   }
 }
 
+// ---- block FP8 -----------------------------------------------------------
+// Codes are E4M3 bytes [N][K], packed by pack_codes_wide_kernel<8> (the
+// canonical 8-bit stream is the bytes in k order). The float32 scale of
+// block (n / 128, p) (128 rows x the 128 k of group pair p) goes into both
+// group words of pair p for column n (zero past G).
+__global__ void pack_scale_fp8_kernel(const float* __restrict__ sc, int64_t N, int64_t K, u32x2* __restrict__ out) {
+  const int64_t P = n_pairs(K), G = K / kGroup;
+  const int64_t total = (N / kTileN) * P * kTileN;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(e & 15);
+    const int64_t blk = e >> 4;
+    const int64_t t = blk / P, p = blk - t * P;
+    const int64_t n = t * kTileN + c;
+    const uint32_t v = __float_as_uint(sc[(n / 128) * P + p]);
+    out[e] = u32x2{v, 2 * p + 1 < G ? v : 0u};
+  }
+}
+
+// Inverse: block (i, p) read back from column 128 i of pair p.
+__global__ void unpack_scale_fp8_kernel(const u32x2* __restrict__ sb, int64_t N, int64_t K, float* __restrict__ sc) {
+  const int64_t P = n_pairs(K), NB = (N + 127) / 128;
+  const int64_t total = NB * P;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = e / P, p = e - i * P;
+    const int64_t t = (i * 128) / kTileN;
+    sc[e] = __uint_as_float(sb[(t * P + p) * kTileN].x);
+  }
+}
+
 }  // namespace q4

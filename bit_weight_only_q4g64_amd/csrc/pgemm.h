@@ -61,7 +61,7 @@ constexpr int kCStageBytes = kPgemmSlots * kPairCodeBytes;  // 16 KiB
 // workgroups per CU): per slot, 8-bit is the group's 1 KiB sub-block as is;
 // 6-bit is the group's two nibble words of every lane then its high-pair
 // word of every lane, each as a 256-byte row (three dword copies).
-__host__ __device__ constexpr int pgemm_group_code_bytes(int bits) { return bits == 8 ? 1024 : 768; }
+__host__ __device__ constexpr int pgemm_group_code_bytes(int bits) { return code_bits(bits) == 8 ? 1024 : 768; }
 __host__ __device__ constexpr int pgemm_cstage_bytes(int bits) {
   return bits == 4 ? kCStageBytes : kPgemmSlots * pgemm_group_code_bytes(bits);
 }
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_kernel(const uint8_t* 
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const uint32_t blk = (uint32_t)((tsl[u] - t0) * P + p) * kPcb;
-      if constexpr (BITS == 8) {
+      if constexpr (code_bits(BITS) == 8) {
         dma_b128(cr, cvo, blk + (uint32_t)gh * 1024u, dst + u * kSlotStage);
       } else {
         dma_b32(cr, (uint32_t)lane * 16u + (uint32_t)gh * 8u, blk, dst + u * kSlotStage);
@@ -301,11 +301,12 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_kernel(const uint8_t* 
 #pragma unroll
     for (int s = 0; s < kPgemmNT; ++s) {
       w[s] = *(const uint32_t*)(sb0 + lslot[s] * kPairSbBytes + jj * 8 + gh * 4);
-      sc[s] = bf16_lo(w[s]);
+      sc[s] = BITS == kFmtFp8 ? __uint_as_float(w[s]) : bf16_lo(w[s]);
     }
 
-    // activation sums of this wave's 32 of the 128 rows (16 x 16 tiles)
-    {
+    // activation sums of this wave's 32 of the 128 rows (16 x 16 tiles);
+    // block FP8 has no bias term and needs none
+    if constexpr (BITS != kFmtFp8) {
       const int i = lane & 15, kc = lane >> 4;
       float* sw = ssum + ((g / kPgemmChunk) & 1) * kPgemmRows * kPgemmChunk + gg;
 #pragma unroll
@@ -337,6 +338,13 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_kernel(const uint8_t* 
         q[s][2] = bytes_to_bf16(c02[2], c02[3]);
         q[s][1] = bytes_to_bf16(c13[0], c13[1]);
         q[s][3] = bytes_to_bf16(c13[2], c13[3]);
+      } else if constexpr (BITS == kFmtFp8) {
+        const uint8_t* cl = cb0 + lslot[s] * kSlotStage + L * 16;
+        const u32x4 c02 = *(const u32x4*)cl, c13 = *(const u32x4*)(cl + 512);
+        q[s][0] = fp8_to_bf16(c02[0], c02[1]);
+        q[s][2] = fp8_to_bf16(c02[2], c02[3]);
+        q[s][1] = fp8_to_bf16(c13[0], c13[1]);
+        q[s][3] = fp8_to_bf16(c13[2], c13[3]);
       } else {
         const uint32_t* cl = (const uint32_t*)(cb0 + lslot[s] * kSlotStage);
         q[s][0] = six_to_bf16<0>(cl[L], cl[128 + L]);
@@ -364,14 +372,25 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_kernel(const uint8_t* 
     // the previous chunk's bias term follows the fold of its next chunk's
     // first group (its sums are visible since this group's barrier); only
     // then does this group's bias word join the new chunk's operand
-    if constexpr (gh == 0) {
-      if (gg == 0 && g > 0) bias_chunk(g / kPgemmChunk - 1);
-    }
-    const bool take = ((gg >> 1) & 1) == hl;
+    if constexpr (BITS == kFmtFp8) {
+      // No bias term: an empty statement that takes and returns every
+      // accumulator ends the group instead, so that the scheduler does not
+      // interleave consecutive groups (their live ranges overflow the
+      // register file: 100 to 1800 spilled registers without it).
 #pragma unroll
-    for (int s = 0; s < kPgemmNT; ++s) {
-      if (take && gg < 4) bsel[s][0][gh] = w[s];
-      if (take && gg >= 4) bsel[s][1][gh] = w[s];
+      for (int rt = 0; rt < kPgemmRT; ++rt)
+#pragma unroll
+        for (int s = 0; s < kPgemmNT; ++s) asm volatile("" : "+v"(acc[rt][s]));
+    } else {
+      if constexpr (gh == 0) {
+        if (gg == 0 && g > 0) bias_chunk(g / kPgemmChunk - 1);
+      }
+      const bool take = ((gg >> 1) & 1) == hl;
+#pragma unroll
+      for (int s = 0; s < kPgemmNT; ++s) {
+        if (take && gg < 4) bsel[s][0][gh] = w[s];
+        if (take && gg >= 4) bsel[s][1][gh] = w[s];
+      }
     }
   };
 
@@ -424,7 +443,7 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_kernel(const uint8_t* 
     }
   }
   dma_wait_barrier<0>();  // the last group's sums from every wave
-  bias_chunk((G - 1) / kPgemmChunk);
+  if constexpr (BITS != kFmtFp8) bias_chunk((G - 1) / kPgemmChunk);
 
   // ---- epilogue: element r of tile (rt, s) is row rbase + 32 rt + 8 (r / 4)
   // + 4 hl + r % 4, column jj of the lane's weight slot

@@ -83,7 +83,7 @@ __device__ __forceinline__ void qmv_issue_weights(QmvWeights<NMAT, SPW, BITS>& w
       for (int m = 0; m < NMAT; ++m) {
         w.cw[j][m][pp].a = buf_load16(cres[m], cv, (uint32_t)p * kPcb);
         if constexpr (BITS == 6) w.cw[j][m][pp].b = buf_load8(cres[m], cv8, (uint32_t)p * kPcb + 1024u);
-        if constexpr (BITS == 8) w.cw[j][m][pp].b = buf_load16(cres[m], cv, (uint32_t)p * kPcb + 1024u);
+        if constexpr (code_bits(BITS) == 8) w.cw[j][m][pp].b = buf_load16(cres[m], cv, (uint32_t)p * kPcb + 1024u);
         w.sbw[j][m][pp] = buf_load8(sres[m], sv, (uint32_t)p * kPairSbBytes);
       }
     }
@@ -96,7 +96,8 @@ __device__ __forceinline__ void qmv_issue_weights(QmvWeights<NMAT, SPW, BITS>& w
 //   P = mfma(x[g, 32..63], q, mfma(x[g, 0..31], q, 0))
 //   S = the same with q replaced by ones
 //   acc = fma(s_g, P, fma(b_g, S, acc))
-// with float32 rows combining their three pieces in-lane first.
+// with float32 rows combining their three pieces in-lane first. Block FP8
+// has no bias: acc = fma(s_g, P, acc) with s_g the float32 block scale.
 template <int XF32, int NMAT, int kRT, int kPerLane, int BITS, typename XF>
 __device__ __forceinline__ void qmv_fold_segment(float (&acc)[NMAT][kRT][kPerLane], const CodeWords<BITS> (&cw)[NMAT][kSegPairs],
                                                  const u32x2 (&sbw)[NMAT][kSegPairs], int g0, int G, const XF& xfrag) {
@@ -119,19 +120,35 @@ __device__ __forceinline__ void qmv_fold_segment(float (&acc)[NMAT][kRT][kPerLan
       q[m][0] = gh ? code_frag<BITS, 1, 0>(cw[m][pp]) : code_frag<BITS, 0, 0>(cw[m][pp]);
       q[m][1] = gh ? code_frag<BITS, 1, 1>(cw[m][pp]) : code_frag<BITS, 0, 1>(cw[m][pp]);
       const uint32_t w = gh ? sbw[m][pp][1] : sbw[m][pp][0];
-      sc[m] = bf16_lo(w);
-      bs[m] = bf16_hi(w);
+      if constexpr (BITS == kFmtFp8) {
+        sc[m] = __uint_as_float(w);
+        bs[m] = 0.f;
+      } else {
+        sc[m] = bf16_lo(w);
+        bs[m] = bf16_hi(w);
+      }
     }
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
       const bf16x8 xa0 = xfrag(rt, g, 0), xa1 = xfrag(rt, g, 1);
-      f32x4 S = mfma16(xa0, ones, f32x4{0.f, 0.f, 0.f, 0.f});
-      S = mfma16(xa1, ones, S);
+      f32x4 S = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BITS != kFmtFp8) {
+        S = mfma16(xa0, ones, S);
+        S = mfma16(xa1, ones, S);
+      }
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
         f32x4 Pm = mfma16(xa0, q[m][0], f32x4{0.f, 0.f, 0.f, 0.f});
         Pm = mfma16(xa1, q[m][1], Pm);
-        if constexpr (!XF32) {
+        if constexpr (BITS == kFmtFp8) {
+          if constexpr (!XF32) {
+#pragma unroll
+            for (int v = 0; v < kPerLane; ++v) acc[m][rt][v] = __builtin_fmaf(sc[m], Pm[v], acc[m][rt][v]);
+          } else {
+            const float Pr = (Pm[0] + Pm[1]) + Pm[2];
+            acc[m][rt][0] = __builtin_fmaf(sc[m], Pr, acc[m][rt][0]);
+          }
+        } else if constexpr (!XF32) {
 #pragma unroll
           for (int v = 0; v < kPerLane; ++v) acc[m][rt][v] = __builtin_fmaf(sc[m], Pm[v], __builtin_fmaf(bs[m], S[v], acc[m][rt][v]));
         } else {
@@ -461,13 +478,15 @@ inline void qmv_launch_bits(const uint8_t* pk0, const uint8_t* pk1, int nmat, in
   }
 }
 
-// bits: 4, 6 or 8 (checked by the caller).
+// bits: 4, 6, 8 or kFmtFp8 (checked by the caller).
 inline void qmv_launch(const uint8_t* pk0, const uint8_t* pk1, int nmat, int N, int K, const void* x, int xf32, int64_t ldx,
                        int R, float* y, int64_t ldy, hipStream_t s, int bits = 4) {
   if (bits == 6)
     qmv_launch_bits<6>(pk0, pk1, nmat, N, K, x, xf32, ldx, R, y, ldy, s);
   else if (bits == 8)
     qmv_launch_bits<8>(pk0, pk1, nmat, N, K, x, xf32, ldx, R, y, ldy, s);
+  else if (bits == kFmtFp8)
+    qmv_launch_bits<kFmtFp8>(pk0, pk1, nmat, N, K, x, xf32, ldx, R, y, ldy, s);
   else
     qmv_launch_bits<4>(pk0, pk1, nmat, N, K, x, xf32, ldx, R, y, ldy, s);
 }

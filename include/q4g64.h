@@ -199,12 +199,38 @@ int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2,
 /* Message of the last failed call on this thread ("" if none). */
 const char* q4_last_error(void);
 
+/* Block FP8, weight-only (PR #1696, first revision, "What it adds": the
+ * CUDA engine serves the LFM3 block FP8 export weight-only; the pages give
+ * no format, so this reading is the common block-FP8 checkpoint layout):
+ *     w8      uint8 [N][K]   OCP FP8 E4M3 bytes (bias 7, 3 mantissa bits,
+ *                            exponent field 0 subnormal, 0x7F/0xFF NaN)
+ *     scales  float32 [ceil(N/128)][ceil(K/128)], one per 128 x 128 block
+ *     w[n][k] = e4m3(w8[n][k]) * scales[n/128][k/128]
+ * Packed layout: the 8-bit code layout above holding the E4M3 bytes, then
+ * the scale/bias blocks with both 32-bit words of pair p of column n set to
+ * the float32 scale of block (n/128, p) (fp8b_packed_bytes = the 8-bit size).
+ * The calls mirror their q4g64 counterparts (same arguments, limits and
+ * row/cut bit rules). Every finite E4M3 value is a bf16 value, so the codes
+ * enter the matrix cores exactly; there is no bias, so each group folds as
+ * acc = fma(s_g, P_g, acc) in the decode order and the window order. */
+size_t fp8b_packed_bytes(int64_t N, int64_t K);
+int pack_fp8b(const uint8_t* w8, const float* scales, int64_t N, int64_t K, void* packed, void* stream);
+int unpack_fp8b(const void* packed, int64_t N, int64_t K, uint8_t* w8, float* scales, void* stream);
+int qmv_rows_fp8b(const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R, float* y,
+                  int64_t ldy, void* stream);
+int qmv_w13_swiglu_fp8b(const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                        int R, float* y, int64_t ldy, void* stream);
+int qmm_window_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                    int64_t M, void* y, int y_dtype, int64_t ldy, void* stream);
+int qmm_cut_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                 const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, void* stream);
+
 /* Window-cost table (PR #1514, "What changes": window costs are timed at
  * load for 1, 2, 4, 8 and 16 rows and interpolated between them, for the
  * planner that picks how many streams' rows share a decode step).
  *
  * qmv_window_costs times qmv_rows_qg64 on `packed` at R = 1, 2, 4, 8, 16
- * (x and y must hold 16 rows), each as the average of `reps` (1..10000)
+ * (bits = 4, 6 or 8; x and y must hold 16 rows), each as the average of `reps` (1..10000)
  * back-to-back launches between two HIP events on `stream`, and writes the
  * five averages in microseconds to the HOST array us_out[5]. It blocks until
  * the timing is done (a load-time call) and creates and destroys its two

@@ -90,3 +90,22 @@ def pack_model_bits(codes, scales, biases, N, K, bits):
     dev = np.concatenate(blocks).astype(np.uint32)
     sb_part = pack_model(np.zeros((N, K // 8), dtype=np.uint32), scales, biases, N, K)[(N // 16) * P * 1024 :]
     return np.concatenate([dev.view(np.uint8), sb_part])
+
+
+def pack_model_fp8(w8, scales, N, K):
+    """Packed layout of block-FP8 weights, from the header: the E4M3 bytes in
+    the 8-bit code layout, then for column n of pair p both words set to the
+    float32 scale of block (n // 128, p) (the second zero past G)."""
+    T, G = N // 16, K // 64
+    P = (G + 1) // 2
+    codes = pack_model_bits(np.asarray(w8, dtype=np.uint8), np.zeros((N, G), np.uint16), np.zeros((N, G), np.uint16), N, K, 8)
+    codes = codes[: T * P * 2048]
+    s = np.asarray(scales, dtype=np.float32).view(np.uint32)
+    sb = np.zeros((T, P, 16, 2), dtype=np.uint32)
+    for t in range(T):
+        for p in range(P):
+            for c in range(16):
+                v = s[(16 * t + c) // 128, p]
+                sb[t, p, c, 0] = v
+                sb[t, p, c, 1] = v if 2 * p + 1 < G else 0
+    return np.concatenate([codes, sb.reshape(-1).view(np.uint8)])

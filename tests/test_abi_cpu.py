@@ -223,3 +223,20 @@ def test_window_costs_rejects_bad_arguments():
     assert rc == q4.Q4_EINVAL
     rc, _ = _rc("qmv_window_costs", 4, FAKE, 512, 256, FAKE, q4.Q4_BF16, 256, FAKE, 100, 10, ctypes.addressof(out), None)
     assert rc == q4.Q4_EINVAL  # ldy < N
+
+
+def test_fp8_packed_bytes_and_rejections():
+    assert q4.fp8b_packed_bytes(512, 256) == q4.packed_bytes(512, 256, bits=8)
+    assert q4.fp8b_packed_bytes(100, 256) == 0
+    rc, _ = _rc("pack_fp8b", FAKE, FAKE, 100, 256, FAKE, None)
+    assert rc == q4.Q4_EINVAL
+    rc, _ = _rc("pack_fp8b", FAKE + 8, FAKE, 512, 256, FAKE, None)
+    assert rc == q4.Q4_EALIGN
+    rc, _ = _rc("pack_fp8b", FAKE, FAKE + 2, 512, 256, FAKE, None)
+    assert rc == q4.Q4_EALIGN
+    rc, _ = _rc("qmv_rows_fp8b", FAKE, 512, 256, FAKE, q4.Q4_BF16, 256, 17, FAKE, 512, None)
+    assert rc == q4.Q4_EINVAL
+    rc, _ = _rc("qmm_window_fp8b", FAKE, None, 512, 256, FAKE, 256, 0, FAKE, q4.Q4_F32, 512, None)
+    assert rc == q4.Q4_EINVAL
+    rc, _ = _rc("qmv_window_costs", 9, FAKE, 512, 256, FAKE, q4.Q4_BF16, 256, FAKE, 512, 10, FAKE, None)
+    assert rc == q4.Q4_EINVAL  # the public width argument takes 4, 6 or 8 only
