@@ -489,3 +489,67 @@ def test_fp8_planted_mistakes_fail(kind):
     y = oracle.activations_f64(x) @ W.T
     T = tol(oracle.error_weight_fp8(w.w8, w.scales, x), 256)
     assert np.any(np.abs(y - exact) > T)
+
+
+# --------------------------------------- QK norm, partial RoPE, KV store
+# PR #1696 lists QK norm with partial RoPE and a KV ring, and fuses RoPE
+# with the KV store on decode; the formulas are readings (half-split pairs,
+# angle pos * theta^(-2i/rot)), pinned by the properties that define a
+# rotary embedding.
+
+
+def test_rope_position_zero_and_rot_zero_are_identity():
+    rng = np.random.default_rng(800)
+    x = rng.normal(0, 1, (3, 4, 64))
+    assert np.array_equal(oracle.rope(x, [0, 0, 0], 64, 10000.0), x)
+    assert np.array_equal(oracle.rope(x, [5, 9, 100], 0, 10000.0), x)
+
+
+def test_rope_hand_worked_pair():
+    # rot = 2: one pair (0, 1) at angle pos * theta^0 = pos radians
+    x = np.zeros((1, 1, 64))
+    x[0, 0, 0], x[0, 0, 1], x[0, 0, 5] = 3.0, 4.0, 7.0
+    y = oracle.rope(x, [1], 2, 10000.0)[0, 0]
+    assert np.allclose(y[0], 3 * math.cos(1) - 4 * math.sin(1), rtol=0, atol=1e-15)
+    assert np.allclose(y[1], 4 * math.cos(1) + 3 * math.sin(1), rtol=0, atol=1e-15)
+    assert y[5] == 7.0 and np.count_nonzero(y) == 3
+    # rot = 4, theta = 16: pairs (0, 2) at pos and (1, 3) at pos / 4
+    x = np.zeros((1, 1, 64))
+    x[0, 0, 1] = 1.0
+    y = oracle.rope(x, [2], 4, 16.0)[0, 0]
+    assert np.allclose(y[[1, 3]], [math.cos(0.5), math.sin(0.5)], rtol=0, atol=1e-15)
+
+
+def test_rope_keeps_pair_norms_and_relative_positions():
+    """A rotation keeps every pair's length, and <rope(q, p1), rope(k, p2)>
+    depends on p1 - p2 only (the property attention relies on)."""
+    rng = np.random.default_rng(801)
+    q, k = rng.normal(0, 1, (1, 1, 64)), rng.normal(0, 1, (1, 1, 64))
+    rot, h = 48, 24
+    qr = oracle.rope(q, [37], rot, 10000.0)
+    n0 = q[0, 0, :h] ** 2 + q[0, 0, h:rot] ** 2
+    n1 = qr[0, 0, :h] ** 2 + qr[0, 0, h:rot] ** 2
+    assert np.allclose(n0, n1, rtol=1e-14, atol=0)
+    assert np.array_equal(qr[0, 0, rot:], q[0, 0, rot:])
+    dots = [float(np.sum(oracle.rope(q, [p + 11], rot, 10000.0) * oracle.rope(k, [p], rot, 10000.0))) for p in (0, 5, 1000, 65536)]
+    assert np.allclose(dots, dots[0], rtol=1e-12, atol=1e-12)
+
+
+def test_rms_norm_closed_forms():
+    x = np.full((1, 64), 3.0)
+    assert np.allclose(oracle.rms_norm(x, np.ones(64), 0.0), 1.0, rtol=1e-15)
+    g = np.arange(64, dtype=np.float64)
+    assert np.allclose(oracle.rms_norm(-x, g, 0.0), -g, rtol=1e-15)
+    rng = np.random.default_rng(802)
+    y = oracle.rms_norm(rng.normal(0, 5, (7, 64)), np.ones(64), 1e-6)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-6)
+
+
+def test_rope_kv_splits_heads_in_order():
+    rng = np.random.default_rng(803)
+    n_q, n_kv = 4, 2
+    qkv = rng.normal(0, 1, (2, (n_q + 2 * n_kv) * 64))
+    q, k, v = oracle.rope_kv(qkv, [0, 0], n_q, n_kv, 64, 10000.0)
+    assert np.array_equal(q, qkv[:, :256])
+    assert np.array_equal(k.reshape(2, -1), qkv[:, 256:384])
+    assert np.array_equal(v.reshape(2, -1), qkv[:, 384:512])
