@@ -332,6 +332,8 @@ def main():
     if not args.no_pgemm:
         result["pgemm"] = bench_pgemm(dev)
     if not args.no_wide:
+        result["qkv_rope"] = bench_qkv_rope(dev, K, W, args.pool_mb)
+    if not args.no_wide:
         result["wide_codes"] = {str(b): bench_wide(dev, b, K, W, args.pool_mb, graph=g_used) for b in (6, 8, "fp8")}
 
     if not args.no_cpu_baseline:
@@ -443,6 +445,47 @@ def bench_wide(dev, bits, K, W, pool_mb, graph=True, reps=5):
                              "frac": round(b2 / (t2 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "pgemm_swiglu_8192": {"avg_ms": round(tw * 1e3, 4), "TFLOP/s": round(tf, 2), "frac": round(tf / BF16_PEAK_TFLOPS, 4)},
     }
+
+
+def bench_qkv_rope(dev, K, W, pool_mb):
+    """The stacked q/k/v decode matvec (3072 x 2048, 4-bit) with partial RoPE
+    and the KV store: fused in one launch against qmv_rows + rope_kv_store,
+    at 1 and 16 rows, cold weights, graph-batch averages."""
+    import torch
+
+    import bit_weight_only_q4g64_amd as q4
+    import synthetic
+
+    log("q/k/v matvec with RoPE and the KV store")
+    d = synthetic.config(2)
+    w = synthetic.concat_rows(d["wq"], d["wk"], d["wv"], name="qkv")
+    base = pack_dev(w, dev)
+    ncopies = max(2, -(-pool_mb * (1 << 20) // base.numel()))
+    pool = [base] + [base.clone() for _ in range(ncopies - 1)]
+    x = to_dev(d["x"], np.int16, dev).view(torch.bfloat16)
+    ring = 4096
+    pos = torch.arange(100, 116, dtype=torch.int32, device=dev)
+    q = torch.empty((16, 2048), device=dev)
+    kc = torch.empty((ring, 8, 64), device=dev, dtype=torch.bfloat16)
+    vc = torch.empty((ring, 8, 64), device=dev, dtype=torch.bfloat16)
+    y = torch.empty((16, w.N), device=dev)
+    out = {}
+    for R in (1, 16):
+        fused = batch_average_us(torch, lambda i: q4.qmv_qkv_rope(pool[i % ncopies], w.K, x[:R], pos[:R], 32, 8, 64, 1e6, q[:R], kc, vc), W, K)
+
+        def unfused(i):
+            q4.qmv_rows(pool[i % ncopies], w.N, w.K, x[:R], y=y[:R])
+            q4.rope_kv_store(y[:R], pos[:R], 32, 8, 64, 1e6, q[:R], kc, vc)
+
+        two = batch_average_us(torch, unfused, W, K)
+        mv = batch_average_us(torch, lambda i: q4.qmv_rows(pool[i % ncopies], w.N, w.K, x[:R], y=y[:R]), W, K)
+        b = qbytes(w.N, w.K) + R * w.K * 2
+        out[f"R{R}"] = {"fused_us": round(fused, 3), "qmv_rows_plus_epilogue_us": round(two, 3), "qmv_rows_alone_us": round(mv, 3),
+                        "fused_GB/s": round(b / (fused * 1e-6) / 1e9, 1)}
+    del pool, base
+    torch.cuda.empty_cache()
+    out["workload"] = "stacked q/k/v 3072x2048 q4g64 (32 q + 8 kv heads x 64), rot 64, theta 1e6, bf16 KV ring of 4096"
+    return out
 
 
 def bench_pgemm(dev, reps=10):

@@ -49,6 +49,8 @@ _SIGNATURES = {
     "qmv_w13_swiglu_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
     "qmm_window_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P]),
     "qmm_cut_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _I64, _P]),
+    "rope_kv_store": (ctypes.c_int, [_P, _I64, ctypes.c_int, _P, _P]),
+    "qmv_qkv_rope": (ctypes.c_int, [ctypes.c_int, _P, _I64, _P, _I64, ctypes.c_int, _P, _P]),
     "qmv_window_costs": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P, _I64, ctypes.c_int, _P, _P]),
     "qmv_window_cost": (ctypes.c_float, [_P, ctypes.c_int]),
     "q4g64_ffn_work_bytes": (ctypes.c_size_t, [_I64, ctypes.c_int]),
@@ -418,3 +420,59 @@ def qmm_cut_fp8b(pa: torch.Tensor, pb: torch.Tensor | None, N: int, K: int, x: t
                                               _rowmajor(x, "x"), arr, len(windows), y.data_ptr(), _out_dtype(y.dtype), _rowmajor(y, "y"),
                                               _stream()))
     return y
+
+
+# ---- attention-side decode epilogue: QK norm, partial RoPE, KV store -------
+
+
+class RopeKv(ctypes.Structure):
+    """Mirror of the C struct q4_rope_kv (device pointers as integers)."""
+
+    _fields_ = [("pos", ctypes.c_void_p), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("rot_dims", ctypes.c_int32), ("theta", ctypes.c_float), ("gamma_q", ctypes.c_void_p),
+                ("gamma_k", ctypes.c_void_p), ("eps", ctypes.c_float), ("q_out", ctypes.c_void_p), ("ldq", ctypes.c_int64),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("cache_dtype", ctypes.c_int32),
+                ("ring_len", ctypes.c_int64)]
+
+
+def _rope_args(pos, n_q, n_kv, rot, theta, q_out, k_cache, v_cache, gamma_q, gamma_k, eps):
+    for t, name in ((pos, "pos"), (q_out, "q_out"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, name)
+    if pos.dtype != torch.int32 or q_out.dtype != torch.float32:
+        raise ValueError("pos is int32 and q_out float32")
+    if k_cache.dtype != v_cache.dtype or k_cache.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("the caches are both float32 or both bfloat16")
+    if tuple(k_cache.shape[1:]) != (n_kv, 64) or tuple(v_cache.shape) != tuple(k_cache.shape) or not k_cache.is_contiguous() \
+            or not v_cache.is_contiguous():
+        raise ValueError("the caches are contiguous [ring][n_kv_heads][64]")
+    for g, name in ((gamma_q, "gamma_q"), (gamma_k, "gamma_k")):
+        if g is not None:
+            _dev(g, name)
+            if g.dtype != torch.float32 or g.numel() != 64:
+                raise ValueError(f"{name} is a float32 [64] vector")
+    return RopeKv(pos.data_ptr(), n_q, n_kv, rot, theta, None if gamma_q is None else gamma_q.data_ptr(),
+                  None if gamma_k is None else gamma_k.data_ptr(), eps, q_out.data_ptr(), _rowmajor(q_out, "q_out"),
+                  k_cache.data_ptr(), v_cache.data_ptr(), Q4_F32 if k_cache.dtype == torch.float32 else Q4_BF16, k_cache.shape[0])
+
+
+def rope_kv_store(qkv: torch.Tensor, pos: torch.Tensor, n_q: int, n_kv: int, rot: int, theta: float, q_out: torch.Tensor,
+                  k_cache: torch.Tensor, v_cache: torch.Tensor, gamma_q=None, gamma_k=None, eps: float = 1e-6) -> None:
+    """QK norm (when gammas are given), partial RoPE and the KV store on a float32 q/k/v output [R][(n_q+2n_kv)*64]."""
+    _dev(qkv, "qkv")
+    if qkv.dtype != torch.float32:
+        raise ValueError("qkv must be float32")
+    a = _rope_args(pos, n_q, n_kv, rot, theta, q_out, k_cache, v_cache, gamma_q, gamma_k, eps)
+    _check("rope_kv_store", lib().rope_kv_store(qkv.data_ptr(), _rowmajor(qkv, "qkv"), qkv.shape[0], ctypes.addressof(a), _stream()))
+
+
+def qmv_qkv_rope(packed: torch.Tensor, K: int, x: torch.Tensor, pos: torch.Tensor, n_q: int, n_kv: int, rot: int, theta: float,
+                 q_out: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, gamma_q=None, gamma_k=None, eps: float = 1e-6,
+                 bits: int = 4) -> None:
+    """The stacked q/k/v decode matvec with QK norm, partial RoPE and the KV store in one launch (1..16 bf16 rows)."""
+    _dev(packed, "packed_qkv")
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    a = _rope_args(pos, n_q, n_kv, rot, theta, q_out, k_cache, v_cache, gamma_q, gamma_k, eps)
+    _check("qmv_qkv_rope", lib().qmv_qkv_rope(bits, packed.data_ptr(), K, x.data_ptr(), _rowmajor(x, "x"), x.shape[0],
+                                              ctypes.addressof(a), _stream()))

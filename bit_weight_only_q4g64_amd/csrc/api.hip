@@ -12,6 +12,7 @@
 #include "pack.h"
 #include "pgemm.h"
 #include "qmv.h"
+#include "rope.h"
 
 namespace {
 
@@ -306,6 +307,72 @@ int qmm_cut_impl(const char* fn, int bits, const void* packed_a, const void* pac
   return Q4_OK;
 }
 
+int check_rope_args(const char* fn, const q4_rope_kv* a, int R, q4::RopeKvArgs* out) {
+  if (a == nullptr) return fail(Q4_EINVAL, "%s: args is NULL", fn);
+  if (a->n_q_heads < 1 || a->n_kv_heads < 1 || a->n_q_heads > 4096 || a->n_kv_heads > 4096)
+    return fail(Q4_EINVAL, "%s: n_q_heads=%d and n_kv_heads=%d must be 1..4096", fn, a->n_q_heads, a->n_kv_heads);
+  if (a->rot_dims < 0 || a->rot_dims > 64 || (a->rot_dims & 1))
+    return fail(Q4_EINVAL, "%s: rot_dims=%d is not an even number in 0..64", fn, a->rot_dims);
+  if (!(a->theta > 0.f) || !isfinite(a->theta)) return fail(Q4_EINVAL, "%s: theta must be positive and finite", fn);
+  if (!(a->eps >= 0.f) || !isfinite(a->eps)) return fail(Q4_EINVAL, "%s: eps must be >= 0 and finite", fn);
+  if (a->cache_dtype != Q4_F32 && a->cache_dtype != Q4_BF16) return fail(Q4_EINVAL, "%s: cache_dtype %d is not Q4_F32 or Q4_BF16", fn, a->cache_dtype);
+  if (a->ring_len < 1) return fail(Q4_EINVAL, "%s: ring_len=%lld < 1", fn, (long long)a->ring_len);
+  if (a->ldq < (int64_t)a->n_q_heads * 64) return fail(Q4_EINVAL, "%s: ldq=%lld < n_q_heads * 64", fn, (long long)a->ldq);
+  if (int rc = check_ptr(fn, "pos", a->pos, 4)) return rc;
+  if (int rc = check_ptr(fn, "q_out", a->q_out, 4)) return rc;
+  const uintptr_t ce = a->cache_dtype == Q4_F32 ? 4 : 2;
+  if (int rc = check_ptr(fn, "k_cache", a->k_cache, ce)) return rc;
+  if (int rc = check_ptr(fn, "v_cache", a->v_cache, ce)) return rc;
+  if (a->gamma_q != nullptr && !aligned(a->gamma_q, 4)) return fail(Q4_EALIGN, "%s: gamma_q is not 4-byte aligned", fn);
+  if (a->gamma_k != nullptr && !aligned(a->gamma_k, 4)) return fail(Q4_EALIGN, "%s: gamma_k is not 4-byte aligned", fn);
+  (void)R;
+  q4::RopeKvArgs r{};
+  for (int i = 0; i < a->rot_dims / 2; ++i) r.inv[i] = pow((double)a->theta, -2.0 * (double)i / (double)a->rot_dims);
+  r.pos = a->pos;
+  r.n_q = a->n_q_heads;
+  r.n_kv = a->n_kv_heads;
+  r.rot = a->rot_dims;
+  r.theta = a->theta;
+  r.eps = a->eps;
+  r.gamma_q = a->gamma_q;
+  r.gamma_k = a->gamma_k;
+  r.q_out = a->q_out;
+  r.ldq = a->ldq;
+  r.k_cache = a->k_cache;
+  r.v_cache = a->v_cache;
+  r.cache_bf16 = a->cache_dtype == Q4_BF16;
+  r.ring = a->ring_len;
+  *out = r;
+  return Q4_OK;
+}
+
+template <int SPW, int NV, int BITS>
+int qkv_rope_launch_t(const uint8_t* pk, int N, int K, const uint16_t* x, int64_t ldx, int R, const q4::RopeKvArgs& a, size_t lds,
+                      int heads, hipStream_t s) {
+  auto kern = q4::qkv_rope_kernel<SPW, NV, BITS>;
+  static const bool lds_ok =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)q4::qmv_max_lds()) == hipSuccess;
+  (void)lds_ok;
+  hipLaunchKernelGGL(kern, dim3((unsigned)heads), dim3(q4::kQkvWaves * 64), lds, s, pk, N, K, x, ldx, R, a);
+  return launched("qmv_qkv_rope");
+}
+
+template <int SPW, int BITS>
+int qkv_rope_launch_nv(int nv, const uint8_t* pk, int N, int K, const uint16_t* x, int64_t ldx, int R, const q4::RopeKvArgs& a,
+                       size_t lds, int heads, hipStream_t s) {
+  if (nv == 1) return qkv_rope_launch_t<SPW, 1, BITS>(pk, N, K, x, ldx, R, a, lds, heads, s);
+  if (nv == 2) return qkv_rope_launch_t<SPW, 2, BITS>(pk, N, K, x, ldx, R, a, lds, heads, s);
+  return qkv_rope_launch_t<SPW, 4, BITS>(pk, N, K, x, ldx, R, a, lds, heads, s);
+}
+
+template <int BITS>
+int qkv_rope_launch_bits(int spw, int nv, const uint8_t* pk, int N, int K, const uint16_t* x, int64_t ldx, int R,
+                         const q4::RopeKvArgs& a, size_t lds, int heads, hipStream_t s) {
+  if (spw <= 1) return qkv_rope_launch_nv<1, BITS>(nv, pk, N, K, x, ldx, R, a, lds, heads, s);
+  if (spw <= 2) return qkv_rope_launch_nv<2, BITS>(nv, pk, N, K, x, ldx, R, a, lds, heads, s);
+  return qkv_rope_launch_nv<4, BITS>(nv, pk, N, K, x, ldx, R, a, lds, heads, s);
+}
+
 extern "C" {
 
 int q4g64_abi_version(void) { return 1; }
@@ -480,6 +547,44 @@ int qmm_cut_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64_t 
                  const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, void* stream) {
   return qmm_cut_impl("qmm_cut_fp8b", q4::kFmtFp8, packed_a, packed_b, N, K, x, ldx, window_rows, n_windows, y, y_dtype, ldy,
                       (hipStream_t)stream);
+}
+
+int rope_kv_store(const float* qkv, int64_t ldqkv, int R, const q4_rope_kv* args, void* stream) {
+  const char* fn = "rope_kv_store";
+  q4::RopeKvArgs a;
+  if (int rc = check_rope_args(fn, args, R, &a)) return rc;
+  if (R < 1 || R > 65535) return fail(Q4_EINVAL, "%s: R=%d is outside 1..65535", fn, R);
+  if (int rc = check_ptr(fn, "qkv", qkv, 4)) return rc;
+  const int heads = a.n_q + 2 * a.n_kv;
+  if (ldqkv < (int64_t)heads * 64) return fail(Q4_EINVAL, "%s: ldqkv=%lld < (n_q_heads + 2 n_kv_heads) * 64", fn, (long long)ldqkv);
+  hipLaunchKernelGGL(q4::rope_kv_kernel, dim3((unsigned)heads, (unsigned)R), dim3(64), 0, (hipStream_t)stream, qkv, ldqkv, a);
+  return launched(fn);
+}
+
+int qmv_qkv_rope(int bits, const void* packed_qkv, int64_t K, const uint16_t* x, int64_t ldx, int R, const q4_rope_kv* args,
+                 void* stream) {
+  const char* fn = "qmv_qkv_rope";
+  if (int rc = check_bits(fn, bits)) return rc;
+  q4::RopeKvArgs a;
+  if (int rc = check_rope_args(fn, args, R, &a)) return rc;
+  const int heads = a.n_q + 2 * a.n_kv;
+  const int64_t N = (int64_t)heads * 64;
+  if (int rc = check_nk(fn, N, K)) return rc;
+  if (R < 1 || R > 16) return fail(Q4_EINVAL, "%s: R=%d is outside 1..16", fn, R);
+  if (int rc = check_ptr(fn, "packed_qkv", packed_qkv, 16)) return rc;
+  if (int rc = check_x(fn, x, Q4_BF16, ldx, K)) return rc;
+  if ((int64_t)R * ldx * 2 >= (int64_t(1) << 31)) return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
+  // four waves per 16-column tile, up to 4 segments each
+  if (K > 4096) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the fused limit of 4096", fn, (long long)K);
+  const int nv = q4::qmv_nv(R);
+  const size_t lds = q4::qkv_rope_lds_bytes(K, nv, R);
+  if (lds > q4::qmv_max_lds()) return fail(Q4_EUNSUPPORTED, "%s: K=%lld with R=%d needs %zu bytes of LDS", fn, (long long)K, R, lds);
+  const int nseg = q4::qmv_segments(K), spw = (nseg + 3) / 4;
+  const uint8_t* pk = (const uint8_t*)packed_qkv;
+  hipStream_t s = (hipStream_t)stream;
+  if (bits == 6) return qkv_rope_launch_bits<6>(spw, nv, pk, (int)N, (int)K, x, ldx, R, a, lds, heads, s);
+  if (bits == 8) return qkv_rope_launch_bits<8>(spw, nv, pk, (int)N, (int)K, x, ldx, R, a, lds, heads, s);
+  return qkv_rope_launch_bits<4>(spw, nv, pk, (int)N, (int)K, x, ldx, R, a, lds, heads, s);
 }
 
 static const int kCostRows[5] = {1, 2, 4, 8, 16};

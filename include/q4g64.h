@@ -225,6 +225,50 @@ int qmm_window_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64
 int qmm_cut_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                  const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, void* stream);
 
+/* Attention-side decode epilogue (PR #1696, "What it adds": the LFM3 kernels
+ * include QK norm with partial RoPE and GQA attention over a KV ring; decode
+ * fuses RoPE with the KV store). The pages give no formulas; readings:
+ *   - a row of the stacked q/k/v matvec output is [q heads | k heads | v
+ *     heads], 64 values per head, N = (n_q_heads + 2 n_kv_heads) * 64;
+ *   - QK norm (when gamma_q / gamma_k is not NULL): per q (k) head,
+ *     x <- (x * r) * gamma[d], r = 1 / sqrt(sum(x^2) / 64 + eps);
+ *   - partial RoPE on q and k: the first rot_dims dims of a head rotate in
+ *     half-split pairs (i, i + rot_dims/2) by pos * theta^(-2i/rot_dims)
+ *     (cos and sin of the angle formed in double, rounded once to float);
+ *   - q goes to q_out; k and v go to slot pos mod ring_len of k_cache and
+ *     v_cache, each [ring_len][n_kv_heads][64] of cache_dtype (Q4_F32, or
+ *     Q4_BF16 rounded to nearest even). Other slots are not touched.
+ * All pointers in the struct are DEVICE pointers except the struct itself,
+ * which is read on the host when the call is made. */
+typedef struct q4_rope_kv {
+  const int32_t* pos;     /* [R] position of each row (slot = pos mod ring_len) */
+  int32_t n_q_heads;      /* >= 1 */
+  int32_t n_kv_heads;     /* >= 1 */
+  int32_t rot_dims;       /* even, 0..64 */
+  float theta;            /* rotary base, > 0 */
+  const float* gamma_q;   /* [64] or NULL: no norm on q */
+  const float* gamma_k;   /* [64] or NULL: no norm on k */
+  float eps;              /* >= 0 */
+  float* q_out;           /* float32 [R][ldq], ldq >= n_q_heads * 64 */
+  int64_t ldq;
+  void* k_cache;          /* [ring_len][n_kv_heads][64] */
+  void* v_cache;
+  int32_t cache_dtype;    /* Q4_F32 or Q4_BF16 */
+  int64_t ring_len;       /* >= 1 */
+} q4_rope_kv;
+
+/* The epilogue alone, on a float32 q/k/v output qkv [R][ldqkv] (for example
+ * qmv_rows over the stacked [Wq; Wk; Wv]); R >= 1. */
+int rope_kv_store(const float* qkv, int64_t ldqkv, int R, const q4_rope_kv* args, void* stream);
+
+/* The stacked q/k/v matvec (bits = 4, 6 or 8, bf16 x [R][ldx], R = 1..16,
+ * K <= 4096, N = (n_q_heads + 2 n_kv_heads) * 64) with the epilogue in the
+ * same launch, one workgroup per head. q_out and the cache contents are
+ * bit-identical to qmv_rows_qg64 followed by rope_kv_store, and a row's
+ * results do not depend on R or on the other rows. */
+int qmv_qkv_rope(int bits, const void* packed_qkv, int64_t K, const uint16_t* x, int64_t ldx, int R, const q4_rope_kv* args,
+                 void* stream);
+
 /* Window-cost table (PR #1514, "What changes": window costs are timed at
  * load for 1, 2, 4, 8 and 16 rows and interpolated between them, for the
  * planner that picks how many streams' rows share a decode step).

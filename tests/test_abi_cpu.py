@@ -240,3 +240,35 @@ def test_fp8_packed_bytes_and_rejections():
     assert rc == q4.Q4_EINVAL
     rc, _ = _rc("qmv_window_costs", 9, FAKE, 512, 256, FAKE, q4.Q4_BF16, 256, FAKE, 512, 10, FAKE, None)
     assert rc == q4.Q4_EINVAL  # the public width argument takes 4, 6 or 8 only
+
+
+def _rope(**kw):
+    base = dict(pos=FAKE, n_q_heads=32, n_kv_heads=8, rot_dims=64, theta=10000.0, gamma_q=None, gamma_k=None, eps=1e-6,
+                q_out=FAKE, ldq=2048, k_cache=FAKE, v_cache=FAKE, cache_dtype=q4.Q4_F32, ring_len=64)
+    base.update(kw)
+    return q4.RopeKv(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_q_heads=0), q4.Q4_EINVAL), (dict(n_kv_heads=0), q4.Q4_EINVAL), (dict(rot_dims=3), q4.Q4_EINVAL),
+    (dict(rot_dims=66), q4.Q4_EINVAL), (dict(theta=0.0), q4.Q4_EINVAL), (dict(theta=float("inf")), q4.Q4_EINVAL),
+    (dict(eps=-1.0), q4.Q4_EINVAL), (dict(cache_dtype=7), q4.Q4_EINVAL), (dict(ring_len=0), q4.Q4_EINVAL),
+    (dict(ldq=100), q4.Q4_EINVAL), (dict(pos=None), q4.Q4_EALIGN), (dict(q_out=FAKE + 2), q4.Q4_EALIGN),
+    (dict(k_cache=None), q4.Q4_EALIGN), (dict(gamma_q=FAKE + 1), q4.Q4_EALIGN)])
+def test_rope_args_rejected(kw, code):
+    a = _rope(**kw)
+    rc, _ = _rc("rope_kv_store", FAKE, 3072, 1, ctypes.addressof(a), None)
+    assert rc == code
+    rc, _ = _rc("qmv_qkv_rope", 4, FAKE, 2048, FAKE, 2048, 1, ctypes.addressof(a), None)
+    assert rc == code
+
+
+def test_rope_calls_reject_bad_shapes():
+    a = _rope()
+    assert _rc("rope_kv_store", FAKE, 3072, 1, None, None)[0] == q4.Q4_EINVAL
+    assert _rc("rope_kv_store", FAKE, 3000, 1, ctypes.addressof(a), None)[0] == q4.Q4_EINVAL  # ldqkv < N
+    assert _rc("rope_kv_store", FAKE, 3072, 0, ctypes.addressof(a), None)[0] == q4.Q4_EINVAL
+    assert _rc("qmv_qkv_rope", 5, FAKE, 2048, FAKE, 2048, 1, ctypes.addressof(a), None)[0] == q4.Q4_EINVAL
+    assert _rc("qmv_qkv_rope", 4, FAKE, 2048, FAKE, 2048, 17, ctypes.addressof(a), None)[0] == q4.Q4_EINVAL
+    rc, msg = _rc("qmv_qkv_rope", 4, FAKE, 8192, FAKE, 8192, 1, ctypes.addressof(a), None)
+    assert rc == q4.Q4_EUNSUPPORTED and "4096" in msg
