@@ -167,8 +167,11 @@ __device__ __forceinline__ int qmv_part_index(int seg, int m, int rt, int v, int
   return (((seg * NMAT + m) * kRT + rt) * kPerLane + v) * 64 + lane;
 }
 
-// The segments' partials added in ascending order (read eight segments at a
-// time so the reads are in flight together).
+// The segments' partials added in ascending order, eight reads in flight at a
+// time: every read of a batch is issued (indices clamped to the last
+// segment) before its adds, and the adds past the last segment are dropped
+// by a select rather than a branch, so the compiler cannot sink the reads
+// into the adds (which costs one LDS round trip per segment).
 template <int NMAT, int kRT, int kPerLane>
 __device__ __forceinline__ void qmv_ordered_sum(float (&tot)[NMAT][kRT][kPerLane], const float* part, int nseg, int lane) {
 #pragma unroll
@@ -192,13 +195,16 @@ __device__ __forceinline__ void qmv_ordered_sum(float (&tot)[NMAT][kRT][kPerLane
     }
 #pragma unroll
     for (int b = 0; b < kSumBatch; ++b) {
-      if (seg0 + b >= nseg) break;
+      const bool in = seg0 + b < nseg;
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
-          for (int v = 0; v < kPerLane; ++v) tot[m][rt][v] = tot[m][rt][v] + pv[b][m][rt][v];
+          for (int v = 0; v < kPerLane; ++v) {
+            const float t = tot[m][rt][v] + pv[b][m][rt][v];
+            tot[m][rt][v] = in ? t : tot[m][rt][v];
+          }
     }
   }
 }
