@@ -484,7 +484,30 @@ def bench_qkv_rope(dev, K, W, pool_mb):
                         "fused_GB/s": round(b / (fused * 1e-6) / 1e9, 1)}
     del pool, base
     torch.cuda.empty_cache()
-    out["workload"] = "stacked q/k/v 3072x2048 q4g64 (32 q + 8 kv heads x 64), rot 64, theta 1e6, bf16 KV ring of 4096"
+    # gated attention: a gate projection of the q projection's shape stacked after v (the fourth matvec)
+    wg = synthetic.draw_qweight(np.random.default_rng(951), "wg", 2048, 2048)
+    w4 = synthetic.concat_rows(d["wq"], d["wk"], d["wv"], wg, name="qkvg")
+    base = pack_dev(w4, dev)
+    ncopies = max(2, -(-pool_mb * (1 << 20) // base.numel()))
+    pool = [base] + [base.clone() for _ in range(ncopies - 1)]
+    g = torch.empty((16, 2048), device=dev)
+    y4 = torch.empty((16, w4.N), device=dev)
+    for R in (1, 16):
+        fused = batch_average_us(
+            torch, lambda i: q4.qmv_qkv_rope(pool[i % ncopies], w4.K, x[:R], pos[:R], 32, 8, 64, 1e6, q[:R], kc, vc, gate_out=g[:R]), W, K)
+
+        def unfused4(i):
+            q4.qmv_rows(pool[i % ncopies], w4.N, w4.K, x[:R], y=y4[:R])
+            q4.rope_kv_store(y4[:R], pos[:R], 32, 8, 64, 1e6, q[:R], kc, vc, gate_out=g[:R])
+
+        two = batch_average_us(torch, unfused4, W, K)
+        b = qbytes(w4.N, w4.K) + R * w4.K * 2
+        out[f"gated_R{R}"] = {"fused_us": round(fused, 3), "qmv_rows_plus_epilogue_us": round(two, 3),
+                              "fused_GB/s": round(b / (fused * 1e-6) / 1e9, 1)}
+    del pool, base
+    torch.cuda.empty_cache()
+    out["workload"] = ("stacked q/k/v 3072x2048 q4g64 (32 q + 8 kv heads x 64), rot 64, theta 1e6, bf16 KV ring of 4096; "
+                       "gated_*: q/k/v/gate 5120x2048 (32 gate heads after v)")
     return out
 
 

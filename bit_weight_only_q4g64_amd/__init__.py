@@ -432,12 +432,19 @@ class RopeKv(ctypes.Structure):
                 ("rot_dims", ctypes.c_int32), ("theta", ctypes.c_float), ("gamma_q", ctypes.c_void_p),
                 ("gamma_k", ctypes.c_void_p), ("eps", ctypes.c_float), ("q_out", ctypes.c_void_p), ("ldq", ctypes.c_int64),
                 ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("cache_dtype", ctypes.c_int32),
-                ("ring_len", ctypes.c_int64)]
+                ("ring_len", ctypes.c_int64), ("n_gate_heads", ctypes.c_int32), ("gate_out", ctypes.c_void_p),
+                ("ldg", ctypes.c_int64)]
 
 
-def _rope_args(pos, n_q, n_kv, rot, theta, q_out, k_cache, v_cache, gamma_q, gamma_k, eps):
+def _rope_args(pos, n_q, n_kv, rot, theta, q_out, k_cache, v_cache, gamma_q, gamma_k, eps, gate_out=None):
     for t, name in ((pos, "pos"), (q_out, "q_out"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, name)
+    n_gate, gate_ptr, ldg = 0, None, 0
+    if gate_out is not None:
+        _dev(gate_out, "gate_out")
+        if gate_out.dtype != torch.float32 or gate_out.dim() != 2 or gate_out.shape[1] % 64:
+            raise ValueError("gate_out is a float32 [R][n_gate_heads * 64] tensor")
+        n_gate, gate_ptr, ldg = gate_out.shape[1] // 64, gate_out.data_ptr(), _rowmajor(gate_out, "gate_out")
     if pos.dtype != torch.int32 or q_out.dtype != torch.float32:
         raise ValueError("pos is int32 and q_out float32")
     if k_cache.dtype != v_cache.dtype or k_cache.dtype not in (torch.float32, torch.bfloat16):
@@ -452,27 +459,31 @@ def _rope_args(pos, n_q, n_kv, rot, theta, q_out, k_cache, v_cache, gamma_q, gam
                 raise ValueError(f"{name} is a float32 [64] vector")
     return RopeKv(pos.data_ptr(), n_q, n_kv, rot, theta, None if gamma_q is None else gamma_q.data_ptr(),
                   None if gamma_k is None else gamma_k.data_ptr(), eps, q_out.data_ptr(), _rowmajor(q_out, "q_out"),
-                  k_cache.data_ptr(), v_cache.data_ptr(), Q4_F32 if k_cache.dtype == torch.float32 else Q4_BF16, k_cache.shape[0])
+                  k_cache.data_ptr(), v_cache.data_ptr(), Q4_F32 if k_cache.dtype == torch.float32 else Q4_BF16, k_cache.shape[0],
+                  n_gate, gate_ptr, ldg)
 
 
 def rope_kv_store(qkv: torch.Tensor, pos: torch.Tensor, n_q: int, n_kv: int, rot: int, theta: float, q_out: torch.Tensor,
-                  k_cache: torch.Tensor, v_cache: torch.Tensor, gamma_q=None, gamma_k=None, eps: float = 1e-6) -> None:
-    """QK norm (when gammas are given), partial RoPE and the KV store on a float32 q/k/v output [R][(n_q+2n_kv)*64]."""
+                  k_cache: torch.Tensor, v_cache: torch.Tensor, gamma_q=None, gamma_k=None, eps: float = 1e-6,
+                  gate_out=None) -> None:
+    """QK norm (when gammas are given), partial RoPE and the KV store on a float32 q/k/v output
+    [R][(n_q+2n_kv)*64]; with ``gate_out`` [R][n_gate*64], the gate heads that follow v are copied there."""
     _dev(qkv, "qkv")
     if qkv.dtype != torch.float32:
         raise ValueError("qkv must be float32")
-    a = _rope_args(pos, n_q, n_kv, rot, theta, q_out, k_cache, v_cache, gamma_q, gamma_k, eps)
+    a = _rope_args(pos, n_q, n_kv, rot, theta, q_out, k_cache, v_cache, gamma_q, gamma_k, eps, gate_out)
     _check("rope_kv_store", lib().rope_kv_store(qkv.data_ptr(), _rowmajor(qkv, "qkv"), qkv.shape[0], ctypes.addressof(a), _stream()))
 
 
 def qmv_qkv_rope(packed: torch.Tensor, K: int, x: torch.Tensor, pos: torch.Tensor, n_q: int, n_kv: int, rot: int, theta: float,
                  q_out: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, gamma_q=None, gamma_k=None, eps: float = 1e-6,
-                 bits: int = 4) -> None:
-    """The stacked q/k/v decode matvec with QK norm, partial RoPE and the KV store in one launch (1..16 bf16 rows)."""
+                 bits: int = 4, gate_out=None) -> None:
+    """The stacked q/k/v(/gate) decode matvec with QK norm, partial RoPE and the KV store in one launch
+    (1..16 bf16 rows); ``gate_out`` [R][n_gate*64] receives the gate heads stacked after v."""
     _dev(packed, "packed_qkv")
     _dev(x, "x")
     if x.dtype != torch.bfloat16:
         raise ValueError("x must be bfloat16")
-    a = _rope_args(pos, n_q, n_kv, rot, theta, q_out, k_cache, v_cache, gamma_q, gamma_k, eps)
+    a = _rope_args(pos, n_q, n_kv, rot, theta, q_out, k_cache, v_cache, gamma_q, gamma_k, eps, gate_out)
     _check("qmv_qkv_rope", lib().qmv_qkv_rope(bits, packed.data_ptr(), K, x.data_ptr(), _rowmajor(x, "x"), x.shape[0],
                                               ctypes.addressof(a), _stream()))

@@ -325,6 +325,11 @@ int check_rope_args(const char* fn, const q4_rope_kv* a, int R, q4::RopeKvArgs* 
   if (int rc = check_ptr(fn, "v_cache", a->v_cache, ce)) return rc;
   if (a->gamma_q != nullptr && !aligned(a->gamma_q, 4)) return fail(Q4_EALIGN, "%s: gamma_q is not 4-byte aligned", fn);
   if (a->gamma_k != nullptr && !aligned(a->gamma_k, 4)) return fail(Q4_EALIGN, "%s: gamma_k is not 4-byte aligned", fn);
+  if (a->n_gate_heads < 0 || a->n_gate_heads > 4096) return fail(Q4_EINVAL, "%s: n_gate_heads=%d must be 0..4096", fn, a->n_gate_heads);
+  if (a->n_gate_heads > 0) {
+    if (a->ldg < (int64_t)a->n_gate_heads * 64) return fail(Q4_EINVAL, "%s: ldg=%lld < n_gate_heads * 64", fn, (long long)a->ldg);
+    if (int rc = check_ptr(fn, "gate_out", a->gate_out, 4)) return rc;
+  }
   (void)R;
   q4::RopeKvArgs r{};
   for (int i = 0; i < a->rot_dims / 2; ++i) r.inv[i] = pow((double)a->theta, -2.0 * (double)i / (double)a->rot_dims);
@@ -342,6 +347,9 @@ int check_rope_args(const char* fn, const q4_rope_kv* a, int R, q4::RopeKvArgs* 
   r.v_cache = a->v_cache;
   r.cache_bf16 = a->cache_dtype == Q4_BF16;
   r.ring = a->ring_len;
+  r.n_gate = a->n_gate_heads;
+  r.gate_out = a->n_gate_heads > 0 ? a->gate_out : nullptr;
+  r.ldg = a->n_gate_heads > 0 ? a->ldg : 0;
   *out = r;
   return Q4_OK;
 }
@@ -375,7 +383,7 @@ int qkv_rope_launch_bits(int spw, int nv, const uint8_t* pk, int N, int K, const
 
 extern "C" {
 
-int q4g64_abi_version(void) { return 1; }
+int q4g64_abi_version(void) { return 2; }
 
 const char* q4_last_error(void) { return g_err; }
 
@@ -555,8 +563,9 @@ int rope_kv_store(const float* qkv, int64_t ldqkv, int R, const q4_rope_kv* args
   if (int rc = check_rope_args(fn, args, R, &a)) return rc;
   if (R < 1 || R > 65535) return fail(Q4_EINVAL, "%s: R=%d is outside 1..65535", fn, R);
   if (int rc = check_ptr(fn, "qkv", qkv, 4)) return rc;
-  const int heads = a.n_q + 2 * a.n_kv;
-  if (ldqkv < (int64_t)heads * 64) return fail(Q4_EINVAL, "%s: ldqkv=%lld < (n_q_heads + 2 n_kv_heads) * 64", fn, (long long)ldqkv);
+  const int heads = a.n_q + 2 * a.n_kv + a.n_gate;
+  if (ldqkv < (int64_t)heads * 64)
+    return fail(Q4_EINVAL, "%s: ldqkv=%lld < (n_q_heads + 2 n_kv_heads + n_gate_heads) * 64", fn, (long long)ldqkv);
   hipLaunchKernelGGL(q4::rope_kv_kernel, dim3((unsigned)heads, (unsigned)R), dim3(64), 0, (hipStream_t)stream, qkv, ldqkv, a);
   return launched(fn);
 }
@@ -567,7 +576,7 @@ int qmv_qkv_rope(int bits, const void* packed_qkv, int64_t K, const uint16_t* x,
   if (int rc = check_bits(fn, bits)) return rc;
   q4::RopeKvArgs a;
   if (int rc = check_rope_args(fn, args, R, &a)) return rc;
-  const int heads = a.n_q + 2 * a.n_kv;
+  const int heads = a.n_q + 2 * a.n_kv + a.n_gate;
   const int64_t N = (int64_t)heads * 64;
   if (int rc = check_nk(fn, N, K)) return rc;
   if (R < 1 || R > 16) return fail(Q4_EINVAL, "%s: R=%d is outside 1..16", fn, R);

@@ -13,7 +13,9 @@
 //     modulo 2 pi in double and rounded once to float for sincosf:
 //       x_i' = fma(x_i, c, -(x_{i+h} s)),  x_{i+h}' = fma(x_{i+h}, c, x_i s);
 //   * q goes to q_out[r], k and v to slot pos mod ring of their caches
-//     ([ring][kv_heads][64], float32 or bf16 rounded to nearest even).
+//     ([ring][kv_heads][64], float32 or bf16 rounded to nearest even);
+//   * gate heads (gated attention's fourth matvec, after the v heads) go to
+//     gate_out[r] unchanged.
 // The same function serves the stand-alone epilogue and the fused matvec, so
 // the fused results are bit-identical to the composition.
 #pragma once
@@ -38,10 +40,18 @@ struct RopeKvArgs {
   void* v_cache;
   int cache_bf16;
   int64_t ring;
+  int n_gate;
+  float* gate_out;
+  int64_t ldg;
 };
 
 // Head hd (wave-uniform) of row r; x is this lane's value of dimension d.
 __device__ __forceinline__ void rope_kv_head(float x, int d, int hd, int r, const RopeKvArgs& a) {
+  const int n_qkv = a.n_q + 2 * a.n_kv;
+  if (hd >= n_qkv) {
+    a.gate_out[(int64_t)r * a.ldg + (int64_t)(hd - n_qkv) * kHeadDim + d] = x;
+    return;
+  }
   const bool is_q = hd < a.n_q, is_k = !is_q && hd < a.n_q + a.n_kv;
   const int p = a.pos[r];
   if (is_q || is_k) {

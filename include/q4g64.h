@@ -237,7 +237,12 @@ int qmm_cut_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64_t 
  *     (cos and sin of the angle formed in double, rounded once to float);
  *   - q goes to q_out; k and v go to slot pos mod ring_len of k_cache and
  *     v_cache, each [ring_len][n_kv_heads][64] of cache_dtype (Q4_F32, or
- *     Q4_BF16 rounded to nearest even). Other slots are not touched.
+ *     Q4_BF16 rounded to nearest even). Other slots are not touched;
+ *   - gated attention's fourth matvec: n_gate_heads further heads may follow
+ *     the v heads in the stacked output (PR #1696, "What it adds": gated GQA
+ *     attention; decode fuses the four attention matvecs). Their values go
+ *     to gate_out unchanged (no norm, no rotation): the gate acts inside
+ *     attention, which these calls do not compute.
  * All pointers in the struct are DEVICE pointers except the struct itself,
  * which is read on the host when the call is made. */
 typedef struct q4_rope_kv {
@@ -255,17 +260,22 @@ typedef struct q4_rope_kv {
   void* v_cache;
   int32_t cache_dtype;    /* Q4_F32 or Q4_BF16 */
   int64_t ring_len;       /* >= 1 */
+  int32_t n_gate_heads;   /* >= 0 gate heads after the v heads */
+  float* gate_out;        /* float32 [R][ldg], ldg >= n_gate_heads * 64; may be NULL when n_gate_heads = 0 */
+  int64_t ldg;
 } q4_rope_kv;
 
-/* The epilogue alone, on a float32 q/k/v output qkv [R][ldqkv] (for example
- * qmv_rows over the stacked [Wq; Wk; Wv]); R >= 1. */
+/* The epilogue alone, on a float32 q/k/v(/gate) output qkv [R][ldqkv], ldqkv
+ * >= (n_q_heads + 2 n_kv_heads + n_gate_heads) * 64 (for example qmv_rows
+ * over the stacked [Wq; Wk; Wv; Wg]); R >= 1. */
 int rope_kv_store(const float* qkv, int64_t ldqkv, int R, const q4_rope_kv* args, void* stream);
 
 /* The stacked q/k/v matvec (bits = 4, 6 or 8, bf16 x [R][ldx], R = 1..16,
- * K <= 4096, N = (n_q_heads + 2 n_kv_heads) * 64) with the epilogue in the
- * same launch, one workgroup per head. q_out and the cache contents are
- * bit-identical to qmv_rows_qg64 followed by rope_kv_store, and a row's
- * results do not depend on R or on the other rows. */
+ * K <= 4096, N = (n_q_heads + 2 n_kv_heads + n_gate_heads) * 64) with the
+ * epilogue in the same launch, one workgroup per head. q_out, gate_out and
+ * the cache contents are bit-identical to qmv_rows_qg64 followed by
+ * rope_kv_store, and a row's results do not depend on R or on the other
+ * rows. */
 int qmv_qkv_rope(int bits, const void* packed_qkv, int64_t K, const uint16_t* x, int64_t ldx, int R, const q4_rope_kv* args,
                  void* stream);
 

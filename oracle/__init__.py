@@ -27,4 +27,4 @@ from .fp8block import (  # noqa: F401
     matmul_rows_fp8_exact,
     matmul_rows_fp8_fraction,
 )
-from .rope_kv import rms_norm, rope, rope_angles, rope_kv  # noqa: F401,E402
+from .rope_kv import attention_gate, rms_norm, rope, rope_angles, rope_kv  # noqa: F401,E402

@@ -70,3 +70,11 @@ def rope_kv(qkv, pos, n_q: int, n_kv: int, rot: int, theta: float, gamma_q=None,
     if gamma_k is not None:
         k = rms_norm(k, gamma_k, eps)
     return rope(q, pos, rot, theta).reshape(R, n_q * HEAD), rope(k, pos, rot, theta), v.copy()
+
+
+def attention_gate(qkvg, n_q: int, n_kv: int, n_gate: int) -> np.ndarray:
+    """The gate heads stacked after v (gated attention's fourth matvec), [R][n_gate * 64] float64: the epilogue passes
+    them through unchanged, since the gate acts inside attention."""
+    qkvg = np.asarray(qkvg, dtype=np.float64)
+    lo = (n_q + 2 * n_kv) * HEAD
+    return qkvg[:, lo : lo + n_gate * HEAD].copy()

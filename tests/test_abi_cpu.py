@@ -7,6 +7,8 @@ import ctypes
 import math
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -36,7 +38,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared():
         assert hasattr(lib, name), name
     assert set(_declared()) == set(q4._SIGNATURES)
-    assert lib.q4g64_abi_version() == 1
+    assert lib.q4g64_abi_version() == 2
 
 
 def test_packed_bytes():
@@ -261,6 +263,44 @@ def test_rope_args_rejected(kw, code):
     assert rc == code
     rc, _ = _rc("qmv_qkv_rope", 4, FAKE, 2048, FAKE, 2048, 1, ctypes.addressof(a), None)
     assert rc == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_gate_heads=-1), q4.Q4_EINVAL), (dict(n_gate_heads=4097, gate_out=FAKE, ldg=4097 * 64), q4.Q4_EINVAL),
+    (dict(n_gate_heads=32, gate_out=FAKE, ldg=100), q4.Q4_EINVAL), (dict(n_gate_heads=32, gate_out=None, ldg=2048), q4.Q4_EALIGN),
+    (dict(n_gate_heads=32, gate_out=FAKE + 2, ldg=2048), q4.Q4_EALIGN)])
+def test_rope_gate_args_rejected(kw, code):
+    a = _rope(**kw)
+    rc, _ = _rc("rope_kv_store", FAKE, 5120, 1, ctypes.addressof(a), None)
+    assert rc == code
+    rc, _ = _rc("qmv_qkv_rope", 4, FAKE, 2048, FAKE, 2048, 1, ctypes.addressof(a), None)
+    assert rc == code
+
+
+def test_rope_gate_widens_the_stacked_rows():
+    # with 32 gate heads the stacked output is (32 + 2 * 8 + 32) * 64 = 5120 wide
+    a = _rope(n_gate_heads=32, gate_out=FAKE, ldg=2048)
+    rc, msg = _rc("rope_kv_store", FAKE, 3072, 1, ctypes.addressof(a), None)
+    assert rc == q4.Q4_EINVAL and "n_gate_heads" in msg
+    rc, msg = _rc("qmv_qkv_rope", 4, FAKE, 8192, FAKE, 8192, 1, ctypes.addressof(a), None)
+    assert rc == q4.Q4_EUNSUPPORTED and "4096" in msg
+
+
+def test_rope_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror has the C struct's size and field offsets (checked with the host C compiler)."""
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no host C compiler")
+    fields = [f for f, _ in q4.RopeKv._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"q4g64.h\"\nint main(void) {\n"
+                   "  printf(\"%zu\\n\", sizeof(q4_rope_kv));\n"
+                   + "".join(f"  printf(\"%zu\\n\", offsetof(q4_rope_kv, {f}));\n" for f in fields) + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([gcc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(q4.RopeKv)
+    assert got[1:] == [getattr(q4.RopeKv, f).offset for f in fields]
 
 
 def test_rope_calls_reject_bad_shapes():

@@ -7,7 +7,10 @@ a KV ring, and decode fusing RoPE with the KV store) on the GPU.
   epilogue applied to the same float32 q/k/v values; v is copied exactly;
   the bf16 cache holds the round-to-nearest-even of the float32 cache.
 * Only the rows' ring slots are written.
-* End to end, q/k/v against the float64 matvec and epilogue."""
+* End to end, q/k/v against the float64 matvec and epilogue.
+* Gated attention's fourth matvec: gate heads stacked after v pass through
+  both calls unchanged (bit-equal to qmv_rows' columns), leave q/k/v as
+  they are without them, and every row equals its one-row call."""
 
 import numpy as np
 import pytest
@@ -22,6 +25,7 @@ from tests.tolerance import tol
 pytestmark = pytest.mark.gpu
 
 NQ, NKV, RING = 32, 8, 64
+NG = 32  # gate heads (one per q head)
 CASES = [dict(rot=64, theta=1e6, norm=False), dict(rot=32, theta=10000.0, norm=True), dict(rot=0, theta=10000.0, norm=True)]
 
 
@@ -180,3 +184,72 @@ def test_end_to_end_against_float64_matvec(c2):
     assert np.all(np.abs(host_f64(q).reshape(R, NQ, 64) - q64.reshape(R, NQ, 64)) <= carried(Tq, yq))
     assert np.all(np.abs(host_f64(k[slots]) - k64) <= carried(Tk, yk))
     assert np.all(np.abs(host_f64(v[slots]) - v64) <= Tv)
+
+
+@pytest.fixture(scope="module")
+def c2g(c2):
+    """config 2's q/k/v with a gate projection of the q projection's shape stacked after v."""
+    d = dict(c2)
+    wg = synthetic.draw_qweight(np.random.default_rng(951), "wg", NG * 64, 2048)
+    d["wg"] = wg
+    d["qkvg"] = synthetic.concat_rows(c2["wq"], c2["wk"], c2["wv"], wg, name="qkvg")
+    d["pg"] = dev_weight(d["qkvg"])
+    return d
+
+
+def _run_gate(d, case, R, fused, rows=None):
+    rows = slice(0, R) if rows is None else rows
+    pos = torch.from_numpy(d["pos"][rows]).to(DEV)
+    gq, gk = _gammas(d, case)
+    q, k, v = _outs(R)
+    g = torch.full((R, NG * 64), float("nan"), device=DEV)
+    w = d["qkvg"]
+    if fused:
+        q4.qmv_qkv_rope(d["pg"], w.K, d["xd"][rows], pos, NQ, NKV, case["rot"], case["theta"], q, k, v, gq, gk, gate_out=g)
+    else:
+        y = q4.qmv_rows(d["pg"], w.N, w.K, d["xd"][rows])
+        q4.rope_kv_store(y, pos, NQ, NKV, case["rot"], case["theta"], q, k, v, gq, gk, gate_out=g)
+    torch.cuda.synchronize()
+    return q, k, v, g
+
+
+@pytest.mark.parametrize("ci", [0, 1])
+@pytest.mark.parametrize("R", [1, 5, 16])
+def test_gate_fused_equals_composition(c2g, ci, R):
+    case = CASES[ci]
+    say(f"qmv_qkv_rope with gate R={R} {case}")
+    a = _run_gate(c2g, case, R, fused=True)
+    b = _run_gate(c2g, case, R, fused=False)
+    for t1, t2 in zip(a, b):
+        assert np.array_equal(bits32(t1), bits32(t2))
+    # the gate is qmv_rows' gate columns, unchanged; q/k/v are those of the call without a gate
+    w = c2g["qkvg"]
+    y = q4.qmv_rows(c2g["pg"], w.N, w.K, c2g["xd"][:R])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits32(a[3]), bits32(y[:, (NQ + 2 * NKV) * 64 :]))
+    plain = _run(c2g, case, R, fused=True)
+    for t1, t2 in zip(a[:3], plain):
+        assert np.array_equal(bits32(t1), bits32(t2))
+
+
+def test_gate_rows_equal_one_row(c2g):
+    case = CASES[1]
+    q16, k16, v16, g16 = _run_gate(c2g, case, 16, fused=True)
+    for r in (0, 9, 15):
+        q, k, v, g = _run_gate(c2g, case, 1, fused=True, rows=slice(r, r + 1))
+        s = int(c2g["pos"][r]) % RING
+        assert np.array_equal(bits32(g)[0], bits32(g16)[r]) and np.array_equal(bits32(q)[0], bits32(q16)[r])
+        assert np.array_equal(bits32(k[s]), bits32(k16[s])) and np.array_equal(bits32(v[s]), bits32(v16[s]))
+
+
+def test_gate_against_float64_matvec(c2g):
+    """The gate is a plain matvec output: within the matvec bound T of the float64 oracle."""
+    R = 4
+    _, _, _, g = _run_gate(c2g, CASES[0], R, fused=True)
+    wg, xs = c2g["wg"], c2g["x"][:R]
+    y64 = oracle.matmul_rows(wg.wq, wg.scales, wg.biases, xs)
+    T = tol(oracle.error_weight(wg.wq, wg.scales, wg.biases, xs), wg.K)
+    assert np.all(np.abs(host_f64(g) - y64) <= T)
+    qkvg64 = np.concatenate([oracle.matmul_rows(c2g["qkv"].wq, c2g["qkv"].scales, c2g["qkv"].biases, xs), y64], axis=1)
+    assert np.array_equal(oracle.attention_gate(qkvg64, NQ, NKV, NG), y64)
+

@@ -553,3 +553,20 @@ def test_rope_kv_splits_heads_in_order():
     assert np.array_equal(q, qkv[:, :256])
     assert np.array_equal(k.reshape(2, -1), qkv[:, 256:384])
     assert np.array_equal(v.reshape(2, -1), qkv[:, 384:512])
+
+
+def test_attention_gate_is_the_section_after_v():
+    """Gated attention's fourth matvec (PR #1696, "What it adds": gated GQA): the gate heads follow the v heads in
+    the stacked output and pass through the epilogue unchanged; appending them changes nothing for q, k and v."""
+    rng = np.random.default_rng(804)
+    n_q, n_kv, n_gate = 4, 2, 3
+    qkvg = rng.normal(0, 1, (3, (n_q + 2 * n_kv + n_gate) * 64))
+    gate = oracle.attention_gate(qkvg, n_q, n_kv, n_gate)
+    assert gate.shape == (3, n_gate * 64)
+    assert np.array_equal(gate, qkvg[:, 512:704])
+    pos = [3, 70, 1000]
+    with_gate = oracle.rope_kv(qkvg, pos, n_q, n_kv, 48, 10000.0, np.ones(64), np.ones(64))
+    without = oracle.rope_kv(qkvg[:, :512], pos, n_q, n_kv, 48, 10000.0, np.ones(64), np.ones(64))
+    for a, b in zip(with_gate, without):
+        assert np.array_equal(a, b)
+    assert oracle.attention_gate(qkvg, n_q, n_kv, 0).shape == (3, 0)
