@@ -396,16 +396,15 @@ inline int qmv_row_tiles(int xf32, int R) {
   return rtf <= 1 ? 1 : (rtf <= 2 ? 2 : 4);
 }
 
-// Largest dynamic LDS a workgroup may use on this device (queried once).
+// Largest dynamic LDS a workgroup may use (queried once per process, on the
+// device current at the first call; the initialisation is thread-safe).
 inline size_t qmv_max_lds() {
-  static size_t cached = 0;
-  if (cached == 0) {
+  static const size_t cached = [] {
     int dev = 0, v = 0;
     if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
-      cached = (size_t)v;
-    else
-      cached = 64 * 1024;
-  }
+      return (size_t)v;
+    return (size_t)64 * 1024;
+  }();
   return cached;
 }
 
