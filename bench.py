@@ -332,6 +332,7 @@ def main():
     if not args.no_pgemm:
         result["pgemm"] = bench_pgemm(dev)
     if not args.no_wide:
+        result["decode_rows"] = bench_rows(dev, K, W, args.pool_mb)
         result["qkv_rope"] = bench_qkv_rope(dev, K, W, args.pool_mb)
     if not args.no_wide:
         result["wide_codes"] = {str(b): bench_wide(dev, b, K, W, args.pool_mb, graph=g_used) for b in (6, 8, "fp8")}
@@ -445,6 +446,58 @@ def bench_wide(dev, bits, K, W, pool_mb, graph=True, reps=5):
                              "frac": round(b2 / (t2 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "pgemm_swiglu_8192": {"avg_ms": round(tw * 1e3, 4), "TFLOP/s": round(tf, 2), "frac": round(tf / BF16_PEAK_TFLOPS, 4)},
     }
+
+
+def bench_rows(dev, K, W, pool_mb):
+    """The 4-bit decode FFN step with 2, 4, 8 and 16 activation rows sharing
+    it (streams in one decode step): same shapes, cold weight pool and graph
+    timing as the one-row step. rows/s = rows / step time."""
+    import torch
+
+    import bit_weight_only_q4g64_amd as q4
+    import synthetic
+
+    log("decode FFN step at 2..16 rows")
+    d = synthetic.config(1)
+    w1, w3, w2 = d["w1"], d["w3"], d["w2"]
+    copy_bytes = q4.packed_bytes(w1.N, w1.K) * 2 + q4.packed_bytes(w2.N, w2.K)
+    ncopies = max(2, -(-pool_mb * (1 << 20) // copy_bytes))
+    base = [pack_dev(w1, dev), pack_dev(w3, dev), pack_dev(w2, dev)]
+    pool = [base] + [[t.clone() for t in base] for _ in range(ncopies - 1)]
+    xs = to_dev(synthetic.draw_bf16_rows(np.random.default_rng(11), 16, w1.K), np.int16, dev).view(torch.bfloat16)
+    z = torch.empty((16, w1.N), dtype=torch.float32, device=dev)
+    y = torch.empty((16, w2.N), dtype=torch.float32, device=dev)
+    z3s = {R: torch.empty((3, R, w1.N), dtype=torch.bfloat16, device=dev) for R in (1, 2, 4, 8, 16)}
+    out = {}
+    for R in (1, 2, 4, 8, 16):
+        z3 = z3s[R]
+
+        def step(i):
+            p1, p3, p2 = pool[i % ncopies]
+            q4.qmv_w13_swiglu(p1, p3, w1.N, w1.K, xs[:R], y=z[:R])
+            q4.qmv_rows(p2, w2.N, w2.K, z[:R], y=y[:R])
+
+        def step3(i):
+            p1, p3, p2 = pool[i % ncopies]
+            q4.qmv_w13_swiglu(p1, p3, w1.N, w1.K, xs[:R], y=z3, planes=True)
+            q4.qmv_rows(p2, w2.N, w2.K, z3, y=y[:R])
+
+        us = batch_average_us(torch, step, W, K)
+        us3 = batch_average_us(torch, step3, W, K)
+        t13 = batch_average_us(torch, lambda i: q4.qmv_w13_swiglu(pool[i % ncopies][0], pool[i % ncopies][1], w1.N, w1.K, xs[:R],
+                                                                  y=z[:R]), W, K)
+        t2 = batch_average_us(torch, lambda i: q4.qmv_rows(pool[i % ncopies][2], w2.N, w2.K, z[:R], y=y[:R]), W, K)
+        t2p = batch_average_us(torch, lambda i: q4.qmv_rows(pool[i % ncopies][2], w2.N, w2.K, z3, y=y[:R]), W, K)
+        b = 2 * qbytes(w1.N, w1.K) + qbytes(w2.N, w2.K) + R * (w1.K * 2 + w1.N * 4 + w2.K * 4 + w2.N * 4)
+        out[f"R{R}"] = {"us_per_step": round(us, 3), "rows_per_s": round(R / (us * 1e-6), 1), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                        "qmv_w13_swiglu_us": round(t13, 3), "qmv_rows_w2_f32x_us": round(t2, 3),
+                        "planes_us_per_step": round(us3, 3), "planes_rows_per_s": round(R / (us3 * 1e-6), 1),
+                        "qmv_rows_w2_planes_us": round(t2p, 3)}
+    del pool, base
+    torch.cuda.empty_cache()
+    out["workload"] = ("decode FFN step (w1/w3 8192x2048 + SwiGLU, w2 2048x8192, q4g64) with R bf16 rows, graph of K steps; "
+                       "planes_*: the SwiGLU output handed to w2 as its three exact bf16 planes instead of float32 (same bits)")
+    return out
 
 
 def bench_qkv_rope(dev, K, W, pool_mb):

@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4g64.so")
 
 Q4_OK, Q4_EINVAL, Q4_EALIGN, Q4_EDEVICE, Q4_EUNSUPPORTED = 0, -1, -2, -3, -4
-Q4_BF16, Q4_F32 = 0, 1
+Q4_BF16, Q4_F32, Q4_BF16X3 = 0, 1, 2
 
 _lib = None
 
@@ -40,6 +40,7 @@ _SIGNATURES = {
     "unpack_qg64": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, _P, _P, _P]),
     "qmv_rows_qg64": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, ctypes.c_int, _I64, ctypes.c_int, _P, _I64, _P]),
     "qmv_w13_swiglu_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
+    "qmv_w13_swiglu_x3": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
     "qmm_window_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P]),
     "qmm_cut_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _I64, _P]),
     "fp8b_packed_bytes": (ctypes.c_size_t, [_I64, _I64]),
@@ -47,6 +48,7 @@ _SIGNATURES = {
     "unpack_fp8b": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "qmv_rows_fp8b": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, _I64, ctypes.c_int, _P, _I64, _P]),
     "qmv_w13_swiglu_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
+    "qmv_w13_swiglu_x3_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
     "qmm_window_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P]),
     "qmm_cut_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _I64, _P]),
     "rope_kv_store": (ctypes.c_int, [_P, _I64, ctypes.c_int, _P, _P]),
@@ -104,6 +106,25 @@ def _rowmajor(t: torch.Tensor, name: str) -> int:
     return t.stride(0)
 
 
+def _planes_ld(t: torch.Tensor, name: str) -> int:
+    """Row stride of a [3][R][ld] bf16 planes tensor (Q4_BF16X3): contiguous rows, plane p at p * R * ld."""
+    if t.dim() != 3 or t.shape[0] != 3 or t.dtype != torch.bfloat16 or t.stride(2) != 1 or t.stride(0) != t.shape[1] * t.stride(1):
+        raise ValueError(f"{name} must be bfloat16 planes [3][R][ld] with rows of stride ld and planes of stride R * ld")
+    return t.stride(1)
+
+
+def _x_arg(x: torch.Tensor):
+    """(x_dtype, ldx, R) of decode activations: bf16 or float32 rows [R][ldx], or the three bf16 planes of float32
+    rows [3][R][ldx] (Q4_BF16X3, as qmv_w13_swiglu(..., planes=True) writes them)."""
+    if x.dim() == 3:
+        return Q4_BF16X3, _planes_ld(x, "x"), x.shape[1]
+    if x.dtype == torch.bfloat16:
+        return Q4_BF16, _rowmajor(x, "x"), x.shape[0]
+    if x.dtype == torch.float32:
+        return Q4_F32, _rowmajor(x, "x"), x.shape[0]
+    raise ValueError("x must be bfloat16 or float32 rows, or bfloat16 planes [3][R][ld]")
+
+
 def packed_bytes(N: int, K: int, bits: int = 4) -> int:
     if bits == 4:
         return int(lib().q4g64_packed_bytes(N, K))
@@ -149,17 +170,11 @@ def unpack(packed: torch.Tensor, N: int, K: int, bits: int = 4):
 
 
 def qmv_rows(packed: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None, bits: int = 4) -> torch.Tensor:
-    """y[r] = W x[r] for the R = x.shape[0] (1..16) rows of x (bf16 or float32); W has 4-, 6- or 8-bit codes."""
+    """y[r] = W x[r] for the R (1..16) rows of x (bf16 or float32 [R][ld], or float32 as bf16 planes [3][R][ld]);
+    W has 4-, 6- or 8-bit codes."""
     _dev(packed, "packed")
     _dev(x, "x")
-    ldx = _rowmajor(x, "x")
-    if x.dtype == torch.bfloat16:
-        xd = Q4_BF16
-    elif x.dtype == torch.float32:
-        xd = Q4_F32
-    else:
-        raise ValueError("x must be bfloat16 or float32")
-    R = x.shape[0]
+    xd, ldx, R = _x_arg(x)
     if y is None:
         y = torch.empty((R, N), dtype=torch.float32, device=x.device)
     if y.dtype != torch.float32 or y.shape[0] < R:
@@ -173,14 +188,21 @@ def qmv_rows(packed: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Ten
 
 
 def qmv_w13_swiglu(p1: torch.Tensor, p3: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None,
-                   bits: int = 4) -> torch.Tensor:
-    """y[r] = silu(W1 x[r]) * (W3 x[r]) for the 1..16 bf16 rows of x; W1, W3 have 4-, 6- or 8-bit codes."""
+                   bits: int = 4, planes: bool = False) -> torch.Tensor:
+    """y[r] = silu(W1 x[r]) * (W3 x[r]) for the 1..16 bf16 rows of x; W1, W3 have 4-, 6- or 8-bit codes.
+    planes=True: y is written as the three exact bf16 pieces of each float32 result, planes [3][R][N]."""
     _dev(p1, "packed_w1")
     _dev(p3, "packed_w3")
     _dev(x, "x")
     if x.dtype != torch.bfloat16:
         raise ValueError("x must be bfloat16")
     R = x.shape[0]
+    if planes:
+        if y is None:
+            y = torch.empty((3, R, N), dtype=torch.bfloat16, device=x.device)
+        _check("qmv_w13_swiglu_x3", lib().qmv_w13_swiglu_x3(bits, p1.data_ptr(), p3.data_ptr(), N, K, x.data_ptr(), _rowmajor(x, "x"), R,
+                                                            y.data_ptr(), _planes_ld(y, "y"), _stream()))
+        return y
     if y is None:
         y = torch.empty((R, N), dtype=torch.float32, device=x.device)
     if bits == 4:
@@ -362,25 +384,29 @@ def qmv_rows_fp8b(packed: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torc
     """y[r] = W x[r] for the 1..16 rows of x (bf16 or float32), W block FP8."""
     _dev(packed, "packed")
     _dev(x, "x")
-    xd = Q4_BF16 if x.dtype == torch.bfloat16 else Q4_F32 if x.dtype == torch.float32 else None
-    if xd is None:
-        raise ValueError("x must be bfloat16 or float32")
-    R = x.shape[0]
+    xd, ldx, R = _x_arg(x)
     if y is None:
         y = torch.empty((R, N), dtype=torch.float32, device=x.device)
-    _check("qmv_rows_fp8b", lib().qmv_rows_fp8b(packed.data_ptr(), N, K, x.data_ptr(), xd, _rowmajor(x, "x"), R, y.data_ptr(),
+    _check("qmv_rows_fp8b", lib().qmv_rows_fp8b(packed.data_ptr(), N, K, x.data_ptr(), xd, ldx, R, y.data_ptr(),
                                                 _rowmajor(y, "y"), _stream()))
     return y
 
 
-def qmv_w13_swiglu_fp8b(p1: torch.Tensor, p3: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
-    """y[r] = silu(W1 x[r]) * (W3 x[r]) for the 1..16 bf16 rows of x, W1 and W3 block FP8."""
+def qmv_w13_swiglu_fp8b(p1: torch.Tensor, p3: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None,
+                        planes: bool = False) -> torch.Tensor:
+    """y[r] = silu(W1 x[r]) * (W3 x[r]) for the 1..16 bf16 rows of x, W1 and W3 block FP8 (planes: as qmv_w13_swiglu)."""
     _dev(p1, "packed_w1")
     _dev(p3, "packed_w3")
     _dev(x, "x")
     if x.dtype != torch.bfloat16:
         raise ValueError("x must be bfloat16")
     R = x.shape[0]
+    if planes:
+        if y is None:
+            y = torch.empty((3, R, N), dtype=torch.bfloat16, device=x.device)
+        _check("qmv_w13_swiglu_x3_fp8b", lib().qmv_w13_swiglu_x3_fp8b(p1.data_ptr(), p3.data_ptr(), N, K, x.data_ptr(), _rowmajor(x, "x"),
+                                                                      R, y.data_ptr(), _planes_ld(y, "y"), _stream()))
+        return y
     if y is None:
         y = torch.empty((R, N), dtype=torch.float32, device=x.device)
     _check("qmv_w13_swiglu_fp8b", lib().qmv_w13_swiglu_fp8b(p1.data_ptr(), p3.data_ptr(), N, K, x.data_ptr(), _rowmajor(x, "x"), R,

@@ -67,10 +67,11 @@ unsigned grid_for(int64_t total, int block) {
 }
 
 int check_x(const char* fn, const void* x, int x_dtype, int64_t ldx, int64_t K) {
-  if (x_dtype != Q4_BF16 && x_dtype != Q4_F32) return fail(Q4_EINVAL, "%s: x_dtype %d is not Q4_BF16 or Q4_F32", fn, x_dtype);
+  if (x_dtype != Q4_BF16 && x_dtype != Q4_F32 && x_dtype != Q4_BF16X3)
+    return fail(Q4_EINVAL, "%s: x_dtype %d is not Q4_BF16, Q4_F32 or Q4_BF16X3", fn, x_dtype);
   if (int rc = check_ptr(fn, "x", x, 16)) return rc;
   if (ldx < K) return fail(Q4_EINVAL, "%s: ldx=%lld < K=%lld", fn, (long long)ldx, (long long)K);
-  const int64_t es = x_dtype == Q4_BF16 ? 2 : 4;
+  const int64_t es = x_dtype == Q4_F32 ? 4 : 2;
   if ((ldx * es) % 16 != 0) return fail(Q4_EALIGN, "%s: ldx=%lld elements does not keep rows 16-byte aligned", fn, (long long)ldx);
   return Q4_OK;
 }
@@ -146,33 +147,36 @@ int qmv_rows_impl(const char* fn, int bits, const void* packed, int64_t N, int64
   if (int rc = check_x(fn, x, x_dtype, ldx, K)) return rc;
   if (int rc = check_ptr(fn, "y", y, 4)) return rc;
   if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
-  if ((int64_t)R * ldx * (x_dtype == Q4_F32 ? 4 : 2) >= (int64_t(1) << 31))
+  const int64_t xrows = x_dtype == Q4_BF16X3 ? 3 * (int64_t)R : R;  // planes: three rows per activation row
+  if (xrows * ldx * (x_dtype == Q4_F32 ? 4 : 2) >= (int64_t(1) << 31))
     return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
   // up to 4 segments per wave, 16 waves: K <= 16384
   if (K > q4::kQmvMaxK) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
-  const size_t lds = q4::qmv_lds_bytes(K, x_dtype == Q4_F32, 1, R);
+  const size_t lds = q4::qmv_lds_bytes(K, x_dtype != Q4_BF16, 1, R);
   if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
-  q4::qmv_launch((const uint8_t*)packed, (const uint8_t*)packed, 1, (int)N, (int)K, x, x_dtype == Q4_F32, ldx, R, y, ldy, s, bits);
+  const int xmode = x_dtype == Q4_F32 ? 1 : (x_dtype == Q4_BF16X3 ? 2 : 0);
+  q4::qmv_launch((const uint8_t*)packed, (const uint8_t*)packed, 1, (int)N, (int)K, x, xmode, ldx, R, y, ldy, s, bits);
   return launched(fn);
 }
 
 int qmv_w13_impl(const char* fn, int bits, const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
-                 int64_t ldx, int R, float* y, int64_t ldy, hipStream_t s) {
+                 int64_t ldx, int R, void* y, int64_t ldy, hipStream_t s, bool y3 = false) {
   if (int rc = check_fmt(fn, bits)) return rc;
   if (int rc = check_nk(fn, N, K)) return rc;
   if (R < 1 || R > 16) return fail(Q4_EINVAL, "%s: R=%d is outside 1..16", fn, R);
   if (int rc = check_ptr(fn, "packed_w1", packed_w1, 16)) return rc;
   if (int rc = check_ptr(fn, "packed_w3", packed_w3, 16)) return rc;
   if (int rc = check_x(fn, x, Q4_BF16, ldx, K)) return rc;
-  if (int rc = check_ptr(fn, "y", y, 4)) return rc;
-  if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  if (int rc = check_ptr(fn, y3 ? "z3" : "y", y, y3 ? 16 : 4)) return rc;
+  if (ldy < N) return fail(Q4_EINVAL, "%s: %s=%lld < N=%lld", fn, y3 ? "ldz" : "ldy", (long long)ldy, (long long)N);
+  if (y3 && (ldy * 2) % 16 != 0) return fail(Q4_EALIGN, "%s: ldz=%lld elements does not keep rows 16-byte aligned", fn, (long long)ldy);
   if ((int64_t)R * ldx * 2 >= (int64_t(1) << 31))
     return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
   // up to 2 segments per wave, 16 waves: K <= 8192
   if (K > q4::kQmvMaxK / 2) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the fused decode limit of 8192", fn, (long long)K);
   const size_t lds = q4::qmv_lds_bytes(K, 0, 2, R);
   if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the fused decode limit of 8192", fn, (long long)K);
-  q4::qmv_launch((const uint8_t*)packed_w1, (const uint8_t*)packed_w3, 2, (int)N, (int)K, x, 0, ldx, R, y, ldy, s, bits);
+  q4::qmv_launch((const uint8_t*)packed_w1, (const uint8_t*)packed_w3, 2, (int)N, (int)K, x, 0, ldx, R, (float*)y, ldy, s, bits, y3);
   return launched(fn);
 }
 
@@ -433,6 +437,12 @@ int qmv_w13_swiglu_qg64(int bits, const void* packed_w1, const void* packed_w3, 
   return qmv_w13_impl("qmv_w13_swiglu_qg64", bits, packed_w1, packed_w3, N, K, x, ldx, R, y, ldy, (hipStream_t)stream);
 }
 
+int qmv_w13_swiglu_x3(int bits, const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
+                      int64_t ldx, int R, uint16_t* z3, int64_t ldz, void* stream) {
+  if (int rc = check_bits("qmv_w13_swiglu_x3", bits)) return rc;
+  return qmv_w13_impl("qmv_w13_swiglu_x3", bits, packed_w1, packed_w3, N, K, x, ldx, R, z3, ldz, (hipStream_t)stream, true);
+}
+
 int qmm_window(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx, int64_t M,
                void* y, int y_dtype, int64_t ldy, void* stream) {
   return qmm_window_checked("qmm_window", 4, packed_a, packed_b, N, K, x, ldx, M, y, y_dtype, ldy, (hipStream_t)stream);
@@ -543,6 +553,11 @@ int qmv_rows_fp8b(const void* packed, int64_t N, int64_t K, const void* x, int x
 int qmv_w13_swiglu_fp8b(const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x, int64_t ldx, int R,
                         float* y, int64_t ldy, void* stream) {
   return qmv_w13_impl("qmv_w13_swiglu_fp8b", q4::kFmtFp8, packed_w1, packed_w3, N, K, x, ldx, R, y, ldy, (hipStream_t)stream);
+}
+
+int qmv_w13_swiglu_x3_fp8b(const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                           int R, uint16_t* z3, int64_t ldz, void* stream) {
+  return qmv_w13_impl("qmv_w13_swiglu_x3_fp8b", q4::kFmtFp8, packed_w1, packed_w3, N, K, x, ldx, R, z3, ldz, (hipStream_t)stream, true);
 }
 
 int qmm_window_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx, int64_t M,

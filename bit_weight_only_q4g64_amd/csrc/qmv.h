@@ -210,24 +210,34 @@ __device__ __forceinline__ void qmv_ordered_sum(float (&tot)[NMAT][kRT][kPerLane
 }
 
 // XF32 = 0: bf16 x, one row tile of 16 rows.  XF32 = 1: float32 x, RTF row
-// tiles of 4 rows x 3 pieces.  NMAT = 1: y = W x.  NMAT = 2: y = silu(W1 x) * (W3 x).
+// tiles of 4 rows x 3 pieces.  XF32 = 2: the same float32 values given as
+// their three exact bf16 pieces, planes [3][R][ldx] (x = h + m + l, see
+// split3): the arithmetic of XF32 = 1 without splitting in the kernel.
+// NMAT = 1: y = W x.  NMAT = 2: y = silu(W1 x) * (W3 x); with Y3 the result
+// is written as its three bf16 pieces, planes [3][R][ldy], instead of float32.
 // SPW: maximum segments per wave.  XLDS: activations staged in LDS once per
 // workgroup (else each wave reads its fragments from global memory). NV:
 // row slots per lane group kept by the bf16 path. None of these changes the
 // arithmetic of a stored row.
-template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS>
+template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS, bool Y3 = false>
 __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* __restrict__ pk0, const uint8_t* __restrict__ pk1,
                                                               int N, int K, const void* __restrict__ xv, int64_t ldx, int R,
                                                               float* __restrict__ y, int64_t ldy) {
+  static_assert(!Y3 || NMAT == 2, "the three-plane output is the fused SwiGLU's");
   constexpr int kRT = XF32 ? RTF : 1;  // row tiles
   // accumulators per lane per row tile: bf16 x keeps row slots 4*kc + v for
   // v < NV (NV = 4 when R > 4, else the smallest of 1, 2, 4 covering R); the
   // slots left out hold rows >= R and are never stored
   constexpr int kPerLane = XF32 ? 1 : NV;
-  constexpr int kXElem = XF32 ? 4 : 2;  // bytes per activation element
+  constexpr int kXElem = XF32 == 1 ? 4 : 2;  // bytes per activation element
+  const int XR = XF32 == 2 ? 3 * R : R;        // activation rows in memory (planes: piece-major)
   extern __shared__ __align__(16) uint8_t smem[];
-  float* part = (float*)smem;  // [segment][matrix][row tile][kPerLane][lane]
-  uint16_t* xs = (uint16_t*)(smem + qmv_part_bytes(K, XF32, NMAT, kRT, NV));
+  // The segment partials ([segment][matrix][row tile][kPerLane][lane]) are
+  // written only after every wave has finished reading the staged
+  // activations, so the two share the same LDS: a workgroup needs the larger
+  // of the two, which keeps two workgroups per CU at up to 16 rows.
+  float* part = (float*)smem;
+  uint16_t* xs = (uint16_t*)smem;
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -247,29 +257,39 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
     cres[m] = make_rsrc(pk + (int64_t)t * P * pair_code_bytes(BITS), (uint32_t)P * pair_code_bytes(BITS));
     sres[m] = make_rsrc(pk + cb + (int64_t)t * P * kPairSbBytes, (uint32_t)P * kPairSbBytes);
   }
-  const rsrc_t xres = make_rsrc(xv, (uint32_t)R * xrow);
+  const rsrc_t xres = make_rsrc(xv, (uint32_t)XR * xrow);
 
   // 1) activations: the first batch of staging loads is issued before the
-  //    weight loads, so writing it to LDS waits for nothing else. Staging
-  //    slot (r, j) covers row r, 16-byte chunk threadIdx.x + j * blockDim.x;
-  //    r and j are uniform and walk the rows in order.
-  constexpr int kBatch = 4;
+  //    weight loads, so writing it to LDS waits for nothing else. The R rows
+  //    are cut into 16-byte chunks, numbered row after row; slot u of a
+  //    thread holds chunk threadIdx.x + u * blockDim.x, so every thread has
+  //    work whatever the row length.
+  // eight loads in flight where the weight registers leave room, else four
+  constexpr int kBatch = (XF32 || SPW * NMAT * code_bits(BITS) > 8) ? 4 : 8;
   const int nthr = blockDim.x;
   const int per_row = K * kXElem / 16;  // 16-byte chunks per row
-  const int jmax = (per_row + nthr - 1) / nthr;
-  auto xload = [&](int r, int j) -> u32x4 {
-    int c = (int)threadIdx.x + j * nthr;
-    c = c < per_row ? c : per_row - 1;
-    return buf_load16(xres, (uint32_t)c * 16u, (uint32_t)r * xrow);
+  const int total = XR * per_row;
+  const int nslots = (total + nthr - 1) / nthr;
+  // (row, chunk) of slot 0, and the step from one slot to the next
+  const int r0 = (int)threadIdx.x / per_row, c0 = (int)threadIdx.x - r0 * per_row;
+  const int step_r = nthr / per_row, step_c = nthr - step_r * per_row;
+  auto advance = [&](int& r, int& c) {
+    c += step_c;
+    r += step_r;
+    if (c >= per_row) { c -= per_row; ++r; }
+  };
+  auto xload = [&](int r, int c) -> u32x4 {
+    if (r >= XR) { r = XR - 1; c = per_row - 1; }  // past the last chunk: a valid, unused read
+    return buf_load16(xres, (uint32_t)c * 16u + (uint32_t)r * xrow, 0u);
   };
   u32x4 xv0[kBatch];
   if constexpr (XLDS) {
-    int r = 0, j = 0;
+    int r = r0, c = c0;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      if (r >= R) break;
-      xv0[u] = xload(r, j);
-      if (++j == jmax) { j = 0; ++r; }
+      if (u >= nslots) break;
+      xv0[u] = xload(r, c);
+      advance(r, c);
     }
   }
 
@@ -280,10 +300,9 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   // 3) write the staged activations (float32 rows as three exact bf16 planes)
   if constexpr (XLDS) {
     const int plane = R * xsi;
-    auto put = [&](int r, int j, const u32x4& v) {
-      const int c = (int)threadIdx.x + j * nthr;
-      if (c >= per_row) return;
-      if constexpr (!XF32) {
+    auto put = [&](int r, int c, const u32x4& v) {
+      if (r >= XR) return;
+      if constexpr (XF32 != 1) {  // bf16 rows, or the planes row after row (piece * R + row)
         *(u32x4*)(xs + r * xsi + c * 8) = v;
       } else {
         uint32_t h[4], m[4], l[4];
@@ -295,26 +314,26 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
         *(u32x2*)(d + 2 * plane) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
       }
     };
-    int r = 0, j = 0;
+    int r = r0, c = c0;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      if (r >= R) break;
-      put(r, j, xv0[u]);
-      if (++j == jmax) { j = 0; ++r; }
+      if (u >= nslots) break;
+      put(r, c, xv0[u]);
+      advance(r, c);
     }
     // slots beyond the first batch (large R * K): kBatch loads, then their writes
-    while (r < R) {
+    for (int u0 = kBatch; u0 < nslots; u0 += kBatch) {
       u32x4 v[kBatch];
-      int r2 = r, j2 = j;
+      int rl = r, cl = c;
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        if (r2 < R) v[u] = xload(r2, j2);
-        if (++j2 == jmax) { j2 = 0; ++r2; }
+        if (u0 + u < nslots) v[u] = xload(rl, cl);
+        advance(rl, cl);
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        if (r < R) put(r, j, v[u]);
-        if (++j == jmax) { j = 0; ++r; }
+        if (u0 + u < nslots) put(r, c, v[u]);
+        advance(r, c);
       }
     }
     __syncthreads();
@@ -335,6 +354,7 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
       int piece = i & 3;
       piece = piece < 3 ? piece : 2;
       if constexpr (XLDS) return __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + (piece * R + row) * xsi + k0));
+      else if constexpr (XF32 == 2) return __builtin_bit_cast(bf16x8, buf_load16(xres, (uint32_t)(piece * R + row) * xrow + (uint32_t)k0 * 2u, 0u));
       else {
         const u32x4 a = buf_load16(xres, (uint32_t)row * xrow + (uint32_t)k0 * 4u, 0u);
         const u32x4 b = buf_load16(xres, (uint32_t)row * xrow + (uint32_t)k0 * 4u + 16u, 0u);
@@ -350,19 +370,26 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
     }
   };
 
-  // 4) compute, one segment after another
+  // 4) compute, one segment after another; the partials wait in registers
+  //    until every wave is past its last activation read
+  float keep[SPW][NMAT][kRT][kPerLane];
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int seg = wave + j * nwaves;
     if (seg >= nseg) break;
-    float acc[NMAT][kRT][kPerLane];
-    qmv_fold_segment<XF32, NMAT, kRT, kPerLane>(acc, wts.cw[j], wts.sbw[j], seg * kSegGroups, G, xfrag);
+    qmv_fold_segment<XF32, NMAT, kRT, kPerLane>(keep[j], wts.cw[j], wts.sbw[j], seg * kSegGroups, G, xfrag);
+  }
+  if constexpr (XLDS) __syncthreads();
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int seg = wave + j * nwaves;
+    if (seg >= nseg) break;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
-        for (int v = 0; v < kPerLane; ++v) part[qmv_part_index<NMAT, kRT, kPerLane>(seg, m, rt, v, lane)] = acc[m][rt][v];
+        for (int v = 0; v < kPerLane; ++v) part[qmv_part_index<NMAT, kRT, kPerLane>(seg, m, rt, v, lane)] = keep[j][m][rt][v];
   }
   __syncthreads();
   if (wave != 0) return;
@@ -384,7 +411,17 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
       } else {
         out = silu_f32(tot[0][rt][v]) * tot[1][rt][v];
       }
-      y[(int64_t)r * ldy + n] = out;
+      if constexpr (Y3) {
+        uint32_t h, m, l;
+        split3(out, h, m, l);
+        uint16_t* y3 = (uint16_t*)y;
+        const int64_t plane = (int64_t)R * ldy;
+        y3[(int64_t)r * ldy + n] = (uint16_t)h;
+        y3[plane + (int64_t)r * ldy + n] = (uint16_t)m;
+        y3[2 * plane + (int64_t)r * ldy + n] = (uint16_t)l;
+      } else {
+        y[(int64_t)r * ldy + n] = out;
+      }
     }
   }
 }
@@ -414,10 +451,10 @@ inline size_t qmv_lds_bytes(int64_t K, int xf32, int nmat, int R) {
   return qmv_part_bytes(K, xf32, nmat, qmv_row_tiles(xf32, R), xf32 ? 1 : qmv_nv(R));
 }
 
-template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS>
+template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS, bool Y3>
 inline void qmv_launch_t(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
                          int64_t ldy, int nwaves, size_t lds, hipStream_t s) {
-  auto kern = qmv_kernel<XF32, NMAT, SPW, RTF, XLDS, NV, BITS>;
+  auto kern = qmv_kernel<XF32, NMAT, SPW, RTF, XLDS, NV, BITS, Y3>;
   // allow dynamic LDS beyond the 64 KB default, once per instantiation
   static const bool lds_ok =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)qmv_max_lds()) == hipSuccess;
@@ -425,75 +462,88 @@ inline void qmv_launch_t(const uint8_t* pk0, const uint8_t* pk1, int N, int K, c
   hipLaunchKernelGGL(kern, dim3((unsigned)(N / kTileN)), dim3(nwaves * 64), lds, s, pk0, pk1, N, K, x, ldx, R, y, ldy);
 }
 
-template <int XF32, int NMAT, int RTF, bool XLDS, int NV, int BITS>
+template <int XF32, int NMAT, int RTF, bool XLDS, int NV, int BITS, bool Y3>
 inline void qmv_launch_spw(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
                            int64_t ldy, size_t lds, hipStream_t s) {
   const int nseg = qmv_segments(K);
   const int nwaves = nseg < kQmvMaxWaves ? nseg : kQmvMaxWaves;
   const int spw = (nseg + nwaves - 1) / nwaves;
   if (spw <= 1) {
-    qmv_launch_t<XF32, NMAT, 1, RTF, XLDS, NV, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
+    qmv_launch_t<XF32, NMAT, 1, RTF, XLDS, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
   } else if (spw <= 2) {
-    qmv_launch_t<XF32, NMAT, 2, RTF, XLDS, NV, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
+    qmv_launch_t<XF32, NMAT, 2, RTF, XLDS, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
   } else {
     // the fused two-matrix variant is limited to K <= 8192 (two segments per wave)
-    if constexpr (NMAT == 1) qmv_launch_t<XF32, NMAT, 4, RTF, XLDS, NV, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
+    if constexpr (NMAT == 1) qmv_launch_t<XF32, NMAT, 4, RTF, XLDS, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
   }
 }
 
-template <int XF32, int NMAT, int RTF, int NV, int BITS>
+template <int XF32, int NMAT, int RTF, int NV, int BITS, bool Y3>
 inline void qmv_launch_lds(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
                            int64_t ldy, hipStream_t s) {
   const size_t part = qmv_part_bytes(K, XF32, NMAT, XF32 ? RTF : 1, NV);
-  const size_t staged = part + qmv_xs_bytes(K, XF32, R);
+  const size_t xsb = qmv_xs_bytes(K, XF32, R);
+  const size_t staged = part > xsb ? part : xsb;  // the partials reuse the staging area
   if (staged <= qmv_max_lds())
-    qmv_launch_spw<XF32, NMAT, RTF, true, NV, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, staged, s);
+    qmv_launch_spw<XF32, NMAT, RTF, true, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, staged, s);
   else
-    qmv_launch_spw<XF32, NMAT, RTF, false, NV, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, part, s);
+    qmv_launch_spw<XF32, NMAT, RTF, false, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, part, s);
 }
 
-template <int NMAT, int BITS>
+template <int NMAT, int BITS, bool Y3>
 inline void qmv_launch_bf16(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
                             int64_t ldy, hipStream_t s) {
   const int nv = qmv_nv(R);
   if (nv == 1)
-    qmv_launch_lds<0, NMAT, 1, 1, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<0, NMAT, 1, 1, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
   else if (nv == 2)
-    qmv_launch_lds<0, NMAT, 1, 2, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<0, NMAT, 1, 2, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
   else
-    qmv_launch_lds<0, NMAT, 1, 4, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<0, NMAT, 1, 4, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
 }
 
+template <int XF32, int BITS>
+inline void qmv_launch_pieces(const uint8_t* pk0, int N, int K, const void* x, int64_t ldx, int R, float* y, int64_t ldy,
+                              hipStream_t s) {
+  const int rt = qmv_row_tiles(1, R);
+  if (rt == 1)
+    qmv_launch_lds<XF32, 1, 1, 1, BITS, false>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
+  else if (rt == 2)
+    qmv_launch_lds<XF32, 1, 2, 1, BITS, false>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
+  else
+    qmv_launch_lds<XF32, 1, 4, 1, BITS, false>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
+}
+
+// xmode: 0 bf16 rows, 1 float32 rows, 2 float32 rows as three bf16 planes
+// (one matrix only). y3: the fused SwiGLU writes three bf16 planes.
 template <int BITS>
-inline void qmv_launch_bits(const uint8_t* pk0, const uint8_t* pk1, int nmat, int N, int K, const void* x, int xf32, int64_t ldx,
-                            int R, float* y, int64_t ldy, hipStream_t s) {
-  if (!xf32) {
+inline void qmv_launch_bits(const uint8_t* pk0, const uint8_t* pk1, int nmat, int N, int K, const void* x, int xmode, int64_t ldx,
+                            int R, float* y, int64_t ldy, hipStream_t s, bool y3) {
+  if (xmode == 0) {
     if (nmat == 1)
-      qmv_launch_bf16<1, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+      qmv_launch_bf16<1, BITS, false>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    else if (y3)
+      qmv_launch_bf16<2, BITS, true>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
     else
-      qmv_launch_bf16<2, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+      qmv_launch_bf16<2, BITS, false>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+  } else if (xmode == 1) {
+    qmv_launch_pieces<1, BITS>(pk0, N, K, x, ldx, R, y, ldy, s);
   } else {
-    const int rt = qmv_row_tiles(1, R);
-    if (rt == 1)
-      qmv_launch_lds<1, 1, 1, 1, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
-    else if (rt == 2)
-      qmv_launch_lds<1, 1, 2, 1, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
-    else
-      qmv_launch_lds<1, 1, 4, 1, BITS>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_pieces<2, BITS>(pk0, N, K, x, ldx, R, y, ldy, s);
   }
 }
 
 // bits: 4, 6, 8 or kFmtFp8 (checked by the caller).
-inline void qmv_launch(const uint8_t* pk0, const uint8_t* pk1, int nmat, int N, int K, const void* x, int xf32, int64_t ldx,
-                       int R, float* y, int64_t ldy, hipStream_t s, int bits = 4) {
+inline void qmv_launch(const uint8_t* pk0, const uint8_t* pk1, int nmat, int N, int K, const void* x, int xmode, int64_t ldx,
+                       int R, float* y, int64_t ldy, hipStream_t s, int bits = 4, bool y3 = false) {
   if (bits == 6)
-    qmv_launch_bits<6>(pk0, pk1, nmat, N, K, x, xf32, ldx, R, y, ldy, s);
+    qmv_launch_bits<6>(pk0, pk1, nmat, N, K, x, xmode, ldx, R, y, ldy, s, y3);
   else if (bits == 8)
-    qmv_launch_bits<8>(pk0, pk1, nmat, N, K, x, xf32, ldx, R, y, ldy, s);
+    qmv_launch_bits<8>(pk0, pk1, nmat, N, K, x, xmode, ldx, R, y, ldy, s, y3);
   else if (bits == kFmtFp8)
-    qmv_launch_bits<kFmtFp8>(pk0, pk1, nmat, N, K, x, xf32, ldx, R, y, ldy, s);
+    qmv_launch_bits<kFmtFp8>(pk0, pk1, nmat, N, K, x, xmode, ldx, R, y, ldy, s, y3);
   else
-    qmv_launch_bits<4>(pk0, pk1, nmat, N, K, x, xf32, ldx, R, y, ldy, s);
+    qmv_launch_bits<4>(pk0, pk1, nmat, N, K, x, xmode, ldx, R, y, ldy, s, y3);
 }
 
 }  // namespace q4

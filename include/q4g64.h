@@ -92,8 +92,12 @@ extern "C" {
 #define Q4_EDEVICE (-3)      /* a HIP call or kernel launch failed */
 #define Q4_EUNSUPPORTED (-4) /* valid request outside what this build implements */
 
-#define Q4_BF16 0 /* bf16 bit patterns stored as uint16 */
-#define Q4_F32 1  /* IEEE float32 */
+#define Q4_BF16 0   /* bf16 bit patterns stored as uint16 */
+#define Q4_F32 1    /* IEEE float32 */
+#define Q4_BF16X3 2 /* float32 values as three exact bf16 pieces, planes [3][R][ld] of uint16:
+                     * h = the top 16 bits of x, m = the top 16 bits of x - h, l = x - h - m
+                     * (each exact in bf16), x = h + m + l; plane p starts R * ld elements
+                     * after plane p - 1 */
 
 /* ABI version of this header (incremented on incompatible changes). */
 int q4g64_abi_version(void);
@@ -122,8 +126,11 @@ int unpack_qg64(int bits, const void* packed, int64_t N, int64_t K, uint32_t* wq
 
 /* Decode matvec over R = 1..16 rows (PR #1696, later revision, "What it adds":
  * N-row matvecs for streams that share a decode step).
- *   x: R rows of K activations, row stride ldx elements; x_dtype Q4_BF16 or
- *      Q4_F32 (float32 rows are split into three exact bf16 pieces).
+ *   x: R rows of K activations, row stride ldx elements; x_dtype Q4_BF16,
+ *      Q4_F32 (float32 rows are split into three exact bf16 pieces), or
+ *      Q4_BF16X3 (the same pieces given as planes, as qmv_w13_swiglu_x3
+ *      writes them: bit-identical results to Q4_F32 on the same values,
+ *      without the split in every workgroup).
  *   y: float32 [R][ldy], ldy >= N.
  * Row r of y is bit-identical to the result of the same call with R = 1 on
  * that row alone. Limits: K <= 16384 (bf16 x) / 16384 (float32 x). */
@@ -145,6 +152,14 @@ int qmv_w13_swiglu(const void* packed_w1, const void* packed_w3, int64_t N, int6
 /* qmv_w13_swiglu for bits = 4, 6 or 8 (both matrices packed with that bits). */
 int qmv_w13_swiglu_qg64(int bits, const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
                         int64_t ldx, int R, float* y, int64_t ldy, void* stream);
+
+/* qmv_w13_swiglu (bits = 4, 6 or 8) writing each float32 result as its three
+ * exact bf16 pieces: z3 is Q4_BF16X3 planes [3][R][ldz], ldz >= N, ldz * 2 a
+ * multiple of 16 so the planes feed qmv_rows directly (the decode FFN's w2
+ * takes the SwiGLU output unrounded). h + m + l equals the float32 result of
+ * qmv_w13_swiglu_qg64 bit for bit. */
+int qmv_w13_swiglu_x3(int bits, const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
+                      int64_t ldx, int R, uint16_t* z3, int64_t ldz, void* stream);
 
 /* Prompt-window GEMM (PR #1696, later revision, "What it adds": pgemm).
  *   x: bf16 [M][ldx], any M >= 1.
@@ -220,6 +235,8 @@ int qmv_rows_fp8b(const void* packed, int64_t N, int64_t K, const void* x, int x
                   int64_t ldy, void* stream);
 int qmv_w13_swiglu_fp8b(const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                         int R, float* y, int64_t ldy, void* stream);
+int qmv_w13_swiglu_x3_fp8b(const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                           int R, uint16_t* z3, int64_t ldz, void* stream);
 int qmm_window_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                     int64_t M, void* y, int y_dtype, int64_t ldy, void* stream);
 int qmm_cut_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,

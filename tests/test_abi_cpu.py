@@ -103,6 +103,31 @@ def test_strides_and_dtypes_rejected():
     assert rc == q4.Q4_EINVAL
 
 
+def test_planes_arguments_rejected():
+    """Q4_BF16X3 planes: the planes dtype is accepted only as a decode input, with bf16 stride rules; the planes
+    output of the fused SwiGLU checks its width, pointer and 16-byte row alignment."""
+    rc, _ = _rc("qmv_rows", FAKE, 512, 256, FAKE, 3, 256, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EINVAL
+    rc, _ = _rc("qmv_rows", FAKE, 512, 256, FAKE, q4.Q4_BF16X3, 260, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EALIGN  # 520-byte rows
+    rc, _ = _rc("qmv_rows_qg64", 8, FAKE, 512, 256, FAKE, q4.Q4_BF16X3, 128, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EINVAL  # ldx < K
+    rc, _ = _rc("qmm_window", FAKE, None, 512, 256, FAKE, 256, 4, FAKE, q4.Q4_BF16X3, 512, None)
+    assert rc == q4.Q4_EINVAL  # not a window output type
+    rc, _ = _rc("qmv_w13_swiglu_x3", 5, FAKE, FAKE, 1024, 256, FAKE, 256, 1, FAKE, 1024, None)
+    assert rc == q4.Q4_EINVAL
+    rc, msg = _rc("qmv_w13_swiglu_x3", 4, FAKE, FAKE, 1024, 256, FAKE, 256, 1, FAKE, 1000, None)
+    assert rc == q4.Q4_EINVAL and "ldz" in msg
+    rc, msg = _rc("qmv_w13_swiglu_x3", 4, FAKE, FAKE, 1024, 256, FAKE, 256, 1, FAKE, 1028, None)
+    assert rc == q4.Q4_EALIGN and "ldz" in msg
+    rc, _ = _rc("qmv_w13_swiglu_x3", 6, FAKE, FAKE, 1024, 256, FAKE, 256, 1, None, 1024, None)
+    assert rc == q4.Q4_EALIGN
+    rc, _ = _rc("qmv_w13_swiglu_x3_fp8b", FAKE, FAKE, 1024, 256, FAKE, 256, 1, FAKE + 2, 1024, None)
+    assert rc == q4.Q4_EALIGN
+    rc, _ = _rc("qmv_w13_swiglu_x3_fp8b", FAKE, FAKE, 1024, 256, FAKE, 256, 17, FAKE, 1024, None)
+    assert rc == q4.Q4_EINVAL
+
+
 def test_window_counts_rejected():
     rc, _ = _rc("qmm_window", FAKE, None, 512, 256, FAKE, 256, 0, FAKE, q4.Q4_F32, 512, None)
     assert rc == q4.Q4_EINVAL
