@@ -60,7 +60,8 @@ struct QmvWeights {
   u32x2 sbw[SPW][NMAT][kSegPairs];
 };
 
-// Issue every weight load of segments seg0 + j * step (j < SPW). Pair indices
+// Issue every weight load of segments seg0 + j * step (j < SPW), with the
+// streaming cache policy (each weight is read once per launch). Pair indices
 // past the matrix are clamped to its last pair (those values are never
 // used). Lanes with on == false read past the buffer's end, which the
 // hardware answers with zeros and no memory access: the loads stay
@@ -81,10 +82,10 @@ __device__ __forceinline__ void qmv_issue_weights(QmvWeights<NMAT, SPW, BITS>& w
       p = p < P ? p : P - 1;
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
-        w.cw[j][m][pp].a = buf_load16(cres[m], cv, (uint32_t)p * kPcb);
-        if constexpr (BITS == 6) w.cw[j][m][pp].b = buf_load8(cres[m], cv8, (uint32_t)p * kPcb + 1024u);
-        if constexpr (code_bits(BITS) == 8) w.cw[j][m][pp].b = buf_load16(cres[m], cv, (uint32_t)p * kPcb + 1024u);
-        w.sbw[j][m][pp] = buf_load8(sres[m], sv, (uint32_t)p * kPairSbBytes);
+        w.cw[j][m][pp].a = buf_load16_nt(cres[m], cv, (uint32_t)p * kPcb);
+        if constexpr (BITS == 6) w.cw[j][m][pp].b = buf_load8_nt(cres[m], cv8, (uint32_t)p * kPcb + 1024u);
+        if constexpr (code_bits(BITS) == 8) w.cw[j][m][pp].b = buf_load16_nt(cres[m], cv, (uint32_t)p * kPcb + 1024u);
+        w.sbw[j][m][pp] = buf_load8_nt(sres[m], sv, (uint32_t)p * kPairSbBytes);
       }
     }
   }
