@@ -168,11 +168,12 @@ __device__ __forceinline__ int qmv_part_index(int seg, int m, int rt, int v, int
   return (((seg * NMAT + m) * kRT + rt) * kPerLane + v) * 64 + lane;
 }
 
-// The segments' partials added in ascending order, eight reads in flight at a
-// time: every read of a batch is issued (indices clamped to the last
-// segment) before its adds, and the adds past the last segment are dropped
-// by a select rather than a branch, so the compiler cannot sink the reads
-// into the adds (which costs one LDS round trip per segment).
+// The segments' partials added in ascending order, a batch of reads in flight
+// at a time (8 to 32 segments, by register room): every read of a batch is
+// issued (indices clamped to the last segment) before its adds, and the adds
+// past the last segment are dropped by a select rather than a branch, so the
+// compiler cannot sink the reads into the adds (which costs one LDS round
+// trip per segment).
 template <int NMAT, int kRT, int kPerLane>
 __device__ __forceinline__ void qmv_ordered_sum(float (&tot)[NMAT][kRT][kPerLane], const float* part, int nseg, int lane) {
 #pragma unroll
@@ -181,7 +182,9 @@ __device__ __forceinline__ void qmv_ordered_sum(float (&tot)[NMAT][kRT][kPerLane
     for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
       for (int v = 0; v < kPerLane; ++v) tot[m][rt][v] = part[qmv_part_index<NMAT, kRT, kPerLane>(0, m, rt, v, lane)];
-  constexpr int kSumBatch = 8;
+  // as many reads in flight as 32 registers hold (at least 8)
+  constexpr int kVals = NMAT * kRT * kPerLane;
+  constexpr int kSumBatch = kVals >= 4 ? 8 : 32 / kVals;
   for (int seg0 = 1; seg0 < nseg; seg0 += kSumBatch) {
     float pv[kSumBatch][NMAT][kRT][kPerLane];
 #pragma unroll
