@@ -87,7 +87,7 @@ def cpu_baseline(d, budget_s=12.0):
             break
     step = float(np.median(times))
     nbytes = decode_step_bytes(d)
-    return {
+    out = {
         "value": nbytes / step / 1e9,
         "unit": "GB/s",
         "cores": int(threads),
@@ -95,6 +95,26 @@ def cpu_baseline(d, budget_s=12.0):
         "sample": f"{len(times)} full decode FFN steps (w1/w3 8192x2048 + SwiGLU, w2 2048x8192, 1 row) in numpy float64; "
         f"median {step * 1e3:.1f} ms per step",
     }
+    # the same with the BLAS pool limited to one thread
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        return out
+    times1 = []
+    with threadpool_limits(limits=1):
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            a = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, x)
+            c = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, x)
+            oracle.matmul_rows(w2.wq, w2.scales, w2.biases, oracle.swiglu(a, c))
+            times1.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start > budget_s or len(times1) >= 3:
+                break
+    step1 = float(np.median(times1))
+    out["one_core"] = {"value": nbytes / step1 / 1e9, "unit": "GB/s", "cores": 1,
+                       "sample": f"{len(times1)} steps, median {step1 * 1e3:.1f} ms per step"}
+    return out
 
 
 PROFILES = os.path.join(ROOT, "profiles")
