@@ -119,6 +119,7 @@ def cpu_baseline(d, budget_s=12.0):
 
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["bit_weight_only_q4g64_amd/csrc/common.h", "bit_weight_only_q4g64_amd/csrc/qmv.h",
+                  "bit_weight_only_q4g64_amd/csrc/pgemm_narrow.h",
                   "bit_weight_only_q4g64_amd/csrc/pgemm.h", "bit_weight_only_q4g64_amd/csrc/api.hip"]
 
 

@@ -11,6 +11,7 @@
 #include "ffn.h"
 #include "pack.h"
 #include "pgemm.h"
+#include "pgemm_narrow.h"
 #include "qmv.h"
 #include "rope.h"
 
@@ -206,6 +207,10 @@ void pgemm_launch_bits(bool swiglu, bool obf16, dim3 grid, dim3 block, hipStream
   }
 }
 
+// Below this many 256-column workgroups a window runs on the 64-column
+// workgroups of pgemm_narrow_kernel (4-bit codes; the same bits per row).
+constexpr int64_t kNarrowBelow = 256;
+
 int qmm_window_impl(const char* fn, int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x,
                     int64_t ldx, int64_t M, void* y, int y_dtype, int64_t ldy, hipStream_t s) {
   using namespace q4;
@@ -218,6 +223,19 @@ int qmm_window_impl(const char* fn, int bits, const void* packed_a, const void* 
   const uint8_t* a = (const uint8_t*)packed_a;
   const uint8_t* b = swiglu ? (const uint8_t*)packed_b : a;
   const int n = (int)N, k = (int)K, m = (int)M;
+  if (bits == 4 && blocks < kNarrowBelow) {
+    const int cols = pgemm_narrow_cols(swiglu);
+    const int nb = (n + cols - 1) / cols;
+    const dim3 ngrid((unsigned)((int64_t)nb * mblk));
+    if (swiglu) {
+      if (obf16) hipLaunchKernelGGL((pgemm_narrow_kernel<true, true>), ngrid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
+      else hipLaunchKernelGGL((pgemm_narrow_kernel<true, false>), ngrid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
+    } else {
+      if (obf16) hipLaunchKernelGGL((pgemm_narrow_kernel<false, true>), ngrid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
+      else hipLaunchKernelGGL((pgemm_narrow_kernel<false, false>), ngrid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
+    }
+    return launched(fn);
+  }
   if (bits == 6)
     pgemm_launch_bits<6>(swiglu, obf16, grid, block, s, a, b, n, k, x, ldx, m, y, ldy, nblk, mblk);
   else if (bits == 8)
@@ -620,9 +638,10 @@ int qmv_window_costs(int bits, const void* packed, int64_t N, int64_t K, const v
   if (us_out == nullptr) return fail(Q4_EINVAL, "%s: us_out is NULL", fn);
   if (reps < 1 || reps > 10000) return fail(Q4_EINVAL, "%s: reps=%d is outside 1..10000", fn, reps);
   hipStream_t s = (hipStream_t)stream;
-  // validates every argument at the largest row count (and warms the kernels up)
-  for (int i = 4; i >= 0; --i)
-    if (int rc = qmv_rows_impl(fn, bits, packed, N, K, x, x_dtype, ldx, kCostRows[i], y, ldy, s)) return rc;
+  // validates every argument at the largest row count, and warms every kernel up twice
+  for (int rep = 0; rep < 2; ++rep)
+    for (int i = 4; i >= 0; --i)
+      if (int rc = qmv_rows_impl(fn, bits, packed, N, K, x, x_dtype, ldx, kCostRows[i], y, ldy, s)) return rc;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
     if (e0) (void)hipEventDestroy(e0);
@@ -646,8 +665,10 @@ int qmv_window_costs(int bits, const void* packed, int64_t N, int64_t K, const v
 
 float qmv_window_cost(const float* us, int R) {
   if (us == nullptr || R < 1 || R > 16) return NAN;
+  for (int i = 0; i < 5; ++i)
+    if (R == kCostRows[i]) return us[i];  // a timed row count reads back its own entry
   for (int i = 0; i < 4; ++i) {
-    if (R <= kCostRows[i + 1]) {
+    if (R < kCostRows[i + 1]) {
       const float t = (float)(R - kCostRows[i]) / (float)(kCostRows[i + 1] - kCostRows[i]);
       return us[i] + t * (us[i + 1] - us[i]);
     }

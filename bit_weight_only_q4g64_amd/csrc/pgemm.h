@@ -113,8 +113,9 @@ __device__ __forceinline__ uint32_t lds_addr(T* p) {
 // LDS accesses, then meet the workgroup barrier.
 template <int n>
 __device__ __forceinline__ void dma_wait_barrier() {
-  static_assert(n == 0 || n == 6, "wait depths used by the pipeline");
+  static_assert(n == 0 || n == 2 || n == 6, "wait depths used by the pipelines");
   if constexpr (n == 6) asm volatile("s_waitcnt vmcnt(6)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (n == 2) asm volatile("s_waitcnt vmcnt(2)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 

@@ -10,6 +10,7 @@ import re
 import shutil
 import subprocess
 
+import numpy as np
 import pytest
 
 import bit_weight_only_q4g64_amd as q4
@@ -228,6 +229,10 @@ def test_window_cost_interpolation():
     for R, c in zip((1, 2, 4, 8, 16), us):
         assert q4.window_cost(us, R) == c
     assert q4.window_cost(us, 3) == 7.0
+    # the timed row counts read back exactly even next to a much larger entry
+    far = [203.853515625, 3.8175501823425293, 4.233449935913086, 5.397349834442139, 9.718850135803223]
+    for R, c in zip(q4.WINDOW_COST_ROWS, far):
+        assert q4.window_cost(far, R) == np.float32(c)
     assert q4.window_cost(us, 6) == 8.5
     assert q4.window_cost(us, 12) == 11.0
     assert abs(q4.window_cost(us, 5) - 8.25) < 1e-6
