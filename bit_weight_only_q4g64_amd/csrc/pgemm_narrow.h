@@ -153,21 +153,6 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const ui
       sc[s] = bf16_lo(w[s]);
     }
 
-    // activation sums of this wave's 32 rows (16 x 16 tiles)
-    {
-      const int i = lane & 15, kc = lane >> 4;
-      float* sw = ssum + ((g / kPgemmChunk) & 1) * kPgemmRows * kPgemmChunk + gg;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int row = rbase + 16 * u + i;
-        const bf16x8 xa0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc)));
-        const bf16x8 xa1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc + 4)));
-        f32x4 S = mfma16(ones, xa0, f32x4{0.f, 0.f, 0.f, 0.f});
-        S = mfma16(ones, xa1, S);
-        if (kc == 0) sw[row * kPgemmChunk] = S[0];
-      }
-    }
-
     bf16x8 q[kPgemmNT][4];
 #pragma unroll
     for (int s = 0; s < kPgemmNT; ++s) {
@@ -191,6 +176,21 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const ui
         for (int ks = 1; ks < 4; ++ks) Pm = mfma32(xa[ks], q[s][ks], Pm);
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[s][r] = __builtin_fmaf(sc[s], Pm[r], acc[s][r]);
+      }
+    }
+
+    // activation sums of this wave's 32 rows (16 x 16 tiles)
+    {
+      const int i = lane & 15, kc = lane >> 4;
+      float* sw = ssum + ((g / kPgemmChunk) & 1) * kPgemmRows * kPgemmChunk + gg;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int row = rbase + 16 * u + i;
+        const bf16x8 xa0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc)));
+        const bf16x8 xa1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc + 4)));
+        f32x4 S = mfma16(ones, xa0, f32x4{0.f, 0.f, 0.f, 0.f});
+        S = mfma16(ones, xa1, S);
+        if (kc == 0) sw[row * kPgemmChunk] = S[0];
       }
     }
 
