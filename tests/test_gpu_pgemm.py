@@ -134,3 +134,23 @@ def test_window_and_decode_orders_differ(c3):
     a_win = bits32(q4.qmm_window(c3["p1"], None, w1.N, w1.K, xs))
     a_dec = bits32(q4.qmv_rows(c3["p1"], w1.N, w1.K, xs))
     assert not np.array_equal(a_win, a_dec)
+
+
+@pytest.mark.parametrize("rows", [384, 385])
+def test_c3_windows_at_the_short_window_boundary(c3, c3_whole, rows):
+    """w1/w3 8192 x 2048 with the SwiGLU epilogue: a 384-row window is the
+    last one computed on the 64-column workgroups of short windows (3 row
+    blocks x 64 column blocks of 128 x 256 would be 192 < 256 workgroups),
+    385 rows the first on the 128 x 256 workgroups. Either way every row is
+    bit-identical to the same row of the whole 1000-row prompt. The plain
+    (no SwiGLU) window of w1 runs on the short-window workgroups at both
+    sizes (at most 4 x 32 wide workgroups) and the whole prompt on the wide
+    ones (8 x 32): its rows agree too."""
+    w1 = c3["w1"]
+    say(f"c3 window of {rows} rows at the short-window boundary")
+    z = q4.qmm_window(c3["p1"], c3["p3"], w1.N, w1.K, c3["xd"][:rows])
+    a = q4.qmm_window(c3["p1"], None, w1.N, w1.K, c3["xd"][:rows])
+    a_whole = q4.qmm_window(c3["p1"], None, w1.N, w1.K, c3["xd"])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits32(z), bits32(c3_whole)[:rows])
+    assert np.array_equal(bits32(a), bits32(a_whole)[:rows])
