@@ -611,12 +611,36 @@ def bench_pgemm(dev, reps=10):
     t = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3  # s
     flops = 2.0 * 8192 * (2 * 8192) * 2048
     tf = flops / t.mean() / 1e12
+
+    # the same prompt through the window driver in 128-row windows (64 short
+    # windows, one launch each), checked bit for bit against the whole window
+    log("prompt GEMM: the same 8192 rows as 64 windows of 128 rows (qmm_cut)")
+    cut = [128] * 64
+    zc = torch.empty_like(z)
+    for _ in range(2):
+        q4.qmm_cut(p1, p3, 8192, 2048, x, cut, y=zc)
+    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in evc:
+        e[0].record()
+        q4.qmm_cut(p1, p3, 8192, 2048, x, cut, y=zc)
+        e[1].record()
+    torch.cuda.synchronize()
+    tc = np.array([e[0].elapsed_time(e[1]) for e in evc]) * 1e-3
+    same = bool(torch.equal(zc.view(torch.int16), z.view(torch.int16)))
     return {
         "workload": "qmm_window w1/w3 8192x2048 + SwiGLU, M=8192 prompt rows, bf16 out (seed 4 shapes)",
         "avg_ms": round(float(t.mean() * 1e3), 4),
         "TFLOP/s": round(tf, 2),
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / BF16_PEAK_TFLOPS, 4)},
+        "windows_128": {
+            "workload": "the same prompt through qmm_cut in 64 windows of 128 rows",
+            "avg_ms": round(float(tc.mean() * 1e3), 4),
+            "us_per_window": round(float(tc.mean() * 1e6 / 64), 2),
+            "TFLOP/s": round(flops / tc.mean() / 1e12, 2),
+            "bits_equal_whole_window": same,
+        },
     }
 
 
