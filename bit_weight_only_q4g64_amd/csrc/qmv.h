@@ -99,10 +99,24 @@ __device__ __forceinline__ void qmv_issue_weights(QmvWeights<NMAT, SPW, BITS>& w
 //   acc = fma(s_g, P, fma(b_g, S, acc))
 // with float32 rows combining their three pieces in-lane first. Block FP8
 // has no bias: acc = fma(s_g, P, acc) with s_g the float32 block scale.
-template <int XF32, int NMAT, int kRT, int kPerLane, int BITS, typename XF>
+// AHEAD (fragments read from memory rather than LDS): every fragment of a
+// group is requested before its first use and the next group's during this
+// one, so a wave waits for one memory round trip per segment, not one per
+// row tile and group.
+template <int XF32, int NMAT, int kRT, int kPerLane, bool AHEAD = false, int BITS, typename XF>
 __device__ __forceinline__ void qmv_fold_segment(float (&acc)[NMAT][kRT][kPerLane], const CodeWords<BITS> (&cw)[NMAT][kSegPairs],
                                                  const u32x2 (&sbw)[NMAT][kSegPairs], int g0, int G, const XF& xfrag) {
   const bf16x8 ones = ones_bf16x8();
+  bf16x8 xn[kRT][2];  // AHEAD: the fragments of the next group
+  if constexpr (AHEAD) {
+    if (g0 < G) {
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        xn[rt][0] = xfrag(rt, g0, 0);
+        xn[rt][1] = xfrag(rt, g0, 1);
+      }
+    }
+  }
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -114,6 +128,21 @@ __device__ __forceinline__ void qmv_fold_segment(float (&acc)[NMAT][kRT][kPerLan
     const int g = g0 + gg;
     if (g >= G) break;
     const int pp = gg >> 1, gh = gg & 1;
+    bf16x8 xc[kRT][2];
+    if constexpr (AHEAD) {
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        xc[rt][0] = xn[rt][0];
+        xc[rt][1] = xn[rt][1];
+      }
+      if (gg + 1 < kSegGroups && g + 1 < G) {
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          xn[rt][0] = xfrag(rt, g + 1, 0);
+          xn[rt][1] = xfrag(rt, g + 1, 1);
+        }
+      }
+    }
     bf16x8 q[NMAT][2];
     float sc[NMAT], bs[NMAT];
 #pragma unroll
@@ -131,7 +160,7 @@ __device__ __forceinline__ void qmv_fold_segment(float (&acc)[NMAT][kRT][kPerLan
     }
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
-      const bf16x8 xa0 = xfrag(rt, g, 0), xa1 = xfrag(rt, g, 1);
+      const bf16x8 xa0 = AHEAD ? xc[rt][0] : xfrag(rt, g, 0), xa1 = AHEAD ? xc[rt][1] : xfrag(rt, g, 1);
       f32x4 S = {0.f, 0.f, 0.f, 0.f};
       if constexpr (BITS != kFmtFp8) {
         S = mfma16(xa0, ones, S);
@@ -374,6 +403,11 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
     }
   };
 
+  // fragments read from memory are requested a group ahead where the
+  // registers allow (the weights of at most 8 code bits x segments x
+  // matrices per lane are held; more spills)
+  constexpr bool kAhead = !XLDS && SPW * NMAT * code_bits(BITS) <= 8;
+
   // 4) compute, one segment after another; the partials wait in registers
   //    until every wave is past its last activation read
   float keep[SPW][NMAT][kRT][kPerLane];
@@ -381,7 +415,7 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   for (int j = 0; j < SPW; ++j) {
     const int seg = wave + j * nwaves;
     if (seg >= nseg) break;
-    qmv_fold_segment<XF32, NMAT, kRT, kPerLane>(keep[j], wts.cw[j], wts.sbw[j], seg * kSegGroups, G, xfrag);
+    qmv_fold_segment<XF32, NMAT, kRT, kPerLane, kAhead>(keep[j], wts.cw[j], wts.sbw[j], seg * kSegGroups, G, xfrag);
   }
   if constexpr (XLDS) __syncthreads();
 #pragma unroll
