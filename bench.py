@@ -489,6 +489,7 @@ def bench_rows(dev, K, W, pool_mb):
     z = torch.empty((16, w1.N), dtype=torch.float32, device=dev)
     y = torch.empty((16, w2.N), dtype=torch.float32, device=dev)
     z3s = {R: torch.empty((3, R, w1.N), dtype=torch.bfloat16, device=dev) for R in (1, 2, 4, 8, 16)}
+    z3ts = {R: q4.TiledPlanes.empty(R, w1.N, dev) for R in (1, 2, 4, 8, 16)}
     out = {}
     for R in (1, 2, 4, 8, 16):
         z3 = z3s[R]
@@ -503,21 +504,33 @@ def bench_rows(dev, K, W, pool_mb):
             q4.qmv_w13_swiglu(p1, p3, w1.N, w1.K, xs[:R], y=z3, planes=True)
             q4.qmv_rows(p2, w2.N, w2.K, z3, y=y[:R])
 
+        z3t = z3ts[R]
+
+        def step3t(i):
+            p1, p3, p2 = pool[i % ncopies]
+            q4.qmv_w13_swiglu(p1, p3, w1.N, w1.K, xs[:R], y=z3t, planes="tiled")
+            q4.qmv_rows(p2, w2.N, w2.K, z3t, y=y[:R])
+
         us = batch_average_us(torch, step, W, K)
         us3 = batch_average_us(torch, step3, W, K)
+        us3t = batch_average_us(torch, step3t, W, K)
         t13 = batch_average_us(torch, lambda i: q4.qmv_w13_swiglu(pool[i % ncopies][0], pool[i % ncopies][1], w1.N, w1.K, xs[:R],
                                                                   y=z[:R]), W, K)
         t2 = batch_average_us(torch, lambda i: q4.qmv_rows(pool[i % ncopies][2], w2.N, w2.K, z[:R], y=y[:R]), W, K)
         t2p = batch_average_us(torch, lambda i: q4.qmv_rows(pool[i % ncopies][2], w2.N, w2.K, z3, y=y[:R]), W, K)
+        t2t = batch_average_us(torch, lambda i: q4.qmv_rows(pool[i % ncopies][2], w2.N, w2.K, z3t, y=y[:R]), W, K)
         b = 2 * qbytes(w1.N, w1.K) + qbytes(w2.N, w2.K) + R * (w1.K * 2 + w1.N * 4 + w2.K * 4 + w2.N * 4)
         out[f"R{R}"] = {"us_per_step": round(us, 3), "rows_per_s": round(R / (us * 1e-6), 1), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
                         "qmv_w13_swiglu_us": round(t13, 3), "qmv_rows_w2_f32x_us": round(t2, 3),
                         "planes_us_per_step": round(us3, 3), "planes_rows_per_s": round(R / (us3 * 1e-6), 1),
-                        "qmv_rows_w2_planes_us": round(t2p, 3)}
+                        "qmv_rows_w2_planes_us": round(t2p, 3),
+                        "tiled_us_per_step": round(us3t, 3), "tiled_rows_per_s": round(R / (us3t * 1e-6), 1),
+                        "qmv_rows_w2_tiled_us": round(t2t, 3)}
     del pool, base
     torch.cuda.empty_cache()
     out["workload"] = ("decode FFN step (w1/w3 8192x2048 + SwiGLU, w2 2048x8192, q4g64) with R bf16 rows, graph of K steps; "
-                       "planes_*: the SwiGLU output handed to w2 as its three exact bf16 planes instead of float32 (same bits)")
+                       "planes_*: the SwiGLU output handed to w2 as its three exact bf16 planes instead of float32 (same bits); "
+                       "tiled_*: the same planes in the matvec's fragment order (Q4_BF16X3T, same bits)")
     return out
 
 

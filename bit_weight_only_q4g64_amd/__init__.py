@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4g64.so")
 
 Q4_OK, Q4_EINVAL, Q4_EALIGN, Q4_EDEVICE, Q4_EUNSUPPORTED = 0, -1, -2, -3, -4
-Q4_BF16, Q4_F32, Q4_BF16X3 = 0, 1, 2
+Q4_BF16, Q4_F32, Q4_BF16X3, Q4_BF16X3T = 0, 1, 2, 3
 
 _lib = None
 
@@ -29,6 +29,7 @@ _P = ctypes.c_void_p
 _SIGNATURES = {
     "q4g64_abi_version": (ctypes.c_int, []),
     "q4g64_packed_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "q4g64_x3t_bytes": (ctypes.c_size_t, [_I64, ctypes.c_int]),
     "pack_q4g64": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P]),
     "unpack_q4g64": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
     "qmv_rows": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, _I64, ctypes.c_int, _P, _I64, _P]),
@@ -41,6 +42,7 @@ _SIGNATURES = {
     "qmv_rows_qg64": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, ctypes.c_int, _I64, ctypes.c_int, _P, _I64, _P]),
     "qmv_w13_swiglu_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
     "qmv_w13_swiglu_x3": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
+    "qmv_w13_swiglu_x3t": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _P]),
     "qmm_window_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P]),
     "qmm_cut_qg64": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _I64, _P]),
     "fp8b_packed_bytes": (ctypes.c_size_t, [_I64, _I64]),
@@ -49,6 +51,7 @@ _SIGNATURES = {
     "qmv_rows_fp8b": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, _I64, ctypes.c_int, _P, _I64, _P]),
     "qmv_w13_swiglu_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
     "qmv_w13_swiglu_x3_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P]),
+    "qmv_w13_swiglu_x3t_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, ctypes.c_int, _P, _P]),
     "qmm_window_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P]),
     "qmm_cut_fp8b": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _I64, _P]),
     "rope_kv_store": (ctypes.c_int, [_P, _I64, ctypes.c_int, _P, _P]),
@@ -113,9 +116,38 @@ def _planes_ld(t: torch.Tensor, name: str) -> int:
     return t.stride(1)
 
 
-def _x_arg(x: torch.Tensor):
-    """(x_dtype, ldx, R) of decode activations: bf16 or float32 rows [R][ldx], or the three bf16 planes of float32
-    rows [3][R][ldx] (Q4_BF16X3, as qmv_w13_swiglu(..., planes=True) writes them)."""
+class TiledPlanes:
+    """R rows of K float32 activations as their three exact bf16 pieces in the
+    matvec's fragment order (Q4_BF16X3T), as qmv_w13_swiglu(..., planes="tiled")
+    writes them: `data` is a flat bfloat16 tensor of x3t_bytes(K, R) / 2 values."""
+
+    def __init__(self, data: torch.Tensor, rows: int, k: int):
+        if data.dtype != torch.bfloat16 or not data.is_contiguous() or data.numel() * 2 < x3t_bytes(k, rows):
+            raise ValueError("data must be a contiguous bfloat16 tensor of at least x3t_bytes(K, R) bytes")
+        self.data, self.rows, self.k = data, rows, k
+
+    @staticmethod
+    def empty(rows: int, k: int, device) -> "TiledPlanes":
+        n = x3t_bytes(k, rows)
+        if n == 0:
+            raise ValueError(f"no fragment-ordered planes for K={k}, R={rows}")
+        return TiledPlanes(torch.empty(n // 2, dtype=torch.bfloat16, device=device), rows, k)
+
+
+def x3t_bytes(K: int, R: int) -> int:
+    """Bytes of R rows of K activations as Q4_BF16X3T (0 if invalid)."""
+    return int(lib().q4g64_x3t_bytes(K, R))
+
+
+def _x_ptr(x) -> int:
+    return x.data.data_ptr() if isinstance(x, TiledPlanes) else x.data_ptr()
+
+
+def _x_arg(x):
+    """(x_dtype, ldx, R) of decode activations: bf16 or float32 rows [R][ldx], the three bf16 planes of float32
+    rows [3][R][ldx] (Q4_BF16X3, as qmv_w13_swiglu(..., planes=True) writes them), or TiledPlanes (Q4_BF16X3T)."""
+    if isinstance(x, TiledPlanes):
+        return Q4_BF16X3T, x.k, x.rows
     if x.dim() == 3:
         return Q4_BF16X3, _planes_ld(x, "x"), x.shape[1]
     if x.dtype == torch.bfloat16:
@@ -170,33 +202,41 @@ def unpack(packed: torch.Tensor, N: int, K: int, bits: int = 4):
 
 
 def qmv_rows(packed: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None, bits: int = 4) -> torch.Tensor:
-    """y[r] = W x[r] for the R (1..16) rows of x (bf16 or float32 [R][ld], or float32 as bf16 planes [3][R][ld]);
-    W has 4-, 6- or 8-bit codes."""
+    """y[r] = W x[r] for the R (1..16) rows of x (bf16 or float32 [R][ld], float32 as bf16 planes [3][R][ld], or
+    TiledPlanes); W has 4-, 6- or 8-bit codes."""
     _dev(packed, "packed")
-    _dev(x, "x")
+    _dev(x.data if isinstance(x, TiledPlanes) else x, "x")
     xd, ldx, R = _x_arg(x)
+    dev = x.data.device if isinstance(x, TiledPlanes) else x.device
     if y is None:
-        y = torch.empty((R, N), dtype=torch.float32, device=x.device)
+        y = torch.empty((R, N), dtype=torch.float32, device=dev)
     if y.dtype != torch.float32 or y.shape[0] < R:
         raise ValueError("y must be float32 with at least R rows")
     if bits == 4:
-        _check("qmv_rows", lib().qmv_rows(packed.data_ptr(), N, K, x.data_ptr(), xd, ldx, R, y.data_ptr(), _rowmajor(y, "y"), _stream()))
+        _check("qmv_rows", lib().qmv_rows(packed.data_ptr(), N, K, _x_ptr(x), xd, ldx, R, y.data_ptr(), _rowmajor(y, "y"), _stream()))
     else:
         _check("qmv_rows_qg64",
-               lib().qmv_rows_qg64(bits, packed.data_ptr(), N, K, x.data_ptr(), xd, ldx, R, y.data_ptr(), _rowmajor(y, "y"), _stream()))
+               lib().qmv_rows_qg64(bits, packed.data_ptr(), N, K, _x_ptr(x), xd, ldx, R, y.data_ptr(), _rowmajor(y, "y"), _stream()))
     return y
 
 
 def qmv_w13_swiglu(p1: torch.Tensor, p3: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None,
-                   bits: int = 4, planes: bool = False) -> torch.Tensor:
+                   bits: int = 4, planes=False):
     """y[r] = silu(W1 x[r]) * (W3 x[r]) for the 1..16 bf16 rows of x; W1, W3 have 4-, 6- or 8-bit codes.
-    planes=True: y is written as the three exact bf16 pieces of each float32 result, planes [3][R][N]."""
+    planes=True: y is written as the three exact bf16 pieces of each float32 result, planes [3][R][N];
+    planes="tiled": the same pieces in fragment order (returns TiledPlanes)."""
     _dev(p1, "packed_w1")
     _dev(p3, "packed_w3")
     _dev(x, "x")
     if x.dtype != torch.bfloat16:
         raise ValueError("x must be bfloat16")
     R = x.shape[0]
+    if planes == "tiled":
+        if y is None:
+            y = TiledPlanes.empty(R, N, x.device)
+        _check("qmv_w13_swiglu_x3t", lib().qmv_w13_swiglu_x3t(bits, p1.data_ptr(), p3.data_ptr(), N, K, x.data_ptr(), _rowmajor(x, "x"),
+                                                              R, y.data.data_ptr(), _stream()))
+        return y
     if planes:
         if y is None:
             y = torch.empty((3, R, N), dtype=torch.bfloat16, device=x.device)
@@ -380,20 +420,20 @@ def unpack_fp8b(packed: torch.Tensor, N: int, K: int):
     return w8, sc
 
 
-def qmv_rows_fp8b(packed: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
-    """y[r] = W x[r] for the 1..16 rows of x (bf16 or float32), W block FP8."""
+def qmv_rows_fp8b(packed: torch.Tensor, N: int, K: int, x, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[r] = W x[r] for the 1..16 rows of x (as qmv_rows), W block FP8."""
     _dev(packed, "packed")
-    _dev(x, "x")
+    _dev(x.data if isinstance(x, TiledPlanes) else x, "x")
     xd, ldx, R = _x_arg(x)
     if y is None:
-        y = torch.empty((R, N), dtype=torch.float32, device=x.device)
-    _check("qmv_rows_fp8b", lib().qmv_rows_fp8b(packed.data_ptr(), N, K, x.data_ptr(), xd, ldx, R, y.data_ptr(),
+        y = torch.empty((R, N), dtype=torch.float32, device=x.data.device if isinstance(x, TiledPlanes) else x.device)
+    _check("qmv_rows_fp8b", lib().qmv_rows_fp8b(packed.data_ptr(), N, K, _x_ptr(x), xd, ldx, R, y.data_ptr(),
                                                 _rowmajor(y, "y"), _stream()))
     return y
 
 
 def qmv_w13_swiglu_fp8b(p1: torch.Tensor, p3: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tensor | None = None,
-                        planes: bool = False) -> torch.Tensor:
+                        planes=False):
     """y[r] = silu(W1 x[r]) * (W3 x[r]) for the 1..16 bf16 rows of x, W1 and W3 block FP8 (planes: as qmv_w13_swiglu)."""
     _dev(p1, "packed_w1")
     _dev(p3, "packed_w3")
@@ -401,6 +441,12 @@ def qmv_w13_swiglu_fp8b(p1: torch.Tensor, p3: torch.Tensor, N: int, K: int, x: t
     if x.dtype != torch.bfloat16:
         raise ValueError("x must be bfloat16")
     R = x.shape[0]
+    if planes == "tiled":
+        if y is None:
+            y = TiledPlanes.empty(R, N, x.device)
+        _check("qmv_w13_swiglu_x3t_fp8b", lib().qmv_w13_swiglu_x3t_fp8b(p1.data_ptr(), p3.data_ptr(), N, K, x.data_ptr(),
+                                                                        _rowmajor(x, "x"), R, y.data.data_ptr(), _stream()))
+        return y
     if planes:
         if y is None:
             y = torch.empty((3, R, N), dtype=torch.bfloat16, device=x.device)

@@ -68,9 +68,12 @@ unsigned grid_for(int64_t total, int block) {
 }
 
 int check_x(const char* fn, const void* x, int x_dtype, int64_t ldx, int64_t K) {
-  if (x_dtype != Q4_BF16 && x_dtype != Q4_F32 && x_dtype != Q4_BF16X3)
-    return fail(Q4_EINVAL, "%s: x_dtype %d is not Q4_BF16, Q4_F32 or Q4_BF16X3", fn, x_dtype);
+  if (x_dtype != Q4_BF16 && x_dtype != Q4_F32 && x_dtype != Q4_BF16X3 && x_dtype != Q4_BF16X3T)
+    return fail(Q4_EINVAL, "%s: x_dtype %d is not Q4_BF16, Q4_F32, Q4_BF16X3 or Q4_BF16X3T", fn, x_dtype);
   if (int rc = check_ptr(fn, "x", x, 16)) return rc;
+  if (x_dtype == Q4_BF16X3T && ldx != K)
+    return fail(Q4_EINVAL, "%s: fragment-ordered planes have no row stride (ldx=%lld must equal K=%lld)", fn, (long long)ldx,
+                (long long)K);
   if (ldx < K) return fail(Q4_EINVAL, "%s: ldx=%lld < K=%lld", fn, (long long)ldx, (long long)K);
   const int64_t es = x_dtype == Q4_F32 ? 4 : 2;
   if ((ldx * es) % 16 != 0) return fail(Q4_EALIGN, "%s: ldx=%lld elements does not keep rows 16-byte aligned", fn, (long long)ldx);
@@ -155,13 +158,15 @@ int qmv_rows_impl(const char* fn, int bits, const void* packed, int64_t N, int64
   if (K > q4::kQmvMaxK) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
   const size_t lds = q4::qmv_lds_bytes(K, x_dtype != Q4_BF16, 1, R);
   if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
-  const int xmode = x_dtype == Q4_F32 ? 1 : (x_dtype == Q4_BF16X3 ? 2 : 0);
+  const int xmode = x_dtype == Q4_F32 ? 1 : (x_dtype == Q4_BF16X3 ? 2 : (x_dtype == Q4_BF16X3T ? 3 : 0));
   q4::qmv_launch((const uint8_t*)packed, (const uint8_t*)packed, 1, (int)N, (int)K, x, xmode, ldx, R, y, ldy, s, bits);
   return launched(fn);
 }
 
+// y3: 0 float32 y [R][ldy]; 1 Q4_BF16X3 planes [3][R][ldy]; 2 Q4_BF16X3T
+// (ldy is then N, the activations per row).
 int qmv_w13_impl(const char* fn, int bits, const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
-                 int64_t ldx, int R, void* y, int64_t ldy, hipStream_t s, bool y3 = false) {
+                 int64_t ldx, int R, void* y, int64_t ldy, hipStream_t s, int y3 = 0) {
   if (int rc = check_fmt(fn, bits)) return rc;
   if (int rc = check_nk(fn, N, K)) return rc;
   if (R < 1 || R > 16) return fail(Q4_EINVAL, "%s: R=%d is outside 1..16", fn, R);
@@ -170,7 +175,10 @@ int qmv_w13_impl(const char* fn, int bits, const void* packed_w1, const void* pa
   if (int rc = check_x(fn, x, Q4_BF16, ldx, K)) return rc;
   if (int rc = check_ptr(fn, y3 ? "z3" : "y", y, y3 ? 16 : 4)) return rc;
   if (ldy < N) return fail(Q4_EINVAL, "%s: %s=%lld < N=%lld", fn, y3 ? "ldz" : "ldy", (long long)ldy, (long long)N);
-  if (y3 && (ldy * 2) % 16 != 0) return fail(Q4_EALIGN, "%s: ldz=%lld elements does not keep rows 16-byte aligned", fn, (long long)ldy);
+  if (y3 == 1 && (ldy * 2) % 16 != 0)
+    return fail(Q4_EALIGN, "%s: ldz=%lld elements does not keep rows 16-byte aligned", fn, (long long)ldy);
+  if (y3 == 2 && N > q4::kQmvMaxK)
+    return fail(Q4_EUNSUPPORTED, "%s: N=%lld exceeds the decode limit of 16384 for the next matvec's K", fn, (long long)N);
   if ((int64_t)R * ldx * 2 >= (int64_t(1) << 31))
     return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
   // up to 2 segments per wave, 16 waves: K <= 8192
@@ -413,6 +421,11 @@ size_t q4g64_packed_bytes(int64_t N, int64_t K) { return packed_bytes_impl(4, N,
 
 size_t qg64_packed_bytes(int bits, int64_t N, int64_t K) { return packed_bytes_impl(bits, N, K); }
 
+size_t q4g64_x3t_bytes(int64_t K, int R) {
+  if (K <= 0 || K % 64 != 0 || K > q4::kQmvMaxK || R < 1 || R > 16) return 0;
+  return (size_t)q4::qmv_x3t_bytes(K, R);
+}
+
 int pack_q4g64(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, int64_t N, int64_t K, void* packed,
                void* stream) {
   return pack_impl("pack_q4g64", 4, wq, scales, biases, N, K, packed, (hipStream_t)stream);
@@ -458,7 +471,13 @@ int qmv_w13_swiglu_qg64(int bits, const void* packed_w1, const void* packed_w3, 
 int qmv_w13_swiglu_x3(int bits, const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
                       int64_t ldx, int R, uint16_t* z3, int64_t ldz, void* stream) {
   if (int rc = check_bits("qmv_w13_swiglu_x3", bits)) return rc;
-  return qmv_w13_impl("qmv_w13_swiglu_x3", bits, packed_w1, packed_w3, N, K, x, ldx, R, z3, ldz, (hipStream_t)stream, true);
+  return qmv_w13_impl("qmv_w13_swiglu_x3", bits, packed_w1, packed_w3, N, K, x, ldx, R, z3, ldz, (hipStream_t)stream, 1);
+}
+
+int qmv_w13_swiglu_x3t(int bits, const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
+                       int64_t ldx, int R, uint16_t* z3t, void* stream) {
+  if (int rc = check_bits("qmv_w13_swiglu_x3t", bits)) return rc;
+  return qmv_w13_impl("qmv_w13_swiglu_x3t", bits, packed_w1, packed_w3, N, K, x, ldx, R, z3t, N, (hipStream_t)stream, 2);
 }
 
 int qmm_window(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx, int64_t M,
@@ -575,7 +594,12 @@ int qmv_w13_swiglu_fp8b(const void* packed_w1, const void* packed_w3, int64_t N,
 
 int qmv_w13_swiglu_x3_fp8b(const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                            int R, uint16_t* z3, int64_t ldz, void* stream) {
-  return qmv_w13_impl("qmv_w13_swiglu_x3_fp8b", q4::kFmtFp8, packed_w1, packed_w3, N, K, x, ldx, R, z3, ldz, (hipStream_t)stream, true);
+  return qmv_w13_impl("qmv_w13_swiglu_x3_fp8b", q4::kFmtFp8, packed_w1, packed_w3, N, K, x, ldx, R, z3, ldz, (hipStream_t)stream, 1);
+}
+
+int qmv_w13_swiglu_x3t_fp8b(const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                            int R, uint16_t* z3t, void* stream) {
+  return qmv_w13_impl("qmv_w13_swiglu_x3t_fp8b", q4::kFmtFp8, packed_w1, packed_w3, N, K, x, ldx, R, z3t, N, (hipStream_t)stream, 2);
 }
 
 int qmm_window_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx, int64_t M,

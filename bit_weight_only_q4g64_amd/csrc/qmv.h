@@ -48,6 +48,25 @@ __host__ __device__ inline size_t qmv_part_bytes(int64_t K, int xf32, int nmat, 
 }
 // Row slots per lane group the bf16 path keeps for R rows.
 __host__ __device__ inline int qmv_nv(int R) { return R <= 1 ? 1 : (R <= 2 ? 2 : 4); }
+// Row tiles the float32 path instantiates for R rows (1, 2 or 4 tiles of 4 rows).
+__host__ __device__ inline int qmv_row_tiles(int xf32, int R) {
+  if (!xf32) return 1;
+  const int rtf = (R + 3) / 4;
+  return rtf <= 1 ? 1 : (rtf <= 2 ? 2 : 4);
+}
+// Planes in fragment order: piece p (0..2) of element k of row r sits where
+// the matvec's lane reads it, so one 16-byte read per lane covers a whole
+// fragment and a wave's read is 1 KiB of consecutive bytes. Layout
+// [K/64 groups][tiles][2 halves][64 lanes][8 values]: lane i + 16 kc holds
+// matrix row i = 4 (r % 4) + p of tile r / 4, values kc * 8 .. + 7 of the
+// half. Slots of piece 3 and of rows >= R are never written and never enter
+// a stored result.
+__host__ __device__ inline int64_t qmv_x3t_offset(int k, int r, int p, int tiles) {
+  const int g = k >> 6, hh = (k >> 5) & 1, kc = (k >> 3) & 3, e = k & 7;
+  const int ln = 4 * (r & 3) + p + 16 * kc;
+  return ((((int64_t)g * tiles + (r >> 2)) * 2 + hh) * 64 + ln) * 8 + e;
+}
+__host__ __device__ inline int64_t qmv_x3t_bytes(int64_t K, int R) { return (K / kGroup) * qmv_row_tiles(1, R) * 2048; }
 __host__ __device__ inline size_t qmv_xs_bytes(int64_t K, int xf32, int R) {
   return (size_t)(xf32 ? 3 : 1) * R * qmv_xs_stride(K) * sizeof(uint16_t);
 }
@@ -252,11 +271,16 @@ __device__ __forceinline__ void qmv_ordered_sum(float (&tot)[NMAT][kRT][kPerLane
 // workgroup (else each wave reads its fragments from global memory). NV:
 // row slots per lane group kept by the bf16 path. None of these changes the
 // arithmetic of a stored row.
-template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS, bool Y3 = false>
+// XF32: 0 bf16 rows, 1 float32 rows, 2 float32 rows as three bf16 planes
+// [3][R][ldx], 3 the same planes in fragment order (qmv_x3t_offset; read
+// from memory, never staged). Y3: 0 float32 output, 1 three bf16 planes
+// [3][R][ldy], 2 the planes in fragment order.
+template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS, int Y3 = 0>
 __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* __restrict__ pk0, const uint8_t* __restrict__ pk1,
                                                               int N, int K, const void* __restrict__ xv, int64_t ldx, int R,
                                                               float* __restrict__ y, int64_t ldy) {
   static_assert(!Y3 || NMAT == 2, "the three-plane output is the fused SwiGLU's");
+  static_assert(XF32 != 3 || !XLDS, "fragment-ordered planes are read from memory");
   constexpr int kRT = XF32 ? RTF : 1;  // row tiles
   // accumulators per lane per row tile: bf16 x keeps row slots 4*kc + v for
   // v < NV (NV = 4 when R > 4, else the smallest of 1, 2, 4 covering R); the
@@ -290,7 +314,7 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
     cres[m] = make_rsrc(pk + (int64_t)t * P * pair_code_bytes(BITS), (uint32_t)P * pair_code_bytes(BITS));
     sres[m] = make_rsrc(pk + cb + (int64_t)t * P * kPairSbBytes, (uint32_t)P * kPairSbBytes);
   }
-  const rsrc_t xres = make_rsrc(xv, (uint32_t)XR * xrow);
+  const rsrc_t xres = make_rsrc(xv, XF32 == 3 ? (uint32_t)qmv_x3t_bytes(K, R) : (uint32_t)XR * xrow);
 
   // 1) activations: the first batch of staging loads is issued before the
   //    weight loads, so writing it to LDS waits for nothing else. The R rows
@@ -381,6 +405,8 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
     if constexpr (!XF32) {
       if constexpr (XLDS) return __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + frow * xsi + k0));
       else return __builtin_bit_cast(bf16x8, buf_load16(xres, (uint32_t)frow * xrow + (uint32_t)k0 * 2u, 0u));
+    } else if constexpr (XF32 == 3) {
+      return __builtin_bit_cast(bf16x8, buf_load16(xres, (uint32_t)((((g * kRT + rt) * 2 + hh) * 64 + lane) * 16), 0u));
     } else {
       int row = rt * 4 + (i >> 2);
       row = row < R ? row : R - 1;
@@ -449,7 +475,7 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
       } else {
         out = silu_f32(tot[0][rt][v]) * tot[1][rt][v];
       }
-      if constexpr (Y3) {
+      if constexpr (Y3 == 1) {
         uint32_t h, m, l;
         split3(out, h, m, l);
         uint16_t* y3 = (uint16_t*)y;
@@ -457,18 +483,19 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
         y3[(int64_t)r * ldy + n] = (uint16_t)h;
         y3[plane + (int64_t)r * ldy + n] = (uint16_t)m;
         y3[2 * plane + (int64_t)r * ldy + n] = (uint16_t)l;
+      } else if constexpr (Y3 == 2) {
+        uint32_t h, m, l;
+        split3(out, h, m, l);
+        uint16_t* y3 = (uint16_t*)y;
+        const int tiles = qmv_row_tiles(1, R);
+        y3[qmv_x3t_offset((int)n, r, 0, tiles)] = (uint16_t)h;
+        y3[qmv_x3t_offset((int)n, r, 1, tiles)] = (uint16_t)m;
+        y3[qmv_x3t_offset((int)n, r, 2, tiles)] = (uint16_t)l;
       } else {
         y[(int64_t)r * ldy + n] = out;
       }
     }
   }
-}
-
-// Row tiles the float32 path instantiates for R rows (1, 2 or 4 tiles of 4 rows).
-inline int qmv_row_tiles(int xf32, int R) {
-  if (!xf32) return 1;
-  const int rtf = (R + 3) / 4;
-  return rtf <= 1 ? 1 : (rtf <= 2 ? 2 : 4);
 }
 
 // Largest dynamic LDS a workgroup may use (queried once per process, on the
@@ -489,7 +516,7 @@ inline size_t qmv_lds_bytes(int64_t K, int xf32, int nmat, int R) {
   return qmv_part_bytes(K, xf32, nmat, qmv_row_tiles(xf32, R), xf32 ? 1 : qmv_nv(R));
 }
 
-template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS, bool Y3>
+template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS, int Y3>
 inline void qmv_launch_t(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
                          int64_t ldy, int nwaves, size_t lds, hipStream_t s) {
   auto kern = qmv_kernel<XF32, NMAT, SPW, RTF, XLDS, NV, BITS, Y3>;
@@ -500,7 +527,7 @@ inline void qmv_launch_t(const uint8_t* pk0, const uint8_t* pk1, int N, int K, c
   hipLaunchKernelGGL(kern, dim3((unsigned)(N / kTileN)), dim3(nwaves * 64), lds, s, pk0, pk1, N, K, x, ldx, R, y, ldy);
 }
 
-template <int XF32, int NMAT, int RTF, bool XLDS, int NV, int BITS, bool Y3>
+template <int XF32, int NMAT, int RTF, bool XLDS, int NV, int BITS, int Y3>
 inline void qmv_launch_spw(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
                            int64_t ldy, size_t lds, hipStream_t s) {
   const int nseg = qmv_segments(K);
@@ -516,19 +543,23 @@ inline void qmv_launch_spw(const uint8_t* pk0, const uint8_t* pk1, int N, int K,
   }
 }
 
-template <int XF32, int NMAT, int RTF, int NV, int BITS, bool Y3>
+template <int XF32, int NMAT, int RTF, int NV, int BITS, int Y3>
 inline void qmv_launch_lds(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
                            int64_t ldy, hipStream_t s) {
   const size_t part = qmv_part_bytes(K, XF32, NMAT, XF32 ? RTF : 1, NV);
-  const size_t xsb = qmv_xs_bytes(K, XF32, R);
-  const size_t staged = part > xsb ? part : xsb;  // the partials reuse the staging area
-  if (staged <= qmv_max_lds())
-    qmv_launch_spw<XF32, NMAT, RTF, true, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, staged, s);
-  else
+  if constexpr (XF32 == 3) {
     qmv_launch_spw<XF32, NMAT, RTF, false, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, part, s);
+  } else {
+    const size_t xsb = qmv_xs_bytes(K, XF32, R);
+    const size_t staged = part > xsb ? part : xsb;  // the partials reuse the staging area
+    if (staged <= qmv_max_lds())
+      qmv_launch_spw<XF32, NMAT, RTF, true, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, staged, s);
+    else
+      qmv_launch_spw<XF32, NMAT, RTF, false, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, part, s);
+  }
 }
 
-template <int NMAT, int BITS, bool Y3>
+template <int NMAT, int BITS, int Y3>
 inline void qmv_launch_bf16(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
                             int64_t ldy, hipStream_t s) {
   const int nv = qmv_nv(R);
@@ -545,35 +576,40 @@ inline void qmv_launch_pieces(const uint8_t* pk0, int N, int K, const void* x, i
                               hipStream_t s) {
   const int rt = qmv_row_tiles(1, R);
   if (rt == 1)
-    qmv_launch_lds<XF32, 1, 1, 1, BITS, false>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<XF32, 1, 1, 1, BITS, 0>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
   else if (rt == 2)
-    qmv_launch_lds<XF32, 1, 2, 1, BITS, false>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<XF32, 1, 2, 1, BITS, 0>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
   else
-    qmv_launch_lds<XF32, 1, 4, 1, BITS, false>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<XF32, 1, 4, 1, BITS, 0>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
 }
 
-// xmode: 0 bf16 rows, 1 float32 rows, 2 float32 rows as three bf16 planes
-// (one matrix only). y3: the fused SwiGLU writes three bf16 planes.
+// xmode: 0 bf16 rows, 1 float32 rows, 2 float32 rows as three bf16 planes,
+// 3 the planes in fragment order (one matrix only). y3: the fused SwiGLU
+// writes three bf16 planes (1) or the planes in fragment order (2).
 template <int BITS>
 inline void qmv_launch_bits(const uint8_t* pk0, const uint8_t* pk1, int nmat, int N, int K, const void* x, int xmode, int64_t ldx,
-                            int R, float* y, int64_t ldy, hipStream_t s, bool y3) {
+                            int R, float* y, int64_t ldy, hipStream_t s, int y3) {
   if (xmode == 0) {
     if (nmat == 1)
-      qmv_launch_bf16<1, BITS, false>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
-    else if (y3)
-      qmv_launch_bf16<2, BITS, true>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+      qmv_launch_bf16<1, BITS, 0>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    else if (y3 == 1)
+      qmv_launch_bf16<2, BITS, 1>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    else if (y3 == 2)
+      qmv_launch_bf16<2, BITS, 2>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
     else
-      qmv_launch_bf16<2, BITS, false>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+      qmv_launch_bf16<2, BITS, 0>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
   } else if (xmode == 1) {
     qmv_launch_pieces<1, BITS>(pk0, N, K, x, ldx, R, y, ldy, s);
-  } else {
+  } else if (xmode == 2) {
     qmv_launch_pieces<2, BITS>(pk0, N, K, x, ldx, R, y, ldy, s);
+  } else {
+    qmv_launch_pieces<3, BITS>(pk0, N, K, x, ldx, R, y, ldy, s);
   }
 }
 
 // bits: 4, 6, 8 or kFmtFp8 (checked by the caller).
 inline void qmv_launch(const uint8_t* pk0, const uint8_t* pk1, int nmat, int N, int K, const void* x, int xmode, int64_t ldx,
-                       int R, float* y, int64_t ldy, hipStream_t s, int bits = 4, bool y3 = false) {
+                       int R, float* y, int64_t ldy, hipStream_t s, int bits = 4, int y3 = 0) {
   if (bits == 6)
     qmv_launch_bits<6>(pk0, pk1, nmat, N, K, x, xmode, ldx, R, y, ldy, s, y3);
   else if (bits == 8)

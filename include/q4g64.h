@@ -98,12 +98,23 @@ extern "C" {
                      * h = the top 16 bits of x, m = the top 16 bits of x - h, l = x - h - m
                      * (each exact in bf16), x = h + m + l; plane p starts R * ld elements
                      * after plane p - 1 */
+#define Q4_BF16X3T 3 /* the same pieces in fragment order, q4g64_x3t_bytes(K, R) bytes:
+                      * piece p (0..2) of element k of row r is uint16 number
+                      * ((((k/64) * T + r/4) * 2 + (k/32)%2) * 64 + 4*(r%4) + p + 16*((k/8)%4)) * 8 + k%8,
+                      * T = 1, 2 or 4 row tiles for R <= 4, <= 8, <= 16. Slots of
+                      * p = 3 and of rows >= R are not read into any result. One
+                      * 16-byte read per lane then fetches a whole matrix fragment
+                      * (a wave reads 1 KiB of consecutive bytes) */
 
 /* ABI version of this header (incremented on incompatible changes). */
 int q4g64_abi_version(void);
 
 /* Bytes of the packed device layout for an N x K matrix; 0 if (N, K) is invalid. */
 size_t q4g64_packed_bytes(int64_t N, int64_t K);
+
+/* Bytes of R rows of K activations as Q4_BF16X3T; 0 if K is not a positive
+ * multiple of 64 (at most 16384) or R is outside 1..16. */
+size_t q4g64_x3t_bytes(int64_t K, int R);
 
 /* Canonical MLX q4g64 (wq, scales, biases on the device) -> packed layout.
  * An integer permutation of the input bits: bit-exact and invertible.
@@ -130,7 +141,10 @@ int unpack_qg64(int bits, const void* packed, int64_t N, int64_t K, uint32_t* wq
  *      Q4_F32 (float32 rows are split into three exact bf16 pieces), or
  *      Q4_BF16X3 (the same pieces given as planes, as qmv_w13_swiglu_x3
  *      writes them: bit-identical results to Q4_F32 on the same values,
- *      without the split in every workgroup).
+ *      without the split in every workgroup), or Q4_BF16X3T (the pieces in
+ *      fragment order, as qmv_w13_swiglu_x3t writes them; ldx must equal K;
+ *      bit-identical results again; from 4 rows on the fragments come from
+ *      memory, where this order reads whole cache lines).
  *   y: float32 [R][ldy], ldy >= N.
  * Row r of y is bit-identical to the result of the same call with R = 1 on
  * that row alone. Limits: K <= 16384 (bf16 x) / 16384 (float32 x). */
@@ -160,6 +174,13 @@ int qmv_w13_swiglu_qg64(int bits, const void* packed_w1, const void* packed_w3, 
  * qmv_w13_swiglu_qg64 bit for bit. */
 int qmv_w13_swiglu_x3(int bits, const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
                       int64_t ldx, int R, uint16_t* z3, int64_t ldz, void* stream);
+
+/* The same with the pieces written as Q4_BF16X3T for N activations per row:
+ * z3t holds q4g64_x3t_bytes(N, R) bytes (16-byte aligned), the x of a
+ * following qmv_rows over a matrix with K = N. Slots the layout leaves
+ * unread are not written. */
+int qmv_w13_swiglu_x3t(int bits, const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x,
+                       int64_t ldx, int R, uint16_t* z3t, void* stream);
 
 /* Prompt-window GEMM (PR #1696, later revision, "What it adds": pgemm).
  *   x: bf16 [M][ldx], any M >= 1.
@@ -237,6 +258,8 @@ int qmv_w13_swiglu_fp8b(const void* packed_w1, const void* packed_w3, int64_t N,
                         int R, float* y, int64_t ldy, void* stream);
 int qmv_w13_swiglu_x3_fp8b(const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                            int R, uint16_t* z3, int64_t ldz, void* stream);
+int qmv_w13_swiglu_x3t_fp8b(const void* packed_w1, const void* packed_w3, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                            int R, uint16_t* z3t, void* stream);
 int qmm_window_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                     int64_t M, void* y, int y_dtype, int64_t ldy, void* stream);
 int qmm_cut_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,

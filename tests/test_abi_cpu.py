@@ -107,7 +107,7 @@ def test_strides_and_dtypes_rejected():
 def test_planes_arguments_rejected():
     """Q4_BF16X3 planes: the planes dtype is accepted only as a decode input, with bf16 stride rules; the planes
     output of the fused SwiGLU checks its width, pointer and 16-byte row alignment."""
-    rc, _ = _rc("qmv_rows", FAKE, 512, 256, FAKE, 3, 256, 1, FAKE, 512, None)
+    rc, _ = _rc("qmv_rows", FAKE, 512, 256, FAKE, 4, 256, 1, FAKE, 512, None)
     assert rc == q4.Q4_EINVAL
     rc, _ = _rc("qmv_rows", FAKE, 512, 256, FAKE, q4.Q4_BF16X3, 260, 1, FAKE, 512, None)
     assert rc == q4.Q4_EALIGN  # 520-byte rows
@@ -126,6 +126,43 @@ def test_planes_arguments_rejected():
     rc, _ = _rc("qmv_w13_swiglu_x3_fp8b", FAKE, FAKE, 1024, 256, FAKE, 256, 1, FAKE + 2, 1024, None)
     assert rc == q4.Q4_EALIGN
     rc, _ = _rc("qmv_w13_swiglu_x3_fp8b", FAKE, FAKE, 1024, 256, FAKE, 256, 17, FAKE, 1024, None)
+    assert rc == q4.Q4_EINVAL
+
+
+def test_tiled_planes_bytes():
+    """Q4_BF16X3T: K/64 groups x (1, 2 or 4 row tiles) x 2 KiB; 0 for invalid K or R."""
+    f = q4.lib().q4g64_x3t_bytes
+    assert f(2048, 1) == 32 * 1 * 2048
+    assert f(2048, 4) == 32 * 1 * 2048
+    assert f(2048, 5) == 32 * 2 * 2048
+    assert f(8192, 9) == 128 * 4 * 2048
+    assert f(16384, 16) == 256 * 4 * 2048
+    for K, R in ((100, 1), (2048, 0), (2048, 17), (16448, 1), (0, 1), (-64, 1)):
+        assert f(K, R) == 0, (K, R)
+
+
+def test_tiled_planes_arguments_rejected():
+    """Q4_BF16X3T is a decode input without a row stride (ldx must equal K) and never a window output type; the
+    tiled output of the fused SwiGLU checks its bits, pointer, row count and the width the next matvec can take."""
+    rc, msg = _rc("qmv_rows", FAKE, 512, 256, FAKE, q4.Q4_BF16X3T, 264, 1, FAKE, 512, None)
+    assert rc == q4.Q4_EINVAL and "ldx" in msg
+    rc, _ = _rc("qmv_rows_fp8b", FAKE, 512, 256, FAKE, q4.Q4_BF16X3T, 128, 4, FAKE, 512, None)
+    assert rc == q4.Q4_EINVAL
+    rc, _ = _rc("qmv_rows", FAKE, 512, 256, FAKE + 8, q4.Q4_BF16X3T, 256, 4, FAKE, 512, None)
+    assert rc == q4.Q4_EALIGN
+    rc, _ = _rc("qmm_window", FAKE, None, 512, 256, FAKE, 256, 4, FAKE, q4.Q4_BF16X3T, 512, None)
+    assert rc == q4.Q4_EINVAL
+    rc, _ = _rc("qmv_w13_swiglu_x3t", 5, FAKE, FAKE, 1024, 256, FAKE, 256, 1, FAKE, None)
+    assert rc == q4.Q4_EINVAL
+    rc, _ = _rc("qmv_w13_swiglu_x3t", 4, FAKE, FAKE, 1024, 256, FAKE, 256, 1, None, None)
+    assert rc == q4.Q4_EALIGN
+    rc, _ = _rc("qmv_w13_swiglu_x3t", 8, FAKE, FAKE, 1024, 256, FAKE, 256, 1, FAKE + 2, None)
+    assert rc == q4.Q4_EALIGN
+    rc, _ = _rc("qmv_w13_swiglu_x3t", 4, FAKE, FAKE, 1024, 256, FAKE, 256, 17, FAKE, None)
+    assert rc == q4.Q4_EINVAL
+    rc, _ = _rc("qmv_w13_swiglu_x3t", 4, FAKE, FAKE, 16448, 256, FAKE, 256, 1, FAKE, None)
+    assert rc == q4.Q4_EUNSUPPORTED
+    rc, _ = _rc("qmv_w13_swiglu_x3t_fp8b", FAKE, FAKE, 1024, 256, FAKE, 256, 0, FAKE, None)
     assert rc == q4.Q4_EINVAL
 
 

@@ -125,3 +125,69 @@ def test_ffn_step_through_planes(ffn, fmt, R):
     y3 = _rows(p2, fmt, 2048, 1024, _w13(p1, p3, fmt, 1024, 2048, x, planes=True))
     torch.cuda.synchronize()
     assert np.array_equal(bits32(y3), bits32(y32))
+
+
+# ---- the same pieces in fragment order (Q4_BF16X3T) -------------------------
+
+
+def tile_planes(pl: np.ndarray, fill: int = 0) -> np.ndarray:
+    """[3][R][K] uint16 planes -> Q4_BF16X3T, written from the layout's definition: piece p of element k of row r at
+    ((((k/64) * T + r/4) * 2 + (k/32)%2) * 64 + 4*(r%4) + p + 16*((k/8)%4)) * 8 + k%8, T = 1, 2, 4 tiles for
+    R <= 4, 8, 16. Unused slots get `fill`."""
+    _, R, K = pl.shape
+    T = 1 if R <= 4 else (2 if R <= 8 else 4)
+    out = np.full((K // 64) * T * 1024, fill, dtype=np.uint16)
+    k = np.arange(K)
+    for r in range(R):
+        for p in range(3):
+            pos = ((((k // 64) * T + r // 4) * 2 + (k // 32) % 2) * 64 + 4 * (r % 4) + p + 16 * ((k // 8) % 4)) * 8 + k % 8
+            out[pos] = pl[p, r]
+    return out
+
+
+def used_slots(R: int, K: int) -> np.ndarray:
+    return tile_planes(np.ones((3, R, K), dtype=np.uint16), fill=0).astype(bool)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("R", [1, 4, 5, 9, 16])
+def test_w13_tiled_planes_are_the_exact_split(ffn, fmt, R):
+    say(f"w13 tiled planes fmt={fmt} R={R}")
+    p1, p3, _ = ffn[fmt]
+    z32 = _w13(p1, p3, fmt, 1024, 2048, ffn["x"][:R], planes=False)
+    zt = _w13(p1, p3, fmt, 1024, 2048, ffn["x"][:R], planes="tiled")
+    torch.cuda.synchronize()
+    assert isinstance(zt, q4.TiledPlanes) and zt.rows == R and zt.k == 1024
+    got = zt.data.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = tile_planes(split_planes(z32.cpu().numpy()))
+    used = used_slots(R, 1024)
+    assert got.size == want.size == q4.x3t_bytes(1024, R) // 2
+    assert np.array_equal(got[used], want[used])
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("R", [1, 3, 4, 7, 8, 9, 16])
+def test_rows_on_tiled_planes_equal_rows_on_float32(fmt, R):
+    """K = 8192; the slots the layout leaves unread hold NaN patterns, which must not reach any result."""
+    say(f"qmv_rows tiled planes vs float32 fmt={fmt} R={R}")
+    rng = np.random.default_rng(971 + R)
+    N, K = 2048, 8192
+    p = _weight(rng, fmt, "w2", N, K)
+    xf = synthetic.draw_f32_rows(rng, R, K, sigma=0.05)
+    xt = tile_planes(split_planes(xf), fill=0x7FC1)
+    x3t = q4.TiledPlanes(torch.from_numpy(xt.view(np.int16)).to(DEV).view(torch.bfloat16), R, K)
+    y32 = _rows(p, fmt, N, K, torch.from_numpy(xf).to(DEV))
+    yt = _rows(p, fmt, N, K, x3t)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits32(yt), bits32(y32))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("R", [1, 4, 16])
+def test_ffn_step_through_tiled_planes(ffn, fmt, R):
+    p1, p3, p2 = ffn[fmt]
+    x = ffn["x"][:R]
+    y32 = _rows(p2, fmt, 2048, 1024, _w13(p1, p3, fmt, 1024, 2048, x, planes=False))
+    yt = _rows(p2, fmt, 2048, 1024, _w13(p1, p3, fmt, 1024, 2048, x, planes="tiled"))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits32(yt), bits32(y32))
