@@ -354,6 +354,8 @@ def main():
         result["pgemm"] = bench_pgemm(dev)
     if not args.no_wide:
         result["decode_rows"] = bench_rows(dev, K, W, args.pool_mb)
+        r16 = result["decode_rows"]["R16"]
+        result["rows_per_s_at_16_rows"] = max(r16["rows_per_s"], r16["planes_rows_per_s"], r16["tiled_rows_per_s"])
         result["qkv_rope"] = bench_qkv_rope(dev, K, W, args.pool_mb)
     if not args.no_wide:
         result["wide_codes"] = {str(b): bench_wide(dev, b, K, W, args.pool_mb, graph=g_used) for b in (6, 8, "fp8")}
