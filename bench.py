@@ -123,13 +123,38 @@ KERNEL_SOURCES = ["bit_weight_only_q4g64_amd/csrc/common.h", "bit_weight_only_q4
                   "bit_weight_only_q4g64_amd/csrc/pgemm.h", "bit_weight_only_q4g64_amd/csrc/api.hip"]
 
 
+def _code_only(text):
+    """C++ source without its comments and blank lines (string literals kept), so
+    that editing a comment does not count as changing a kernel."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(line.rstrip() for line in "".join(out).splitlines() if line.strip())
+
+
 def kernel_source_hash():
+    """Hash of the kernel sources' code (comments and blank lines left out)."""
     import hashlib
 
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

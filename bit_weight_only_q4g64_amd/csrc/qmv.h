@@ -18,8 +18,10 @@
 // bf16 activations: the 16 row slots of the instruction hold rows 0..15.
 // float32 activations: each float is split exactly into three bf16 pieces
 // h + m + l; row r of a 4-row tile uses slots 4r (h), 4r+1 (m), 4r+2 (l)
-// (slot 4r+3 is zero), and P = (P_h + P_m) + P_l, S = (S_h + S_m) + S_l are
-// combined in-lane before the fold. R > 4 uses ceil(R/4) row tiles.
+// (slot 4r+3 repeats a piece or holds anything: its result is never used),
+// and P = (P_h + P_m) + P_l, S = (S_h + S_m) + S_l are combined in-lane
+// before the fold. R > 4 uses 2 or 4 row tiles; with the pieces given in
+// fragment order the tiles may be spread over workgroups along y.
 //
 // Nothing in the order depends on R, on the slot a row occupies or on the
 // launch shape, so every row is bit-equal to its one-row result (TensorFold
