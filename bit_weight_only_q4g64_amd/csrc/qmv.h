@@ -69,7 +69,7 @@ __host__ __device__ inline int64_t qmv_x3t_offset(int k, int r, int p, int tiles
   return ((((int64_t)g * tiles + (r >> 2)) * 2 + hh) * 64 + ln) * 8 + e;
 }
 __host__ __device__ inline int64_t qmv_x3t_bytes(int64_t K, int R) { return (K / kGroup) * qmv_row_tiles(1, R) * 2048; }
-// workgroups up to which fragment-ordered planes split the row tiles
+// workgroups up to which float32 rows read from memory split their row tiles
 constexpr int64_t kQmvSplitBelow = 256;
 __host__ __device__ inline size_t qmv_xs_bytes(int64_t K, int xf32, int R) {
   return (size_t)(xf32 ? 3 : 1) * R * qmv_xs_stride(K) * sizeof(uint16_t);
@@ -300,11 +300,11 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   float* part = (float*)smem;
   uint16_t* xs = (uint16_t*)smem;
   const int t = blockIdx.x;
-  // fragment-ordered planes may split the row tiles over blockIdx.y: this
-  // workgroup's first tile of the T = qmv_row_tiles(R) in memory (a row's
-  // arithmetic is the same whichever workgroup computes it)
-  const int rt0 = XF32 == 3 ? (int)blockIdx.y * kRT : 0;
-  const int T = XF32 == 3 ? qmv_row_tiles(1, R) : kRT;
+  // float32 rows read from memory may split their row tiles over
+  // blockIdx.y: this workgroup's first tile of the T = qmv_row_tiles(R)
+  // (a row's arithmetic is the same whichever workgroup computes it)
+  const int rt0 = XF32 ? (int)blockIdx.y * kRT : 0;
+  const int T = XF32 ? qmv_row_tiles(1, R) : kRT;
   const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int i = lane & 15, kc = lane >> 4;
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
     } else if constexpr (XF32 == 3) {
       return __builtin_bit_cast(bf16x8, buf_load16(xres, (uint32_t)((((g * T + rt0 + rt) * 2 + hh) * 64 + lane) * 16), 0u));
     } else {
-      int row = rt * 4 + (i >> 2);
+      int row = (rt0 + rt) * 4 + (i >> 2);
       row = row < R ? row : R - 1;
       int piece = i & 3;
       piece = piece < 3 ? piece : 2;
@@ -528,9 +528,8 @@ inline size_t qmv_lds_bytes(int64_t K, int xf32, int nmat, int R) {
 template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS, int Y3>
 inline void qmv_launch_t(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
                          int64_t ldy, int nwaves, size_t lds, hipStream_t s) {
-  // fragment-ordered planes: the row tiles not covered by RTF go to more
-  // workgroups along y
-  const unsigned ysplit = XF32 == 3 ? (unsigned)(qmv_row_tiles(1, R) / RTF) : 1u;
+  // float32 rows: the row tiles not covered by RTF go to more workgroups along y
+  const unsigned ysplit = XF32 ? (unsigned)(qmv_row_tiles(1, R) / RTF) : 1u;
   auto kern = qmv_kernel<XF32, NMAT, SPW, RTF, XLDS, NV, BITS, Y3>;
   // allow dynamic LDS beyond the 64 KB default, once per instantiation
   static const bool lds_ok =
@@ -564,7 +563,8 @@ inline void qmv_launch_lds(const uint8_t* pk0, const uint8_t* pk1, int N, int K,
   } else {
     const size_t xsb = qmv_xs_bytes(K, XF32, R);
     const size_t staged = part > xsb ? part : xsb;  // the partials reuse the staging area
-    if (staged <= qmv_max_lds())
+    // staged rows are not split: a workgroup then covers every row tile
+    if ((!XF32 || RTF == qmv_row_tiles(1, R)) && staged <= qmv_max_lds())
       qmv_launch_spw<XF32, NMAT, RTF, true, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, staged, s);
     else
       qmv_launch_spw<XF32, NMAT, RTF, false, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, part, s);
@@ -587,11 +587,16 @@ template <int XF32, int BITS>
 inline void qmv_launch_pieces(const uint8_t* pk0, int N, int K, const void* x, int64_t ldx, int R, float* y, int64_t ldy,
                               hipStream_t s) {
   int rt = qmv_row_tiles(1, R);
-  // fragment-ordered planes: while the column tiles leave CUs idle, each
-  // workgroup takes fewer row tiles (1, 2 or 4 per workgroup)
-  if constexpr (XF32 == 3) {
-    while (rt > 1 && (int64_t)(N / kTileN) * (qmv_row_tiles(1, R) / rt) * 2 <= kQmvSplitBelow) rt /= 2;
+  // rows read from memory (fragment-ordered planes, or rows that do not fit
+  // in LDS): while the column tiles leave CUs idle, each workgroup takes
+  // fewer row tiles (1, 2 or 4 per workgroup)
+  bool from_memory = XF32 == 3;
+  if constexpr (XF32 != 3) {
+    const size_t part = qmv_part_bytes(K, XF32, 1, rt, 1), xsb = qmv_xs_bytes(K, XF32, R);
+    from_memory = (part > xsb ? part : xsb) > qmv_max_lds();
   }
+  if (from_memory)
+    while (rt > 1 && (int64_t)(N / kTileN) * (qmv_row_tiles(1, R) / rt) * 2 <= kQmvSplitBelow) rt /= 2;
   if (rt == 1)
     qmv_launch_lds<XF32, 1, 1, 1, BITS, 0>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
   else if (rt == 2)
