@@ -191,3 +191,28 @@ def test_ffn_step_through_tiled_planes(ffn, fmt, R):
     yt = _rows(p2, fmt, 2048, 1024, _w13(p1, p3, fmt, 1024, 2048, x, planes="tiled"))
     torch.cuda.synchronize()
     assert np.array_equal(bits32(yt), bits32(y32))
+
+
+@pytest.mark.parametrize("N", [64, 512, 8192])
+@pytest.mark.parametrize("R", [5, 12, 16])
+def test_row_tile_split_keeps_the_bits(N, R):
+    """Float32 rows read from memory spread their row tiles over more workgroups while the column tiles leave CUs
+    idle (N = 64: 4 column tiles, each row tile its own workgroup; N = 8192: no split). Every float32 form gives
+    the same bits, and every row equals its one-row call."""
+    say(f"row-tile split N={N} R={R}")
+    rng = np.random.default_rng(990 + N + R)
+    K = 8192
+    p = _weight(rng, 4, "w", N, K)
+    xf = synthetic.draw_f32_rows(rng, R, K, sigma=0.2)
+    x32 = torch.from_numpy(xf).to(DEV)
+    pl = split_planes(xf)
+    x3 = torch.from_numpy(pl.view(np.int16)).to(DEV).view(torch.bfloat16)
+    xt = q4.TiledPlanes(torch.from_numpy(tile_planes(pl).view(np.int16)).to(DEV).view(torch.bfloat16), R, K)
+    y32, y3, yt = (q4.qmv_rows(p, N, K, x) for x in (x32, x3, xt))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits32(y3), bits32(y32))
+    assert np.array_equal(bits32(yt), bits32(y32))
+    for r in sorted({0, 4, R // 2, R - 1}):
+        y1 = q4.qmv_rows(p, N, K, x32[r : r + 1])
+        torch.cuda.synchronize()
+        assert np.array_equal(bits32(y1)[0], bits32(y32)[r]), r
