@@ -29,6 +29,9 @@
 // summed as the one-row kernels sum them).
 #pragma once
 
+#include <cstddef>
+#include <type_traits>
+
 #include "common.h"
 
 namespace q4 {
@@ -126,9 +129,12 @@ __device__ __forceinline__ void qmv_issue_weights(QmvWeights<NMAT, SPW, BITS>& w
 // group is requested before its first use and the next group's during this
 // one, so a wave waits for one memory round trip per segment, not one per
 // row tile and group.
-template <int XF32, int NMAT, int kRT, int kPerLane, bool AHEAD = false, int BITS, typename XF>
+// QF: nullptr (codes converted here), or qfrag(m, gg, half) returning codes
+// converted earlier.
+template <int XF32, int NMAT, int kRT, int kPerLane, bool AHEAD = false, int BITS, typename XF, typename QF = std::nullptr_t>
 __device__ __forceinline__ void qmv_fold_segment(float (&acc)[NMAT][kRT][kPerLane], const CodeWords<BITS> (&cw)[NMAT][kSegPairs],
-                                                 const u32x2 (&sbw)[NMAT][kSegPairs], int g0, int G, const XF& xfrag) {
+                                                 const u32x2 (&sbw)[NMAT][kSegPairs], int g0, int G, const XF& xfrag,
+                                                 const QF& qfrag = nullptr) {
   const bf16x8 ones = ones_bf16x8();
   bf16x8 xn[kRT][2];  // AHEAD: the fragments of the next group
   if constexpr (AHEAD) {
@@ -170,8 +176,13 @@ __device__ __forceinline__ void qmv_fold_segment(float (&acc)[NMAT][kRT][kPerLan
     float sc[NMAT], bs[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
-      q[m][0] = gh ? code_frag<BITS, 1, 0>(cw[m][pp]) : code_frag<BITS, 0, 0>(cw[m][pp]);
-      q[m][1] = gh ? code_frag<BITS, 1, 1>(cw[m][pp]) : code_frag<BITS, 0, 1>(cw[m][pp]);
+      if constexpr (std::is_same_v<QF, std::nullptr_t>) {
+        q[m][0] = gh ? code_frag<BITS, 1, 0>(cw[m][pp]) : code_frag<BITS, 0, 0>(cw[m][pp]);
+        q[m][1] = gh ? code_frag<BITS, 1, 1>(cw[m][pp]) : code_frag<BITS, 0, 1>(cw[m][pp]);
+      } else {
+        q[m][0] = qfrag(m, gg, 0);
+        q[m][1] = qfrag(m, gg, 1);
+      }
       const uint32_t w = gh ? sbw[m][pp][1] : sbw[m][pp][0];
       if constexpr (BITS == kFmtFp8) {
         sc[m] = __uint_as_float(w);
@@ -348,6 +359,13 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
     if (r >= XR) { r = XR - 1; c = per_row - 1; }  // past the last chunk: a valid, unused read
     return buf_load16(xres, (uint32_t)c * 16u + (uint32_t)r * xrow, 0u);
   };
+  // PRE (one row tile, one slot per lane, codes of at most 64 registers once
+  // converted): the weights are requested first and their codes converted
+  // while the activations are still in flight; the folds after the staging
+  // barrier then run only matrix steps and fmas
+  constexpr bool kPre = XLDS && kRT == 1 && kPerLane == 1 && SPW * NMAT * kSegGroups * 2 <= 16;
+  QmvWeights<NMAT, SPW, BITS> wts;
+  if constexpr (kPre) qmv_issue_weights<NMAT, SPW, BITS>(wts, cres, sres, wave, nwaves, P, lane, true);
   u32x4 xv0[kBatch];
   if constexpr (XLDS) {
     int r = r0, c = c0;
@@ -360,8 +378,27 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   }
 
   // 2) every weight load of this wave's segments
-  QmvWeights<NMAT, SPW, BITS> wts;
-  qmv_issue_weights<NMAT, SPW, BITS>(wts, cres, sres, wave, nwaves, P, lane, true);
+  if constexpr (!kPre) qmv_issue_weights<NMAT, SPW, BITS>(wts, cres, sres, wave, nwaves, P, lane, true);
+  bf16x8 qpre[SPW][NMAT][kSegGroups][2];
+  if constexpr (kPre) {
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int gg = 0; gg < kSegGroups; ++gg) {
+          const int pp = gg >> 1;
+          if (gg & 1) {
+            qpre[j][m][gg][0] = code_frag<BITS, 1, 0>(wts.cw[j][m][pp]);
+            qpre[j][m][gg][1] = code_frag<BITS, 1, 1>(wts.cw[j][m][pp]);
+          } else {
+            qpre[j][m][gg][0] = code_frag<BITS, 0, 0>(wts.cw[j][m][pp]);
+            qpre[j][m][gg][1] = code_frag<BITS, 0, 1>(wts.cw[j][m][pp]);
+          }
+          // converted here, before the activations are waited for
+          asm volatile("" : "+v"(qpre[j][m][gg][0]), "+v"(qpre[j][m][gg][1]));
+        }
+  }
 
   // 3) write the staged activations (float32 rows as three exact bf16 planes)
   if constexpr (XLDS) {
@@ -450,7 +487,12 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   for (int j = 0; j < SPW; ++j) {
     const int seg = wave + j * nwaves;
     if (seg >= nseg) break;
-    qmv_fold_segment<XF32, NMAT, kRT, kPerLane, kAhead>(keep[j], wts.cw[j], wts.sbw[j], seg * kSegGroups, G, xfrag);
+    if constexpr (kPre) {
+      auto qfrag = [&](int m, int gg, int h) { return qpre[j][m][gg][h]; };
+      qmv_fold_segment<XF32, NMAT, kRT, kPerLane, kAhead>(keep[j], wts.cw[j], wts.sbw[j], seg * kSegGroups, G, xfrag, qfrag);
+    } else {
+      qmv_fold_segment<XF32, NMAT, kRT, kPerLane, kAhead>(keep[j], wts.cw[j], wts.sbw[j], seg * kSegGroups, G, xfrag);
+    }
   }
   if constexpr (XLDS) __syncthreads();
 #pragma unroll
