@@ -228,6 +228,8 @@ def main():
                     help="launch the timed steps directly instead of replaying a graph (for per-dispatch counters)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (the reference for scaling HBM byte counters)")
+    ap.add_argument("--pgemm-only", action="store_true",
+                    help="only the prompt GEMM measurement (for its per-dispatch counters); prints its JSON object")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -239,6 +241,13 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.pgemm_only:
+        import bit_weight_only_q4g64_amd as q4
+
+        q4.lib()
+        torch.cuda.set_device(0)
+        print(json.dumps(bench_pgemm("cuda:0")))
         return
 
     import bit_weight_only_q4g64_amd as q4
@@ -625,6 +634,11 @@ def bench_qkv_rope(dev, K, W, pool_mb):
     return out
 
 
+# HBM bytes the 8192-row w1/w3 + SwiGLU window must move at least: both
+# packed weights once, the bf16 prompt once, the bf16 output once
+PGEMM_BYTES = 2 * (8192 * 2048 * 9 // 16) + 8192 * 2048 * 2 + 8192 * 8192 * 2
+
+
 def bench_pgemm(dev, reps=10):
     """w1/w3 + SwiGLU (bf16 out) over the 8192-row prompt as one window."""
     import torch
@@ -673,7 +687,8 @@ def bench_pgemm(dev, reps=10):
         "avg_ms": round(float(t.mean() * 1e3), 4),
         "TFLOP/s": round(tf, 2),
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf / BF16_PEAK_TFLOPS, 4)},
+                     "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": traffic_per_launch("pgemm_swiglu_8192"),
+                     "algorithmic_bytes_per_launch": PGEMM_BYTES},
         "windows_128": {
             "workload": "the same prompt through qmm_cut in 64 windows of 128 rows",
             "avg_ms": round(float(tc.mean() * 1e3), 4),
