@@ -81,7 +81,7 @@ def _window(pa, pb, fmt, N, K, x, y):
     return q4.qmm_window(pa, pb, N, K, x, y=y, bits=fmt)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_decode_sweep(seed):
     rng, fmt, N, K, R, pad_x, pad_y = _draw_case(seed, decode=True)
     xf32 = bool(seed % 3 == 2)
@@ -111,7 +111,7 @@ def test_decode_sweep(seed):
         assert np.array_equal(bits32(y1)[0], bits32(y)[r])
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_window_sweep(seed):
     rng, fmt, N, K, M, pad_x, pad_y = _draw_case(100 + seed, decode=False)
     swiglu = bool(seed % 2)
