@@ -337,7 +337,8 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   const rsrc_t xres = make_rsrc(xv, XF32 == 3 ? (uint32_t)qmv_x3t_bytes(K, R) : (uint32_t)XR * xrow);
 
   // 1) activations: the first batch of staging loads is issued before the
-  //    weight loads, so writing it to LDS waits for nothing else. The R rows
+  //    weight loads (after them with PRE below), so writing it to LDS waits
+  //    for nothing else. The R rows
   //    are cut into 16-byte chunks, numbered row after row; slot u of a
   //    thread holds chunk threadIdx.x + u * blockDim.x, so every thread has
   //    work whatever the row length.
