@@ -74,6 +74,9 @@ __host__ __device__ inline int64_t qmv_x3t_offset(int k, int r, int p, int tiles
 __host__ __device__ inline int64_t qmv_x3t_bytes(int64_t K, int R) { return (K / kGroup) * qmv_row_tiles(1, R) * 2048; }
 // workgroups up to which float32 rows read from memory split their row tiles
 constexpr int64_t kQmvSplitBelow = 256;
+// column tiles from which a bf16 matvec of one matrix runs two tiles per
+// workgroup (at least 512 column tiles; K up to 8192, as the fused kernel)
+constexpr int64_t kQmvPairTilesFrom = 512;
 __host__ __device__ inline size_t qmv_xs_bytes(int64_t K, int xf32, int R) {
   return (size_t)(xf32 ? 3 : 1) * R * qmv_xs_stride(K) * sizeof(uint16_t);
 }
@@ -289,7 +292,10 @@ __device__ __forceinline__ void qmv_ordered_sum(float (&tot)[NMAT][kRT][kPerLane
 // XF32: 0 bf16 rows, 1 float32 rows, 2 float32 rows as three bf16 planes
 // [3][R][ldx], 3 the same planes in fragment order (qmv_x3t_offset; read
 // from memory, never staged). Y3: 0 float32 output, 1 three bf16 planes
-// [3][R][ldy], 2 the planes in fragment order.
+// [3][R][ldy], 2 the planes in fragment order, 3 no SwiGLU: the two
+// "matrices" are column tiles 2t and 2t + 1 of one matrix, each written as
+// its own float32 columns (twice the weight loads in flight per wave; every
+// column's arithmetic is the one-tile kernel's).
 template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS, int Y3 = 0>
 __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* __restrict__ pk0, const uint8_t* __restrict__ pk1,
                                                               int N, int K, const void* __restrict__ xv, int64_t ldx, int R,
@@ -331,8 +337,9 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
 #pragma unroll
   for (int m = 0; m < NMAT; ++m) {
     const uint8_t* pk = m ? pk1 : pk0;
-    cres[m] = make_rsrc(pk + (int64_t)t * P * pair_code_bytes(BITS), (uint32_t)P * pair_code_bytes(BITS));
-    sres[m] = make_rsrc(pk + cb + (int64_t)t * P * kPairSbBytes, (uint32_t)P * kPairSbBytes);
+    const int64_t tm = Y3 == 3 ? 2 * (int64_t)t + m : t;  // this matrix's column tile
+    cres[m] = make_rsrc(pk + tm * P * pair_code_bytes(BITS), (uint32_t)P * pair_code_bytes(BITS));
+    sres[m] = make_rsrc(pk + cb + tm * P * kPairSbBytes, (uint32_t)P * kPairSbBytes);
   }
   const rsrc_t xres = make_rsrc(xv, XF32 == 3 ? (uint32_t)qmv_x3t_bytes(K, R) : (uint32_t)XR * xrow);
 
@@ -521,6 +528,11 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
     for (int v = 0; v < kPerLane; ++v) {
       const int r = XF32 ? (rt0 + rt) * 4 + kc : 4 * kc + v;
       if (r >= R) continue;
+      if constexpr (Y3 == 3) {
+        y[(int64_t)r * ldy + 2 * (int64_t)t * kTileN + i] = tot[0][rt][v];
+        y[(int64_t)r * ldy + (2 * (int64_t)t + 1) * kTileN + i] = tot[1][rt][v];
+        continue;
+      }
       float out;
       if constexpr (NMAT == 1) {
         out = tot[0][rt][v];
@@ -578,7 +590,8 @@ inline void qmv_launch_t(const uint8_t* pk0, const uint8_t* pk1, int N, int K, c
   static const bool lds_ok =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)qmv_max_lds()) == hipSuccess;
   (void)lds_ok;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(N / kTileN), ysplit), dim3(nwaves * 64), lds, s, pk0, pk1, N, K, x, ldx, R, y, ldy);
+  const unsigned gx = (unsigned)(N / kTileN / (Y3 == 3 ? 2 : 1));
+  hipLaunchKernelGGL(kern, dim3(gx, ysplit), dim3(nwaves * 64), lds, s, pk0, pk1, N, K, x, ldx, R, y, ldy);
 }
 
 template <int XF32, int NMAT, int RTF, bool XLDS, int NV, int BITS, int Y3>
@@ -655,7 +668,9 @@ template <int BITS>
 inline void qmv_launch_bits(const uint8_t* pk0, const uint8_t* pk1, int nmat, int N, int K, const void* x, int xmode, int64_t ldx,
                             int R, float* y, int64_t ldy, hipStream_t s, int y3) {
   if (xmode == 0) {
-    if (nmat == 1)
+    if (nmat == 1 && N / kTileN >= kQmvPairTilesFrom && K <= kQmvMaxK / 2)
+      qmv_launch_bf16<2, BITS, 3>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
+    else if (nmat == 1)
       qmv_launch_bf16<1, BITS, 0>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
     else if (y3 == 1)
       qmv_launch_bf16<2, BITS, 1>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);

@@ -167,3 +167,24 @@ def test_zero_activations_give_zero():
     y = q4.qmv_rows(dev_weight(w), w.N, w.K, torch.zeros((3, w.K), dtype=torch.bfloat16, device=DEV))
     torch.cuda.synchronize()
     assert torch.count_nonzero(y).item() == 0
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("R", [1, 3, 16])
+def test_two_tile_workgroups_keep_the_columns(bits, R):
+    """A one-matrix bf16 matvec over at least 512 column tiles runs two column tiles per workgroup. Its columns
+    equal, bit for bit, the same columns computed by the one-tile kernel on a narrower matrix made of the same
+    rows (the first 1024 rows of an 8192-row matrix, packed on their own), and every row equals its one-row call."""
+    say(f"two-tile workgroups bits={bits} R={R}")
+    rng = np.random.default_rng(1200 + bits + R)
+    N, K, n = 8192, 2048, 1024
+    w = synthetic.draw_qweight(rng, "w", N, K, bits=bits)
+    part = synthetic.QWeight("w_head", n, K, w.wq[:n].copy(), w.scales[:n].copy(), w.biases[:n].copy(), bits)
+    x = dev_bf16(synthetic.draw_bf16_rows(rng, R, K))
+    y = q4.qmv_rows(dev_weight(w), N, K, x, bits=bits)
+    yp = q4.qmv_rows(dev_weight(part), n, K, x, bits=bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits32(y)[:, :n], bits32(yp))
+    y1 = q4.qmv_rows(dev_weight(w), N, K, x[R - 1 : R], bits=bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits32(y1)[0], bits32(y)[R - 1])
