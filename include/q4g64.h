@@ -142,9 +142,11 @@ int unpack_qg64(int bits, const void* packed, int64_t N, int64_t K, uint32_t* wq
  *      Q4_BF16X3 (the same pieces given as planes, as qmv_w13_swiglu_x3
  *      writes them: bit-identical results to Q4_F32 on the same values,
  *      without the split in every workgroup), or Q4_BF16X3T (the pieces in
- *      fragment order, as qmv_w13_swiglu_x3t writes them; ldx must equal K;
- *      bit-identical results again; from 4 rows on the fragments come from
- *      memory, where this order reads whole cache lines).
+ *      fragment order, as qmv_w13_swiglu_x3t writes them for the same R;
+ *      ldx must equal K; bit-identical results again; from 4 rows on the
+ *      fragments come from memory, where this order reads whole cache
+ *      lines). The layout depends on R through its row-tile count, so a
+ *      buffer written for one R is read with that R.
  *   y: float32 [R][ldy], ldy >= N.
  * Row r of y is bit-identical to the result of the same call with R = 1 on
  * that row alone. Limits: K <= 16384 (bf16 x) / 16384 (float32 x). */
