@@ -448,6 +448,31 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_kernel(const uint8_t* 
 
   // ---- epilogue: element r of tile (rt, s) is row rbase + 32 rt + 8 (r / 4)
   // + 4 hl + r % 4, column jj of the lane's weight slot
+  if constexpr (SWIGLU && OUT_BF16) {
+    // the workgroup's 128 x 128 bf16 block goes through LDS (the activation
+    // stages are free once every wave is past its last group) and out as
+    // whole 16-byte pieces of rows, when the output allows 16-byte stores
+    if ((((uintptr_t)yv) & 15) == 0 && (ldy & 7) == 0) {
+      uint16_t* ob = (uint16_t*)xs;  // [128 rows][128 columns]
+      __syncthreads();
+#pragma unroll
+      for (int rt = 0; rt < kPgemmRT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + rt * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
+          ob[row * 128 + 32 * cw + j] = f32_to_bf16_rne(silu_f32(acc[rt][0][r]) * acc[rt][1][r]);
+        }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = (int)threadIdx.x + u * kPgemmThreads;
+        const int row = idx >> 4, col = (idx & 15) * 8;  // 8 output columns of one 16-column tile
+        if (row >= mt || nb * 8 + (col >> 4) >= ntiles) continue;
+        *(u32x4*)((uint16_t*)yv + (int64_t)(m0 + row) * ldy + (int64_t)nb * 128 + col) = *(const u32x4*)(ob + row * 128 + col);
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int rt = 0; rt < kPgemmRT; ++rt) {
 #pragma unroll
