@@ -237,9 +237,10 @@ int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2,
 /* Message of the last failed call on this thread ("" if none). */
 const char* q4_last_error(void);
 
-/* Block FP8, weight-only (PR #1696, first revision, "What it adds": the
- * CUDA engine serves the LFM3 block FP8 export weight-only; the pages give
- * no format, so this reading is the common block-FP8 checkpoint layout):
+/* Block FP8, weight-only (TensorFold PR #1696, first revision, "Stacked on"
+ * and "Checks": the CUDA engine it builds on and checks against serves the
+ * LFM3 block FP8 export weight-only; the pages give no format, so this
+ * reading is the common block-FP8 checkpoint layout):
  *     w8      uint8 [N][K]   OCP FP8 E4M3 bytes (bias 7, 3 mantissa bits,
  *                            exponent field 0 subnormal, 0x7F/0xFF NaN)
  *     scales  float32 [ceil(N/128)][ceil(K/128)], one per 128 x 128 block
@@ -321,9 +322,11 @@ int rope_kv_store(const float* qkv, int64_t ldqkv, int R, const q4_rope_kv* args
 int qmv_qkv_rope(int bits, const void* packed_qkv, int64_t K, const uint16_t* x, int64_t ldx, int R, const q4_rope_kv* args,
                  void* stream);
 
-/* Window-cost table (PR #1514, "What changes": window costs are timed at
- * load for 1, 2, 4, 8 and 16 rows and interpolated between them, for the
- * planner that picks how many streams' rows share a decode step).
+/* Window-cost table (TensorFold PR #1696, later revision, "What it adds" >
+ * Exact speed work: the cost of a window is measured once, when the model
+ * loads, at five row counts from 1 to 16, and costs in between are
+ * interpolated; a planner uses them to choose how many streams' rows share
+ * a decode step).
  *
  * qmv_window_costs times qmv_rows_qg64 on `packed` at R = 1, 2, 4, 8, 16
  * (bits = 4, 6 or 8; x and y must hold 16 rows), each as the average of `reps` (1..10000)

@@ -4,10 +4,11 @@ TEST INFRASTRUCTURE, like the rest of ``oracle/``: only tests, the smoke
 check and the benchmark's CPU baseline use it; it shares no code with the
 HIP kernels or their binding.
 
-What it computes (TensorFold PR #1696, first revision, "What it adds": the
-CUDA engine serves the LFM3 block FP8 export weight-only beside the MLX
-4-bit export). The pages name the format without describing it; the reading
-here is the common block-FP8 checkpoint layout:
+What it computes (TensorFold PR #1696, first revision, "Stacked on" and
+"Checks": the CUDA engine this backend builds on and is checked against
+serves the LFM3 block FP8 export weight-only beside the MLX 4-bit export).
+The pages name the format without describing it; the reading here is the
+common block-FP8 checkpoint layout:
 
     w8[n][k]     one OCP FP8 E4M3 byte per weight (sign, 4 exponent bits with
                  bias 7, 3 mantissa bits; exponent field 0 is subnormal,

@@ -46,13 +46,14 @@ def bits16(t):
     return t.detach().contiguous().view(torch.int16).cpu().numpy()
 
 
-def check_within(y_gpu, w, x, cols=None, x_dtype="bf16", rows=None, label=""):
-    """|y_gpu - y64| <= T elementwise; returns (max err/T, max err/A)."""
+def check_within(y_gpu, w, x, cols=None, x_dtype="bf16", rows=None, label="", *, order):
+    """|y_gpu - y64| <= T elementwise, T for the kernel family ``order``
+    (decode or window); returns (max err/T, max err/A)."""
     xs = x if rows is None else x[rows]
     bits = getattr(w, "bits", 4)
     y64 = oracle.matmul_rows(w.wq, w.scales, w.biases, xs, cols=cols, bits=bits)
     A = oracle.error_weight(w.wq, w.scales, w.biases, xs, cols=cols, bits=bits)
-    T = tol(A, w.K, x_dtype)
+    T = tol(A, w.K, x_dtype, order=order)
     err = np.abs(y_gpu - y64)
     ratio = float(np.max(err / T))
     assert np.all(np.isfinite(y_gpu)), label

@@ -36,7 +36,7 @@ def test_c4_qkv_and_o(c4):
         say(f"c4 {name} M=8192")
         y = q4.qmm_window(c4["p_" + name], None, w.N, w.K, c4["xd"])
         torch.cuda.synchronize()
-        check_within(host_f64(y[ROWS]), w, c4["x"], rows=ROWS, label=f"c4 {name}")
+        check_within(host_f64(y[ROWS]), w, c4["x"], rows=ROWS, label=f"c4 {name}", order="window")
         if name == "qkv":
             yc = q4.qmm_cut(c4["p_" + name], None, w.N, w.K, c4["xd"], [128] * 64)
             torch.cuda.synchronize()
@@ -54,8 +54,8 @@ def test_c4_ffn_chain(c4):
     a64 = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, xs)
     c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, xs)
     z64 = oracle.swiglu(a64, c64)
-    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, xs), w1.K),
-                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, xs), w3.K))
+    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, xs), w1.K, order="window"),
+                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, xs), w3.K, order="window"))
     Ez = tol_bf16_out(z64, Tz)
     zg = oracle.bf16_to_f64(bits16(z[ROWS]).view(np.uint16))
     assert np.all(np.abs(zg - z64) <= Ez)
@@ -63,7 +63,7 @@ def test_c4_ffn_chain(c4):
     y2 = q4.qmm_window(c4["p_w2"], None, w2.N, w2.K, z)
     torch.cuda.synchronize()
     y64 = oracle.matmul_rows(w2.wq, w2.scales, w2.biases, z64)
-    bound = tol(oracle.error_weight(w2.wq, w2.scales, w2.biases, np.abs(z64) + Ez), w2.K) + \
+    bound = tol(oracle.error_weight(w2.wq, w2.scales, w2.biases, np.abs(z64) + Ez), w2.K, order="window") + \
         oracle.error_weight(w2.wq, w2.scales, w2.biases, Ez)
     assert np.all(np.abs(host_f64(y2[ROWS]) - y64) <= bound)
 
@@ -74,7 +74,7 @@ def test_c4_w2_standalone_bf16_input(c4):
     x = c4["x_w2_bf16"]
     y = q4.qmm_window(c4["p_w2"], None, w2.N, w2.K, dev_bf16(x))
     torch.cuda.synchronize()
-    check_within(host_f64(y[:24]), w2, x[:24], label="c4 w2")
+    check_within(host_f64(y[:24]), w2, x[:24], label="c4 w2", order="window")
 
 
 def test_c4_head_last_128_rows(c4):
@@ -86,7 +86,7 @@ def test_c4_head_last_128_rows(c4):
     cols = np.random.default_rng(4).choice(w.N, 1024, replace=False)
     rows = [0, 63, 64, 127]
     yg = host_f64(y[rows])[:, cols]
-    check_within(yg, w, c4["x"][-128:][rows], cols=cols, label="c4 head")
+    check_within(yg, w, c4["x"][-128:][rows], cols=cols, label="c4 head", order="window")
     # row 8191 of the prompt computed alone equals row 127 of the head window
     y1 = q4.qmm_window(c4["p_head"], None, w.N, w.K, xl[127:128])
     assert np.array_equal(bits32(y1)[0], bits32(y)[127])

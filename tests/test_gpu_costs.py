@@ -1,5 +1,6 @@
-"""Window-cost table (PR #1514, "What changes": window costs timed at load
-for 1, 2, 4, 8 and 16 rows and interpolated between them) on the GPU: five
+"""Window-cost table (TensorFold PR #1696, later revision, "What it adds" >
+Exact speed work: costs measured at load at five row counts from 1 to 16,
+interpolated in between) on the GPU: five
 positive timings, the interpolation reads them back at the timed row counts,
 and the timed launches compute the same bits as a plain call."""
 

@@ -57,11 +57,11 @@ def test_c1_step_equals_composition_and_oracle(c1):
     a64 = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, c1["x"])
     c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, c1["x"])
     z64 = oracle.swiglu(a64, c64)
-    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, c1["x"]), K1),
-                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, c1["x"]), K1))
+    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, c1["x"]), K1, order="decode"),
+                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, c1["x"]), K1, order="decode"))
     assert np.all(np.abs(host_f64(z) - z64) <= Tz)
     y64 = oracle.matmul_rows(w2.wq, w2.scales, w2.biases, z64)
-    bound = tol(oracle.error_weight(w2.wq, w2.scales, w2.biases, np.abs(z64) + Tz), w2.K, "f32") + \
+    bound = tol(oracle.error_weight(w2.wq, w2.scales, w2.biases, np.abs(z64) + Tz), w2.K, "f32", order="decode") + \
         oracle.error_weight(w2.wq, w2.scales, w2.biases, Tz)
     ratio = float(np.max(np.abs(host_f64(y) - y64) / bound))
     say(f"qmv_ffn c1 y max err/bound {ratio:.3g}")

@@ -21,10 +21,10 @@ def dev_fp8(w):
     return q4.pack_fp8b(torch.from_numpy(np.ascontiguousarray(w.w8)).to(DEV), torch.from_numpy(np.ascontiguousarray(w.scales)).to(DEV))
 
 
-def check_fp8(y, w, x, cols=None, x_dtype="bf16", label=""):
+def check_fp8(y, w, x, cols=None, x_dtype="bf16", label="", *, order):
     """|y - y64| <= T elementwise on the sampled columns."""
     y64 = oracle.matmul_rows_fp8(w.w8, w.scales, x, cols=cols)
-    T = tol(oracle.error_weight_fp8(w.w8, w.scales, x, cols=cols), w.K, x_dtype)
+    T = tol(oracle.error_weight_fp8(w.w8, w.scales, x, cols=cols), w.K, x_dtype, order=order, fmt="fp8")
     r = float(np.max(np.abs(y - y64) / T))
     assert np.all(np.isfinite(y)), label
     assert r <= 1.0, f"{label}: max err/T {r}"
@@ -67,7 +67,7 @@ def test_fp8_qmv_bf16_within_tolerance(fp8, R):
     y = q4.qmv_rows_fp8b(fp8["p_qkv"], w.N, w.K, dev_bf16(fp8["x"][:R]))
     torch.cuda.synchronize()
     cols = np.arange(0, w.N, 5)
-    check_fp8(host_f64(y)[:, cols], w, fp8["x"][:R], cols=cols, label=f"fp8 R={R}")
+    check_fp8(host_f64(y)[:, cols], w, fp8["x"][:R], cols=cols, label=f"fp8 R={R}", order="decode")
 
 
 @pytest.mark.parametrize("R", [1, 5])
@@ -77,7 +77,7 @@ def test_fp8_qmv_f32_within_tolerance(fp8, R):
     y = q4.qmv_rows_fp8b(fp8["p_w2"], w.N, w.K, dev_f32(fp8["xf"][:R]))
     torch.cuda.synchronize()
     cols = np.arange(1, w.N, 3)
-    check_fp8(host_f64(y)[:, cols], w, fp8["xf"][:R], cols=cols, x_dtype="f32", label=f"fp8 f32 R={R}")
+    check_fp8(host_f64(y)[:, cols], w, fp8["xf"][:R], cols=cols, x_dtype="f32", label=f"fp8 f32 R={R}", order="decode")
 
 
 def test_fp8_rows_bit_equal_to_one_row(fp8):
@@ -102,8 +102,8 @@ def test_fp8_w13_swiglu(fp8, R):
     torch.cuda.synchronize()
     a64 = oracle.matmul_rows_fp8(w1.w8, w1.scales, xs)
     c64 = oracle.matmul_rows_fp8(w3.w8, w3.scales, xs)
-    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight_fp8(w1.w8, w1.scales, xs), w1.K),
-                    tol(oracle.error_weight_fp8(w3.w8, w3.scales, xs), w3.K))
+    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight_fp8(w1.w8, w1.scales, xs), w1.K, order="decode", fmt="fp8"),
+                    tol(oracle.error_weight_fp8(w3.w8, w3.scales, xs), w3.K, order="decode", fmt="fp8"))
     assert np.all(np.abs(host_f64(z) - oracle.swiglu(a64, c64)) <= Tz)
 
 
@@ -126,10 +126,11 @@ def test_fp8_window_parity(fp8_win):
     a, b = fp8_win["a"], fp8_win["b"]
     xs = fp8_win["x"][WIN_ROWS]
     say("qmm_window_fp8b parity")
-    check_fp8(host_f64(fp8_win["plain"])[WIN_ROWS], a, xs, label="fp8 window")
+    check_fp8(host_f64(fp8_win["plain"])[WIN_ROWS], a, xs, label="fp8 window", order="window")
     a64 = oracle.matmul_rows_fp8(a.w8, a.scales, xs)
     c64 = oracle.matmul_rows_fp8(b.w8, b.scales, xs)
-    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight_fp8(a.w8, a.scales, xs), a.K), tol(oracle.error_weight_fp8(b.w8, b.scales, xs), b.K))
+    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight_fp8(a.w8, a.scales, xs), a.K, order="window", fmt="fp8"),
+                    tol(oracle.error_weight_fp8(b.w8, b.scales, xs), b.K, order="window", fmt="fp8"))
     assert np.all(np.abs(host_f64(fp8_win["swiglu"])[WIN_ROWS] - oracle.swiglu(a64, c64)) <= Tz)
 
 

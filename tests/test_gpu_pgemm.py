@@ -40,8 +40,8 @@ def test_c3_swiglu_parity(c3, c3_whole):
     xs = c3["x"][SAMPLE_ROWS]
     a64 = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, xs)
     c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, xs)
-    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, xs), w1.K),
-                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, xs), w3.K))
+    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, xs), w1.K, order="window"),
+                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, xs), w3.K, order="window"))
     z = host_f64(c3_whole)[SAMPLE_ROWS]
     ratio = float(np.max(np.abs(z - oracle.swiglu(a64, c64)) / Tz))
     say(f"c3 max err/Tz {ratio:.3g}")
@@ -79,8 +79,8 @@ def test_c3_bf16_output_is_rne_of_float32(c3, c3_whole):
     a64 = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, xs)
     c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, xs)
     z64 = oracle.swiglu(a64, c64)
-    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, xs), w1.K),
-                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, xs), w3.K))
+    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, xs), w1.K, order="window"),
+                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, xs), w3.K, order="window"))
     zb64 = oracle.bf16_to_f64(bits16(zb).view(np.uint16)[SAMPLE_ROWS[:6]])
     assert np.all(np.abs(zb64 - z64) <= tol_bf16_out(z64, Tz))
 
@@ -96,7 +96,7 @@ def test_plain_window_parity_and_row_permutation(M):
     xd = dev_bf16(x)
     y = q4.qmm_window(pk, None, w.N, w.K, xd)
     torch.cuda.synchronize()
-    check_within(host_f64(y), w, x, label=f"pgemm plain M={M}")
+    check_within(host_f64(y), w, x, label=f"pgemm plain M={M}", order="window")
     perm = rng.permutation(M)
     yp = q4.qmm_window(pk, None, w.N, w.K, xd[torch.from_numpy(perm).to(DEV)])
     assert np.array_equal(bits32(yp), bits32(y)[perm])
@@ -116,12 +116,12 @@ def test_pgemm_edge_shapes(N, K, M):
     x = synthetic.bf16_bits_from_f64(rng.normal(0, 1, (M, K)) * rng.choice([1e-4, 1.0, 50.0], (M, K)))
     pk, pk3, xd = dev_weight(w), dev_weight(w3), dev_bf16(x)
     y = host_f64(q4.qmm_window(pk, None, N, K, xd))
-    check_within(y, w, x, label="edge pgemm")
+    check_within(y, w, x, label="edge pgemm", order="window")
     z = host_f64(q4.qmm_window(pk, pk3, N, K, xd))
     a64 = oracle.matmul_rows(w.wq, w.scales, w.biases, x)
     c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, x)
-    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w.wq, w.scales, w.biases, x), K),
-                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, x), K))
+    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w.wq, w.scales, w.biases, x), K, order="window"),
+                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, x), K, order="window"))
     assert np.all(np.abs(z - oracle.swiglu(a64, c64)) <= Tz)
 
 

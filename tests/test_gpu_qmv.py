@@ -30,7 +30,7 @@ def test_c0_single_matvec():
     say("c0 qmv_rows N=512 K=256 R=1")
     y = q4.qmv_rows(dev_weight(w), w.N, w.K, dev_bf16(d["x"]))
     torch.cuda.synchronize()
-    r, ra = check_within(host_f64(y), w, d["x"], label="c0")
+    r, ra = check_within(host_f64(y), w, d["x"], label="c0", order="decode")
     say(f"c0 max err/T {r:.3g} max err/A {ra:.3g}")
 
 
@@ -41,7 +41,7 @@ def test_c2_attention_projections(c2, R):
         w = c2[name]
         y = q4.qmv_rows(c2[pk], w.N, w.K, c2["xd"][:R])
         torch.cuda.synchronize()
-        check_within(host_f64(y), w, c2["x"][:R], label=f"c2 {name} R={R}")
+        check_within(host_f64(y), w, c2["x"][:R], label=f"c2 {name} R={R}", order="decode")
 
 
 def test_c2_rows_bit_equal_to_one_row(c2):
@@ -87,8 +87,8 @@ def test_c1_fused_w13_swiglu():
     z = host_f64(q4.qmv_w13_swiglu(p1, p3, w1.N, w1.K, dev_bf16(d["x"])))
     a64 = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, d["x"])
     c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, d["x"])
-    Ta = tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, d["x"]), w1.K)
-    Tc = tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, d["x"]), w3.K)
+    Ta = tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, d["x"]), w1.K, order="decode")
+    Tc = tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, d["x"]), w3.K, order="decode")
     z64 = oracle.swiglu(a64, c64)
     Tz = tol_swiglu(a64, c64, Ta, Tc)
     ratio = float(np.max(np.abs(z - z64) / Tz))
@@ -116,7 +116,7 @@ def test_c1_w2_float32_input():
     p2 = dev_weight(w2)
     x = d["x_w2_f32"]
     y = host_f64(q4.qmv_rows(p2, w2.N, w2.K, dev_f32(x)))
-    r, _ = check_within(y, w2, x, x_dtype="f32", label="c1 w2 f32")
+    r, _ = check_within(y, w2, x, x_dtype="f32", label="c1 w2 f32", order="decode")
     y1 = bits32(q4.qmv_rows(p2, w2.N, w2.K, dev_f32(x[2:3])))
     y4 = bits32(q4.qmv_rows(p2, w2.N, w2.K, dev_f32(x)))
     assert np.array_equal(y4[2], y1[0])
@@ -133,10 +133,10 @@ def test_c1_decode_chain_against_float64_chain():
     a64 = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, d["x"])
     c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, d["x"])
     z64 = oracle.swiglu(a64, c64)
-    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, d["x"]), w1.K),
-                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, d["x"]), w3.K))
+    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, d["x"]), w1.K, order="decode"),
+                    tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, d["x"]), w3.K, order="decode"))
     y64 = oracle.matmul_rows(w2.wq, w2.scales, w2.biases, z64)
-    bound = tol(oracle.error_weight(w2.wq, w2.scales, w2.biases, np.abs(z64) + Tz), w2.K, "f32") + \
+    bound = tol(oracle.error_weight(w2.wq, w2.scales, w2.biases, np.abs(z64) + Tz), w2.K, "f32", order="decode") + \
         oracle.error_weight(w2.wq, w2.scales, w2.biases, Tz)
     ratio = float(np.max(np.abs(y2 - y64) / bound))
     say(f"c1 chain max err/bound {ratio:.3g}")
@@ -156,10 +156,10 @@ def test_edge_shapes_signed_scales(N, K, R):
     x = synthetic.bf16_bits_from_f64(rng.normal(0, 1, (R, K)) * rng.choice([1e-4, 1.0, 50.0], (R, K)))
     pk = dev_weight(w)
     y = host_f64(q4.qmv_rows(pk, N, K, dev_bf16(x)))
-    check_within(y, w, x, label=f"edge {N}x{K} R={R}")
+    check_within(y, w, x, label=f"edge {N}x{K} R={R}", order="decode")
     xf = (rng.normal(0, 1, (R, K)) * rng.choice([1e-3, 1.0, 30.0], (R, K))).astype(np.float32)
     yf = host_f64(q4.qmv_rows(pk, N, K, dev_f32(xf)))
-    check_within(yf, w, xf, x_dtype="f32", label=f"edge f32 {N}x{K} R={R}")
+    check_within(yf, w, xf, x_dtype="f32", label=f"edge f32 {N}x{K} R={R}", order="decode")
 
 
 def test_zero_activations_give_zero():

@@ -164,7 +164,7 @@ def test_end_to_end_against_float64_matvec(c2):
     q, k, v = _run(c2, case, R, fused=True)
     xs = c2["x"][:R]
     y64 = oracle.matmul_rows(w.wq, w.scales, w.biases, xs)
-    T = tol(oracle.error_weight(w.wq, w.scales, w.biases, xs), w.K)
+    T = tol(oracle.error_weight(w.wq, w.scales, w.biases, xs), w.K, order="decode")
     pos = c2["pos"][:R]
     q64, k64, v64 = oracle.rope_kv(y64, pos, NQ, NKV, case["rot"], case["theta"])
     Tq = T[:, : NQ * 64].reshape(R, NQ, 64)
@@ -248,7 +248,7 @@ def test_gate_against_float64_matvec(c2g):
     _, _, _, g = _run_gate(c2g, CASES[0], R, fused=True)
     wg, xs = c2g["wg"], c2g["x"][:R]
     y64 = oracle.matmul_rows(wg.wq, wg.scales, wg.biases, xs)
-    T = tol(oracle.error_weight(wg.wq, wg.scales, wg.biases, xs), wg.K)
+    T = tol(oracle.error_weight(wg.wq, wg.scales, wg.biases, xs), wg.K, order="decode")
     assert np.all(np.abs(host_f64(g) - y64) <= T)
     qkvg64 = np.concatenate([oracle.matmul_rows(c2g["qkv"].wq, c2g["qkv"].scales, c2g["qkv"].biases, xs), y64], axis=1)
     assert np.array_equal(oracle.attention_gate(qkvg64, NQ, NKV, NG), y64)

@@ -51,6 +51,10 @@ def _oracle(w, fmt, xs):
             oracle.error_weight(w.wq, w.scales, w.biases, xs, bits=fmt))
 
 
+def _tol_fmt(fmt):
+    return "fp8" if fmt == "fp8" else "affine"
+
+
 def _padded_bf16(x_bits, pad):
     M, K = x_bits.shape
     buf = torch.zeros((M, K + pad), dtype=torch.bfloat16, device=DEV)
@@ -99,7 +103,7 @@ def test_decode_sweep(seed):
     _qmv(p, fmt, N, K, xd, y)
     torch.cuda.synchronize()
     y64, A = _oracle(w, fmt, xs)
-    T = tol(A, K, "f32" if xf32 else "bf16")
+    T = tol(A, K, "f32" if xf32 else "bf16", order="decode", fmt=_tol_fmt(fmt))
     got = host_f64(y)
     assert np.all(np.isfinite(got))
     assert np.all(np.abs(got - y64) <= T), f"max err/T {float(np.max(np.abs(got - y64) / T))}"
@@ -125,10 +129,10 @@ def test_window_sweep(seed):
     _window(pa, pb, fmt, N, K, xd, y)
     torch.cuda.synchronize()
     a64, Aa = _oracle(wa, fmt, x)
-    Ta = tol(Aa, K)
+    Ta = tol(Aa, K, order="window", fmt=_tol_fmt(fmt))
     if swiglu:
         c64, Ac = _oracle(wb, fmt, x)
-        ref, bound = oracle.swiglu(a64, c64), tol_swiglu(a64, c64, Ta, tol(Ac, K))
+        ref, bound = oracle.swiglu(a64, c64), tol_swiglu(a64, c64, Ta, tol(Ac, K, order="window", fmt=_tol_fmt(fmt)))
     else:
         ref, bound = a64, Ta
     if out_dtype == torch.bfloat16:

@@ -64,7 +64,7 @@ def test_wide_qmv_bf16_within_tolerance(wide, R):
     cols = np.arange(0, w.N, 7)
     y = q4.qmv_rows(wide["p_qkv"], w.N, w.K, dev_bf16(wide["x"][:R]), bits=wide["bits"])
     torch.cuda.synchronize()
-    check_within(host_f64(y)[:, cols], w, wide["x"][:R], cols=cols, label=f"bits={wide['bits']} R={R}")
+    check_within(host_f64(y)[:, cols], w, wide["x"][:R], cols=cols, label=f"bits={wide['bits']} R={R}", order="decode")
 
 
 @pytest.mark.parametrize("R", [1, 5])
@@ -74,7 +74,7 @@ def test_wide_qmv_f32_within_tolerance(wide, R):
     cols = np.arange(3, w.N, 5)
     y = q4.qmv_rows(wide["p_w2"], w.N, w.K, dev_f32(wide["xf"][:R]), bits=wide["bits"])
     torch.cuda.synchronize()
-    check_within(host_f64(y)[:, cols], w, wide["xf"][:R], cols=cols, x_dtype="f32", label=f"bits={wide['bits']} f32 R={R}")
+    check_within(host_f64(y)[:, cols], w, wide["xf"][:R], cols=cols, x_dtype="f32", label=f"bits={wide['bits']} f32 R={R}", order="decode")
 
 
 def test_wide_rows_bit_equal_to_one_row(wide):
@@ -106,8 +106,8 @@ def test_wide_w13_swiglu(wide, R):
     # the two matrices share the fold of qmv_rows: a and c are the same bits
     a64 = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, wide["x"][:R], bits=bits)
     c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, wide["x"][:R], bits=bits)
-    Ta = tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, wide["x"][:R], bits=bits), w1.K)
-    Tc = tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, wide["x"][:R], bits=bits), w3.K)
+    Ta = tol(oracle.error_weight(w1.wq, w1.scales, w1.biases, wide["x"][:R], bits=bits), w1.K, order="decode")
+    Tc = tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, wide["x"][:R], bits=bits), w3.K, order="decode")
     assert np.all(np.abs(host_f64(a) - a64) <= Ta)
     assert np.all(np.abs(host_f64(c) - c64) <= Tc)
     Tz = tol_swiglu(a64, c64, Ta, Tc)
@@ -138,7 +138,7 @@ def wide_win(request):
 def test_wide_window_plain_parity(wide_win):
     bits, a = wide_win["bits"], wide_win["a"]
     say(f"qmm_window bits={bits} {a.N}x{a.K} M=450 plain")
-    check_within(host_f64(wide_win["plain"])[WIN_ROWS], a, wide_win["x"], rows=WIN_ROWS, label=f"window bits={bits}")
+    check_within(host_f64(wide_win["plain"])[WIN_ROWS], a, wide_win["x"], rows=WIN_ROWS, label=f"window bits={bits}", order="window")
 
 
 def test_wide_window_swiglu_parity(wide_win):
@@ -147,8 +147,8 @@ def test_wide_window_swiglu_parity(wide_win):
     xs = wide_win["x"][WIN_ROWS]
     a64 = oracle.matmul_rows(a.wq, a.scales, a.biases, xs, bits=bits)
     c64 = oracle.matmul_rows(b.wq, b.scales, b.biases, xs, bits=bits)
-    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(a.wq, a.scales, a.biases, xs, bits=bits), a.K),
-                    tol(oracle.error_weight(b.wq, b.scales, b.biases, xs, bits=bits), b.K))
+    Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(a.wq, a.scales, a.biases, xs, bits=bits), a.K, order="window"),
+                    tol(oracle.error_weight(b.wq, b.scales, b.biases, xs, bits=bits), b.K, order="window"))
     z = host_f64(wide_win["swiglu"])[WIN_ROWS]
     assert np.all(np.abs(z - oracle.swiglu(a64, c64)) <= Tz)
 

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synthetic
-from tests.tolerance import tol
+from tests.tolerance import tol_loosest
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -276,7 +276,7 @@ def test_planted_mistakes_fail_the_tolerance(kind, cfg):
     A = oracle.error_weight(wq, sb, bb, x)
     W_bad = _plant(kind, wq, sb, bb, w.K)
     y_bad = oracle.activations_f64(x) @ W_bad.T
-    ratio = np.max(np.abs(y_bad - y) / tol(A, w.K))
+    ratio = np.max(np.abs(y_bad - y) / tol_loosest(A, w.K))
     assert ratio > 1.0, (kind, cfg, ratio)
 
 
@@ -403,7 +403,7 @@ def test_6bit_read_without_straddling_fails():
     exact = oracle.matmul_rows_exact(wq, sb, bb, x, bits=6)
     wrong_wq = synthetic.pack_codes_bits(wrong, 6)
     y_wrong = oracle.matmul_rows(wrong_wq, sb, bb, x, bits=6)
-    T = tol(oracle.error_weight(wq, sb, bb, x, bits=6), K)
+    T = tol_loosest(oracle.error_weight(wq, sb, bb, x, bits=6), K)
     assert np.any(np.abs(y_wrong - exact) > T)
 
 
@@ -468,6 +468,81 @@ def test_fp8_fsum_equals_fraction_bruteforce():
     assert np.all(np.abs(y - exact) <= (192 + 2) * 2.0 ** -52 * A)
 
 
+def _fp8_error_weight_pins(fn):
+    """Facts about A = sum_k |w[n][k]| |x[m][k]| for block-FP8 weights that
+    hold by definition; returns the names of those ``fn`` violates.
+
+    * one-hot: x = c * e_k gives A[n] = |e4m3(w8[n][k])| * |s(n, k)| * |c|,
+      with scales of both signs and a negative c;
+    * all terms positive (positive codes, scales and x): A equals y;
+    * A depends on x through |x| only, and A >= |y| for mixed signs."""
+    failed = set()
+    rng = np.random.default_rng(630)
+    N, K = 256, 256
+    w = _fp8(rng, N, K)
+    sc = w.scales.astype(np.float32).copy()
+    sc[1, 0] = -sc[1, 0]  # a negative block scale
+    s64 = sc.astype(np.float64)
+    for k in (0, 127, 128, 255):
+        for c, pat in ((1.5, 0x3FC0), (-2.0, 0xC000)):
+            x = np.zeros((1, K), dtype=np.uint16)
+            x[0, k] = pat
+            A = fn(w.w8, sc, x)[0]
+            expect = np.abs(oracle.e4m3_to_f64(w.w8[:, k])) * np.abs(s64[np.arange(N) // 128, k // 128]) * abs(c)
+            if not np.array_equal(A, expect):
+                failed.add("one_hot")
+    wp = (w.w8 & 0x7F).astype(np.uint8)
+    wp[wp == 0x7F] = 0x7E
+    xp = _bf16(np.abs(rng.normal(0, 1, (2, K))) + 0.01)
+    sp = np.abs(w.scales).astype(np.float32)
+    yp = oracle.matmul_rows_fp8(wp, sp, xp)
+    if not np.allclose(fn(wp, sp, xp), yp, rtol=1e-13, atol=0):
+        failed.add("positive_equals_y")
+    xm = _bf16(rng.normal(0, 1, (2, K)))
+    neg = (xm ^ 0x8000).astype(np.uint16)
+    absx = (xm & 0x7FFF).astype(np.uint16)
+    A = fn(w.w8, sc, xm)
+    if not (np.array_equal(A, fn(w.w8, sc, neg)) and np.array_equal(A, fn(w.w8, sc, absx))):
+        failed.add("abs_x")
+    if not np.all(np.abs(oracle.matmul_rows_fp8(w.w8, sc, xm)) <= A):
+        failed.add("dominates")
+    return failed
+
+
+def test_fp8_error_weight_pins():
+    assert _fp8_error_weight_pins(oracle.error_weight_fp8) == set()
+
+
+def _ew_fp8_planted(kind):
+    """error_weight_fp8 with one planted slip."""
+
+    def fn(w8, scales, x):
+        X = oracle.activations_f64(x)
+        K = X.shape[1]
+        w8 = np.asarray(w8, dtype=np.uint8)
+        N = w8.shape[0]
+        vals = oracle.e4m3_to_f64(w8)
+        s = np.asarray(scales, dtype=np.float32).astype(np.float64)[np.arange(N) // 128][:, np.arange(K) // 128]
+        if kind == "scale_dropped":
+            W = np.abs(vals)
+        elif kind == "scale_not_abs":
+            W = np.abs(vals) * s
+        elif kind == "x_not_abs":
+            return X @ (np.abs(vals * s)).T
+        elif kind == "w_not_abs":
+            W = vals * s
+        else:
+            raise ValueError(kind)
+        return np.abs(X) @ W.T
+
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["scale_dropped", "scale_not_abs", "x_not_abs", "w_not_abs"])
+def test_fp8_error_weight_planted_slips_fail_its_pins(kind):
+    assert _fp8_error_weight_pins(_ew_fp8_planted(kind)), kind
+
+
 @pytest.mark.parametrize("kind", ["bias8", "block64", "e5m2"])
 def test_fp8_planted_mistakes_fail(kind):
     """Plausible misreadings of the format, planted in a copy of the decode,
@@ -487,7 +562,7 @@ def test_fp8_planted_mistakes_fail(kind):
         vals = sign * np.where(e == 0, m / 4 * 2.0 ** -14, (1 + m / 4) * np.exp2(e - 15.0))
         W = vals * w.scales.astype(np.float64)[np.arange(256) // 128][:, np.arange(256) // 128]
     y = oracle.activations_f64(x) @ W.T
-    T = tol(oracle.error_weight_fp8(w.w8, w.scales, x), 256)
+    T = tol_loosest(oracle.error_weight_fp8(w.w8, w.scales, x), 256, fmt="fp8")
     assert np.any(np.abs(y - exact) > T)
 
 
