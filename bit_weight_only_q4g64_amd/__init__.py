@@ -505,7 +505,7 @@ class RopeKv(ctypes.Structure):
                 ("gamma_k", ctypes.c_void_p), ("eps", ctypes.c_float), ("q_out", ctypes.c_void_p), ("ldq", ctypes.c_int64),
                 ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("cache_dtype", ctypes.c_int32),
                 ("ring_len", ctypes.c_int64), ("n_gate_heads", ctypes.c_int32), ("gate_out", ctypes.c_void_p),
-                ("ldg", ctypes.c_int64)]
+                ("ldg", ctypes.c_int64), ("cache_row_stride", ctypes.c_int64)]
 
 
 def _rope_args(pos, n_q, n_kv, rot, theta, q_out, k_cache, v_cache, gamma_q, gamma_k, eps, gate_out=None):
@@ -521,9 +521,14 @@ def _rope_args(pos, n_q, n_kv, rot, theta, q_out, k_cache, v_cache, gamma_q, gam
         raise ValueError("pos is int32 and q_out float32")
     if k_cache.dtype != v_cache.dtype or k_cache.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("the caches are both float32 or both bfloat16")
-    if tuple(k_cache.shape[1:]) != (n_kv, 64) or tuple(v_cache.shape) != tuple(k_cache.shape) or not k_cache.is_contiguous() \
-            or not v_cache.is_contiguous():
-        raise ValueError("the caches are contiguous [ring][n_kv_heads][64]")
+    if tuple(k_cache.shape[-2:]) != (n_kv, 64) or k_cache.dim() not in (3, 4) or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or not k_cache.is_contiguous() or not v_cache.is_contiguous():
+        raise ValueError("the caches are contiguous [ring][n_kv_heads][64] (one ring for every row) or "
+                         "[rows][ring][n_kv_heads][64] (a ring per row)")
+    if k_cache.dim() == 4 and k_cache.shape[0] < pos.numel():
+        raise ValueError("a per-row cache needs a ring for every row")
+    ring = k_cache.shape[-3]
+    row_stride = ring * n_kv * 64 if k_cache.dim() == 4 else 0
     for g, name in ((gamma_q, "gamma_q"), (gamma_k, "gamma_k")):
         if g is not None:
             _dev(g, name)
@@ -531,8 +536,8 @@ def _rope_args(pos, n_q, n_kv, rot, theta, q_out, k_cache, v_cache, gamma_q, gam
                 raise ValueError(f"{name} is a float32 [64] vector")
     return RopeKv(pos.data_ptr(), n_q, n_kv, rot, theta, None if gamma_q is None else gamma_q.data_ptr(),
                   None if gamma_k is None else gamma_k.data_ptr(), eps, q_out.data_ptr(), _rowmajor(q_out, "q_out"),
-                  k_cache.data_ptr(), v_cache.data_ptr(), Q4_F32 if k_cache.dtype == torch.float32 else Q4_BF16, k_cache.shape[0],
-                  n_gate, gate_ptr, ldg)
+                  k_cache.data_ptr(), v_cache.data_ptr(), Q4_F32 if k_cache.dtype == torch.float32 else Q4_BF16, ring,
+                  n_gate, gate_ptr, ldg, row_stride)
 
 
 def rope_kv_store(qkv: torch.Tensor, pos: torch.Tensor, n_q: int, n_kv: int, rot: int, theta: float, q_out: torch.Tensor,

@@ -360,6 +360,10 @@ int check_rope_args(const char* fn, const q4_rope_kv* a, int R, q4::RopeKvArgs* 
     if (a->ldg < (int64_t)a->n_gate_heads * 64) return fail(Q4_EINVAL, "%s: ldg=%lld < n_gate_heads * 64", fn, (long long)a->ldg);
     if (int rc = check_ptr(fn, "gate_out", a->gate_out, 4)) return rc;
   }
+  if (a->cache_row_stride < 0) return fail(Q4_EINVAL, "%s: cache_row_stride=%lld < 0", fn, (long long)a->cache_row_stride);
+  if (a->cache_row_stride > 0 && a->cache_row_stride < a->ring_len * a->n_kv_heads * 64)
+    return fail(Q4_EINVAL, "%s: cache_row_stride=%lld is below ring_len * n_kv_heads * 64: the rows' rings would overlap", fn,
+                (long long)a->cache_row_stride);
   (void)R;
   q4::RopeKvArgs r{};
   for (int i = 0; i < a->rot_dims / 2; ++i) r.inv[i] = pow((double)a->theta, -2.0 * (double)i / (double)a->rot_dims);
@@ -377,6 +381,7 @@ int check_rope_args(const char* fn, const q4_rope_kv* a, int R, q4::RopeKvArgs* 
   r.v_cache = a->v_cache;
   r.cache_bf16 = a->cache_dtype == Q4_BF16;
   r.ring = a->ring_len;
+  r.row_stride = a->cache_row_stride;
   r.n_gate = a->n_gate_heads;
   r.gate_out = a->n_gate_heads > 0 ? a->gate_out : nullptr;
   r.ldg = a->n_gate_heads > 0 ? a->ldg : 0;
@@ -413,7 +418,7 @@ int qkv_rope_launch_bits(int spw, int nv, const uint8_t* pk, int N, int K, const
 
 extern "C" {
 
-int q4g64_abi_version(void) { return 2; }
+int q4g64_abi_version(void) { return 3; }
 
 const char* q4_last_error(void) { return g_err; }
 

@@ -13,7 +13,8 @@
 //     modulo 2 pi in double and rounded once to float for sincosf:
 //       x_i' = fma(x_i, c, -(x_{i+h} s)),  x_{i+h}' = fma(x_{i+h}, c, x_i s);
 //   * q goes to q_out[r], k and v to slot pos mod ring of their caches
-//     ([ring][kv_heads][64], float32 or bf16 rounded to nearest even);
+//     ([ring][kv_heads][64], float32 or bf16 rounded to nearest even; row r's
+//     ring starts row_stride * r elements in, 0 = one ring for all rows);
 //   * gate heads (gated attention's fourth matvec, after the v heads) go to
 //     gate_out[r] unchanged.
 // The same function serves the stand-alone epilogue and the fused matvec, so
@@ -40,6 +41,7 @@ struct RopeKvArgs {
   void* v_cache;
   int cache_bf16;
   int64_t ring;
+  int64_t row_stride;  // elements between the rows' rings (0: one shared ring)
   int n_gate;
   float* gate_out;
   int64_t ldg;
@@ -85,7 +87,7 @@ __device__ __forceinline__ void rope_kv_head(float x, int d, int hd, int r, cons
   int64_t slot = a.ring > 0 ? (int64_t)p % a.ring : 0;
   if (slot < 0) slot += a.ring;
   const int kvh = is_k ? hd - a.n_q : hd - a.n_q - a.n_kv;
-  const int64_t at = (slot * a.n_kv + kvh) * kHeadDim + d;
+  const int64_t at = (int64_t)r * a.row_stride + (slot * a.n_kv + kvh) * kHeadDim + d;
   void* cache = is_k ? a.k_cache : a.v_cache;
   if (a.cache_bf16) ((uint16_t*)cache)[at] = f32_to_bf16_rne(x);
   else ((float*)cache)[at] = x;

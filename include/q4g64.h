@@ -281,6 +281,13 @@ int qmm_cut_fp8b(const void* packed_a, const void* packed_b, int64_t N, int64_t 
  *   - q goes to q_out; k and v go to slot pos mod ring_len of k_cache and
  *     v_cache, each [ring_len][n_kv_heads][64] of cache_dtype (Q4_F32, or
  *     Q4_BF16 rounded to nearest even). Other slots are not touched;
+ *   - rows of separate streams keep separate rings: row r writes the ring
+ *     that starts cache_row_stride * r elements after k_cache (v_cache).
+ *     cache_row_stride = 0 makes every row write one shared ring; rows whose
+ *     slots coincide then write the same words and which row's values
+ *     remain is undefined (the positions are device data, so the host
+ *     cannot check). A nonzero stride must be at least ring_len *
+ *     n_kv_heads * 64, so the rows' rings do not overlap;
  *   - gated attention's fourth matvec: n_gate_heads further heads may follow
  *     the v heads in the stacked output (PR #1696, "What it adds": gated GQA
  *     attention; decode fuses the four attention matvecs). Their values go
@@ -306,6 +313,7 @@ typedef struct q4_rope_kv {
   int32_t n_gate_heads;   /* >= 0 gate heads after the v heads */
   float* gate_out;        /* float32 [R][ldg], ldg >= n_gate_heads * 64; may be NULL when n_gate_heads = 0 */
   int64_t ldg;
+  int64_t cache_row_stride; /* elements between row r's ring and row r+1's; 0 = one shared ring (ABI 3) */
 } q4_rope_kv;
 
 /* The epilogue alone, on a float32 q/k/v(/gate) output qkv [R][ldqkv], ldqkv

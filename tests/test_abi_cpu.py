@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared():
         assert hasattr(lib, name), name
     assert set(_declared()) == set(q4._SIGNATURES)
-    assert lib.q4g64_abi_version() == 2
+    assert lib.q4g64_abi_version() == 3
 
 
 def test_packed_bytes():
@@ -323,7 +323,8 @@ def _rope(**kw):
     (dict(rot_dims=66), q4.Q4_EINVAL), (dict(theta=0.0), q4.Q4_EINVAL), (dict(theta=float("inf")), q4.Q4_EINVAL),
     (dict(eps=-1.0), q4.Q4_EINVAL), (dict(cache_dtype=7), q4.Q4_EINVAL), (dict(ring_len=0), q4.Q4_EINVAL),
     (dict(ldq=100), q4.Q4_EINVAL), (dict(pos=None), q4.Q4_EALIGN), (dict(q_out=FAKE + 2), q4.Q4_EALIGN),
-    (dict(k_cache=None), q4.Q4_EALIGN), (dict(gamma_q=FAKE + 1), q4.Q4_EALIGN)])
+    (dict(k_cache=None), q4.Q4_EALIGN), (dict(gamma_q=FAKE + 1), q4.Q4_EALIGN),
+    (dict(cache_row_stride=-1), q4.Q4_EINVAL), (dict(cache_row_stride=64 * 8 * 64 - 1), q4.Q4_EINVAL)])
 def test_rope_args_rejected(kw, code):
     a = _rope(**kw)
     rc, _ = _rc("rope_kv_store", FAKE, 3072, 1, ctypes.addressof(a), None)

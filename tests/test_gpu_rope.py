@@ -253,3 +253,43 @@ def test_gate_against_float64_matvec(c2g):
     qkvg64 = np.concatenate([oracle.matmul_rows(c2g["qkv"].wq, c2g["qkv"].scales, c2g["qkv"].biases, xs), y64], axis=1)
     assert np.array_equal(oracle.attention_gate(qkvg64, NQ, NKV, NG), y64)
 
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_rows_at_the_same_position_keep_separate_rings(c2, fused):
+    """Rows of separate streams at one position (equal ring slots) write
+    rings of their own ([rows][ring][kv][64] caches): each row's ring equals
+    that row's one-row call, and the other slots stay untouched."""
+    case = CASES[1]
+    R = 4
+    pos_np = np.array([7, 7, 7 + RING, 300], dtype=np.int32)  # rows 0..2 share slot 7
+    say(f"per-row rings, equal slots, fused={fused}")
+    gq, gk = _gammas(c2, case)
+    w = c2["qkv"]
+
+    def call(rows, pos, k, v):
+        q = torch.full((len(rows), NQ * 64), float("nan"), device=DEV)
+        xr = c2["xd"][rows[0] : rows[-1] + 1]
+        if fused:
+            q4.qmv_qkv_rope(c2["p"], w.K, xr, pos, NQ, NKV, case["rot"], case["theta"], q, k, v, gq, gk)
+        else:
+            y = q4.qmv_rows(c2["p"], w.N, w.K, xr)
+            q4.rope_kv_store(y, pos, NQ, NKV, case["rot"], case["theta"], q, k, v, gq, gk)
+        return q
+
+    k = torch.full((R, RING, NKV, 64), float("nan"), device=DEV)
+    v = torch.full((R, RING, NKV, 64), float("nan"), device=DEV)
+    q = call(list(range(R)), torch.from_numpy(pos_np).to(DEV), k, v)
+    torch.cuda.synchronize()
+    for r in range(R):
+        k1 = torch.full((RING, NKV, 64), float("nan"), device=DEV)
+        v1 = torch.full((RING, NKV, 64), float("nan"), device=DEV)
+        q1 = call([r], torch.from_numpy(pos_np[r : r + 1]).to(DEV), k1, v1)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits32(q1)[0], bits32(q)[r])
+        assert np.array_equal(bits32(k1), bits32(k[r])), r
+        assert np.array_equal(bits32(v1), bits32(v[r])), r
+        slot = int(pos_np[r]) % RING
+        written = torch.zeros(RING, dtype=torch.bool)
+        written[slot] = True
+        assert torch.isnan(k[r][~written]).all() and not torch.isnan(k[r][slot]).any()
