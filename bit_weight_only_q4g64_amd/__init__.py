@@ -59,6 +59,9 @@ _SIGNATURES = {
     "qmv_window_costs": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P, _I64, ctypes.c_int, _P, _P]),
     "qmv_window_cost": (ctypes.c_float, [_P, ctypes.c_int]),
     "q4g64_ffn_work_bytes": (ctypes.c_size_t, [_I64, ctypes.c_int]),
+    "qmv_split_work_bytes": (ctypes.c_size_t, [ctypes.c_int, _I64, _I64, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "qmv_rows_split": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, ctypes.c_int, _I64, ctypes.c_int, _P, _I64, ctypes.c_int,
+                                      _P, ctypes.c_size_t, _P]),
     "qmv_ffn": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P, _I64, _P, _P]),
     "q4_last_error": (ctypes.c_char_p, []),
 }
@@ -217,6 +220,34 @@ def qmv_rows(packed: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Ten
     else:
         _check("qmv_rows_qg64",
                lib().qmv_rows_qg64(bits, packed.data_ptr(), N, K, _x_ptr(x), xd, ldx, R, y.data_ptr(), _rowmajor(y, "y"), _stream()))
+    return y
+
+
+def split_work_bytes(N: int, K: int, x_dtype: int, R: int, splits: int = 0, bits: int = 4) -> int:
+    """Workspace bytes qmv_rows_split needs for this shape (0: invalid arguments)."""
+    return int(lib().qmv_split_work_bytes(bits, N, K, x_dtype, R, splits))
+
+
+def split_workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled, 256-byte aligned device workspace for qmv_rows_split (torch's allocations are)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def qmv_rows_split(packed: torch.Tensor, N: int, K: int, x: torch.Tensor, work: torch.Tensor, y: torch.Tensor | None = None,
+                   splits: int = 0, bits: int = 4) -> torch.Tensor:
+    """qmv_rows with K split over several workgroups per column tile (bit-identical to qmv_rows); ``work`` is a
+    workspace from split_workspace() of at least split_work_bytes() bytes, not shared by concurrent calls."""
+    _dev(packed, "packed")
+    _dev(x.data if isinstance(x, TiledPlanes) else x, "x")
+    _dev(work, "work")
+    xd, ldx, R = _x_arg(x)
+    dev = x.data.device if isinstance(x, TiledPlanes) else x.device
+    if y is None:
+        y = torch.empty((R, N), dtype=torch.float32, device=dev)
+    if y.dtype != torch.float32 or y.shape[0] < R:
+        raise ValueError("y must be float32 with at least R rows")
+    _check("qmv_rows_split", lib().qmv_rows_split(bits, packed.data_ptr(), N, K, _x_ptr(x), xd, ldx, R, y.data_ptr(),
+                                                  _rowmajor(y, "y"), splits, work.data_ptr(), work.numel(), _stream()))
     return y
 
 

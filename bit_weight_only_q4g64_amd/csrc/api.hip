@@ -142,6 +142,10 @@ int unpack_impl(const char* fn, int bits, const void* packed, int64_t N, int64_t
   return launched(fn);
 }
 
+// Decode activation forms: 0 bf16 rows, 1 float32 rows, 2 float32 rows as three
+// bf16 planes, 3 the planes in fragment order.
+int xmode_of(int x_dtype) { return x_dtype == Q4_F32 ? 1 : (x_dtype == Q4_BF16X3 ? 2 : (x_dtype == Q4_BF16X3T ? 3 : 0)); }
+
 int qmv_rows_impl(const char* fn, int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx,
                   int R, float* y, int64_t ldy, hipStream_t s) {
   if (int rc = check_fmt(fn, bits)) return rc;
@@ -158,8 +162,57 @@ int qmv_rows_impl(const char* fn, int bits, const void* packed, int64_t N, int64
   if (K > q4::kQmvMaxK) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
   const size_t lds = q4::qmv_lds_bytes(K, x_dtype != Q4_BF16, 1, R);
   if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
-  const int xmode = x_dtype == Q4_F32 ? 1 : (x_dtype == Q4_BF16X3 ? 2 : (x_dtype == Q4_BF16X3T ? 3 : 0));
-  q4::qmv_launch((const uint8_t*)packed, (const uint8_t*)packed, 1, (int)N, (int)K, x, xmode, ldx, R, y, ldy, s, bits);
+  q4::qmv_launch((const uint8_t*)packed, (const uint8_t*)packed, 1, (int)N, (int)K, x, xmode_of(x_dtype), ldx, R, y, ldy, s, bits);
+  return launched(fn);
+}
+
+// K split of a one-matrix matvec: workgroups per column tile. 0 picks the
+// smallest power of two that gives at least one workgroup per CU, with at
+// least one segment each; the result never depends on the choice.
+constexpr int kSplitMax = 16;
+constexpr int kSplitTargetWgs = 256;
+int split_shares(int splits, int xmode, int64_t N, int64_t K, int R) {
+  const int nseg = q4::qmv_segments(K);
+  if (splits > 0) return splits < nseg ? splits : nseg;
+  int s = 1;
+  while (2 * s <= nseg && 2 * s <= kSplitMax) {
+    const q4::QmvSplitShape sh = q4::qmv_split_shape(1, xmode, (int)N, (int)K, R, s);
+    if (sh.tile_ids * s >= kSplitTargetWgs) break;
+    s *= 2;
+  }
+  return s;
+}
+
+int qmv_split_check(const char* fn, int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx,
+                    int R, float* y, int64_t ldy, int splits) {
+  if (int rc = check_fmt(fn, bits)) return rc;
+  if (int rc = check_nk(fn, N, K)) return rc;
+  if (R < 1 || R > 16) return fail(Q4_EINVAL, "%s: R=%d is outside 1..16", fn, R);
+  if (splits < 0 || splits > kSplitMax) return fail(Q4_EINVAL, "%s: splits=%d is outside 0..%d", fn, splits, kSplitMax);
+  if (int rc = check_ptr(fn, "packed", packed, 16)) return rc;
+  if (int rc = check_x(fn, x, x_dtype, ldx, K)) return rc;
+  if (int rc = check_ptr(fn, "y", y, 4)) return rc;
+  if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  const int64_t xrows = x_dtype == Q4_BF16X3 ? 3 * (int64_t)R : R;
+  if (xrows * ldx * (x_dtype == Q4_F32 ? 4 : 2) >= (int64_t(1) << 31))
+    return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
+  if (K > q4::kQmvMaxK) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
+  const size_t lds = q4::qmv_lds_bytes(K, x_dtype != Q4_BF16, 1, R);
+  if (lds > kMaxLds) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the decode limit of 16384", fn, (long long)K);
+  return Q4_OK;
+}
+
+// The split matvec on a workspace of at least work_bytes (checked by the caller).
+int qmv_split_launch(const char* fn, int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx,
+                     int R, float* y, int64_t ldy, int nshare, uint8_t* work, hipStream_t s) {
+  const int xmode = xmode_of(x_dtype);
+  q4::QmvSplit sp{nshare, nullptr, nullptr};
+  if (nshare > 1) {
+    const q4::QmvSplitShape sh = q4::qmv_split_shape(1, xmode, (int)N, (int)K, R, nshare);
+    sp.cnt = (uint32_t*)work;
+    sp.part = (float*)(work + q4::qmv_split_counter_bytes(sh));
+  }
+  q4::qmv_launch((const uint8_t*)packed, (const uint8_t*)packed, 1, (int)N, (int)K, x, xmode, ldx, R, y, ldy, s, bits, 0, sp);
   return launched(fn);
 }
 
@@ -276,8 +329,7 @@ int ffn_launch_t(const uint8_t* p1, const uint8_t* p3, const uint8_t* p2, int N1
   const int xl2 = q4::ffn_lds_bytes(K1, N1, R, true) <= q4::qmv_max_lds();
   lds = q4::ffn_lds_bytes(K1, N1, R, xl2 != 0);
   auto kern = q4::ffn_kernel<NV, RTF, SPW1, SPW2>;
-  static const bool lds_ok =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)q4::qmv_max_lds()) == hipSuccess;
+  static const bool lds_ok = q4::allow_max_dynamic_lds((const void*)kern);
   (void)lds_ok;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -393,8 +445,7 @@ template <int SPW, int NV, int BITS>
 int qkv_rope_launch_t(const uint8_t* pk, int N, int K, const uint16_t* x, int64_t ldx, int R, const q4::RopeKvArgs& a, size_t lds,
                       int heads, hipStream_t s) {
   auto kern = q4::qkv_rope_kernel<SPW, NV, BITS>;
-  static const bool lds_ok =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)q4::qmv_max_lds()) == hipSuccess;
+  static const bool lds_ok = q4::allow_max_dynamic_lds((const void*)kern);
   (void)lds_ok;
   hipLaunchKernelGGL(kern, dim3((unsigned)heads), dim3(q4::kQkvWaves * 64), lds, s, pk, N, K, x, ldx, R, a);
   return launched("qmv_qkv_rope");
@@ -418,7 +469,7 @@ int qkv_rope_launch_bits(int spw, int nv, const uint8_t* pk, int N, int K, const
 
 extern "C" {
 
-int q4g64_abi_version(void) { return 3; }
+int q4g64_abi_version(void) { return 4; }
 
 const char* q4_last_error(void) { return g_err; }
 
@@ -656,6 +707,30 @@ int qmv_qkv_rope(int bits, const void* packed_qkv, int64_t K, const uint16_t* x,
   if (bits == 6) return qkv_rope_launch_bits<6>(spw, nv, pk, (int)N, (int)K, x, ldx, R, a, lds, heads, s);
   if (bits == 8) return qkv_rope_launch_bits<8>(spw, nv, pk, (int)N, (int)K, x, ldx, R, a, lds, heads, s);
   return qkv_rope_launch_bits<4>(spw, nv, pk, (int)N, (int)K, x, ldx, R, a, lds, heads, s);
+}
+
+size_t qmv_split_work_bytes(int bits, int64_t N, int64_t K, int x_dtype, int R, int splits) {
+  if ((bits != 4 && bits != 6 && bits != 8) || N <= 0 || K <= 0 || N % 64 || K % 64 || N > kMaxDim || K > q4::kQmvMaxK || R < 1 ||
+      R > 16 || splits < 0 || splits > kSplitMax)
+    return 0;
+  if (x_dtype != Q4_BF16 && x_dtype != Q4_F32 && x_dtype != Q4_BF16X3 && x_dtype != Q4_BF16X3T) return 0;
+  const int xmode = xmode_of(x_dtype);
+  const int nshare = split_shares(splits, xmode, N, K, R);
+  return q4::qmv_split_work_bytes(1, xmode, (int)N, (int)K, R, nshare);
+}
+
+int qmv_rows_split(int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R, float* y,
+                   int64_t ldy, int splits, void* work, size_t work_bytes, void* stream) {
+  const char* fn = "qmv_rows_split";
+  if (int rc = qmv_split_check(fn, bits, packed, N, K, x, x_dtype, ldx, R, y, ldy, splits)) return rc;
+  const int xmode = xmode_of(x_dtype);
+  const int nshare = split_shares(splits, xmode, N, K, R);
+  if (nshare > 1) {
+    const size_t need = q4::qmv_split_work_bytes(1, xmode, (int)N, (int)K, R, nshare);
+    if (int rc = check_ptr(fn, "work", work, 256)) return rc;
+    if (work_bytes < need) return fail(Q4_EINVAL, "%s: work_bytes=%zu < %zu needed for this shape", fn, work_bytes, need);
+  }
+  return qmv_split_launch(fn, bits, packed, N, K, x, x_dtype, ldx, R, y, ldy, nshare, (uint8_t*)work, (hipStream_t)stream);
 }
 
 static const int kCostRows[5] = {1, 2, 4, 8, 16};

@@ -92,19 +92,21 @@ struct QmvWeights {
 // Issue every weight load of segments seg0 + j * step (j < SPW), with the
 // streaming cache policy (each weight is read once per launch). Pair indices
 // past the matrix are clamped to its last pair (those values are never
-// used). Lanes with on == false read past the buffer's end, which the
-// hardware answers with zeros and no memory access: the loads stay
-// unconditional, so the count of loads in flight is the same on every path.
+// used). Lanes with on == false, and slots at or past seg_end, read past the
+// buffer's end, which the hardware answers with zeros and no memory access:
+// the loads stay unconditional, so the count of loads in flight is the same
+// on every path.
 template <int NMAT, int SPW, int BITS = 4>
 __device__ __forceinline__ void qmv_issue_weights(QmvWeights<NMAT, SPW, BITS>& w, const rsrc_t (&cres)[NMAT], const rsrc_t (&sres)[NMAT],
-                                                  int seg0, int step, int P, int lane, bool on) {
+                                                  int seg0, int step, int P, int lane, bool on, int seg_end = 0x7fffffff) {
   const int i = lane & 15;
   constexpr uint32_t kPcb = pair_code_bytes(BITS);
-  const uint32_t cv = on ? (uint32_t)lane * 16u : kOffBuffer, sv = on ? (uint32_t)i * 8u : kOffBuffer;
-  const uint32_t cv8 = on ? (uint32_t)lane * 8u : kOffBuffer;
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int seg = seg0 + j * step;
+    const bool onj = on && seg < seg_end;
+    const uint32_t cv = onj ? (uint32_t)lane * 16u : kOffBuffer, sv = onj ? (uint32_t)i * 8u : kOffBuffer;
+    const uint32_t cv8 = onj ? (uint32_t)lane * 8u : kOffBuffer;
 #pragma unroll
     for (int pp = 0; pp < kSegPairs; ++pp) {
       int p = seg * kSegPairs + pp;
@@ -296,10 +298,23 @@ __device__ __forceinline__ void qmv_ordered_sum(float (&tot)[NMAT][kRT][kPerLane
 // "matrices" are column tiles 2t and 2t + 1 of one matrix, each written as
 // its own float32 columns (twice the weight loads in flight per wave; every
 // column's arithmetic is the one-tile kernel's).
+//
+// K split (sp.nshare > 1): the sp.nshare workgroups along z of one column
+// tile each fold a run of consecutive segments and store their partials in
+// the caller's workspace; the last of them to arrive (an agent-scope counter
+// per tile, which it resets) reads the others' partials and adds all of the
+// tile's segments in the same ascending order, so the results are the
+// unsplit kernel's bit for bit.
+struct QmvSplit {
+  int nshare;     // workgroups per column tile along z (1: no split)
+  float* part;    // [tile id][segment][values per segment], tile id = x + gridDim.x * y
+  uint32_t* cnt;  // [tile id] arrival counters, zero between calls
+};
+
 template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS, int Y3 = 0>
 __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* __restrict__ pk0, const uint8_t* __restrict__ pk1,
                                                               int N, int K, const void* __restrict__ xv, int64_t ldx, int R,
-                                                              float* __restrict__ y, int64_t ldy) {
+                                                              float* __restrict__ y, int64_t ldy, QmvSplit sp) {
   static_assert(!Y3 || NMAT == 2, "the three-plane output is the fused SwiGLU's");
   static_assert(XF32 != 3 || !XLDS, "fragment-ordered planes are read from memory");
   constexpr int kRT = XF32 ? RTF : 1;  // row tiles
@@ -329,7 +344,13 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   const int P = (G + 1) / 2;
   const int nseg = qmv_segments(K);
   const int64_t cb = codes_bytes(N, K, BITS);
-  const int xsi = (int)qmv_xs_stride(K);
+  // this workgroup's segments [sb, se) and the k range [kb, kb + kl) they read
+  const int per = (nseg + sp.nshare - 1) / sp.nshare;
+  const int sb = (int)blockIdx.z * per;
+  const int se = sb + per < nseg ? sb + per : nseg;
+  const int kb = sb * kSegGroups * kGroup;
+  const int kl = (se * kSegGroups * kGroup < K ? se * kSegGroups * kGroup : K) - kb;
+  const int xsi = (int)qmv_xs_stride(kl);
   const uint32_t xrow = (uint32_t)(ldx * kXElem);  // bytes per activation row
 
   // buffer resources: this column tile's codes and scale/bias, and x
@@ -352,7 +373,7 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   // eight loads in flight where the weight registers leave room, else four
   constexpr int kBatch = (XF32 || SPW * NMAT * code_bits(BITS) > 8) ? 4 : 8;
   const int nthr = blockDim.x;
-  const int per_row = K * kXElem / 16;  // 16-byte chunks per row
+  const int per_row = kl * kXElem / 16;  // 16-byte chunks per staged row
   const int total = XR * per_row;
   const int nslots = (total + nthr - 1) / nthr;
   // (row, chunk) of slot 0, and the step from one slot to the next
@@ -365,7 +386,7 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   };
   auto xload = [&](int r, int c) -> u32x4 {
     if (r >= XR) { r = XR - 1; c = per_row - 1; }  // past the last chunk: a valid, unused read
-    return buf_load16(xres, (uint32_t)c * 16u + (uint32_t)r * xrow, 0u);
+    return buf_load16(xres, (uint32_t)c * 16u + (uint32_t)r * xrow, (uint32_t)kb * kXElem);
   };
   // PRE (one row tile, one slot per lane, codes of at most 64 registers once
   // converted): the weights are requested first and their codes converted
@@ -373,7 +394,7 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   // barrier then run only matrix steps and fmas
   constexpr bool kPre = XLDS && kRT == 1 && kPerLane == 1 && SPW * NMAT * kSegGroups * 2 <= 16;
   QmvWeights<NMAT, SPW, BITS> wts;
-  if constexpr (kPre) qmv_issue_weights<NMAT, SPW, BITS>(wts, cres, sres, wave, nwaves, P, lane, true);
+  if constexpr (kPre) qmv_issue_weights<NMAT, SPW, BITS>(wts, cres, sres, sb + wave, nwaves, P, lane, true, se);
   u32x4 xv0[kBatch];
   if constexpr (XLDS) {
     int r = r0, c = c0;
@@ -386,7 +407,7 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   }
 
   // 2) every weight load of this wave's segments
-  if constexpr (!kPre) qmv_issue_weights<NMAT, SPW, BITS>(wts, cres, sres, wave, nwaves, P, lane, true);
+  if constexpr (!kPre) qmv_issue_weights<NMAT, SPW, BITS>(wts, cres, sres, sb + wave, nwaves, P, lane, true, se);
   bf16x8 qpre[SPW][NMAT][kSegGroups][2];
   if constexpr (kPre) {
 #pragma unroll
@@ -457,7 +478,7 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   auto xfrag = [&](int rt, int g, int hh) -> bf16x8 {
     const int k0 = g * kGroup + hh * 32 + kc * 8;
     if constexpr (!XF32) {
-      if constexpr (XLDS) return __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + frow * xsi + k0));
+      if constexpr (XLDS) return __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + frow * xsi + (k0 - kb)));
       else return __builtin_bit_cast(bf16x8, buf_load16(xres, (uint32_t)frow * xrow + (uint32_t)k0 * 2u, 0u));
     } else if constexpr (XF32 == 3) {
       return __builtin_bit_cast(bf16x8, buf_load16(xres, (uint32_t)((((g * T + rt0 + rt) * 2 + hh) * 64 + lane) * 16), 0u));
@@ -466,7 +487,7 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
       row = row < R ? row : R - 1;
       int piece = i & 3;
       piece = piece < 3 ? piece : 2;
-      if constexpr (XLDS) return __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + (piece * R + row) * xsi + k0));
+      if constexpr (XLDS) return __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + (piece * R + row) * xsi + (k0 - kb)));
       else if constexpr (XF32 == 2) return __builtin_bit_cast(bf16x8, buf_load16(xres, (uint32_t)(piece * R + row) * xrow + (uint32_t)k0 * 2u, 0u));
       else {
         const u32x4 a = buf_load16(xres, (uint32_t)row * xrow + (uint32_t)k0 * 4u, 0u);
@@ -493,8 +514,8 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
   float keep[SPW][NMAT][kRT][kPerLane];
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
-    const int seg = wave + j * nwaves;
-    if (seg >= nseg) break;
+    const int seg = sb + wave + j * nwaves;
+    if (seg >= se) break;
     if constexpr (kPre) {
       auto qfrag = [&](int m, int gg, int h) { return qpre[j][m][gg][h]; };
       qmv_fold_segment<XF32, NMAT, kRT, kPerLane, kAhead>(keep[j], wts.cw[j], wts.sbw[j], seg * kSegGroups, G, xfrag, qfrag);
@@ -503,18 +524,49 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
     }
   }
   if constexpr (XLDS) __syncthreads();
+  constexpr int kSegVals = NMAT * kRT * kPerLane * 64;  // partials per segment
+  const int64_t tid = (int64_t)t + (int64_t)gridDim.x * blockIdx.y;
+  uint32_t* wpart = (uint32_t*)sp.part + tid * nseg * kSegVals;
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
-    const int seg = wave + j * nwaves;
-    if (seg >= nseg) break;
+    const int seg = sb + wave + j * nwaves;
+    if (seg >= se) break;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
-        for (int v = 0; v < kPerLane; ++v) part[qmv_part_index<NMAT, kRT, kPerLane>(seg, m, rt, v, lane)] = keep[j][m][rt][v];
+        for (int v = 0; v < kPerLane; ++v) {
+          const int at = qmv_part_index<NMAT, kRT, kPerLane>(seg, m, rt, v, lane);
+          part[at] = keep[j][m][rt][v];
+          // agent-scope stores: coherent for a workgroup on any XCD
+          if (sp.nshare > 1) __hip_atomic_store(wpart + at, __float_as_uint(keep[j][m][rt][v]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+  }
+  if (sp.nshare > 1) {
+    // every partial of this wave is stored before the workgroup arrives
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
+  if (sp.nshare > 1) {
+    __shared__ uint32_t s_last;
+    if (threadIdx.x == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(sp.cnt + tid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t last = old == (uint32_t)(sp.nshare - 1);
+      // every workgroup of this tile has arrived: the counter is free for the next call
+      if (last) __hip_atomic_store(sp.cnt + tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // the last arrival: the other workgroups' segments, from the workspace
+    for (int at = (int)threadIdx.x; at < nseg * kSegVals; at += nthr) {
+      const int seg = at / kSegVals;
+      if (seg >= sb && seg < se) continue;
+      part[at] = __uint_as_float(__hip_atomic_load(wpart + at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    }
+    __syncthreads();
+  }
   if (wave != 0) return;
 
   // 5) add the segments in ascending order; epilogue
@@ -574,91 +626,123 @@ inline size_t qmv_max_lds() {
   return cached;
 }
 
+// Let a kernel use the largest dynamic LDS a workgroup may have beside the
+// kernel's own static LDS. A failed query or setting keeps the 64 KiB default
+// and clears the error it raised, so that the launch after it reports only
+// its own status.
+inline bool allow_max_dynamic_lds(const void* kern) {
+  hipFuncAttributes fa{};
+  size_t stat = 0;
+  if (hipFuncGetAttributes(&fa, kern) == hipSuccess) stat = fa.sharedSizeBytes;
+  const size_t mx = qmv_max_lds();
+  const bool ok = mx > stat && hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(mx - stat)) == hipSuccess;
+  if (!ok) (void)hipGetLastError();
+  return ok;
+}
+
 // LDS needed without staging (partials only); the launch adds the staged
 // activations when they fit.
 inline size_t qmv_lds_bytes(int64_t K, int xf32, int nmat, int R) {
   return qmv_part_bytes(K, xf32, nmat, qmv_row_tiles(xf32, R), xf32 ? 1 : qmv_nv(R));
 }
 
+// Segments per workgroup of a tile split nshare ways, and the k extent of
+// the activations such a workgroup stages.
+__host__ __device__ inline int qmv_share_segments(int64_t K, int nshare) { return (qmv_segments(K) + nshare - 1) / nshare; }
+__host__ __device__ inline int64_t qmv_share_k(int64_t K, int nshare) {
+  const int64_t k = (int64_t)qmv_share_segments(K, nshare) * kSegGroups * kGroup;
+  return k < K ? k : K;
+}
+
 template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS, int Y3>
 inline void qmv_launch_t(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
-                         int64_t ldy, int nwaves, size_t lds, hipStream_t s) {
+                         int64_t ldy, int nwaves, size_t lds, hipStream_t s, const QmvSplit& sp) {
   // float32 rows: the row tiles not covered by RTF go to more workgroups along y
   const unsigned ysplit = XF32 ? (unsigned)(qmv_row_tiles(1, R) / RTF) : 1u;
   auto kern = qmv_kernel<XF32, NMAT, SPW, RTF, XLDS, NV, BITS, Y3>;
   // allow dynamic LDS beyond the 64 KB default, once per instantiation
-  static const bool lds_ok =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)qmv_max_lds()) == hipSuccess;
+  static const bool lds_ok = allow_max_dynamic_lds((const void*)kern);
   (void)lds_ok;
   const unsigned gx = (unsigned)(N / kTileN / (Y3 == 3 ? 2 : 1));
-  hipLaunchKernelGGL(kern, dim3(gx, ysplit), dim3(nwaves * 64), lds, s, pk0, pk1, N, K, x, ldx, R, y, ldy);
+  hipLaunchKernelGGL(kern, dim3(gx, ysplit, (unsigned)sp.nshare), dim3(nwaves * 64), lds, s, pk0, pk1, N, K, x, ldx, R, y, ldy, sp);
 }
 
 template <int XF32, int NMAT, int RTF, bool XLDS, int NV, int BITS, int Y3>
 inline void qmv_launch_spw(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
-                           int64_t ldy, size_t lds, hipStream_t s) {
-  const int nseg = qmv_segments(K);
-  const int nwaves = nseg < kQmvMaxWaves ? nseg : kQmvMaxWaves;
-  const int spw = (nseg + nwaves - 1) / nwaves;
+                           int64_t ldy, size_t lds, hipStream_t s, const QmvSplit& sp) {
+  const int per = qmv_share_segments(K, sp.nshare);
+  const int nwaves = per < kQmvMaxWaves ? per : kQmvMaxWaves;
+  const int spw = (per + nwaves - 1) / nwaves;
   if (spw <= 1) {
-    qmv_launch_t<XF32, NMAT, 1, RTF, XLDS, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
+    qmv_launch_t<XF32, NMAT, 1, RTF, XLDS, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s, sp);
   } else if (spw <= 2) {
-    qmv_launch_t<XF32, NMAT, 2, RTF, XLDS, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
+    qmv_launch_t<XF32, NMAT, 2, RTF, XLDS, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s, sp);
   } else {
     // the fused two-matrix variant is limited to K <= 8192 (two segments per wave)
-    if constexpr (NMAT == 1) qmv_launch_t<XF32, NMAT, 4, RTF, XLDS, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s);
+    if constexpr (NMAT == 1) qmv_launch_t<XF32, NMAT, 4, RTF, XLDS, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, nwaves, lds, s, sp);
   }
 }
 
 template <int XF32, int NMAT, int RTF, int NV, int BITS, int Y3>
 inline void qmv_launch_lds(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
-                           int64_t ldy, hipStream_t s) {
+                           int64_t ldy, hipStream_t s, const QmvSplit& sp) {
   const size_t part = qmv_part_bytes(K, XF32, NMAT, XF32 ? RTF : 1, NV);
   if constexpr (XF32 == 3) {
-    qmv_launch_spw<XF32, NMAT, RTF, false, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, part, s);
+    qmv_launch_spw<XF32, NMAT, RTF, false, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, part, s, sp);
   } else {
-    const size_t xsb = qmv_xs_bytes(K, XF32, R);
+    const size_t xsb = qmv_xs_bytes(qmv_share_k(K, sp.nshare), XF32, R);
     const size_t staged = part > xsb ? part : xsb;  // the partials reuse the staging area
     // staged rows are not split: a workgroup then covers every row tile
     if ((!XF32 || RTF == qmv_row_tiles(1, R)) && staged <= qmv_max_lds())
-      qmv_launch_spw<XF32, NMAT, RTF, true, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, staged, s);
+      qmv_launch_spw<XF32, NMAT, RTF, true, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, staged, s, sp);
     else
-      qmv_launch_spw<XF32, NMAT, RTF, false, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, part, s);
+      qmv_launch_spw<XF32, NMAT, RTF, false, NV, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, part, s, sp);
   }
 }
 
 template <int NMAT, int BITS, int Y3>
 inline void qmv_launch_bf16(const uint8_t* pk0, const uint8_t* pk1, int N, int K, const void* x, int64_t ldx, int R, float* y,
-                            int64_t ldy, hipStream_t s) {
+                            int64_t ldy, hipStream_t s, const QmvSplit& sp) {
   const int nv = qmv_nv(R);
   if (nv == 1)
-    qmv_launch_lds<0, NMAT, 1, 1, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<0, NMAT, 1, 1, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, s, sp);
   else if (nv == 2)
-    qmv_launch_lds<0, NMAT, 1, 2, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<0, NMAT, 1, 2, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, s, sp);
   else
-    qmv_launch_lds<0, NMAT, 1, 4, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<0, NMAT, 1, 4, BITS, Y3>(pk0, pk1, N, K, x, ldx, R, y, ldy, s, sp);
+}
+
+// Row tiles per workgroup of a float32 matvec: rows read from memory
+// (fragment-ordered planes, or rows that do not fit in LDS) split their row
+// tiles over more workgroups (1, 2 or 4 tiles each) while the column tiles
+// and K shares leave CUs idle.
+inline int qmv_pieces_rt(int xf32, int N, int K, int R, int nshare) {
+  int rt = qmv_row_tiles(1, R);
+  bool from_memory = xf32 == 3;
+  if (!from_memory) {
+    const size_t part = qmv_part_bytes(K, xf32, 1, rt, 1), xsb = qmv_xs_bytes(qmv_share_k(K, nshare), xf32, R);
+    from_memory = (part > xsb ? part : xsb) > qmv_max_lds();
+  }
+  if (from_memory)
+    while (rt > 1 && (int64_t)(N / kTileN) * nshare * (qmv_row_tiles(1, R) / rt) * 2 <= kQmvSplitBelow) rt /= 2;
+  return rt;
 }
 
 template <int XF32, int BITS>
 inline void qmv_launch_pieces(const uint8_t* pk0, int N, int K, const void* x, int64_t ldx, int R, float* y, int64_t ldy,
-                              hipStream_t s) {
-  int rt = qmv_row_tiles(1, R);
-  // rows read from memory (fragment-ordered planes, or rows that do not fit
-  // in LDS): while the column tiles leave CUs idle, each workgroup takes
-  // fewer row tiles (1, 2 or 4 per workgroup)
-  bool from_memory = XF32 == 3;
-  if constexpr (XF32 != 3) {
-    const size_t part = qmv_part_bytes(K, XF32, 1, rt, 1), xsb = qmv_xs_bytes(K, XF32, R);
-    from_memory = (part > xsb ? part : xsb) > qmv_max_lds();
-  }
-  if (from_memory)
-    while (rt > 1 && (int64_t)(N / kTileN) * (qmv_row_tiles(1, R) / rt) * 2 <= kQmvSplitBelow) rt /= 2;
+                              hipStream_t s, const QmvSplit& sp) {
+  const int rt = qmv_pieces_rt(XF32, N, K, R, sp.nshare);
   if (rt == 1)
-    qmv_launch_lds<XF32, 1, 1, 1, BITS, 0>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<XF32, 1, 1, 1, BITS, 0>(pk0, pk0, N, K, x, ldx, R, y, ldy, s, sp);
   else if (rt == 2)
-    qmv_launch_lds<XF32, 1, 2, 1, BITS, 0>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<XF32, 1, 2, 1, BITS, 0>(pk0, pk0, N, K, x, ldx, R, y, ldy, s, sp);
   else
-    qmv_launch_lds<XF32, 1, 4, 1, BITS, 0>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_lds<XF32, 1, 4, 1, BITS, 0>(pk0, pk0, N, K, x, ldx, R, y, ldy, s, sp);
+}
+
+// Whether a bf16 matvec of one matrix runs two column tiles per workgroup.
+inline bool qmv_pairs_tiles(int nmat, int xmode, int N, int K, int nshare) {
+  return nmat == 1 && xmode == 0 && nshare == 1 && N / kTileN >= kQmvPairTilesFrom && K <= kQmvMaxK / 2;
 }
 
 // xmode: 0 bf16 rows, 1 float32 rows, 2 float32 rows as three bf16 planes,
@@ -666,38 +750,66 @@ inline void qmv_launch_pieces(const uint8_t* pk0, int N, int K, const void* x, i
 // writes three bf16 planes (1) or the planes in fragment order (2).
 template <int BITS>
 inline void qmv_launch_bits(const uint8_t* pk0, const uint8_t* pk1, int nmat, int N, int K, const void* x, int xmode, int64_t ldx,
-                            int R, float* y, int64_t ldy, hipStream_t s, int y3) {
+                            int R, float* y, int64_t ldy, hipStream_t s, int y3, const QmvSplit& sp) {
   if (xmode == 0) {
-    if (nmat == 1 && N / kTileN >= kQmvPairTilesFrom && K <= kQmvMaxK / 2)
-      qmv_launch_bf16<2, BITS, 3>(pk0, pk0, N, K, x, ldx, R, y, ldy, s);
+    if (qmv_pairs_tiles(nmat, xmode, N, K, sp.nshare))
+      qmv_launch_bf16<2, BITS, 3>(pk0, pk0, N, K, x, ldx, R, y, ldy, s, sp);
     else if (nmat == 1)
-      qmv_launch_bf16<1, BITS, 0>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+      qmv_launch_bf16<1, BITS, 0>(pk0, pk1, N, K, x, ldx, R, y, ldy, s, sp);
     else if (y3 == 1)
-      qmv_launch_bf16<2, BITS, 1>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+      qmv_launch_bf16<2, BITS, 1>(pk0, pk1, N, K, x, ldx, R, y, ldy, s, sp);
     else if (y3 == 2)
-      qmv_launch_bf16<2, BITS, 2>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+      qmv_launch_bf16<2, BITS, 2>(pk0, pk1, N, K, x, ldx, R, y, ldy, s, sp);
     else
-      qmv_launch_bf16<2, BITS, 0>(pk0, pk1, N, K, x, ldx, R, y, ldy, s);
+      qmv_launch_bf16<2, BITS, 0>(pk0, pk1, N, K, x, ldx, R, y, ldy, s, sp);
   } else if (xmode == 1) {
-    qmv_launch_pieces<1, BITS>(pk0, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_pieces<1, BITS>(pk0, N, K, x, ldx, R, y, ldy, s, sp);
   } else if (xmode == 2) {
-    qmv_launch_pieces<2, BITS>(pk0, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_pieces<2, BITS>(pk0, N, K, x, ldx, R, y, ldy, s, sp);
   } else {
-    qmv_launch_pieces<3, BITS>(pk0, N, K, x, ldx, R, y, ldy, s);
+    qmv_launch_pieces<3, BITS>(pk0, N, K, x, ldx, R, y, ldy, s, sp);
   }
 }
 
-// bits: 4, 6, 8 or kFmtFp8 (checked by the caller).
+// Workspace of a K split: one arrival counter per tile id (a 256-byte
+// aligned block), then the partials [tile id][segment][values per segment].
+// Tile ids are column tiles (pairs for the fused two-matrix kernel count
+// once) times the row-tile workgroups of float32 rows read from memory.
+struct QmvSplitShape {
+  int64_t tile_ids;
+  int64_t seg_vals;  // floats per segment and tile id
+};
+inline QmvSplitShape qmv_split_shape(int nmat, int xmode, int N, int K, int R, int nshare) {
+  QmvSplitShape sh{};
+  const int64_t tiles = N / kTileN;
+  if (xmode == 0) {
+    sh.tile_ids = tiles;
+    sh.seg_vals = (int64_t)nmat * qmv_nv(R) * 64;
+  } else {
+    const int rt = qmv_pieces_rt(xmode, N, K, R, nshare);
+    sh.tile_ids = tiles * (qmv_row_tiles(1, R) / rt);
+    sh.seg_vals = (int64_t)rt * 64;
+  }
+  return sh;
+}
+inline size_t qmv_split_counter_bytes(const QmvSplitShape& sh) { return (size_t)((sh.tile_ids * 4 + 255) / 256 * 256); }
+inline size_t qmv_split_work_bytes(int nmat, int xmode, int N, int K, int R, int nshare) {
+  const QmvSplitShape sh = qmv_split_shape(nmat, xmode, N, K, R, nshare);
+  return qmv_split_counter_bytes(sh) + (size_t)sh.tile_ids * qmv_segments(K) * sh.seg_vals * sizeof(float);
+}
+
+// bits: 4, 6, 8 or kFmtFp8 (checked by the caller). sp: the K split and its
+// workspace (nshare = 1: none).
 inline void qmv_launch(const uint8_t* pk0, const uint8_t* pk1, int nmat, int N, int K, const void* x, int xmode, int64_t ldx,
-                       int R, float* y, int64_t ldy, hipStream_t s, int bits = 4, int y3 = 0) {
+                       int R, float* y, int64_t ldy, hipStream_t s, int bits = 4, int y3 = 0, QmvSplit sp = QmvSplit{1, nullptr, nullptr}) {
   if (bits == 6)
-    qmv_launch_bits<6>(pk0, pk1, nmat, N, K, x, xmode, ldx, R, y, ldy, s, y3);
+    qmv_launch_bits<6>(pk0, pk1, nmat, N, K, x, xmode, ldx, R, y, ldy, s, y3, sp);
   else if (bits == 8)
-    qmv_launch_bits<8>(pk0, pk1, nmat, N, K, x, xmode, ldx, R, y, ldy, s, y3);
+    qmv_launch_bits<8>(pk0, pk1, nmat, N, K, x, xmode, ldx, R, y, ldy, s, y3, sp);
   else if (bits == kFmtFp8)
-    qmv_launch_bits<kFmtFp8>(pk0, pk1, nmat, N, K, x, xmode, ldx, R, y, ldy, s, y3);
+    qmv_launch_bits<kFmtFp8>(pk0, pk1, nmat, N, K, x, xmode, ldx, R, y, ldy, s, y3, sp);
   else
-    qmv_launch_bits<4>(pk0, pk1, nmat, N, K, x, xmode, ldx, R, y, ldy, s, y3);
+    qmv_launch_bits<4>(pk0, pk1, nmat, N, K, x, xmode, ldx, R, y, ldy, s, y3, sp);
 }
 
 }  // namespace q4

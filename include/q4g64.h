@@ -157,6 +157,30 @@ int qmv_rows(const void* packed, int64_t N, int64_t K, const void* x, int x_dtyp
 int qmv_rows_qg64(int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R,
                   float* y, int64_t ldy, void* stream);
 
+/* qmv_rows (bits = 4, 6 or 8) with K split over several workgroups per
+ * 16-column tile, for matrices with too few column tiles to give every CU
+ * one (TensorFold PR #1696, later revision, "What it adds" > Exact speed
+ * work: the rows sharing a decode step are summed as the one-row kernels sum
+ * them). Each workgroup of a tile folds a run of consecutive 256-wide k
+ * segments; the last of them to finish adds all of the tile's segment
+ * partials in the same ascending order as qmv_rows, so y is bit-identical to
+ * qmv_rows_qg64 on the same arguments, for every value of splits.
+ *   splits: workgroups per tile, 1..16 (at most the K/256 segments), or 0
+ *           for the smallest power of two that gives each CU a workgroup.
+ *   work:   a DEVICE buffer of at least qmv_split_work_bytes(bits, N, K,
+ *           x_dtype, R, splits) bytes (work_bytes says how many it holds),
+ *           256-byte aligned, zero-filled by the caller before its first
+ *           use: it holds one arrival counter per tile, which every
+ *           completed call returns to zero, and the segment partials. One
+ *           workspace serves any later call of any shape that fits in it;
+ *           calls that share a workspace must not run concurrently. When
+ *           the split comes out as 1, work may be NULL.
+ * Other arguments and limits as qmv_rows. qmv_split_work_bytes returns 0 for
+ * invalid arguments. */
+size_t qmv_split_work_bytes(int bits, int64_t N, int64_t K, int x_dtype, int R, int splits);
+int qmv_rows_split(int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R, float* y,
+                   int64_t ldy, int splits, void* work, size_t work_bytes, void* stream);
+
 /* Fused decode FFN gate (PR #1696, "What it adds": w1 + w3 + SwiGLU in one
  * pass): y[r][n] = silu(a) * c with a = (w1 x)[r][n], c = (w3 x)[r][n], each
  * computed in qmv_rows' order; bit-equal to composing two qmv_rows results

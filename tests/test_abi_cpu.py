@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared():
         assert hasattr(lib, name), name
     assert set(_declared()) == set(q4._SIGNATURES)
-    assert lib.q4g64_abi_version() == 3
+    assert lib.q4g64_abi_version() == 4
 
 
 def test_packed_bytes():
@@ -380,3 +380,23 @@ def test_rope_calls_reject_bad_shapes():
     assert _rc("qmv_qkv_rope", 4, FAKE, 2048, FAKE, 2048, 17, ctypes.addressof(a), None)[0] == q4.Q4_EINVAL
     rc, msg = _rc("qmv_qkv_rope", 4, FAKE, 8192, FAKE, 8192, 1, ctypes.addressof(a), None)
     assert rc == q4.Q4_EUNSUPPORTED and "4096" in msg
+
+
+def test_split_work_bytes_and_rejections():
+    f = q4.lib().qmv_split_work_bytes
+    # w2 of the decode FFN step (128 column tiles, 32 segments), one float32 row, two shares:
+    # 128 counters in a 512-byte block, then 128 tiles x 32 segments x 64 partials
+    assert f(4, 2048, 8192, q4.Q4_F32, 1, 2) == 512 + 128 * 32 * 64 * 4
+    assert f(4, 2048, 8192, q4.Q4_F32, 1, 0) == f(4, 2048, 8192, q4.Q4_F32, 1, 2)  # automatic: 2 x 128 tiles fill 256 CUs
+    assert f(4, 2048, 8192, q4.Q4_BF16, 16, 0) == 512 + 128 * 32 * 4 * 64 * 4  # 16 bf16 rows: 4 row slots per lane group
+    for bad in ((5, 2048, 8192, q4.Q4_F32, 1, 0), (4, 100, 8192, q4.Q4_F32, 1, 0), (4, 2048, 8192, 7, 1, 0),
+                (4, 2048, 8192, q4.Q4_F32, 17, 0), (4, 2048, 8192, q4.Q4_F32, 1, 17), (4, 2048, 32768, q4.Q4_F32, 1, 0)):
+        assert f(*bad) == 0, bad
+    base = (4, FAKE, 2048, 8192, FAKE, q4.Q4_F32, 8192, 1, FAKE, 2048)
+    assert _rc("qmv_rows_split", *base, 17, FAKE, 1 << 20, None)[0] == q4.Q4_EINVAL
+    assert _rc("qmv_rows_split", *base, -1, FAKE, 1 << 20, None)[0] == q4.Q4_EINVAL
+    assert _rc("qmv_rows_split", *base, 2, None, 1 << 20, None)[0] == q4.Q4_EALIGN
+    assert _rc("qmv_rows_split", *base, 2, FAKE + 16, 1 << 20, None)[0] == q4.Q4_EALIGN
+    rc, msg = _rc("qmv_rows_split", *base, 2, FAKE, 1000, None)
+    assert rc == q4.Q4_EINVAL and "work_bytes" in msg
+    assert _rc("qmv_rows_split", 4, FAKE, 2048, 8192, FAKE, q4.Q4_F32, 8192, 0, FAKE, 2048, 2, FAKE, 1 << 20, None)[0] == q4.Q4_EINVAL
