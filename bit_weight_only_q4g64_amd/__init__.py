@@ -62,6 +62,9 @@ _SIGNATURES = {
     "qmv_split_work_bytes": (ctypes.c_size_t, [ctypes.c_int, _I64, _I64, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "qmv_rows_split": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, ctypes.c_int, _I64, ctypes.c_int, _P, _I64, ctypes.c_int,
                                       _P, ctypes.c_size_t, _P]),
+    "qmv_split_noalloc_max_bytes": (ctypes.c_size_t, []),
+    "qmv_rows_split_noalloc": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, ctypes.c_int, _I64, ctypes.c_int, _P, _I64,
+                                              ctypes.c_int, _P]),
     "qmv_ffn": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _I64, ctypes.c_int, _P, _I64, _P, _I64, _P, _P]),
     "q4_last_error": (ctypes.c_char_p, []),
 }

@@ -7,6 +7,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
 #include "ffn.h"
 #include "pack.h"
@@ -467,6 +470,57 @@ int qkv_rope_launch_bits(int spw, int nv, const uint8_t* pk, int N, int K, const
   return qkv_rope_launch_nv<4, BITS>(nv, pk, N, K, x, ldx, R, a, lds, heads, s);
 }
 
+// ---- the split matvec without a caller workspace ---------------------------
+// Its workspace is this file-scope device array: one copy per GPU, held from
+// the library's load until the process ends. In host code `scratch` names a
+// host-side stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::atomic<uint8_t*> g_scratch[kScratchDevices];
+std::mutex g_scratch_mu;
+
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// This device's copy of the scratch array; at the first call on a device its
+// address is looked up and the counter area cleared by a kernel on `s` (a
+// kernel rather than a memset, so that a graph that captures the first call
+// replays correctly). Returns nullptr with the error recorded on failure.
+uint8_t* scratch_on_device(const char* fn, hipStream_t s) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) {
+    fail(Q4_EDEVICE, "%s: no usable current device", fn);
+    return nullptr;
+  }
+  uint8_t* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (p != nullptr) return p;
+  void* addr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || addr == nullptr) {
+    fail(Q4_EDEVICE, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", fn, dev, hipGetErrorString(e));
+    return nullptr;
+  }
+  // every counter block a split matvec can use lies in the first 1 MiB
+  hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, s, (uint32_t*)addr, (int64_t)(size_t(1) << 20) / 4);
+  if (hipGetLastError() != hipSuccess) {
+    fail(Q4_EDEVICE, "%s: clearing the scratch counters failed on device %d", fn, dev);
+    return nullptr;
+  }
+  p = (uint8_t*)addr;
+  g_scratch[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace
+
 extern "C" {
 
 int q4g64_abi_version(void) { return 4; }
@@ -717,6 +771,27 @@ size_t qmv_split_work_bytes(int bits, int64_t N, int64_t K, int x_dtype, int R, 
   const int xmode = xmode_of(x_dtype);
   const int nshare = split_shares(splits, xmode, N, K, R);
   return q4::qmv_split_work_bytes(1, xmode, (int)N, (int)K, R, nshare);
+}
+
+size_t qmv_split_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int qmv_rows_split_noalloc(int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R,
+                           float* y, int64_t ldy, int splits, void* stream) {
+  const char* fn = "qmv_rows_split_noalloc";
+  if (int rc = qmv_split_check(fn, bits, packed, N, K, x, x_dtype, ldx, R, y, ldy, splits)) return rc;
+  const int xmode = xmode_of(x_dtype);
+  const int nshare = split_shares(splits, xmode, N, K, R);
+  uint8_t* work = nullptr;
+  if (nshare > 1) {
+    const size_t need = q4::qmv_split_work_bytes(1, xmode, (int)N, (int)K, R, nshare);
+    const q4::QmvSplitShape sh = q4::qmv_split_shape(1, xmode, (int)N, (int)K, R, nshare);
+    if (need > kScratchBytes || q4::qmv_split_counter_bytes(sh) > (size_t(1) << 20))
+      return fail(Q4_EUNSUPPORTED, "%s: this shape needs %zu bytes of scratch, more than the %zu the library holds per GPU", fn, need,
+                  kScratchBytes);
+    work = scratch_on_device(fn, (hipStream_t)stream);
+    if (work == nullptr) return Q4_EDEVICE;
+  }
+  return qmv_split_launch(fn, bits, packed, N, K, x, x_dtype, ldx, R, y, ldy, nshare, work, (hipStream_t)stream);
 }
 
 int qmv_rows_split(int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R, float* y,

@@ -64,7 +64,13 @@
  *
  * Conventions for every call below:
  *   - All array arguments are DEVICE pointers owned by the caller; the
- *     library allocates nothing and keeps no state between calls.
+ *     library allocates nothing and keeps no device state between calls
+ *     (except the fixed scratch array of qmv_rows_split_noalloc, below).
+ *   - Host-side caches, per process: the largest dynamic LDS a workgroup may
+ *     use is queried once, on the device current at the first call that
+ *     needs it, and each kernel's LDS limit is raised once, at its first
+ *     launch. Every GPU this library runs on must therefore be of the same
+ *     kind (all MI355X); results never depend on these values.
  *   - `stream` is a hipStream_t (NULL = the default stream). Kernels are
  *     enqueued asynchronously on it; execution errors surface at the caller's
  *     next synchronization.
@@ -180,6 +186,20 @@ int qmv_rows_qg64(int bits, const void* packed, int64_t N, int64_t K, const void
 size_t qmv_split_work_bytes(int bits, int64_t N, int64_t K, int x_dtype, int R, int splits);
 int qmv_rows_split(int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R, float* y,
                    int64_t ldy, int splits, void* work, size_t work_bytes, void* stream);
+
+/* qmv_rows_split without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation). It allocates nothing: its workspace is a fixed
+ * device array inside the library, qmv_split_noalloc_max_bytes() bytes
+ * (8 MiB) on each GPU it runs on, held until the process ends. The first
+ * call on a device looks the array up and clears its counters with a kernel
+ * on `stream`. Shapes whose qmv_split_work_bytes exceeds the array return
+ * Q4_EUNSUPPORTED. Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and must not be
+ * issued. Results are bit-identical to qmv_rows_split and qmv_rows. */
+size_t qmv_split_noalloc_max_bytes(void);
+int qmv_rows_split_noalloc(int bits, const void* packed, int64_t N, int64_t K, const void* x, int x_dtype, int64_t ldx, int R,
+                           float* y, int64_t ldy, int splits, void* stream);
 
 /* Fused decode FFN gate (PR #1696, "What it adds": w1 + w3 + SwiGLU in one
  * pass): y[r][n] = silu(a) * c with a = (w1 x)[r][n], c = (w3 x)[r][n], each
