@@ -58,7 +58,7 @@ _SIGNATURES = {
     "qmv_qkv_rope": (ctypes.c_int, [ctypes.c_int, _P, _I64, _P, _I64, ctypes.c_int, _P, _P]),
     "qmv_window_costs": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P, _I64, ctypes.c_int, _P, _P]),
     "qmv_window_cost": (ctypes.c_float, [_P, ctypes.c_int]),
-    "q4g64_ffn_work_bytes": (ctypes.c_size_t, [_I64, ctypes.c_int]),
+    "q4g64_ffn_work_bytes": (ctypes.c_size_t, [_I64, _I64, ctypes.c_int]),
     "qmv_split_work_bytes": (ctypes.c_size_t, [ctypes.c_int, _I64, _I64, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "qmv_rows_split": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, ctypes.c_int, _I64, ctypes.c_int, _P, _I64, ctypes.c_int,
                                       _P, ctypes.c_size_t, _P]),
@@ -351,17 +351,19 @@ FFN_COUNTER_STRIDE = 128
 FFN_TOP_OFFSET = 16 * 128
 FFN_GEN_OFFSET = 17 * 128
 FFN_ERR_OFFSET = 18 * 128
+# The dataflow step (up to 4 rows): its call counter, after the barrier state.
+FFN_FLOW_EPOCH_OFFSET = 4096
 
 
-def ffn_work_bytes(N1: int, R: int) -> int:
-    return int(lib().q4g64_ffn_work_bytes(N1, R))
+def ffn_work_bytes(N1: int, N2: int, R: int) -> int:
+    return int(lib().q4g64_ffn_work_bytes(N1, N2, R))
 
 
-def ffn_workspace(N1: int, R: int, device="cuda") -> torch.Tensor:
-    """A zeroed workspace for qmv_ffn (reusable by later calls on the same stream)."""
-    nbytes = ffn_work_bytes(N1, R)
+def ffn_workspace(N1: int, N2: int, R: int, device="cuda") -> torch.Tensor:
+    """A zeroed workspace for qmv_ffn calls of 1..R rows (reusable by later calls on the same stream)."""
+    nbytes = max(ffn_work_bytes(N1, N2, r) for r in range(1, R + 1)) if R >= 1 else 0
     if nbytes == 0:
-        raise Q4Error("q4g64_ffn_work_bytes", Q4_EINVAL, f"invalid N1={N1} R={R}")
+        raise Q4Error("q4g64_ffn_work_bytes", Q4_EINVAL, f"invalid N1={N1} N2={N2} R={R}")
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
@@ -378,8 +380,8 @@ def qmv_ffn(p1: torch.Tensor, p3: torch.Tensor, p2: torch.Tensor, N1: int, K1: i
     if x.dtype != torch.bfloat16:
         raise ValueError("x must be bfloat16")
     R = x.shape[0]
-    if work.numel() < ffn_work_bytes(N1, R):
-        raise ValueError("work is smaller than ffn_work_bytes(N1, R)")
+    if work.numel() < ffn_work_bytes(N1, N2, R):
+        raise ValueError("work is smaller than ffn_work_bytes(N1, N2, R)")
     if z is None:
         z = torch.empty((R, N1), dtype=torch.float32, device=x.device)
     if y is None:

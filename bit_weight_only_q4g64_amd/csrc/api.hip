@@ -12,6 +12,7 @@
 
 #include "common.h"
 #include "ffn.h"
+#include "ffn_flow.h"
 #include "pack.h"
 #include "pgemm.h"
 #include "pgemm_narrow.h"
@@ -348,6 +349,37 @@ int ffn_launch_t(const uint8_t* p1, const uint8_t* p3, const uint8_t* p2, int N1
   return launched("qmv_ffn");
 }
 
+// The dataflow step (R <= 4, whole 256-wide segments in K1 and N1): one
+// workgroup per CU, every one resident at once.
+bool ffn_flow_applies(int64_t N1, int64_t K1, int R) { return R <= q4::kFlowMaxRows && K1 % 256 == 0 && N1 % 256 == 0; }
+
+template <int NV, int SPW1>
+int flow_launch_t(const uint8_t* p1, const uint8_t* p3, const uint8_t* p2, int N1, int K1, int N2, const uint16_t* x, int64_t ldx,
+                  int R, float* z, int64_t ldz, float* y, int64_t ldy, uint8_t* work, hipStream_t s) {
+  const size_t lds = q4::flow_lds_bytes(K1, R);
+  auto kern = q4::ffn_flow_kernel<NV, SPW1>;
+  static const bool lds_ok = q4::allow_max_dynamic_lds((const void*)kern);
+  (void)lds_ok;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, q4::kFfnThreads, lds) != hipSuccess)
+    return fail(Q4_EDEVICE, "qmv_ffn: device query failed");
+  if (per_cu < 1) return fail(Q4_EUNSUPPORTED, "qmv_ffn: a %zu-byte workgroup does not fit on a CU", lds);
+  // every workgroup produces z (at most one per w1/w3 tile pair), so each
+  // has read the call counter before any upper-half item advances it
+  const int pairs1 = N1 / q4::kTileN / 2;
+  const int nwg = cus < pairs1 ? cus : pairs1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(q4::kFfnThreads), lds, s, p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work);
+  return launched("qmv_ffn");
+}
+
+template <int NV>
+int flow_launch_s1(int spw1, const uint8_t* p1, const uint8_t* p3, const uint8_t* p2, int N1, int K1, int N2, const uint16_t* x,
+                   int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, uint8_t* work, hipStream_t s) {
+  if (spw1 <= 1) return flow_launch_t<NV, 1>(p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, s);
+  return flow_launch_t<NV, 2>(p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, s);
+}
+
 template <int NV, int RTF, int SPW1>
 int ffn_launch_s2(int spw2, const uint8_t* p1, const uint8_t* p3, const uint8_t* p2, int N1, int K1, int N2, const uint16_t* x,
                   int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, uint8_t* work, size_t lds, hipStream_t s) {
@@ -613,8 +645,11 @@ int qmm_cut_qg64(int bits, const void* packed_a, const void* packed_b, int64_t N
                       (hipStream_t)stream);
 }
 
-size_t q4g64_ffn_work_bytes(int64_t N1, int R) {
-  if (N1 <= 0 || N1 % 64 != 0 || N1 > q4::kQmvMaxK || R < 1 || R > 16) return 0;
+size_t q4g64_ffn_work_bytes(int64_t N1, int64_t N2, int R) {
+  if (N1 <= 0 || N1 % 64 != 0 || N1 > kFfnMaxN1 || N2 <= 0 || N2 % 64 != 0 || N2 > kMaxDim || R < 1 || R > 16) return 0;
+  // the dataflow step's tagged copies exist for R <= 4 (whole segments of N1;
+  // K1 is checked at the call); the barrier state for every R
+  if (R <= q4::kFlowMaxRows && N1 % 256 == 0) return q4::flow_work_bytes(N1, N2, R);
   return q4::kFfnWorkBytes;
 }
 
@@ -648,6 +683,11 @@ int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2,
   hipStream_t s = (hipStream_t)stream;
   const int n1 = (int)N1, k1 = (int)K1, n2 = (int)N2;
   const int nv = q4::qmv_nv(R), rtf = q4::qmv_row_tiles(1, R);
+  if (ffn_flow_applies(N1, K1, R) && q4::flow_lds_bytes(K1, R) <= q4::qmv_max_lds()) {
+    if (nv == 1) return flow_launch_s1<1>(spw1, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, s);
+    if (nv == 2) return flow_launch_s1<2>(spw1, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, s);
+    return flow_launch_s1<4>(spw1, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, s);
+  }
   if (nv == 1) return ffn_launch_s1<1, 1>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
   if (nv == 2) return ffn_launch_s1<2, 1>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
   if (rtf == 1) return ffn_launch_s1<4, 1>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);

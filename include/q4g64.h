@@ -262,19 +262,26 @@ int qmm_cut_qg64(int bits, const void* packed_a, const void* packed_b, int64_t N
  *   y = W2 z                  float32 [R][ldy], bit-identical to qmv_rows on z
  *                             with x_dtype = Q4_F32.
  * W1, W3: N1 x K1 packed; W2: N2 x N1 packed. x bf16 [R][ldx], R = 1..16.
- * work: a DEVICE buffer of q4g64_ffn_work_bytes(N1, R) bytes (4096 for
- * every valid N1 and R; 0 means the arguments are invalid), 256-byte
- * aligned, zero-filled by the caller before its first use. It holds only a
- * grid-barrier state, which every completed call leaves ready for the next:
- * one workspace serves any later call on the same stream (not concurrent
- * calls). z is the exchange buffer between the two halves of the step. The
- * call runs one workgroup per CU and needs the whole device: all of them
- * wait at one grid barrier. A workgroup that waits more than about 20 ms
- * gives up, sets the 32-bit word at byte 2304 of work to 1 and leaves y
- * undefined; the workspace must then be zero-filled again. Limits: K1 <= 4096,
- * N1 <= 8192, and the staged activations must fit in LDS
- * (Q4_EUNSUPPORTED otherwise). */
-size_t q4g64_ffn_work_bytes(int64_t N1, int R);
+ * work: a DEVICE buffer of q4g64_ffn_work_bytes(N1, N2, R) bytes (0 means
+ * the arguments are invalid), 256-byte aligned, zero-filled by the caller
+ * before its first use; every completed call leaves it ready for the next,
+ * and one workspace serves any later call of a shape it is large enough for
+ * (calls on one workspace must not run concurrently).
+ * Two schedules, both one workgroup per CU with every workgroup resident at
+ * once (the call needs the whole device):
+ *   - R <= 4 with K1 and N1 multiples of 256: a dataflow step. Each z value
+ *     is also stored in the workspace with this call's number (a counter in
+ *     the workspace that every call advances), and each w2 k segment starts
+ *     as soon as its 256 z values carry that number; the two halves of K of
+ *     a w2 tile hand over a running sum the same way. No workgroup waits for
+ *     the whole grid. The workspace holds 4352 + 8 R N1 + 32 N2 bytes.
+ *   - otherwise: z is written out, all workgroups meet at one grid barrier,
+ *     then w2 runs; the workspace holds the barrier state (4096 bytes).
+ * A workgroup that waits more than about 20 ms gives up, sets the 32-bit
+ * word at byte 2304 of work to 1 and leaves y undefined; the workspace must
+ * then be zero-filled again. Limits: K1 <= 4096, N1 <= 8192, and the staged
+ * activations must fit in LDS (Q4_EUNSUPPORTED otherwise). */
+size_t q4g64_ffn_work_bytes(int64_t N1, int64_t N2, int R);
 int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2, int64_t N1, int64_t K1, int64_t N2,
             const uint16_t* x, int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, void* work, void* stream);
 

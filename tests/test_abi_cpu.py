@@ -192,10 +192,15 @@ def test_binding_refuses_host_tensors():
 
 
 def test_ffn_work_bytes():
-    # the barrier state only: a fixed 4 KiB
-    assert q4.ffn_work_bytes(8192, 1) == 4096
-    assert q4.ffn_work_bytes(64, 16) == 4096
-    for bad in ((0, 1), (100, 1), (8192, 0), (8192, 17), (32768, 1)):
+    # up to 4 rows with whole 256-wide segments of N1: the barrier state (4 KiB),
+    # the call counter block (256 B), the tagged z copy (8 B per value) and the
+    # lower-half sums (64 lanes x 8 B per 16-column tile of w2)
+    assert q4.ffn_work_bytes(8192, 2048, 1) == 4096 + 256 + 8192 * 8 + 128 * 512
+    assert q4.ffn_work_bytes(8192, 2048, 4) == 4096 + 256 + 4 * 8192 * 8 + 128 * 512
+    # otherwise the barrier state only
+    assert q4.ffn_work_bytes(8192, 2048, 5) == 4096
+    assert q4.ffn_work_bytes(64, 64, 1) == 4096
+    for bad in ((0, 64, 1), (100, 64, 1), (8192, 64, 0), (8192, 64, 17), (32768, 64, 1), (8192, 100, 1), (8192, 0, 1)):
         assert q4.ffn_work_bytes(*bad) == 0
 
 

@@ -45,7 +45,7 @@ def test_c1_step_equals_composition_and_oracle(c1):
     N1, K1, N2 = w1.N, w1.K, w2.N
     say(f"qmv_ffn c1 N1={N1} K1={K1} N2={N2} R=1")
     x = dev_bf16(c1["x"])
-    work = q4.ffn_workspace(N1, 1, DEV)
+    work = q4.ffn_workspace(N1, N2, 1, DEV)
     z, y = q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x, work)
     zc, yc = _composed(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x)
     torch.cuda.synchronize()
@@ -76,7 +76,7 @@ def test_rows_equal_composition_and_one_row(c1, R):
     rng = np.random.default_rng(100 + R)
     xb = synthetic.draw_bf16_rows(rng, R, K1)
     x = dev_bf16(xb)
-    work = q4.ffn_workspace(N1, R, DEV)
+    work = q4.ffn_workspace(N1, N2, R, DEV)
     z, y = q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x, work)
     zc, yc = _composed(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x)
     torch.cuda.synchronize()
@@ -90,12 +90,16 @@ def test_rows_equal_composition_and_one_row(c1, R):
         assert np.array_equal(bits32(y1)[0], bits32(y)[r])
 
 
-def test_repeated_calls_reuse_the_workspace(c1):
+@pytest.mark.parametrize("R", [1, 5])
+def test_repeated_calls_reuse_the_workspace(c1, R):
+    """Five calls on one workspace: one row runs the dataflow step (its call
+    counter advances once per call), five rows
+    the barrier step (one barrier generation per call, counters back at 0)."""
     w1, w2 = c1["w1"], c1["w2"]
     N1, K1, N2 = w1.N, w1.K, w2.N
-    say("qmv_ffn c1 five calls on one workspace")
-    x = dev_bf16(c1["x"])
-    work = q4.ffn_workspace(N1, 1, DEV)
+    say(f"qmv_ffn c1 five calls on one workspace R={R}")
+    x = dev_bf16(synthetic.draw_bf16_rows(np.random.default_rng(3), R, K1))
+    work = q4.ffn_workspace(N1, N2, R, DEV)
     ref = None
     for _ in range(5):
         z, y = q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x, work)
@@ -105,20 +109,44 @@ def test_repeated_calls_reuse_the_workspace(c1):
             ref = cur
         assert np.array_equal(cur[0], ref[0]) and np.array_equal(cur[1], ref[1])
     state = work.view(torch.int32).cpu().numpy()
-    counters = state[[c * q4.FFN_COUNTER_STRIDE // 4 for c in range(16)]]
-    assert np.all(counters == 0) and state[q4.FFN_TOP_OFFSET // 4] == 0  # arrival counts back at 0
     assert state[q4.FFN_ERR_OFFSET // 4] == 0
-    assert state[q4.FFN_GEN_OFFSET // 4] == 5  # one barrier generation per call
+    if R == 1:
+        assert state[q4.FFN_FLOW_EPOCH_OFFSET // 4] == 5
+    else:
+        counters = state[[c * q4.FFN_COUNTER_STRIDE // 4 for c in range(16)]]
+        assert np.all(counters == 0) and state[q4.FFN_TOP_OFFSET // 4] == 0  # arrival counts back at 0
+        assert state[q4.FFN_GEN_OFFSET // 4] == 5  # one barrier generation per call
+
+
+def test_new_inputs_each_call_on_one_workspace(c1):
+    """Eight calls in a row on one workspace, each with new activations and
+    row counts 1..4 and 7 (the dataflow and the barrier step in turn): every
+    result equals the composition of the two decode calls, so no call reads
+    values an earlier call left in the workspace."""
+    w1, w2 = c1["w1"], c1["w2"]
+    N1, K1, N2 = w1.N, w1.K, w2.N
+    say("qmv_ffn c1: eight calls with new inputs on one workspace")
+    work = q4.ffn_workspace(N1, N2, 4, DEV)
+    rng = np.random.default_rng(8)
+    for R in (1, 2, 1, 4, 7, 3, 1, 1):
+        x = dev_bf16(synthetic.draw_bf16_rows(rng, R, K1))
+        z, y = q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x, work)
+        zc, yc = _composed(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x)
+        torch.cuda.synchronize()
+        assert q4.ffn_error(work) == 0
+        assert np.array_equal(bits32(z), bits32(zc)), R
+        assert np.array_equal(bits32(y), bits32(yc)), R
 
 
 @pytest.mark.parametrize("N1,K1,N2,R", [(64, 64, 64, 1), (192, 128, 128, 3), (8192, 2048, 4096, 1), (8192, 4096, 2048, 2),
-                                        (4096, 2048, 1024, 16)])
+                                        (4096, 2048, 1024, 16), (512, 256, 64, 4), (256, 2048, 2048, 1), (1024, 512, 8192, 3),
+                                        (7936, 1280, 192, 2)])
 def test_shapes_equal_composition(N1, K1, N2, R):
     say(f"qmv_ffn N1={N1} K1={K1} N2={N2} R={R}")
     rng, w1, w3, w2 = _weights(7 + N1 + K1, N1, K1, N2)
     p1, p3, p2 = dev_weight(w1), dev_weight(w3), dev_weight(w2)
     x = dev_bf16(synthetic.draw_bf16_rows(rng, R, K1))
-    work = q4.ffn_workspace(N1, R, DEV)
+    work = q4.ffn_workspace(N1, N2, R, DEV)
     z, y = q4.qmv_ffn(p1, p3, p2, N1, K1, N2, x, work)
     zc, yc = _composed(p1, p3, p2, N1, K1, N2, x)
     torch.cuda.synchronize()
@@ -132,7 +160,7 @@ def test_graph_replays_equal_eager(c1):
     N1, K1, N2 = w1.N, w1.K, w2.N
     say("qmv_ffn c1 in a HIP graph, four replays")
     x = dev_bf16(c1["x"])
-    work = q4.ffn_workspace(N1, 1, DEV)
+    work = q4.ffn_workspace(N1, N2, 1, DEV)
     z = torch.empty((1, N1), dtype=torch.float32, device=DEV)
     y = torch.empty((1, N2), dtype=torch.float32, device=DEV)
     z_ref, y_ref = q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x, work)
