@@ -2,30 +2,38 @@
 """Benchmark of the q4g64 hot path on one MI355X.
 
 One step is one decode FFN step at one activation row, with the workload's
-sizes: qmv_w13_swiglu over w1 and w3 (8192 x 2048 each, bf16 x, float32
-SwiGLU output), then qmv_rows over w2 (2048 x 8192) on that float32 output.
-Weights rotate over a pool of packed copies larger than the 256 MB MALL plus
-the L2s, so every step streams its 28 MB of weights from HBM, as a real
-decode step streams the model's weights once per token.
+sizes: z = silu(W1 x) * (W3 x) over w1 and w3 (8192 x 2048 each, bf16 x),
+then y = W2 z over w2 (2048 x 8192) on the float32 z. It runs as one launch
+of qmv_ffn (the dataflow step, bit-identical to qmv_w13_swiglu followed by
+qmv_rows). Weights rotate over a pool of packed copies of at least 1 GiB,
+more than the 256 MB MALL plus the L2s, so every step streams its 28 MB of
+weights from HBM, as a real decode step streams the model's weights once per
+token.
 
 The timed region replays a HIP graph of the K steps (host launch cost would
-otherwise dominate a 10 us step), bracketed by torch.cuda.synchronize(). The
-runtime cannot time events inside a graph, and an event between two decode
-kernels costs about as much as the kernel, so each kernel's average duration
-is taken over a graph of the same K launches of that kernel alone (same pool
-rotation and buffers), bracketed by two HIP events on the stream it runs on.
-The prompt GEMM is reported beside it (TFLOP/s against the bf16
-matrix-core peak) on the 8192-row w1/w3 + SwiGLU window.
+otherwise dominate a 12 us step), bracketed by torch.cuda.synchronize() for
+the wall clock and by two HIP events on the graph's stream for the device
+time of the step's kernel. Every other figure is the average over a graph of
+at least as many launches as the pool has copies (so each timed graph reads
+at least 1 GiB of weights), timed with two HIP events on the stream that
+replays it.
 
-The float64 oracle is timed on the host on a bounded sample of the same
-decode step (cpu_baseline).
+Beside the headline, one line per workload: the single matvec (c0), the
+attention projections at 1..16 rows (c2), the 1000-row prompt through every
+cut (c3), the 8192-row layer with the 65536-row head (c4, as whole windows
+and as 128-row windows), the decode step at 1..16 rows, the attention
+epilogue and the 6-/8-bit and block-FP8 codes. The float64 oracle is timed
+on the host on a bounded sample of the decode step (cpu_baseline), which also
+reports the step's accuracy figures.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -38,6 +46,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 METRIC = "GB/s + rows/s for qmv decode; TFLOP/s for pgemm prefill (% of roofline)"
+POOL_BYTES = 1 << 30  # every rotating pool holds at least this many bytes
 
 
 def qbytes(N, K, bits=4):
@@ -63,64 +72,51 @@ def pack_dev(w, dev):
                    bits=getattr(w, "bits", 4))
 
 
-def cpu_baseline(d, budget_s=12.0):
-    """The float64 oracle on the same decode step, repeated while under budget."""
-    import oracle
+def rotating(base, min_bytes=POOL_BYTES, max_copies=None):
+    """[base] plus clones of the list of device tensors `base`, totalling at
+    least min_bytes (at least two copies)."""
+    nbytes = sum(t.numel() * t.element_size() for t in base)
+    n = max(2, -(-min_bytes // nbytes))
+    if max_copies is not None:
+        n = max(2, min(n, max_copies))
+    return [base] + [[t.clone() for t in base] for _ in range(n - 1)]
 
-    try:
-        from threadpoolctl import threadpool_info
 
-        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = os.cpu_count() or 1
-    w1, w3, w2, x = d["w1"], d["w3"], d["w2"], d["x"]
-    times = []
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        a = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, x)
-        c = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, x)
-        z = oracle.swiglu(a, c)
-        oracle.matmul_rows(w2.wq, w2.scales, w2.biases, z)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 5:
-            break
-    step = float(np.median(times))
-    nbytes = decode_step_bytes(d)
-    out = {
-        "value": nbytes / step / 1e9,
-        "unit": "GB/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": f"{len(times)} full decode FFN steps (w1/w3 8192x2048 + SwiGLU, w2 2048x8192, 1 row) in numpy float64; "
-        f"median {step * 1e3:.1f} ms per step",
-    }
-    # the same with the BLAS pool limited to one thread
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        return out
-    times1 = []
-    with threadpool_limits(limits=1):
-        t_start = time.perf_counter()
-        while True:
-            t0 = time.perf_counter()
-            a = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, x)
-            c = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, x)
-            oracle.matmul_rows(w2.wq, w2.scales, w2.biases, oracle.swiglu(a, c))
-            times1.append(time.perf_counter() - t0)
-            if time.perf_counter() - t_start > budget_s or len(times1) >= 3:
-                break
-    step1 = float(np.median(times1))
-    out["one_core"] = {"value": nbytes / step1 / 1e9, "unit": "GB/s", "cores": 1,
-                       "sample": f"{len(times1)} steps, median {step1 * 1e3:.1f} ms per step"}
-    return out
+def graph_us(torch, launch, n):
+    """Average device time per launch of launch(0) .. launch(n - 1) captured
+    in one graph: one untimed replay, then one replay between two HIP events
+    on the stream that replays it."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n):
+                launch(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def r3(v):
+    return round(float(v), 3)
+
+
+# ---------------------------------------------------------------- provenance
 
 
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["bit_weight_only_q4g64_amd/csrc/common.h", "bit_weight_only_q4g64_amd/csrc/qmv.h",
-                  "bit_weight_only_q4g64_amd/csrc/pgemm_narrow.h",
-                  "bit_weight_only_q4g64_amd/csrc/pgemm.h", "bit_weight_only_q4g64_amd/csrc/api.hip"]
+                  "bit_weight_only_q4g64_amd/csrc/ffn.h", "bit_weight_only_q4g64_amd/csrc/ffn_flow.h",
+                  "bit_weight_only_q4g64_amd/csrc/pgemm_narrow.h", "bit_weight_only_q4g64_amd/csrc/pgemm.h",
+                  "bit_weight_only_q4g64_amd/csrc/api.hip"]
 
 
 def _code_only(text):
@@ -149,8 +145,6 @@ def _code_only(text):
 
 def kernel_source_hash():
     """Hash of the kernel sources' code (comments and blank lines left out)."""
-    import hashlib
-
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
@@ -158,21 +152,145 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def summary_json(name):
+    """The machine-readable block of a committed profile summary, or None."""
+    try:
+        with open(os.path.join(PROFILES, name)) as f:
+            text = f.read()
+        return json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+
+
 def traffic_per_launch(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter on a plain copy
     of known size), or None when the summary is missing or was taken on
     different kernel sources."""
-    path = os.path.join(PROFILES, f"traffic_{kernel}.md")
-    try:
-        with open(path) as f:
-            text = f.read()
-        data = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
-    except (OSError, IndexError, ValueError):
-        return None
-    if data.get("kernel_source_hash") != kernel_source_hash():
+    data = summary_json(f"traffic_{kernel}.md")
+    if data is None or data.get("kernel_source_hash") != kernel_source_hash():
         return None
     return data.get("hbm_bytes_per_launch")
+
+
+def _run(cmd):
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+        return r.stdout if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
+def provenance(torch, inputs):
+    """Toolchain, device, clocks, host CPU and the SHA-256 of every input."""
+    import bit_weight_only_q4g64_amd as q4
+
+    p = {"kernel_source_hash": kernel_source_hash()}
+    with open(q4.LIB_PATH, "rb") as f:
+        p["library_sha256"] = hashlib.sha256(f.read()).hexdigest()
+    out = _run(["hipcc", "--version"]) or _run(["/opt/rocm/bin/hipcc", "--version"])
+    p["hipcc"] = [ln for ln in out.splitlines() if ln.strip()][:2] if out else None
+    p["torch"] = torch.__version__
+    p["hip_runtime"] = getattr(torch.version, "hip", None)
+    props = torch.cuda.get_device_properties(0)
+    p["device"] = {"name": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+                   "compute_units": props.multi_processor_count, "memory_gib": round(props.total_memory / 2**30, 1)}
+    smi = _run(["rocm-smi", "--showclocks", "--json"])
+    try:
+        p["clocks"] = json.loads(smi) if smi else None
+    except ValueError:
+        p["clocks"] = smi.strip()[:2000] if smi else None
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    p["host_cpu"] = {"model": cpu, "cores_usable": len(os.sched_getaffinity(0))}
+    p["inputs_sha256"] = inputs
+    return p
+
+
+def input_hashes(d):
+    """SHA-256 of every canonical tensor of a workload dict."""
+    import synthetic
+
+    out = {}
+    for k, v in d.items():
+        if hasattr(v, "wq"):
+            out[k] = {"wq": synthetic.sha256_of(v.wq), "scales": synthetic.sha256_of(v.scales),
+                      "biases": synthetic.sha256_of(v.biases)}
+        elif isinstance(v, np.ndarray):
+            out[k] = synthetic.sha256_of(v)
+    return out
+
+
+# ------------------------------------------------------------ CPU baseline
+
+
+def cpu_baseline(d, z_gpu, y_gpu, budget_s=12.0):
+    """The float64 oracle on the same decode step, repeated while under
+    budget, with the accuracy of the GPU's z and y against it."""
+    import oracle
+    from oracle.diagnostics import accuracy
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count() or 1
+    w1, w3, w2, x = d["w1"], d["w3"], d["w2"], d["x"]
+
+    def step():
+        a = oracle.matmul_rows(w1.wq, w1.scales, w1.biases, x)
+        c = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, x)
+        z = oracle.swiglu(a, c)
+        return a, c, z, oracle.matmul_rows(w2.wq, w2.scales, w2.biases, z)
+
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        a64, c64, z64, y64 = step()
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 5:
+            break
+    med = float(np.median(times))
+    nbytes = decode_step_bytes(d)
+    out = {
+        "value": nbytes / med / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(times)} full decode FFN steps (w1/w3 8192x2048 + SwiGLU, w2 2048x8192, 1 row) in numpy float64 "
+        f"(dequantize, dgemm, silu); median {med * 1e3:.1f} ms per step",
+    }
+    # accuracy of the GPU step (reported, not gated): z against the float64
+    # SwiGLU, y against the float64 chain
+    Az = np.abs(oracle.silu(a64)) * oracle.error_weight(w3.wq, w3.scales, w3.biases, x) + \
+        np.abs(c64) * oracle.error_weight(w1.wq, w1.scales, w1.biases, x)
+    Ay = oracle.error_weight(w2.wq, w2.scales, w2.biases, np.abs(z64))
+    out["accuracy"] = {"z": accuracy(z_gpu, z64, Az), "y": accuracy(y_gpu, y64, Ay),
+                       "note": "z against the float64 SwiGLU; y against the float64 chain (float64 z into w2); "
+                               "A: the error weight sum |w| |x| (for z, the first-order weight of the product)"}
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        return out
+    times1 = []
+    with threadpool_limits(limits=1):
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            step()
+            times1.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start > budget_s or len(times1) >= 3:
+                break
+    med1 = float(np.median(times1))
+    out["one_core"] = {"value": nbytes / med1 / 1e9, "unit": "GB/s", "cores": 1,
+                       "sample": f"{len(times1)} steps, median {med1 * 1e3:.1f} ms per step"}
+    return out
 
 
 def copy_calibration(torch):
@@ -188,106 +306,63 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
 
 
-def batch_average_us(torch, launch, first, K):
-    """Average device time per launch of K launches captured in one graph."""
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
-            for i in range(K):
-                launch(first + i)
+def copy_bandwidth(torch):
+    """Measured device-to-device copy rate (read + write bytes per second) of
+    a 1 GiB buffer: context for the HBM peak."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    a.fill_(1)
+    b.copy_(a)
     torch.cuda.synchronize()
-    g.replay()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     e0.record()
-    g.replay()
+    for _ in range(5):
+        b.copy_(a)
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / K
+    s = e0.elapsed_time(e1) * 1e-3 / 5
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_each_way": n, "GB/s_read_plus_write": round(2 * n / s / 1e9, 1)}
 
 
-def decode_step_bytes(d):
+# ----------------------------------------------------------- decode step
+
+
+def decode_step_bytes(d, R=1):
     w1, w2 = d["w1"], d["w2"]
-    b13 = 2 * qbytes(w1.N, w1.K) + w1.K * 2 + w1.N * 4
-    b2 = qbytes(w2.N, w2.K) + w2.K * 4 + w2.N * 4
+    b13 = 2 * qbytes(w1.N, w1.K) + R * (w1.K * 2 + w1.N * 4)
+    b2 = qbytes(w2.N, w2.K) + R * (w2.K * 4 + w2.N * 4)
     return b13 + b2
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--pool-mb", type=int, default=1200, help="size of the rotating weight pool (cold HBM reads)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-pgemm", action="store_true")
-    ap.add_argument("--no-wide", action="store_true", help="skip the 6- and 8-bit measurements")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="launch the timed steps directly instead of replaying a graph (for per-dispatch counters)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 256 MiB device copy (the reference for scaling HBM byte counters)")
-    ap.add_argument("--pgemm-only", action="store_true",
-                    help="only the prompt GEMM measurement (for its per-dispatch counters); prints its JSON object")
-    args = ap.parse_args()
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (sharding is described in DESIGN.md)", file=sys.stderr)
-        sys.exit(2)
-
+def bench_step(d, dev, K, W, no_graph=False):
+    """The headline: K decode FFN steps at one row, each one qmv_ffn launch on
+    the next copy of a >= 1 GiB weight pool; and the same step as two calls."""
     import torch
 
-    if args.copy_calibration:
-        copy_calibration(torch)
-        return
-    if args.pgemm_only:
-        import bit_weight_only_q4g64_amd as q4
-
-        q4.lib()
-        torch.cuda.set_device(0)
-        print(json.dumps(bench_pgemm("cuda:0")))
-        return
-
     import bit_weight_only_q4g64_amd as q4
-    import synthetic
 
-    q4.lib()
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-    log("generating the decode FFN workload")
-    d = synthetic.config(1)
     w1, w3, w2 = d["w1"], d["w3"], d["w2"]
-    copy_bytes = q4.packed_bytes(w1.N, w1.K) * 2 + q4.packed_bytes(w2.N, w2.K)
-    ncopies = max(2, -(-args.pool_mb * (1 << 20) // copy_bytes))
-    base = [pack_dev(w1, dev), pack_dev(w3, dev), pack_dev(w2, dev)]
-    pool = [base] + [[t.clone() for t in base] for _ in range(ncopies - 1)]
+    pool = rotating([pack_dev(w1, dev), pack_dev(w3, dev), pack_dev(w2, dev)])
+    nc = len(pool)
     torch.cuda.synchronize()
-    log(f"pool: {ncopies} copies of {copy_bytes / 1e6:.1f} MB = {ncopies * copy_bytes / 2**30:.2f} GiB")
+    log(f"decode step pool: {nc} copies = {nc * sum(t.numel() for t in pool[0]) / 2**30:.2f} GiB")
     x = to_dev(d["x"], np.int16, dev).view(torch.bfloat16)
     z = torch.empty((1, w1.N), dtype=torch.float32, device=dev)
     y = torch.empty((1, w2.N), dtype=torch.float32, device=dev)
+    work = q4.ffn_workspace(w1.N, w2.N, 1, dev)
 
-    def step(i, ev=None):
-        p1, p3, p2 = pool[i % ncopies]
-        if ev is not None:
-            ev[0].record()
-        q4.qmv_w13_swiglu(p1, p3, w1.N, w1.K, x, y=z)
-        if ev is not None:
-            ev[1].record()
-        q4.qmv_rows(p2, w2.N, w2.K, z, y=y)
-        if ev is not None:
-            ev[2].record()
+    def step(i):
+        p1, p3, p2 = pool[i % nc]
+        q4.qmv_ffn(p1, p3, p2, w1.N, w1.K, w2.N, x, work, z=z, y=y)
 
-    K, W = args.steps, args.warmup
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
-
-    # graph of K steps (each step on the next pool copy)
     g = None
-    if not args.no_graph:
+    if not no_graph:
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -297,125 +372,332 @@ def main():
                     step(W + i)
         torch.cuda.synchronize()
         g.replay()  # untimed replay: first-launch costs
-        torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-
-    def run_timed():
-        if g is not None:
-            g.replay()
-        else:
-            for i in range(K):
-                step(W + i, evs[i])
-
+    # every copy once, in order, so the last copies touched are not the
+    # timed region's first ones
+    for i in range(nc):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timed region: {K} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run_timed()
+    e0.record()
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(K):
+            step(W + i)
+    e1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
-    if g is not None:
-        # The runtime cannot time events inside a graph, and an event between
-        # two kernels costs about as much as a decode kernel. Each kernel's
-        # average duration is therefore taken over a graph of the same K
-        # launches of that kernel alone (same pool rotation, same buffers),
-        # bracketed by two events on the stream it runs on.
-        t13 = np.array([batch_average_us(torch, lambda i: q4.qmv_w13_swiglu(pool[i % ncopies][0], pool[i % ncopies][1],
-                                                                            w1.N, w1.K, x, y=z), W, K)])
-        t2 = np.array([batch_average_us(torch, lambda i: q4.qmv_rows(pool[i % ncopies][2], w2.N, w2.K, z, y=y), W, K)])
-        timing_src = "HIP events around a graph of the same K launches of each kernel alone, divided by K"
-    else:
-        t13 = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3  # us
-        t2 = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
-        timing_src = "HIP events around each kernel of the timed steps (launched directly)"
+    step_kernel_us = e0.elapsed_time(e1) * 1e3 / K
+    assert q4.ffn_error(work) == 0, "the decode step gave up waiting"
+    z_out, y_out = z.cpu().numpy().astype(np.float64), y.cpu().numpy().astype(np.float64)
+    # the same step as the two decode calls, and each of them alone
+    n = max(K, nc)
+    zz = torch.empty_like(z)
 
-    b13 = 2 * qbytes(w1.N, w1.K) + w1.K * 2 + w1.N * 4
-    b2 = qbytes(w2.N, w2.K) + w2.K * 4 + w2.N * 4
-    step_bytes = b13 + b2
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    ach13 = b13 / (t13.mean() * 1e-6) / 1e9
-    ach2 = b2 / (t2.mean() * 1e-6) / 1e9
+    def two(i):
+        p1, p3, p2 = pool[i % nc]
+        q4.qmv_w13_swiglu(p1, p3, w1.N, w1.K, x, y=zz)
+        q4.qmv_rows(p2, w2.N, w2.K, zz, y=y)
 
-    result = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": "decode FFN step: qmv_w13_swiglu over w1/w3 8192x2048 q4g64 + SwiGLU, then qmv_rows over w2 "
-            "2048x8192 q4g64 on the float32 output; 1 bf16 activation row; seed 1",
-            "rows": 1,
-            "step_bytes": step_bytes,
-            "weight_pool_gib": round(ncopies * copy_bytes / 2**30, 3),
-            "kernel_source_hash": kernel_source_hash(),
-            "timing": ("HIP graph of K steps" if g is not None else "K directly launched steps") + ", wall clock between synchronizes",
-            "kernel_timing": timing_src,
-        },
-        "rows_per_s": round(1.0 / (ms_per_step * 1e-3), 1),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "qmv_w13_swiglu (qmv_kernel<0,2>)",
-            "achieved": round(ach13, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(ach13 / HBM_PEAK_GBS, 4),
-            "traffic": traffic_per_launch("qmv_w13_swiglu"),
-            "algorithmic_bytes_per_launch": b13,
-            "avg_launch_us": round(float(t13.mean()), 3),
-        },
-        "kernels": {
-            "qmv_w13_swiglu": {"avg_us": round(float(t13.mean()), 3), "p10_us": round(float(np.percentile(t13, 10)), 3),
-                               "p90_us": round(float(np.percentile(t13, 90)), 3), "GB/s": round(ach13, 1)},
-            "qmv_rows_w2_f32x": {"avg_us": round(float(t2.mean()), 3), "p10_us": round(float(np.percentile(t2, 10)), 3),
-                                 "p90_us": round(float(np.percentile(t2, 90)), 3), "GB/s": round(ach2, 1),
-                                 "frac": round(ach2 / HBM_PEAK_GBS, 4), "traffic": traffic_per_launch("qmv_rows_w2"),
-                                 "algorithmic_bytes_per_launch": b2},
-        },
-    }
-    g_used = g is not None
+    t_two = graph_us(torch, two, n)
+    t13 = graph_us(torch, lambda i: q4.qmv_w13_swiglu(pool[i % nc][0], pool[i % nc][1], w1.N, w1.K, x, y=zz), n)
+    t2 = graph_us(torch, lambda i: q4.qmv_rows(pool[i % nc][2], w2.N, w2.K, zz, y=y), n)
+    ffn_alone = graph_us(torch, step, n)
     del g, pool
     torch.cuda.empty_cache()
-
-    if not args.no_pgemm:
-        result["pgemm"] = bench_pgemm(dev)
-    if not args.no_wide:
-        result["decode_rows"] = bench_rows(dev, K, W, args.pool_mb)
-        r16 = result["decode_rows"]["R16"]
-        result["rows_per_s_at_16_rows"] = max(r16["rows_per_s"], r16["planes_rows_per_s"], r16["tiled_rows_per_s"])
-        result["qkv_rope"] = bench_qkv_rope(dev, K, W, args.pool_mb)
-    if not args.no_wide:
-        result["wide_codes"] = {str(b): bench_wide(dev, b, K, W, args.pool_mb, graph=g_used) for b in (6, 8, "fp8")}
-
-    if not args.no_cpu_baseline:
-        log("timing the float64 oracle on the host")
-        result["cpu_baseline"] = cpu_baseline(d)
-    print(json.dumps(result), flush=True)
+    return {"ms_per_step": ms_per_step, "step_kernel_us": step_kernel_us, "ffn_graph_us": ffn_alone, "two_calls_us": t_two,
+            "w13_us": t13, "w2_us": t2, "pool_copies": nc, "z": z_out, "y": y_out}
 
 
-def bench_wide(dev, bits, K, W, pool_mb, graph=True, reps=5):
-    """The same decode FFN step and prompt window with MLX 6- or 8-bit codes,
-    or block-FP8 weights (bits == "fp8"): same shapes, same cold weight pool,
-    same timing method."""
+# --------------------------------------------------------------- workloads
+
+
+def bench_c0(dev, K):
+    """Workload 0: one 512 x 256 matvec at one row (latency-bound; reported)."""
+    import torch
+
+    import bit_weight_only_q4g64_amd as q4
+    import synthetic
+
+    d = synthetic.config(0)
+    w = d["w"]
+    pool = rotating([pack_dev(w, dev)], min_bytes=300 << 20, max_copies=4096)
+    nc = len(pool)
+    x = to_dev(d["x"], np.int16, dev).view(torch.bfloat16)
+    y = torch.empty((1, w.N), dtype=torch.float32, device=dev)
+    us = graph_us(torch, lambda i: q4.qmv_rows(pool[i % nc][0], w.N, w.K, x, y=y), max(K, nc))
+    b = qbytes(w.N, w.K) + w.K * 2 + w.N * 4
+    del pool
+    return {"workload": "qmv_rows 512x256 q4g64, 1 bf16 row (seed 0); pool of copies of 300 MB (more than the MALL)",
+            "us": r3(us), "GB/s": round(b / (us * 1e-6) / 1e9, 1), "algorithmic_bytes": b,
+            "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "rows_per_s": round(1 / (us * 1e-6), 1)}
+
+
+def bench_c2(dev, K):
+    """Workload 2: the stacked q/k/v matvec (3072 x 2048) and o (2048 x 2048)
+    on the same R bf16 rows, R = 1, 2, 4, 8, 16: the pair as one decode step,
+    each matvec alone, rows/s and the fraction of the HBM peak."""
+    import torch
+
+    import bit_weight_only_q4g64_amd as q4
+    import synthetic
+
+    d = synthetic.config(2)
+    qkv = synthetic.concat_rows(d["wq"], d["wk"], d["wv"], name="qkv")
+    wo = d["wo"]
+    pool = rotating([pack_dev(qkv, dev), pack_dev(wo, dev)])
+    nc = len(pool)
+    xs = to_dev(d["x"], np.int16, dev).view(torch.bfloat16)
+    yq = torch.empty((16, qkv.N), dtype=torch.float32, device=dev)
+    yo = torch.empty((16, wo.N), dtype=torch.float32, device=dev)
+    n = max(K, nc)
+    out = {"workload": "qkv 3072x2048 (32 q + 8 kv heads x 64) then o 2048x2048 on the same R bf16 rows, q4g64, seed 2; "
+                       f"pool {nc} copies of both ({nc * (qbytes(3072, 2048) + qbytes(2048, 2048)) / 2**30:.2f} GiB)"}
+    for R in (1, 2, 4, 8, 16):
+        x = xs[:R]
+
+        def pair(i):
+            q4.qmv_rows(pool[i % nc][0], qkv.N, qkv.K, x, y=yq[:R])
+            q4.qmv_rows(pool[i % nc][1], wo.N, wo.K, x, y=yo[:R])
+
+        t = graph_us(torch, pair, n)
+        tq = graph_us(torch, lambda i: q4.qmv_rows(pool[i % nc][0], qkv.N, qkv.K, x, y=yq[:R]), n)
+        to = graph_us(torch, lambda i: q4.qmv_rows(pool[i % nc][1], wo.N, wo.K, x, y=yo[:R]), n)
+        bq = qbytes(qkv.N, qkv.K) + R * (qkv.K * 2 + qkv.N * 4)
+        bo = qbytes(wo.N, wo.K) + R * (wo.K * 2 + wo.N * 4)
+        out[f"R{R}"] = {"pair_us": r3(t), "rows_per_s": round(R / (t * 1e-6), 1), "GB/s": round((bq + bo) / (t * 1e-6) / 1e9, 1),
+                        "frac": round((bq + bo) / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "qkv_us": r3(tq), "qkv_frac": round(bq / (tq * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "o_us": r3(to), "o_frac": round(bo / (to * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del pool
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_c3(dev, K):
+    """Workload 3: the 1000-row prompt through w1/w3 with the SwiGLU epilogue
+    (float32 out) as one window and through the cuts 64, 128, 256 and
+    {17, 300, 683}; TFLOP/s per cut and the bits of every cut against the
+    whole window."""
+    import torch
+
+    import bit_weight_only_q4g64_amd as q4
+    import synthetic
+
+    d = synthetic.config(3)
+    w1, w3 = d["w1"], d["w3"]
+    M = d["x"].shape[0]
+    pool = rotating([pack_dev(w1, dev), pack_dev(w3, dev), to_dev(d["x"], np.int16, dev).view(torch.bfloat16)])
+    nc = len(pool)
+    y = torch.empty((M, w1.N), dtype=torch.float32, device=dev)
+    ref = q4.qmm_window(pool[0][0], pool[0][1], w1.N, w1.K, pool[0][2])
+    torch.cuda.synchronize()
+    flops = 2.0 * M * (2 * w1.N) * w1.K
+    out = {"workload": f"qmm_window/qmm_cut w1/w3 8192x2048 + SwiGLU, {M} bf16 rows, float32 out, seed 3; "
+                       f"pool {nc} copies of the weights and prompt"}
+    cuts = {"whole": [M], **d["cuts"]}
+    for name, cut in cuts.items():
+        us = graph_us(torch, lambda i: q4.qmm_cut(pool[i % nc][0], pool[i % nc][1], w1.N, w1.K, pool[i % nc][2], cut, y=y), nc)
+        tf = flops / (us * 1e-6) / 1e12
+        out[name] = {"windows": len(cut), "us": r3(us), "TFLOP/s": round(tf, 2), "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                     "bits_equal_whole_window": bool(torch.equal(y.view(torch.int32), ref.view(torch.int32)))}
+    del pool
+    torch.cuda.empty_cache()
+    return out
+
+
+C4_FLOPS = {"qkv": 2.0 * 8192 * 3072 * 2048, "o": 2.0 * 8192 * 2048 * 2048, "w1w3_swiglu": 2.0 * 8192 * 16384 * 2048,
+            "w2": 2.0 * 8192 * 2048 * 8192, "head": 2.0 * 128 * 65536 * 2048}
+
+
+def bench_c4(dev, reps=4):
+    """Workload 4: one decoder layer's projections over an 8192-row prompt
+    (qkv, o, w1/w3 + SwiGLU with bf16 out, w2 on that output) and the 65536 x
+    2048 head on the last 128 rows; once as whole windows and once in 128-row
+    windows (qmm_cut). Two copies of the weights and prompt alternate, so a
+    copy is read again only after the other's whole layer (over 0.5 GB of
+    traffic) has passed."""
+    import torch
+
+    import bit_weight_only_q4g64_amd as q4
+    import synthetic
+
+    log("c4: generating the 8192-row layer")
+    d = synthetic.config(4)
+    hashes = input_hashes(d)
+    qkv = synthetic.concat_rows(d["wq"], d["wk"], d["wv"], name="qkv")
+    ws = {"qkv": qkv, "o": d["wo"], "w1": d["w1"], "w3": d["w3"], "w2": d["w2"], "head": d["head"]}
+    copies = []
+    for c in range(2):
+        pk = {k: pack_dev(w, dev) for k, w in ws.items()}
+        pk["x"] = to_dev(d["x"], np.int16, dev).view(torch.bfloat16)
+        copies.append(pk)
+    M = d["x"].shape[0]
+    yq = torch.empty((M, qkv.N), dtype=torch.float32, device=dev)
+    yo = torch.empty((M, 2048), dtype=torch.float32, device=dev)
+    z = torch.empty((M, 8192), dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty((M, 2048), dtype=torch.float32, device=dev)
+    yh = torch.empty((128, 65536), dtype=torch.float32, device=dev)
+    cut = [128] * (M // 128)
+
+    def ops(pk, windows):
+        cq = cut if windows else [M]
+        return [
+            ("qkv", lambda: q4.qmm_cut(pk["qkv"], None, qkv.N, 2048, pk["x"], cq, y=yq)),
+            ("o", lambda: q4.qmm_cut(pk["o"], None, 2048, 2048, pk["x"], cq, y=yo)),
+            ("w1w3_swiglu", lambda: q4.qmm_cut(pk["w1"], pk["w3"], 8192, 2048, pk["x"], cq, y=z, out_dtype=torch.bfloat16)),
+            ("w2", lambda: q4.qmm_cut(pk["w2"], None, 2048, 8192, z, cq, y=y2)),
+            ("head", lambda: q4.qmm_window(pk["head"], None, 65536, 2048, pk["x"][-128:], y=yh)),
+        ]
+
+    out = {"workload": "8192-row layer: qkv 3072x2048, o 2048x2048, w1/w3 8192x2048 + SwiGLU (bf16 out), w2 2048x8192 on it, "
+                       "then the 65536x2048 head on the last 128 rows; q4g64, seed 4; two alternating copies",
+           "layer_gflop": round(sum(C4_FLOPS.values()) / 1e9, 1), "inputs_sha256": hashes}
+    whole_bits = None
+    for windows in (False, True):
+        times = {k: [] for k in C4_FLOPS}
+        for rep in range(reps + 1):
+            pk = copies[rep % 2]
+            evs = []
+            for name, fn in ops(pk, windows):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                evs.append((name, e0, e1))
+            torch.cuda.synchronize()
+            if rep > 0:  # the first pass is a warm-up
+                for name, e0, e1 in evs:
+                    times[name].append(e0.elapsed_time(e1) * 1e-3)
+        bits = [t.view(torch.int32 if t.dtype == torch.float32 else torch.int16).clone() for t in (yq, yo, z, y2, yh)]
+        if whole_bits is None:
+            whole_bits = bits
+        key = "windows_128" if windows else "whole"
+        res = {}
+        total = 0.0
+        for name, ts in times.items():
+            t = float(np.median(ts))
+            total += t
+            tf = C4_FLOPS[name] / t / 1e12
+            res[name] = {"us": round(t * 1e6, 2), "TFLOP/s": round(tf, 2), "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+        tf = sum(C4_FLOPS.values()) / total / 1e12
+        res["layer"] = {"us": round(total * 1e6, 2), "TFLOP/s": round(tf, 2), "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+        if windows:
+            res["bits_equal_whole"] = all(bool(torch.equal(a, b)) for a, b in zip(bits, whole_bits))
+        out[key] = res
+    del copies
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_rows(dev, K):
+    """The decode FFN step with R = 1, 2, 4, 8, 16 rows sharing it: qmv_ffn
+    (the dataflow step up to 4 rows, the barrier step beyond), and the two
+    calls with the float32 or fragment-ordered (Q4_BF16X3T) handoff."""
+    import torch
+
+    import bit_weight_only_q4g64_amd as q4
+    import synthetic
+
+    d = synthetic.config(1)
+    w1, w3, w2 = d["w1"], d["w3"], d["w2"]
+    pool = rotating([pack_dev(w1, dev), pack_dev(w3, dev), pack_dev(w2, dev)])
+    nc = len(pool)
+    n = max(K, nc)
+    xs = to_dev(synthetic.draw_bf16_rows(np.random.default_rng(11), 16, w1.K), np.int16, dev).view(torch.bfloat16)
+    z = torch.empty((16, w1.N), dtype=torch.float32, device=dev)
+    y = torch.empty((16, w2.N), dtype=torch.float32, device=dev)
+    work = q4.ffn_workspace(w1.N, w2.N, 16, dev)
+    out = {"workload": "decode FFN step (w1/w3 8192x2048 + SwiGLU, w2 2048x8192, q4g64) with R bf16 rows; "
+                       "graph averages over a >= 1 GiB pool"}
+    for R in (1, 2, 4, 8, 16):
+        x = xs[:R]
+        t_ffn = graph_us(torch, lambda i: q4.qmv_ffn(pool[i % nc][0], pool[i % nc][1], pool[i % nc][2], w1.N, w1.K, w2.N, x, work,
+                                                   z=z[:R], y=y[:R]), n)
+
+        def two(i):
+            q4.qmv_w13_swiglu(pool[i % nc][0], pool[i % nc][1], w1.N, w1.K, x, y=z[:R])
+            q4.qmv_rows(pool[i % nc][2], w2.N, w2.K, z[:R], y=y[:R])
+
+        zt = q4.TiledPlanes.empty(R, w1.N, dev)
+
+        def two_tiled(i):
+            q4.qmv_w13_swiglu(pool[i % nc][0], pool[i % nc][1], w1.N, w1.K, x, y=zt, planes="tiled")
+            q4.qmv_rows(pool[i % nc][2], w2.N, w2.K, zt, y=y[:R])
+
+        t_two = graph_us(torch, two, n)
+        t_tiled = graph_us(torch, two_tiled, n)
+        b = decode_step_bytes(d, R)
+        best = min(t_ffn, t_two, t_tiled)
+        out[f"R{R}"] = {"qmv_ffn_us": r3(t_ffn), "two_calls_us": r3(t_two), "two_calls_tiled_us": r3(t_tiled),
+                        "best_rows_per_s": round(R / (best * 1e-6), 1), "best_GB/s": round(b / (best * 1e-6) / 1e9, 1)}
+    assert q4.ffn_error(work) == 0
+    del pool
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_qkv_rope(dev, K):
+    """The stacked q/k/v decode matvec (3072 x 2048, 4-bit) with partial RoPE
+    and the KV store: fused in one launch against qmv_rows + rope_kv_store,
+    at 1 and 16 rows; and with 32 gate heads stacked after v."""
+    import torch
+
+    import bit_weight_only_q4g64_amd as q4
+    import synthetic
+
+    d = synthetic.config(2)
+    wg = synthetic.draw_qweight(np.random.default_rng(951), "wg", 2048, 2048)
+    x = to_dev(d["x"], np.int16, dev).view(torch.bfloat16)
+    ring = 4096
+    pos = torch.arange(100, 116, dtype=torch.int32, device=dev)
+    q = torch.empty((16, 2048), device=dev)
+    kc = torch.empty((ring, 8, 64), device=dev, dtype=torch.bfloat16)
+    vc = torch.empty((ring, 8, 64), device=dev, dtype=torch.bfloat16)
+    g = torch.empty((16, 2048), device=dev)
+    out = {"workload": "stacked q/k/v 3072x2048 q4g64 (32 q + 8 kv heads x 64), rot 64, theta 1e6, bf16 KV ring of 4096; "
+                       "gated_*: q/k/v/gate 5120x2048 (32 gate heads after v)"}
+    for tag, w in (("", synthetic.concat_rows(d["wq"], d["wk"], d["wv"], name="qkv")),
+                   ("gated_", synthetic.concat_rows(d["wq"], d["wk"], d["wv"], wg, name="qkvg"))):
+        pool = rotating([pack_dev(w, dev)])
+        nc = len(pool)
+        n = max(K, nc)
+        yy = torch.empty((16, w.N), device=dev)
+        gate = g if tag else None
+        for R in (1, 16):
+            fused = graph_us(torch, lambda i: q4.qmv_qkv_rope(pool[i % nc][0], w.K, x[:R], pos[:R], 32, 8, 64, 1e6, q[:R], kc, vc,
+                                                              gate_out=None if gate is None else gate[:R]), n)
+
+            def unfused(i):
+                q4.qmv_rows(pool[i % nc][0], w.N, w.K, x[:R], y=yy[:R])
+                q4.rope_kv_store(yy[:R], pos[:R], 32, 8, 64, 1e6, q[:R], kc, vc, gate_out=None if gate is None else gate[:R])
+
+            two = graph_us(torch, unfused, n)
+            mv = graph_us(torch, lambda i: q4.qmv_rows(pool[i % nc][0], w.N, w.K, x[:R], y=yy[:R]), n)
+            out[f"{tag}R{R}"] = {"fused_us": r3(fused), "qmv_rows_plus_epilogue_us": r3(two), "qmv_rows_alone_us": r3(mv)}
+        del pool
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_wide(dev, bits, K):
+    """The decode FFN step (two calls) and the 8192-row w1/w3 window with MLX
+    6- or 8-bit codes or block-FP8 weights (bits == "fp8"): same shapes, pool
+    and timing as the 4-bit figures."""
     import torch
 
     import bit_weight_only_q4g64_amd as q4
     import synthetic
 
     fp8 = bits == "fp8"
-    log(f"{bits} weights: decode FFN step and prompt window")
     rng = np.random.default_rng(100 + (9 if fp8 else bits))
     if fp8:
         draw = lambda name, N, Kk: synthetic.draw_fp8_weight(rng, name, N, Kk)  # noqa: E731
         pack = lambda w: q4.pack_fp8b(to_dev(w.w8, np.uint8, dev), to_dev(w.scales, np.float32, dev))  # noqa: E731
-        nbytes = q4.fp8b_packed_bytes
         w13_call = lambda p1, p3, x, z: q4.qmv_w13_swiglu_fp8b(p1, p3, 8192, 2048, x, y=z)  # noqa: E731
         rows_call = lambda p2, z, y: q4.qmv_rows_fp8b(p2, 2048, 8192, z, y=y)  # noqa: E731
         win_call = lambda p1, p3, xw, zw: q4.qmm_window_fp8b(p1, p3, 8192, 2048, xw, y=zw)  # noqa: E731
@@ -423,215 +705,41 @@ def bench_wide(dev, bits, K, W, pool_mb, graph=True, reps=5):
     else:
         draw = lambda name, N, Kk: synthetic.draw_qweight(rng, name, N, Kk, bits=bits)  # noqa: E731
         pack = lambda w: pack_dev(w, dev)  # noqa: E731
-        nbytes = lambda N, Kk: q4.packed_bytes(N, Kk, bits)  # noqa: E731
         w13_call = lambda p1, p3, x, z: q4.qmv_w13_swiglu(p1, p3, 8192, 2048, x, y=z, bits=bits)  # noqa: E731
         rows_call = lambda p2, z, y: q4.qmv_rows(p2, 2048, 8192, z, y=y, bits=bits)  # noqa: E731
         win_call = lambda p1, p3, xw, zw: q4.qmm_window(p1, p3, 8192, 2048, xw, y=zw, bits=bits)  # noqa: E731
         algo = lambda N, Kk: qbytes(N, Kk, bits)  # noqa: E731
-    w1 = draw("w1", 8192, 2048)
-    w3 = draw("w3", 8192, 2048)
-    w2 = draw("w2", 2048, 8192)
-    xb = synthetic.draw_bf16_rows(rng, 1, 2048)
-    copy_bytes = nbytes(8192, 2048) * 2 + nbytes(2048, 8192)
-    ncopies = max(2, -(-pool_mb * (1 << 20) // copy_bytes))
-    base = [pack(w1), pack(w3), pack(w2)]
-    pool = [base] + [[t.clone() for t in base] for _ in range(ncopies - 1)]
-    x = to_dev(xb, np.int16, dev).view(torch.bfloat16)
+    w1, w3, w2 = draw("w1", 8192, 2048), draw("w3", 8192, 2048), draw("w2", 2048, 8192)
+    pool = rotating([pack(w1), pack(w3), pack(w2)])
+    nc = len(pool)
+    n = max(K, nc)
+    x = to_dev(synthetic.draw_bf16_rows(rng, 1, 2048), np.int16, dev).view(torch.bfloat16)
     z = torch.empty((1, 8192), dtype=torch.float32, device=dev)
     y = torch.empty((1, 2048), dtype=torch.float32, device=dev)
 
     def step(i):
-        p1, p3, p2 = pool[i % ncopies]
-        w13_call(p1, p3, x, z)
-        rows_call(p2, z, y)
+        w13_call(pool[i % nc][0], pool[i % nc][1], x, z)
+        rows_call(pool[i % nc][2], z, y)
 
-    for i in range(W):
-        step(i)
-    torch.cuda.synchronize()
-    if graph:
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                for i in range(K):
-                    step(W + i)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        g.replay()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        del g
-    else:
-        t0 = time.perf_counter()
-        for i in range(K):
-            step(W + i)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / K
-    t13 = batch_average_us(torch, lambda i: w13_call(pool[i % ncopies][0], pool[i % ncopies][1], x, z), W, K)
-    t2 = batch_average_us(torch, lambda i: rows_call(pool[i % ncopies][2], z, y), W, K)
+    t_step = graph_us(torch, step, n)
+    t13 = graph_us(torch, lambda i: w13_call(pool[i % nc][0], pool[i % nc][1], x, z), n)
+    t2 = graph_us(torch, lambda i: rows_call(pool[i % nc][2], z, y), n)
     b13 = 2 * algo(8192, 2048) + 2048 * 2 + 8192 * 4
     b2 = algo(2048, 8192) + 8192 * 4 + 2048 * 4
-    del pool, base
-    torch.cuda.empty_cache()
-
-    # prompt window: w1/w3 + SwiGLU over 8192 rows, bf16 out
+    # the prompt window over two alternating copies of weights and prompt
     xw = to_dev(synthetic.draw_bf16_rows(rng, 8192, 2048), np.int16, dev).view(torch.bfloat16)
-    p1, p3 = pack(w1), pack(w3)
+    wins = [(pool[0][0], pool[0][1], xw), (pool[1][0], pool[1][1], xw.clone())]
     zw = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
-    for _ in range(2):
-        win_call(p1, p3, xw, zw)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-    torch.cuda.synchronize()
-    for e in evs:
-        e[0].record()
-        win_call(p1, p3, xw, zw)
-        e[1].record()
-    torch.cuda.synchronize()
-    tw = np.array([e[0].elapsed_time(e[1]) for e in evs]).mean() * 1e-3
-    tf = 2.0 * 8192 * (2 * 8192) * 2048 / tw / 1e12
-    del p1, p3, zw, xw
+    tw = graph_us(torch, lambda i: win_call(wins[i % 2][0], wins[i % 2][1], wins[i % 2][2], zw), 6)
+    tf = 2.0 * 8192 * (2 * 8192) * 2048 / (tw * 1e-6) / 1e12
+    del pool, wins, zw, xw
     torch.cuda.empty_cache()
     return {
-        "decode_step": {"ms_per_step": round(ms, 6), "GB/s": round((b13 + b2) / (ms * 1e-3) / 1e9, 2), "step_bytes": b13 + b2},
-        "qmv_w13_swiglu": {"avg_us": round(t13, 3), "GB/s": round(b13 / (t13 * 1e-6) / 1e9, 1),
-                           "frac": round(b13 / (t13 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
-        "qmv_rows_w2_f32x": {"avg_us": round(t2, 3), "GB/s": round(b2 / (t2 * 1e-6) / 1e9, 1),
-                             "frac": round(b2 / (t2 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
-        "pgemm_swiglu_8192": {"avg_ms": round(tw * 1e3, 4), "TFLOP/s": round(tf, 2), "frac": round(tf / BF16_PEAK_TFLOPS, 4)},
+        "decode_step": {"us": r3(t_step), "GB/s": round((b13 + b2) / (t_step * 1e-6) / 1e9, 1)},
+        "qmv_w13_swiglu": {"us": r3(t13), "frac": round(b13 / (t13 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "qmv_rows_w2_f32x": {"us": r3(t2), "frac": round(b2 / (t2 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "pgemm_swiglu_8192": {"us": r3(tw), "TFLOP/s": round(tf, 2), "frac": round(tf / BF16_PEAK_TFLOPS, 4)},
     }
-
-
-def bench_rows(dev, K, W, pool_mb):
-    """The 4-bit decode FFN step with 2, 4, 8 and 16 activation rows sharing
-    it (streams in one decode step): same shapes, cold weight pool and graph
-    timing as the one-row step. rows/s = rows / step time."""
-    import torch
-
-    import bit_weight_only_q4g64_amd as q4
-    import synthetic
-
-    log("decode FFN step at 2..16 rows")
-    d = synthetic.config(1)
-    w1, w3, w2 = d["w1"], d["w3"], d["w2"]
-    copy_bytes = q4.packed_bytes(w1.N, w1.K) * 2 + q4.packed_bytes(w2.N, w2.K)
-    ncopies = max(2, -(-pool_mb * (1 << 20) // copy_bytes))
-    base = [pack_dev(w1, dev), pack_dev(w3, dev), pack_dev(w2, dev)]
-    pool = [base] + [[t.clone() for t in base] for _ in range(ncopies - 1)]
-    xs = to_dev(synthetic.draw_bf16_rows(np.random.default_rng(11), 16, w1.K), np.int16, dev).view(torch.bfloat16)
-    z = torch.empty((16, w1.N), dtype=torch.float32, device=dev)
-    y = torch.empty((16, w2.N), dtype=torch.float32, device=dev)
-    z3s = {R: torch.empty((3, R, w1.N), dtype=torch.bfloat16, device=dev) for R in (1, 2, 4, 8, 16)}
-    z3ts = {R: q4.TiledPlanes.empty(R, w1.N, dev) for R in (1, 2, 4, 8, 16)}
-    out = {}
-    for R in (1, 2, 4, 8, 16):
-        z3 = z3s[R]
-
-        def step(i):
-            p1, p3, p2 = pool[i % ncopies]
-            q4.qmv_w13_swiglu(p1, p3, w1.N, w1.K, xs[:R], y=z[:R])
-            q4.qmv_rows(p2, w2.N, w2.K, z[:R], y=y[:R])
-
-        def step3(i):
-            p1, p3, p2 = pool[i % ncopies]
-            q4.qmv_w13_swiglu(p1, p3, w1.N, w1.K, xs[:R], y=z3, planes=True)
-            q4.qmv_rows(p2, w2.N, w2.K, z3, y=y[:R])
-
-        z3t = z3ts[R]
-
-        def step3t(i):
-            p1, p3, p2 = pool[i % ncopies]
-            q4.qmv_w13_swiglu(p1, p3, w1.N, w1.K, xs[:R], y=z3t, planes="tiled")
-            q4.qmv_rows(p2, w2.N, w2.K, z3t, y=y[:R])
-
-        us = batch_average_us(torch, step, W, K)
-        us3 = batch_average_us(torch, step3, W, K)
-        us3t = batch_average_us(torch, step3t, W, K)
-        t13 = batch_average_us(torch, lambda i: q4.qmv_w13_swiglu(pool[i % ncopies][0], pool[i % ncopies][1], w1.N, w1.K, xs[:R],
-                                                                  y=z[:R]), W, K)
-        t2 = batch_average_us(torch, lambda i: q4.qmv_rows(pool[i % ncopies][2], w2.N, w2.K, z[:R], y=y[:R]), W, K)
-        t2p = batch_average_us(torch, lambda i: q4.qmv_rows(pool[i % ncopies][2], w2.N, w2.K, z3, y=y[:R]), W, K)
-        t2t = batch_average_us(torch, lambda i: q4.qmv_rows(pool[i % ncopies][2], w2.N, w2.K, z3t, y=y[:R]), W, K)
-        b = 2 * qbytes(w1.N, w1.K) + qbytes(w2.N, w2.K) + R * (w1.K * 2 + w1.N * 4 + w2.K * 4 + w2.N * 4)
-        out[f"R{R}"] = {"us_per_step": round(us, 3), "rows_per_s": round(R / (us * 1e-6), 1), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
-                        "qmv_w13_swiglu_us": round(t13, 3), "qmv_rows_w2_f32x_us": round(t2, 3),
-                        "planes_us_per_step": round(us3, 3), "planes_rows_per_s": round(R / (us3 * 1e-6), 1),
-                        "qmv_rows_w2_planes_us": round(t2p, 3),
-                        "tiled_us_per_step": round(us3t, 3), "tiled_rows_per_s": round(R / (us3t * 1e-6), 1),
-                        "qmv_rows_w2_tiled_us": round(t2t, 3)}
-    del pool, base
-    torch.cuda.empty_cache()
-    out["workload"] = ("decode FFN step (w1/w3 8192x2048 + SwiGLU, w2 2048x8192, q4g64) with R bf16 rows, graph of K steps; "
-                       "planes_*: the SwiGLU output handed to w2 as its three exact bf16 planes instead of float32 (same bits); "
-                       "tiled_*: the same planes in the matvec's fragment order (Q4_BF16X3T, same bits)")
-    return out
-
-
-def bench_qkv_rope(dev, K, W, pool_mb):
-    """The stacked q/k/v decode matvec (3072 x 2048, 4-bit) with partial RoPE
-    and the KV store: fused in one launch against qmv_rows + rope_kv_store,
-    at 1 and 16 rows, cold weights, graph-batch averages."""
-    import torch
-
-    import bit_weight_only_q4g64_amd as q4
-    import synthetic
-
-    log("q/k/v matvec with RoPE and the KV store")
-    d = synthetic.config(2)
-    w = synthetic.concat_rows(d["wq"], d["wk"], d["wv"], name="qkv")
-    base = pack_dev(w, dev)
-    ncopies = max(2, -(-pool_mb * (1 << 20) // base.numel()))
-    pool = [base] + [base.clone() for _ in range(ncopies - 1)]
-    x = to_dev(d["x"], np.int16, dev).view(torch.bfloat16)
-    ring = 4096
-    pos = torch.arange(100, 116, dtype=torch.int32, device=dev)
-    q = torch.empty((16, 2048), device=dev)
-    kc = torch.empty((ring, 8, 64), device=dev, dtype=torch.bfloat16)
-    vc = torch.empty((ring, 8, 64), device=dev, dtype=torch.bfloat16)
-    y = torch.empty((16, w.N), device=dev)
-    out = {}
-    for R in (1, 16):
-        fused = batch_average_us(torch, lambda i: q4.qmv_qkv_rope(pool[i % ncopies], w.K, x[:R], pos[:R], 32, 8, 64, 1e6, q[:R], kc, vc), W, K)
-
-        def unfused(i):
-            q4.qmv_rows(pool[i % ncopies], w.N, w.K, x[:R], y=y[:R])
-            q4.rope_kv_store(y[:R], pos[:R], 32, 8, 64, 1e6, q[:R], kc, vc)
-
-        two = batch_average_us(torch, unfused, W, K)
-        mv = batch_average_us(torch, lambda i: q4.qmv_rows(pool[i % ncopies], w.N, w.K, x[:R], y=y[:R]), W, K)
-        b = qbytes(w.N, w.K) + R * w.K * 2
-        out[f"R{R}"] = {"fused_us": round(fused, 3), "qmv_rows_plus_epilogue_us": round(two, 3), "qmv_rows_alone_us": round(mv, 3),
-                        "fused_GB/s": round(b / (fused * 1e-6) / 1e9, 1)}
-    del pool, base
-    torch.cuda.empty_cache()
-    # gated attention: a gate projection of the q projection's shape stacked after v (the fourth matvec)
-    wg = synthetic.draw_qweight(np.random.default_rng(951), "wg", 2048, 2048)
-    w4 = synthetic.concat_rows(d["wq"], d["wk"], d["wv"], wg, name="qkvg")
-    base = pack_dev(w4, dev)
-    ncopies = max(2, -(-pool_mb * (1 << 20) // base.numel()))
-    pool = [base] + [base.clone() for _ in range(ncopies - 1)]
-    g = torch.empty((16, 2048), device=dev)
-    y4 = torch.empty((16, w4.N), device=dev)
-    for R in (1, 16):
-        fused = batch_average_us(
-            torch, lambda i: q4.qmv_qkv_rope(pool[i % ncopies], w4.K, x[:R], pos[:R], 32, 8, 64, 1e6, q[:R], kc, vc, gate_out=g[:R]), W, K)
-
-        def unfused4(i):
-            q4.qmv_rows(pool[i % ncopies], w4.N, w4.K, x[:R], y=y4[:R])
-            q4.rope_kv_store(y4[:R], pos[:R], 32, 8, 64, 1e6, q[:R], kc, vc, gate_out=g[:R])
-
-        two = batch_average_us(torch, unfused4, W, K)
-        b = qbytes(w4.N, w4.K) + R * w4.K * 2
-        out[f"gated_R{R}"] = {"fused_us": round(fused, 3), "qmv_rows_plus_epilogue_us": round(two, 3),
-                              "fused_GB/s": round(b / (fused * 1e-6) / 1e9, 1)}
-    del pool, base
-    torch.cuda.empty_cache()
-    out["workload"] = ("stacked q/k/v 3072x2048 q4g64 (32 q + 8 kv heads x 64), rot 64, theta 1e6, bf16 KV ring of 4096; "
-                       "gated_*: q/k/v/gate 5120x2048 (32 gate heads after v)")
-    return out
 
 
 # HBM bytes the 8192-row w1/w3 + SwiGLU window must move at least: both
@@ -639,64 +747,164 @@ def bench_qkv_rope(dev, K, W, pool_mb):
 PGEMM_BYTES = 2 * (8192 * 2048 * 9 // 16) + 8192 * 2048 * 2 + 8192 * 8192 * 2
 
 
-def bench_pgemm(dev, reps=10):
-    """w1/w3 + SwiGLU (bf16 out) over the 8192-row prompt as one window."""
+def pgemm_only(dev, reps=6):
+    """Only the 8192-row w1/w3 + SwiGLU window (bf16 out), on two alternating
+    copies of weights and prompt: the dispatches the prompt GEMM's counters
+    are taken on."""
     import torch
 
     import bit_weight_only_q4g64_amd as q4
     import synthetic
 
-    log("prompt GEMM: 8192 x (2 x 8192) x 2048 with SwiGLU")
     rng = np.random.default_rng(4)
-    w1 = synthetic.draw_qweight(rng, "w1", 8192, 2048)
-    w3 = synthetic.draw_qweight(rng, "w3", 8192, 2048)
-    x = to_dev(synthetic.draw_bf16_rows(rng, 8192, 2048), np.int16, dev).view(torch.bfloat16)
-    p1, p3 = pack_dev(w1, dev), pack_dev(w3, dev)
+    w1, w3 = synthetic.draw_qweight(rng, "w1", 8192, 2048), synthetic.draw_qweight(rng, "w3", 8192, 2048)
+    xh = synthetic.draw_bf16_rows(rng, 8192, 2048)
+    copies = [(pack_dev(w1, dev), pack_dev(w3, dev), to_dev(xh, np.int16, dev).view(torch.bfloat16)) for _ in range(2)]
     z = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
-    for _ in range(2):
+    ts = []
+    for r in range(reps):
+        p1, p3, x = copies[r % 2]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         q4.qmm_window(p1, p3, 8192, 2048, x, y=z)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-    torch.cuda.synchronize()
-    for e in evs:
-        e[0].record()
-        q4.qmm_window(p1, p3, 8192, 2048, x, y=z)
-        e[1].record()
-    torch.cuda.synchronize()
-    t = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3  # s
-    flops = 2.0 * 8192 * (2 * 8192) * 2048
-    tf = flops / t.mean() / 1e12
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    t = float(np.median(ts[1:]))
+    return {"avg_us": round(t * 1e6, 2), "TFLOP/s": round(2.0 * 8192 * 16384 * 2048 / t / 1e12, 2)}
 
-    # the same prompt through the window driver in 128-row windows (64 short
-    # windows, one launch each), checked bit for bit against the whole window
-    log("prompt GEMM: the same 8192 rows as 64 windows of 128 rows (qmm_cut)")
-    cut = [128] * 64
-    zc = torch.empty_like(z)
-    for _ in range(2):
-        q4.qmm_cut(p1, p3, 8192, 2048, x, cut, y=zc)
-    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-    torch.cuda.synchronize()
-    for e in evc:
-        e[0].record()
-        q4.qmm_cut(p1, p3, 8192, 2048, x, cut, y=zc)
-        e[1].record()
-    torch.cuda.synchronize()
-    tc = np.array([e[0].elapsed_time(e[1]) for e in evc]) * 1e-3
-    same = bool(torch.equal(zc.view(torch.int16), z.view(torch.int16)))
-    return {
-        "workload": "qmm_window w1/w3 8192x2048 + SwiGLU, M=8192 prompt rows, bf16 out (seed 4 shapes)",
-        "avg_ms": round(float(t.mean() * 1e3), 4),
-        "TFLOP/s": round(tf, 2),
-        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": traffic_per_launch("pgemm_swiglu_8192"),
-                     "algorithmic_bytes_per_launch": PGEMM_BYTES},
-        "windows_128": {
-            "workload": "the same prompt through qmm_cut in 64 windows of 128 rows",
-            "avg_ms": round(float(tc.mean() * 1e3), 4),
-            "us_per_window": round(float(tc.mean() * 1e6 / 64), 2),
-            "TFLOP/s": round(flops / tc.mean() / 1e12, 2),
-            "bits_equal_whole_window": same,
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true", help="only the headline decode step (for its per-dispatch counters)")
+    ap.add_argument("--no-wide", action="store_true", help="skip the 6-/8-bit, block-FP8 and attention-epilogue measurements")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the timed steps directly instead of replaying a graph (for per-dispatch counters)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (the reference for scaling HBM byte counters)")
+    ap.add_argument("--pgemm-only", action="store_true",
+                    help="only the 8192-row w1/w3 + SwiGLU window (for its per-dispatch counters); prints its JSON object")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the machines this runs on have one, and the multi-GPU path is a design only "
+              "(sharding over output columns for decode and over prompt rows for windows)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    import bit_weight_only_q4g64_amd as q4
+    import synthetic
+
+    q4.lib()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    if args.pgemm_only:
+        print(json.dumps(pgemm_only(dev)))
+        return
+
+    log("generating the decode FFN workload")
+    d = synthetic.config(1)
+    K, W = args.steps, args.warmup
+    st = bench_step(d, dev, K, W, no_graph=args.no_graph)
+    step_bytes = decode_step_bytes(d)
+    value = step_bytes / (st["ms_per_step"] * 1e-3) / 1e9
+    kernel_gbs = step_bytes / (st["step_kernel_us"] * 1e-6) / 1e9
+    w1, w2 = d["w1"], d["w2"]
+    b13 = 2 * qbytes(w1.N, w1.K) + w1.K * 2 + w1.N * 4
+    b2 = qbytes(w2.N, w2.K) + w2.K * 4 + w2.N * 4
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(st["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode FFN step: z = silu(W1 x) * (W3 x) over w1/w3 8192x2048 q4g64, then y = W2 z over w2 2048x8192 "
+                        "q4g64 on the float32 z, as one qmv_ffn launch; 1 bf16 activation row; seed 1",
+            "rows": 1,
+            "step_bytes": step_bytes,
+            "weight_pool_copies": st["pool_copies"],
+            "timing": ("HIP graph of K steps" if not args.no_graph else "K directly launched steps")
+            + "; value from the wall clock between synchronizes, kernel time from HIP events around the same region",
+        },
+        "rows_per_s": round(1.0 / (st["ms_per_step"] * 1e-3), 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "q4::ffn_flow_kernel<1, 1> (qmv_ffn, the whole step in one launch)",
+            "achieved": round(kernel_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic_per_launch("ffn_flow_step"),
+            "algorithmic_bytes_per_launch": step_bytes,
+            "avg_launch_us": round(st["step_kernel_us"], 3),
+            "step_frac": round(value / HBM_PEAK_GBS, 4),
+            "kernels": {
+                "ffn_flow_step": {"us": r3(st["ffn_graph_us"]), "bytes": step_bytes,
+                                  "frac": round(step_bytes / (st["ffn_graph_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+                "two_calls_step": {"us": r3(st["two_calls_us"]), "bytes": step_bytes,
+                                   "frac": round(step_bytes / (st["two_calls_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+                "qmv_w13_swiglu": {"us": r3(st["w13_us"]), "bytes": b13, "frac": round(b13 / (st["w13_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "traffic": traffic_per_launch("qmv_w13_swiglu")},
+                "qmv_rows_w2_f32x": {"us": r3(st["w2_us"]), "bytes": b2, "frac": round(b2 / (st["w2_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                     "traffic": traffic_per_launch("qmv_rows_w2")},
+            },
+            "target": "0.70 of the HBM peak for decode (28.4 MB in <= 5.1 us)",
         },
     }
+    if args.step_only:
+        print(json.dumps(result), flush=True)
+        return
+    inputs = {"c1": input_hashes(d)}
+    log("c0 single matvec")
+    result["c0"] = bench_c0(dev, K)
+    log("c2 attention projections")
+    result["c2"] = bench_c2(dev, K)
+    log("c3 1000-row prompt cuts")
+    result["c3"] = bench_c3(dev, K)
+    result["c4"] = bench_c4(dev)
+    inputs["c4"] = result["c4"].pop("inputs_sha256")
+    w13 = result["c4"]["whole"]["w1w3_swiglu"]
+    result["pgemm"] = {
+        "workload": "the 8192-row layer's w1/w3 + SwiGLU window (bf16 out), the largest window of the layer",
+        "roofline": {"bound": "mfma", "kernel": "q4::pgemm_kernel<true, true, 4>", "achieved": w13["TFLOP/s"],
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": w13["frac"],
+                     "traffic": traffic_per_launch("pgemm_swiglu_8192"), "algorithmic_bytes_per_launch": PGEMM_BYTES,
+                     "avg_launch_us": w13["us"], "mfma_counters": summary_json("mfma_pgemm_swiglu_8192.md"),
+                     "target": "0.50 of the bf16 matrix-core peak"},
+    }
+    log("decode step at 1..16 rows")
+    result["decode_rows"] = bench_rows(dev, K)
+    result["rows_per_s_at_16_rows"] = result["decode_rows"]["R16"]["best_rows_per_s"]
+    if not args.no_wide:
+        log("attention epilogue")
+        result["qkv_rope"] = bench_qkv_rope(dev, K)
+        log("6-bit, 8-bit and block-FP8 weights")
+        result["wide_codes"] = {str(b): bench_wide(dev, b, K) for b in (6, 8, "fp8")}
+    result["copy_bandwidth"] = copy_bandwidth(torch)
+    for i in (0, 2, 3):
+        inputs[f"c{i}"] = input_hashes(synthetic.config(i))
+    result["provenance"] = provenance(torch, inputs)
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(d, st["z"], st["y"])
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":
