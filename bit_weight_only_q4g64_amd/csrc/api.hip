@@ -35,6 +35,10 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
+// Row strides (elements) and the elements a strided array spans: small enough
+// that no offset a call forms, on the host or in a kernel, overflows int64.
+constexpr int64_t kMaxStride = int64_t(1) << 40;
+constexpr int64_t kMaxSpan = int64_t(1) << 48;
 constexpr size_t kMaxLds = 64 * 1024;
 // Window GEMM: one column tile's codes (K / 128 pairs of 1 KiB) are addressed
 // with 32-bit offsets.
@@ -49,6 +53,11 @@ int check_nk(const char* fn, int64_t N, int64_t K) {
     return fail(Q4_EINVAL, "%s: N=%lld and K=%lld must be positive multiples of 64", fn, (long long)N, (long long)K);
   if (N > kMaxDim || K > kMaxDim || N * K > kMaxElems)
     return fail(Q4_EINVAL, "%s: N=%lld x K=%lld is too large", fn, (long long)N, (long long)K);
+  return Q4_OK;
+}
+
+int check_ld(const char* fn, const char* name, int64_t ld) {
+  if (ld > kMaxStride) return fail(Q4_EINVAL, "%s: %s=%lld exceeds 2^40 elements", fn, name, (long long)ld);
   return Q4_OK;
 }
 
@@ -79,6 +88,7 @@ int check_x(const char* fn, const void* x, int x_dtype, int64_t ldx, int64_t K) 
     return fail(Q4_EINVAL, "%s: fragment-ordered planes have no row stride (ldx=%lld must equal K=%lld)", fn, (long long)ldx,
                 (long long)K);
   if (ldx < K) return fail(Q4_EINVAL, "%s: ldx=%lld < K=%lld", fn, (long long)ldx, (long long)K);
+  if (int rc = check_ld(fn, "ldx", ldx)) return rc;
   const int64_t es = x_dtype == Q4_F32 ? 4 : 2;
   if ((ldx * es) % 16 != 0) return fail(Q4_EALIGN, "%s: ldx=%lld elements does not keep rows 16-byte aligned", fn, (long long)ldx);
   return Q4_OK;
@@ -159,6 +169,7 @@ int qmv_rows_impl(const char* fn, int bits, const void* packed, int64_t N, int64
   if (int rc = check_x(fn, x, x_dtype, ldx, K)) return rc;
   if (int rc = check_ptr(fn, "y", y, 4)) return rc;
   if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  if (int rc = check_ld(fn, "ldy", ldy)) return rc;
   const int64_t xrows = x_dtype == Q4_BF16X3 ? 3 * (int64_t)R : R;  // planes: three rows per activation row
   if (xrows * ldx * (x_dtype == Q4_F32 ? 4 : 2) >= (int64_t(1) << 31))
     return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
@@ -197,6 +208,7 @@ int qmv_split_check(const char* fn, int bits, const void* packed, int64_t N, int
   if (int rc = check_x(fn, x, x_dtype, ldx, K)) return rc;
   if (int rc = check_ptr(fn, "y", y, 4)) return rc;
   if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  if (int rc = check_ld(fn, "ldy", ldy)) return rc;
   const int64_t xrows = x_dtype == Q4_BF16X3 ? 3 * (int64_t)R : R;
   if (xrows * ldx * (x_dtype == Q4_F32 ? 4 : 2) >= (int64_t(1) << 31))
     return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
@@ -232,6 +244,7 @@ int qmv_w13_impl(const char* fn, int bits, const void* packed_w1, const void* pa
   if (int rc = check_x(fn, x, Q4_BF16, ldx, K)) return rc;
   if (int rc = check_ptr(fn, y3 ? "z3" : "y", y, y3 ? 16 : 4)) return rc;
   if (ldy < N) return fail(Q4_EINVAL, "%s: %s=%lld < N=%lld", fn, y3 ? "ldz" : "ldy", (long long)ldy, (long long)N);
+  if (int rc = check_ld(fn, y3 ? "ldz" : "ldy", ldy)) return rc;
   if (y3 == 1 && (ldy * 2) % 16 != 0)
     return fail(Q4_EALIGN, "%s: ldz=%lld elements does not keep rows 16-byte aligned", fn, (long long)ldy);
   if (y3 == 2 && N > q4::kQmvMaxK)
@@ -321,6 +334,7 @@ int check_window_args(const char* fn, const void* packed_a, const void* packed_b
   if (y_dtype != Q4_BF16 && y_dtype != Q4_F32) return fail(Q4_EINVAL, "%s: y_dtype %d is not Q4_BF16 or Q4_F32", fn, y_dtype);
   if (int rc = check_ptr(fn, "y", y, y_dtype == Q4_F32 ? 4 : 2)) return rc;
   if (ldy < N) return fail(Q4_EINVAL, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  if (int rc = check_ld(fn, "ldy", ldy)) return rc;
   if ((int64_t)q4::kPgemmRows * ldx * 2 >= (int64_t(1) << 31))
     return fail(Q4_EUNSUPPORTED, "%s: ldx=%lld is too large for a %d-row window tile", fn, (long long)ldx, q4::kPgemmRows);
   if (K > kPgemmMaxK) return fail(Q4_EUNSUPPORTED, "%s: K=%lld exceeds the window GEMM limit of %lld", fn, (long long)K, (long long)kPgemmMaxK);
@@ -397,11 +411,20 @@ int ffn_launch_s1(int spw1, int spw2, const uint8_t* p1, const uint8_t* p3, cons
 
 }  // namespace
 
+// The rows of a window (a cut) must lie within 2^48 elements of x and of y.
+int check_rows_span(const char* fn, int64_t rows, int64_t ldx, int64_t ldy) {
+  if (rows > kMaxSpan / ldx || rows > kMaxSpan / ldy)
+    return fail(Q4_EINVAL, "%s: %lld rows of strides ldx=%lld, ldy=%lld span more than 2^48 elements", fn, (long long)rows,
+                (long long)ldx, (long long)ldy);
+  return Q4_OK;
+}
+
 int qmm_window_checked(const char* fn, int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K,
                        const uint16_t* x, int64_t ldx, int64_t M, void* y, int y_dtype, int64_t ldy, hipStream_t s) {
   if (int rc = check_fmt(fn, bits)) return rc;
   if (int rc = check_window_args(fn, packed_a, packed_b, N, K, x, ldx, y, y_dtype, ldy)) return rc;
   if (M < 1 || M > kPgemmMaxM) return fail(Q4_EINVAL, "%s: M=%lld is outside 1..%lld", fn, (long long)M, (long long)kPgemmMaxM);
+  if (int rc = check_rows_span(fn, M, ldx, ldy)) return rc;
   return qmm_window_impl(fn, bits, packed_a, packed_b, N, K, x, ldx, M, y, y_dtype, ldy, s);
 }
 
@@ -413,6 +436,9 @@ int qmm_cut_impl(const char* fn, int bits, const void* packed_a, const void* pac
   for (int w = 0; w < n_windows; ++w)
     if (window_rows[w] < 1 || window_rows[w] > kPgemmMaxM)
       return fail(Q4_EINVAL, "%s: window %d has %lld rows", fn, w, (long long)window_rows[w]);
+  int64_t rows = 0;  // at most 2^31 windows of at most 2^24 rows: no overflow
+  for (int w = 0; w < n_windows; ++w) rows += window_rows[w];
+  if (int rc = check_rows_span(fn, rows, ldx, ldy)) return rc;
   const int64_t es = y_dtype == Q4_F32 ? 4 : 2;
   int64_t row0 = 0;
   for (int w = 0; w < n_windows; ++w) {
@@ -433,8 +459,11 @@ int check_rope_args(const char* fn, const q4_rope_kv* a, int R, q4::RopeKvArgs* 
   if (!(a->theta > 0.f) || !isfinite(a->theta)) return fail(Q4_EINVAL, "%s: theta must be positive and finite", fn);
   if (!(a->eps >= 0.f) || !isfinite(a->eps)) return fail(Q4_EINVAL, "%s: eps must be >= 0 and finite", fn);
   if (a->cache_dtype != Q4_F32 && a->cache_dtype != Q4_BF16) return fail(Q4_EINVAL, "%s: cache_dtype %d is not Q4_F32 or Q4_BF16", fn, a->cache_dtype);
-  if (a->ring_len < 1) return fail(Q4_EINVAL, "%s: ring_len=%lld < 1", fn, (long long)a->ring_len);
+  // positions are int32, so a longer ring would never be filled
+  if (a->ring_len < 1 || a->ring_len > (int64_t(1) << 31))
+    return fail(Q4_EINVAL, "%s: ring_len=%lld is outside 1..2^31", fn, (long long)a->ring_len);
   if (a->ldq < (int64_t)a->n_q_heads * 64) return fail(Q4_EINVAL, "%s: ldq=%lld < n_q_heads * 64", fn, (long long)a->ldq);
+  if (int rc = check_ld(fn, "ldq", a->ldq)) return rc;
   if (int rc = check_ptr(fn, "pos", a->pos, 4)) return rc;
   if (int rc = check_ptr(fn, "q_out", a->q_out, 4)) return rc;
   const uintptr_t ce = a->cache_dtype == Q4_F32 ? 4 : 2;
@@ -445,9 +474,11 @@ int check_rope_args(const char* fn, const q4_rope_kv* a, int R, q4::RopeKvArgs* 
   if (a->n_gate_heads < 0 || a->n_gate_heads > 4096) return fail(Q4_EINVAL, "%s: n_gate_heads=%d must be 0..4096", fn, a->n_gate_heads);
   if (a->n_gate_heads > 0) {
     if (a->ldg < (int64_t)a->n_gate_heads * 64) return fail(Q4_EINVAL, "%s: ldg=%lld < n_gate_heads * 64", fn, (long long)a->ldg);
+    if (int rc = check_ld(fn, "ldg", a->ldg)) return rc;
     if (int rc = check_ptr(fn, "gate_out", a->gate_out, 4)) return rc;
   }
   if (a->cache_row_stride < 0) return fail(Q4_EINVAL, "%s: cache_row_stride=%lld < 0", fn, (long long)a->cache_row_stride);
+  if (int rc = check_ld(fn, "cache_row_stride", a->cache_row_stride)) return rc;
   if (a->cache_row_stride > 0 && a->cache_row_stride < a->ring_len * a->n_kv_heads * 64)
     return fail(Q4_EINVAL, "%s: cache_row_stride=%lld is below ring_len * n_kv_heads * 64: the rows' rings would overlap", fn,
                 (long long)a->cache_row_stride);
@@ -668,6 +699,8 @@ int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2,
   if (int rc = check_ptr(fn, "work", work, 256)) return rc;
   if (ldz < N1) return fail(Q4_EINVAL, "%s: ldz=%lld < N1=%lld", fn, (long long)ldz, (long long)N1);
   if (ldy < N2) return fail(Q4_EINVAL, "%s: ldy=%lld < N2=%lld", fn, (long long)ldy, (long long)N2);
+  if (int rc = check_ld(fn, "ldz", ldz)) return rc;
+  if (int rc = check_ld(fn, "ldy", ldy)) return rc;
   if ((int64_t)R * ldx * 2 >= (int64_t(1) << 31))
     return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
   // 8 waves per w1/w3 tile and 16 per w2 half-tile, up to 2 segments each
@@ -773,6 +806,7 @@ int rope_kv_store(const float* qkv, int64_t ldqkv, int R, const q4_rope_kv* args
   const int heads = a.n_q + 2 * a.n_kv + a.n_gate;
   if (ldqkv < (int64_t)heads * 64)
     return fail(Q4_EINVAL, "%s: ldqkv=%lld < (n_q_heads + 2 n_kv_heads + n_gate_heads) * 64", fn, (long long)ldqkv);
+  if (int rc = check_ld(fn, "ldqkv", ldqkv)) return rc;
   hipLaunchKernelGGL(q4::rope_kv_kernel, dim3((unsigned)heads, (unsigned)R), dim3(64), 0, (hipStream_t)stream, qkv, ldqkv, a);
   return launched(fn);
 }

@@ -80,6 +80,9 @@
  *   - N and K must be positive multiples of 64. Packed buffers, x and wq must
  *     be 16-byte aligned; x row strides (ldx, in elements) must keep every row
  *     16-byte aligned. Outputs must not alias inputs.
+ *   - Every row stride (ldx, ldy, ldz, ldq, ldg, ldqkv, cache_row_stride) is
+ *     at most 2^40 elements (Q4_EINVAL otherwise), so no offset a call forms
+ *     overflows 64-bit arithmetic.
  *   - The caller passes the same (N, K) to pack_q4g64 and to every use.
  */
 #ifndef Q4G64_H
@@ -235,7 +238,8 @@ int qmv_w13_swiglu_x3t(int bits, const void* packed_w1, const void* packed_w3, i
  *   changes": paired FFN projections keep their rounding boundaries).
  *   y: [M][ldy], y_dtype Q4_F32 or Q4_BF16 (round to nearest even).
  * A row's result does not depend on M, on its offset or on the other rows.
- * Limits: M <= 2^24, K <= 2^20, 512 * ldx < 2^31 (Q4_EINVAL / Q4_EUNSUPPORTED). */
+ * Limits: M <= 2^24, K <= 2^20, 512 * ldx < 2^31, M * ldx and M * ldy at
+ * most 2^48 elements (Q4_EINVAL / Q4_EUNSUPPORTED). */
 int qmm_window(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                int64_t M, void* y, int y_dtype, int64_t ldy, void* stream);
 
@@ -247,7 +251,9 @@ int qmm_window_qg64(int bits, const void* packed_a, const void* packed_b, int64_
  * window_rows is a HOST array of n_windows positive row counts; window w
  * covers rows [sum of earlier counts, + window_rows[w]) of x and y. The
  * result is bit-identical for every cut (PR #1696, later revision, "Checks":
- * windows of 64, 128, 256 and a ragged cut agree bit for bit). */
+ * windows of 64, 128, 256 and a ragged cut agree bit for bit). Every count
+ * is checked before any window is enqueued, and the total rows obey the
+ * 2^48-element span limit of qmm_window. */
 int qmm_cut(const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
             const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, void* stream);
 
@@ -360,7 +366,7 @@ typedef struct q4_rope_kv {
   void* k_cache;          /* [ring_len][n_kv_heads][64] */
   void* v_cache;
   int32_t cache_dtype;    /* Q4_F32 or Q4_BF16 */
-  int64_t ring_len;       /* >= 1 */
+  int64_t ring_len;       /* 1..2^31 (positions are int32) */
   int32_t n_gate_heads;   /* >= 0 gate heads after the v heads */
   float* gate_out;        /* float32 [R][ldg], ldg >= n_gate_heads * 64; may be NULL when n_gate_heads = 0 */
   int64_t ldg;
