@@ -154,3 +154,69 @@ def test_c3_windows_at_the_short_window_boundary(c3, c3_whole, rows):
     torch.cuda.synchronize()
     assert np.array_equal(bits32(z), bits32(c3_whole)[:rows])
     assert np.array_equal(bits32(a), bits32(a_whole)[:rows])
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_wide_kernel_odd_groups_and_partial_column_block(swiglu):
+    """4-bit windows large enough for the 128 x 256 (SwiGLU: 128 x 128)
+    workgroups, with an odd group count (K = 64 * 9: the pipeline's last
+    group pair is half empty) and a last column block partly past N
+    (N = 16 * 256 + 64). Sampled rows, including the last row block and all
+    N columns, are within the window bound of the oracle; a 100-row window
+    (on the short-window workgroups) and single rows are bit-identical to the
+    same rows of the wide launch."""
+    N, K = 4160, 576
+    M = 1000 if swiglu else 2000
+    cols = 128 if swiglu else 256
+    assert -(-N // cols) * -(-M // 128) >= 256 and -(-N // cols) < 256  # wide, then short-window workgroups
+    say(f"wide pgemm N={N} K={K} M={M} swiglu={swiglu}")
+    rng = np.random.default_rng(4160 + swiglu)
+    w = synthetic.draw_qweight(rng, "wa", N, K)
+    w3 = synthetic.draw_qweight(rng, "wb", N, K)
+    x = synthetic.draw_bf16_rows(rng, M, K)
+    pk, pk3, xd = dev_weight(w), dev_weight(w3), dev_bf16(x)
+    pb = pk3 if swiglu else None
+    y = q4.qmm_window(pk, pb, N, K, xd)
+    y100 = q4.qmm_window(pk, pb, N, K, xd[:100])
+    torch.cuda.synchronize()
+    rows = [0, 1, 99, 100, 127, 128, 500, M - 129, M - 128, M - 2, M - 1]
+    xs = x[rows]
+    if swiglu:
+        a64 = oracle.matmul_rows(w.wq, w.scales, w.biases, xs)
+        c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, xs)
+        Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w.wq, w.scales, w.biases, xs), K, order="window"),
+                        tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, xs), K, order="window"))
+        ratio = float(np.max(np.abs(host_f64(y)[rows] - oracle.swiglu(a64, c64)) / Tz))
+        assert ratio <= 1.0, ratio
+    else:
+        check_within(host_f64(y)[rows], w, x, rows=rows, label="wide pgemm", order="window")
+    ref = bits32(y)
+    assert np.array_equal(bits32(y100), ref[:100])
+    for r in (0, 99, M - 1):
+        y1 = q4.qmm_window(pk, pb, N, K, xd[r : r + 1])
+        assert np.array_equal(bits32(y1)[0], ref[r]), r
+
+
+@pytest.mark.parametrize("layout", ["ldy_not_multiple_of_8", "rows_not_16_byte_aligned"])
+def test_wide_swiglu_bf16_output_rows_of_any_alignment(c3, c3_whole, layout):
+    """The 1000-row w1/w3 window (512 wide workgroups) writing bf16 into rows
+    that a 16-byte store cannot reach: row stride N + 4, or the output
+    starting one element into each row. Values equal the round-to-nearest-even
+    bf16 of the float32 result, and the padding around the rows is untouched."""
+    w1 = c3["w1"]
+    N, K, M = w1.N, w1.K, c3["x"].shape[0]
+    say(f"c3 pgemm SwiGLU bf16 out, {layout}")
+    nan = float("nan")
+    if layout == "ldy_not_multiple_of_8":
+        big = torch.full((M, N + 4), nan, dtype=torch.bfloat16, device=DEV)
+        y, c0 = big[:, :N], 0
+    else:
+        big = torch.full((M, N + 8), nan, dtype=torch.bfloat16, device=DEV)
+        y, c0 = big[:, 1 : N + 1], 1
+    q4.qmm_window(c3["p1"], c3["p3"], N, K, c3["xd"], y=y)
+    torch.cuda.synchronize()
+    expect = synthetic.bf16_bits_from_f64(c3_whole.cpu().numpy().astype(np.float64))
+    got = bits16(big).view(np.uint16)
+    assert np.array_equal(got[:, c0 : c0 + N], expect)
+    pad = np.delete(got, np.arange(c0, c0 + N), axis=1)
+    assert np.all((pad & 0x7FFF) > 0x7F80)  # still NaN
