@@ -113,10 +113,8 @@ def r3(v):
 
 
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["bit_weight_only_q4g64_amd/csrc/common.h", "bit_weight_only_q4g64_amd/csrc/qmv.h",
-                  "bit_weight_only_q4g64_amd/csrc/ffn.h", "bit_weight_only_q4g64_amd/csrc/ffn_flow.h",
-                  "bit_weight_only_q4g64_amd/csrc/pgemm_narrow.h", "bit_weight_only_q4g64_amd/csrc/pgemm.h",
-                  "bit_weight_only_q4g64_amd/csrc/api.hip"]
+CSRC = os.path.join(ROOT, "bit_weight_only_q4g64_amd", "csrc")
+KERNEL_SOURCES = sorted(os.path.relpath(os.path.join(CSRC, f), ROOT) for f in os.listdir(CSRC) if f.endswith((".h", ".hip")))
 
 
 def _code_only(text):
@@ -144,11 +142,15 @@ def _code_only(text):
 
 
 def kernel_source_hash():
-    """Hash of the kernel sources' code (comments and blank lines left out)."""
+    """Hash of the kernel sources' code (comments and blank lines left out) and
+    of the compiler flags they are built with."""
+    from bit_weight_only_q4g64_amd import build as _build
+
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
+    h.update(repr(_build.FLAGS).encode())
     return h.hexdigest()[:16]
 
 

@@ -5,7 +5,8 @@
 compiles ``csrc/api.hip`` (which includes every kernel) into
 ``bit_weight_only_q4g64_amd/libq4g64.so``. Strict IEEE float32: no fast-math and
 no floating-point contraction (every fused multiply-add in the kernels is an
-explicit fma), and no packed-fp32 instructions.
+explicit fma), no packed-fp32 instructions, and matrix-core results kept in
+ordinary vector registers.
 """
 
 from __future__ import annotations
@@ -33,6 +34,12 @@ FLAGS = [
     "-target-feature",
     "-Xclang",
     "-packed-fp32-ops",
+    # matrix-core results in ordinary vector registers rather than the
+    # accumulation registers: the same instructions (so the same bits), minus
+    # the copies between the two files before each fold; measured 1.2x on
+    # the short-window GEMM, no change on the others
+    "-mllvm",
+    "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-result",
 ]

@@ -15,6 +15,7 @@
 #include "ffn_flow.h"
 #include "pack.h"
 #include "pgemm.h"
+#include "pgemm_flow.h"
 #include "pgemm_narrow.h"
 #include "qmv.h"
 #include "rope.h"
@@ -288,6 +289,26 @@ void pgemm_launch_bits(bool swiglu, bool obf16, dim3 grid, dim3 block, hipStream
 // Below this many 256-column workgroups a window runs on the 64-column
 // workgroups of pgemm_narrow_kernel (4-bit codes; the same bits per row).
 constexpr int64_t kNarrowBelow = 256;
+// Among those, a window whose 32 x 32 tiles take at most two rounds of one
+// workgroup per compute unit (SwiGLU: one round) runs on pgemm_flow_kernel.
+// Measured on MI355X against the narrow kernel: 2.3x on a 128-row window of
+// w2 and 2x on o (one round), 1.1x on qkv (1.5 rounds); with SwiGLU 1.7x at
+// 16 rows (one round) but behind it at 64 rows (two rounds).
+constexpr int kFlowProducers = 3, kFlowStages = 2, kFlowRing = 8;
+
+void flow_launch(bool swiglu, bool obf16, const uint8_t* a, const uint8_t* b, int n, int k, const uint16_t* x, int64_t ldx, int m, void* y,
+                 int64_t ldy, int nb, int mb, hipStream_t s) {
+  using namespace q4;
+  const dim3 grid((unsigned)((int64_t)nb * mb)), block(64 * (kFlowProducers + 1));
+  constexpr int NP = kFlowProducers, NS = kFlowStages, R = kFlowRing;
+  if (swiglu) {
+    if (obf16) hipLaunchKernelGGL((pgemm_flow_kernel<true, true, NP, NS, R>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mb);
+    else hipLaunchKernelGGL((pgemm_flow_kernel<true, false, NP, NS, R>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mb);
+  } else {
+    if (obf16) hipLaunchKernelGGL((pgemm_flow_kernel<false, true, NP, NS, R>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mb);
+    else hipLaunchKernelGGL((pgemm_flow_kernel<false, false, NP, NS, R>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mb);
+  }
+}
 
 int qmm_window_impl(const char* fn, int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x,
                     int64_t ldx, int64_t M, void* y, int y_dtype, int64_t ldy, hipStream_t s) {
@@ -302,6 +323,11 @@ int qmm_window_impl(const char* fn, int bits, const void* packed_a, const void* 
   const uint8_t* b = swiglu ? (const uint8_t*)packed_b : a;
   const int n = (int)N, k = (int)K, m = (int)M;
   if (bits == 4 && blocks < kNarrowBelow) {
+    const int64_t fnb = (N + kFlowRows - 1) / kFlowRows, fmb = (M + kFlowRows - 1) / kFlowRows;
+    if (fnb * fmb <= (swiglu ? 1 : 2) * (int64_t)device_cus()) {
+      flow_launch(swiglu, obf16, a, b, n, k, x, ldx, m, y, ldy, (int)fnb, (int)fmb, s);
+      return launched(fn);
+    }
     const int cols = pgemm_narrow_cols(swiglu);
     const int nb = (n + cols - 1) / cols;
     const dim3 ngrid((unsigned)((int64_t)nb * mblk));
@@ -408,8 +434,6 @@ int ffn_launch_s1(int spw1, int spw2, const uint8_t* p1, const uint8_t* p3, cons
   if (spw1 <= 1) return ffn_launch_s2<NV, RTF, 1>(spw2, p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
   return ffn_launch_s2<NV, RTF, 2>(spw2, p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
 }
-
-}  // namespace
 
 // The rows of a window (a cut) must lie within 2^48 elements of x and of y.
 int check_rows_span(const char* fn, int64_t rows, int64_t ldx, int64_t ldy) {
@@ -532,6 +556,8 @@ int qkv_rope_launch_bits(int spw, int nv, const uint8_t* pk, int N, int K, const
   if (spw <= 2) return qkv_rope_launch_nv<2, BITS>(nv, pk, N, K, x, ldx, R, a, lds, heads, s);
   return qkv_rope_launch_nv<4, BITS>(nv, pk, N, K, x, ldx, R, a, lds, heads, s);
 }
+
+}  // namespace
 
 // ---- the split matvec without a caller workspace ---------------------------
 // Its workspace is this file-scope device array: one copy per GPU, held from

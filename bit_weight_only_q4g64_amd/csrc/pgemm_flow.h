@@ -1,0 +1,382 @@
+// Prompt GEMM for short windows (4-bit codes): producer waves and one folder
+// wave per 32 x 32 output tile.
+//
+// A window of up to a few hundred rows has few output tiles: a 128-row window
+// of w2 (2048 x 8192) is 256 tiles of 32 x 32, each a chain over 128 groups
+// of k. Run as one wave per tile, each group costs about 1000 cycles of
+// exposed latency (operand loads, four dependent matrix steps, the fold) on
+// a quarter of the SIMDs. But in the window order only the fold
+// acc = fma(s_g, P_g, acc) is a chain: the products P_g of different groups
+// are independent. So a workgroup here owns one tile (SwiGLU: the w1 tile and
+// the same w3 tile) with NP producer waves and one folder wave:
+//
+//   - producer p takes group pairs p, p + NP, p + 2 NP, ...: it moves the
+//     pair's 32 activation rows, code blocks and scale/bias blocks into NS
+//     private LDS stages by buffer-to-LDS DMA (NS - 1 pairs in flight while
+//     one is computed), forms P_g and the row sums S_g of both groups on the
+//     matrix cores exactly as the other window kernels do, and hands each
+//     group to the folder: P_g and the column scales through a ring of R
+//     entries in LDS, and the exact bf16 pieces of S_g and the biases b_g
+//     into its chunk's bias operands, at the lanes the bias term's matrix
+//     steps read them from;
+//   - the folder takes the entries in ascending g and applies the order step
+//     for step: acc = fma(s_g, P_g, acc), and after the fold of the first
+//     group of each chunk of 8 the previous chunk's bias term on the matrix
+//     cores; then the epilogue.
+//
+// Ring protocol (LDS): entry g % R holds group g once ready[g % R] = g + 1
+// (stored after the entry's writes have completed), and is free again once
+// the folder stores done[g % R] = g + 1 (after its reads have completed).
+// Every wait is bounded (at most 2^22 polls), so no wave can hang.
+//
+// Per output the arithmetic is pgemm_kernel's: the same four chained
+// 32 x 32 x 16 matrix steps per group on the same exact bf16 codes and
+// activation fragments, the same fold, the same activation sums (16 x 16 x 32
+// against ones, two per 16 rows) and the same bias term per chunk of 8
+// groups. A row's bits are the same whichever kernel computes them, and the
+// window cut stays free (TensorFold PR #1696, later revision, "What it adds",
+// prompt GEMM item: a chain per 64-wide k block; "Checks": every row alone
+// equals the row inside a window).
+#pragma once
+
+#include "pgemm.h"
+
+namespace q4 {
+
+constexpr int kFlowRows = 32;  // window rows per workgroup
+
+// Per-producer DMA stage: a pair's activations (2 groups x 32 rows x 128
+// bytes), its code blocks (1 KiB per weight slot) and scale/bias blocks.
+__host__ __device__ constexpr int flow_slots(bool swiglu) { return swiglu ? 4 : 2; }
+__host__ __device__ constexpr int flow_stage_bytes(bool swiglu) {
+  return 2 * kFlowRows * kXRowBytes + flow_slots(swiglu) * (kPairCodeBytes + kPairSbBytes);
+}
+template <bool SWIGLU, int NS>
+__device__ __forceinline__ uint8_t* flow_stage_base(uint8_t* stages, int wave) {
+  return stages + wave * NS * flow_stage_bytes(SWIGLU);
+}
+// Wait until at most N of this wave's DMA loads are in flight.
+template <int N>
+__device__ __forceinline__ void flow_wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// A buffer resource from workgroup-uniform values, pinned to scalar registers.
+__device__ __forceinline__ i32x4 flow_rsrc(const void* base, uint32_t bytes) {
+  const i32x4 r = make_srsrc(base, bytes);
+  return i32x4{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]), __builtin_amdgcn_readfirstlane(r[2]),
+               __builtin_amdgcn_readfirstlane(r[3])};
+}
+
+template <bool SWIGLU, bool OUT_BF16, int NP, int NS, int R>
+__global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t* __restrict__ pa, const uint8_t* __restrict__ pb, int N,
+                                                                   int K, const uint16_t* __restrict__ x, int64_t ldx, int M,
+                                                                   void* __restrict__ yv, int64_t ldy, int nblk, int mblk) {
+  constexpr int kTiles = SWIGLU ? 2 : 1;
+  __shared__ __align__(16) f32x4 ringP[R][kTiles][4][64];  // P_g, element quad i of lane L at [i][L]
+  __shared__ float ringC[R][kTiles][64];                   // the lane's column scale s_g
+  // the bias term's matrix operands of chunks c (at c & 1), in the lanes of
+  // its 32 x 32 x 16 steps m = 0, 1: A = the exact bf16 pieces of S_g of row j
+  // for groups 4 m + 2 hl + e in lane j + 32 hl, B = b_g of column j likewise
+  __shared__ __align__(16) u32x4 biasA[2][2][64];
+  __shared__ __align__(16) u32x4 biasB[2][kTiles][2][64];
+  __shared__ uint32_t ready[R], done[R];
+  constexpr int kSlots = flow_slots(SWIGLU);
+  constexpr int kXBytes = 2 * kFlowRows * kXRowBytes;
+  constexpr int kStageBytes = flow_stage_bytes(SWIGLU);
+  constexpr int kLoads = 8 + kSlots + kSlots / 2;  // DMA loads per pair
+  static_assert(NS >= 2 && NS <= 4 && (NS - 1) * kLoads <= 63, "stages in flight fit the load counter");
+  // at most one chunk of entries in the ring: a producer may write chunk c + 2's
+  // bias operands only after the release that follows chunk c's bias term
+  static_assert(R >= 2 && R <= kPgemmChunk && (R & (R - 1)) == 0, "ring of 2, 4 or 8 entries");
+  __shared__ __align__(16) uint8_t smem_stages[NP * NS * kStageBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int mb, nb;
+  pgemm_tile(blockIdx.x, nblk, mblk, mb, nb);
+  const int m0 = mb * kFlowRows;
+  const int mt = M - m0 < kFlowRows ? M - m0 : kFlowRows;  // rows of this block inside the window
+  const int G = K / kGroup;
+  const int P = (G + 1) / 2;
+  const int ntiles = N / kTileN;
+  const int j = lane & 31, hl = lane >> 5, jj = j & 15;
+  // this lane's weight tile in output tile t: tiles 2 nb and 2 nb + 1 (of w1,
+  // and of w3 for t = 1 with SwiGLU), column jj
+  const int wtile = 2 * nb + (j >> 4);
+
+  if (threadIdx.x < R) ready[threadIdx.x] = done[threadIdx.x] = 0u;
+  for (int i = threadIdx.x; i < 2 * 2 * 64; i += blockDim.x) (&biasA[0][0][0])[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = threadIdx.x; i < 2 * kTiles * 2 * 64; i += blockDim.x) (&biasB[0][0][0][0])[i] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+
+  // Ring flags. Only LDS is ordered (a C++ release would also wait for the
+  // producer's loads in flight): a publisher completes its LDS accesses
+  // (lgkmcnt(0)) before it stores the flag; a waiter polls the flag and
+  // issues its reads after it has seen it. Waits are bounded (2^22 polls).
+  auto publish = [](uint32_t* f, uint32_t v) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  // the producers' wait for a free entry polls gently, so that its LDS
+  // traffic does not slow the folder it waits for
+  auto wait_free = [](uint32_t* f, uint32_t want) {
+    for (int it = 0; it < (1 << 20); ++it) {
+      if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == want) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+  };
+
+  if (wave < NP) {
+    // ---------------- producer --------------------------------------------
+    // the workgroup's two weight tiles 2 nb, 2 nb + 1 (SwiGLU: of w1, then of
+    // w3), clamped at N (columns past N are never stored)
+    const int t0 = 2 * nb < ntiles ? 2 * nb : ntiles - 1;
+    const int t1 = 2 * nb + 1 < ntiles ? 2 * nb + 1 : ntiles - 1;
+    const int64_t cb = codes_bytes(N, K, 4);
+    const i32x4 xr = flow_rsrc(x + (int64_t)m0 * ldx, (uint32_t)((int64_t)mt * ldx * 2));
+    const i32x4 cra = flow_rsrc(pa + (int64_t)t0 * P * kPairCodeBytes, (uint32_t)((t1 - t0 + 1) * P * kPairCodeBytes));
+    const i32x4 sra = flow_rsrc(pa + cb + (int64_t)t0 * P * kPairSbBytes, (uint32_t)((t1 - t0 + 1) * P * kPairSbBytes));
+    const uint8_t* pbm = SWIGLU ? pb : pa;
+    const i32x4 crb = flow_rsrc(pbm + (int64_t)t0 * P * kPairCodeBytes, (uint32_t)((t1 - t0 + 1) * P * kPairCodeBytes));
+    const i32x4 srb = flow_rsrc(pbm + cb + (int64_t)t0 * P * kPairSbBytes, (uint32_t)((t1 - t0 + 1) * P * kPairSbBytes));
+    // activation DMA: load i (0..7) of a pair is group half i / 4, rows
+    // 8 (i % 4) + lane / 8, 16-byte chunk lane % 8 at its swizzled slot; rows
+    // past the window re-read its last row (their results are never stored)
+    uint32_t xvo[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = 8 * u + (lane >> 3);
+      const int rc = r < mt ? r : mt - 1;
+      xvo[u] = (uint32_t)(rc * ldx * 2) + (uint32_t)(xs_slot(r, lane & 7) << 4);
+    }
+    // scale/bias DMA: lanes 0..31 the block of tile t0, lanes 32..63 of t1
+    const uint32_t svo = (uint32_t)((lane >> 5) * (t1 - t0) * P * kPairSbBytes) + (uint32_t)(lane & 31) * 4u;
+    uint8_t* const stage0 = flow_stage_base<SWIGLU, NS>(smem_stages, wave);
+    const uint32_t st_lds = lds_addr(stage0);
+    const bf16x8 ones = ones_bf16x8();
+
+    // pair q into stage b: 8 activation loads, one code block per slot, one
+    // scale/bias load per two slots
+    auto issue = [&](int q, int b) {
+      const int qq = q < P ? q : P - 1;
+      const uint32_t st = st_lds + (uint32_t)b * kStageBytes;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int g = 2 * qq + i / 4;
+        g = g < G ? g : G - 1;
+        dma_b128(xr, xvo[i % 4], (uint32_t)g * kXRowBytes, st + (uint32_t)((i / 4) * kFlowRows * kXRowBytes + (i % 4) * 1024));
+      }
+#pragma unroll
+      for (int sl = 0; sl < kSlots; ++sl) {
+        const uint32_t so = (uint32_t)(((sl & 1) ? t1 - t0 : 0) * P + qq) * kPairCodeBytes;
+        if (sl >= 2) dma_b128(crb, (uint32_t)lane * 16u, so, st + kXBytes + sl * kPairCodeBytes);
+        else dma_b128(cra, (uint32_t)lane * 16u, so, st + kXBytes + sl * kPairCodeBytes);
+      }
+#pragma unroll
+      for (int h = 0; h < kSlots / 2; ++h) {
+        if (h >= 1) dma_b32(srb, svo, (uint32_t)qq * kPairSbBytes, st + kXBytes + kSlots * kPairCodeBytes + 2 * h * kPairSbBytes);
+        else dma_b32(sra, svo, (uint32_t)qq * kPairSbBytes, st + kXBytes + kSlots * kPairCodeBytes + 2 * h * kPairSbBytes);
+      }
+    };
+
+    const int i16 = lane & 15, kc = lane >> 4;
+    auto compute = [&](int q, int b) {
+      const uint8_t* st = stage0 + b * kStageBytes;
+      const uint8_t* cs = st + kXBytes;
+      const uint8_t* sbs = st + kXBytes + kSlots * kPairCodeBytes;
+      f32x16 Pm[2][kTiles];
+      f32x4 Sv[2][2];
+      uint32_t w[2][kTiles];
+#pragma unroll
+      for (int gh = 0; gh < 2; ++gh) {
+        const uint8_t* xb = st + gh * kFlowRows * kXRowBytes;
+        bf16x8 xa[4], qb[kTiles][4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) xa[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(j, 2 * ks + hl)));
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+          const int sl = 2 * t + (j >> 4);
+          w[gh][t] = *(const uint32_t*)(sbs + sl * kPairSbBytes + jj * 8 + gh * 4);
+          const uint8_t* cl = cs + sl * kPairCodeBytes + (jj + 16 * hl) * 16 + gh * 8;
+          const u32x2 c02 = *(const u32x2*)cl, c13 = *(const u32x2*)(cl + 512);
+          qb[t][0] = codes_to_bf16(c02[0]);
+          qb[t][2] = codes_to_bf16(c02[1]);
+          qb[t][1] = codes_to_bf16(c13[0]);
+          qb[t][3] = codes_to_bf16(c13[1]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int t = 0; t < kTiles; ++t) Pm[gh][t] = mfma32(xa[ks], qb[t][ks], ks == 0 ? f32x16{} : Pm[gh][t]);
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          const int row = 16 * v + i16;
+          const bf16x8 xa0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc)));
+          const bf16x8 xa1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc + 4)));
+          Sv[gh][v] = mfma16(ones, xa0, f32x4{0.f, 0.f, 0.f, 0.f});
+          Sv[gh][v] = mfma16(ones, xa1, Sv[gh][v]);
+        }
+      }
+      // hand each group to the folder
+#pragma unroll
+      for (int gh = 0; gh < 2; ++gh) {
+        const int g = 2 * q + gh;
+        if (g >= G) break;
+        const int slot = g % R;
+        if (g >= R) wait_free(&done[slot], (uint32_t)(g - R + 1));
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ringP[slot][t][i][lane] = f32x4{Pm[gh][t][4 * i], Pm[gh][t][4 * i + 1], Pm[gh][t][4 * i + 2], Pm[gh][t][4 * i + 3]};
+          ringC[slot][t][lane] = bf16_lo(w[gh][t]);
+        }
+        // this group's share of its chunk's bias operands: position
+        // (m, hl, e) = (gg / 4, gg / 2 % 2, gg % 2) of chunk c
+        const int c = g / kPgemmChunk, gg = g % kPgemmChunk, m = gg >> 2, hg = (gg >> 1) & 1, e = gg & 1;
+        if (kc == 0) {
+#pragma unroll
+          for (int v = 0; v < 2; ++v) {
+            uint32_t h, mm, l;
+            split3(Sv[gh][v][0], h, mm, l);
+            u32x2* dst = (u32x2*)&biasA[c & 1][m][16 * v + i16 + 32 * hg] + e;
+            *dst = u32x2{h | (mm << 16), l};
+          }
+        }
+        if (hl == 0) {
+#pragma unroll
+          for (int t = 0; t < kTiles; ++t) {
+            const uint32_t bb = w[gh][t] >> 16;
+            u32x2* dst = (u32x2*)&biasB[c & 1][t][m][j + 32 * hg] + e;
+            *dst = u32x2{bb | (bb << 16), bb};
+          }
+        }
+        publish(&ready[slot], (uint32_t)(g + 1));
+      }
+    };
+
+    // pairs wave, wave + NP, ...: NS private stages, pair number n of this
+    // wave in stage n % NS. Pair n + NS - 1 is issued into the stage of pair
+    // n - 1 (its reads complete: lgkmcnt(0)) before pair n is computed, so
+    // NS - 1 pairs are in flight during each computation.
+    const int mine = wave < P ? (P - 1 - wave) / NP + 1 : 0;  // pairs of this wave
+#pragma unroll
+    for (int n = 0; n < NS - 1; ++n)
+      if (n < mine) issue(wave + n * NP, n);
+    for (int n = 0; n < mine; ++n) {
+      if (n + NS - 1 < mine) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue(wave + (n + NS - 1) * NP, (n + NS - 1) % NS);
+      }
+      const int after = mine - 1 - n < NS - 1 ? mine - 1 - n : NS - 1;  // pairs issued after pair n
+      if (NS >= 4 && after >= 3) flow_wait_vm<(NS >= 4 ? 3 * kLoads : 0)>();
+      else if (NS >= 3 && after >= 2) flow_wait_vm<(NS >= 3 ? 2 * kLoads : 0)>();
+      else if (after >= 1) flow_wait_vm<kLoads>();
+      else flow_wait_vm<0>();
+      compute(wave + n * NP, n % NS);
+    }
+    return;
+  }
+
+  // ---------------- folder ------------------------------------------------
+  f32x16 acc[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+
+  // chunk c's bias term on the matrix cores, added into acc; its operand
+  // area is then cleared for chunk c + 2 (no producer writes chunk c + 2
+  // before the entry of group 8 (c + 1) is released, which follows this)
+  auto bias_chunk = [&](int c) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const bf16x8 afr = __builtin_bit_cast(bf16x8, biasA[c & 1][m][lane]);
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) acc[t] = mfma32(afr, __builtin_bit_cast(bf16x8, biasB[c & 1][t][m][lane]), acc[t]);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      biasA[c & 1][m][lane] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) biasB[c & 1][t][m][lane] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  struct Entry {
+    f32x16 P[kTiles];
+    float sc[kTiles];
+  };
+  auto read = [&](Entry& e, int g) {
+    const int slot = g % R;
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 v = ringP[slot][t][i][lane];
+        e.P[t][4 * i] = v[0];
+        e.P[t][4 * i + 1] = v[1];
+        e.P[t][4 * i + 2] = v[2];
+        e.P[t][4 * i + 3] = v[3];
+      }
+      e.sc[t] = ringC[slot][t][lane];
+    }
+  };
+  // the fold of group g; after the fold of a chunk's first group, the
+  // previous chunk's bias term
+  auto fold = [&](const Entry& e, int g) {
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] = __builtin_fmaf(e.sc[t], e.P[t][r], acc[t][r]);
+    if ((g & (kPgemmChunk - 1)) == 0 && g > 0) bias_chunk(g / kPgemmChunk - 1);
+  };
+  // Pair q's entries, in one LDS round trip: the flag of its second group (a
+  // producer publishes the groups of a pair in order) and then the entries
+  // are read back to back (the LDS serves one wave's reads in order, so when
+  // the flag shows the pair, the entries read after it are the pair's); if
+  // the flag does not show it yet, all is read again.
+  auto fetch = [&](Entry& a, Entry& b, int q) {
+    const int g0 = 2 * q, g1 = g0 + 1 < G ? g0 + 1 : g0;
+    for (int it = 0; it < (1 << 22); ++it) {
+      const uint32_t f = __hip_atomic_load(&ready[g1 % R], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      asm volatile("" ::: "memory");
+      read(a, g0);
+      if (g1 != g0) read(b, g1);
+      if (__builtin_amdgcn_readfirstlane(f) == (uint32_t)(g1 + 1)) break;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  };
+  // release pair q's entries after its folds (its reads have completed)
+  auto release = [&](int q) {
+    const int g0 = 2 * q, g1 = g0 + 1 < G ? g0 + 1 : g0;
+    publish(&done[g0 % R], (uint32_t)(g0 + 1));
+    if (g1 != g0) publish(&done[g1 % R], (uint32_t)(g1 + 1));
+  };
+  for (int q = 0; q < P; ++q) {
+    Entry ea, eb;
+    fetch(ea, eb, q);
+    fold(ea, 2 * q);
+    if (2 * q + 1 < G) fold(eb, 2 * q + 1);
+    release(q);
+  }
+  // the last chunk's producers published before the folder consumed their
+  // groups, so its operands are in place
+  bias_chunk((G - 1) / kPgemmChunk);
+
+  // ---- epilogue: element r is row 8 (r / 4) + 4 hl + r % 4, column jj of the
+  // lane's weight tile
+  if (wtile >= ntiles) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = 8 * (r / 4) + 4 * hl + (r % 4);
+    if (row >= mt) continue;
+    const int64_t at = (int64_t)(m0 + row) * ldy + (int64_t)wtile * kTileN + jj;
+    const float z = SWIGLU ? silu_f32(acc[0][r]) * acc[kTiles - 1][r] : acc[0][r];
+    if constexpr (OUT_BF16) ((uint16_t*)yv)[at] = f32_to_bf16_rne(z);
+    else ((float*)yv)[at] = z;
+  }
+}
+
+}  // namespace q4

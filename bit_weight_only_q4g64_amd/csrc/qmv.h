@@ -626,6 +626,18 @@ inline size_t qmv_max_lds() {
   return cached;
 }
 
+// Compute units of the device (queried once per process, like qmv_max_lds;
+// used only to choose among kernels that give the same bits).
+inline int device_cus() {
+  static const int cached = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      return v;
+    return 256;
+  }();
+  return cached;
+}
+
 // Let a kernel use the largest dynamic LDS a workgroup may have beside the
 // kernel's own static LDS. A failed query or setting keeps the 64 KiB default
 // and clears the error it raised, so that the launch after it reports only

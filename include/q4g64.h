@@ -67,9 +67,9 @@
  *     library allocates nothing and keeps no device state between calls
  *     (except the fixed scratch array of qmv_rows_split_noalloc, below).
  *   - Host-side caches, per process: the largest dynamic LDS a workgroup may
- *     use is queried once, on the device current at the first call that
- *     needs it, and each kernel's LDS limit is raised once, at its first
- *     launch. Every GPU this library runs on must therefore be of the same
+ *     use and the number of compute units are queried once, on the device
+ *     current at the first call that needs them, and each kernel's LDS limit
+ *     is raised once, at its first launch. Every GPU this library runs on must therefore be of the same
  *     kind (all MI355X); results never depend on these values.
  *   - `stream` is a hipStream_t (NULL = the default stream). Kernels are
  *     enqueued asynchronously on it; execution errors surface at the caller's

@@ -220,3 +220,44 @@ def test_wide_swiglu_bf16_output_rows_of_any_alignment(c3, c3_whole, layout):
     assert np.array_equal(got[:, c0 : c0 + N], expect)
     pad = np.delete(got, np.arange(c0, c0 + N), axis=1)
     assert np.all((pad & 0x7FFF) > 0x7F80)  # still NaN
+
+
+@pytest.mark.parametrize("swiglu,out_bf16", [(False, False), (False, True), (True, False), (True, True)])
+def test_short_windows_match_the_whole_prompt(swiglu, out_bf16):
+    """Short windows (one to a few hundred rows) of a wide-K weight run on the
+    workgroups of short windows (one 32 x 32 tile each, products of several
+    groups at once, folded in order), the whole prompt on the 128 x 256
+    (SwiGLU 128 x 128) workgroups: every row's bits agree, for w2's shape
+    (2048 x 8192) and an odd group count (K = 64 * 63)."""
+    K = 8192 if not swiglu else 4032
+    N = 2048
+    M = 4096 if not swiglu else 2048  # enough rows for the wide workgroups
+    say(f"short windows vs whole prompt N={N} K={K} swiglu={swiglu} bf16={out_bf16}")
+    rng = np.random.default_rng(N + K + swiglu)
+    w = synthetic.draw_qweight(rng, "a", N, K)
+    w3 = synthetic.draw_qweight(rng, "b", N, K)
+    pk, pk3 = dev_weight(w), dev_weight(w3)
+    pb = pk3 if swiglu else None
+    x = synthetic.draw_bf16_rows(rng, M, K)
+    xd = dev_bf16(x)
+    dt = torch.bfloat16 if out_bf16 else torch.float32
+    whole = q4.qmm_window(pk, pb, N, K, xd, out_dtype=dt)
+    torch.cuda.synchronize()
+    ref = bits16(whole) if out_bf16 else bits32(whole)
+    for r0, rows in ((0, 128), (1000, 128), (4000 % M, 96), (77, 1), (300, 17), (M - 33, 33)):
+        y = q4.qmm_window(pk, pb, N, K, xd[r0 : r0 + rows], out_dtype=dt)
+        torch.cuda.synchronize()
+        got = bits16(y) if out_bf16 else bits32(y)
+        assert np.array_equal(got, ref[r0 : r0 + rows]), (r0, rows)
+    # and one window's rows against the oracle
+    rows = [0, 63, 127]
+    if swiglu:
+        a64 = oracle.matmul_rows(w.wq, w.scales, w.biases, x[rows])
+        c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, x[rows])
+        Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w.wq, w.scales, w.biases, x[rows]), K, order="window"),
+                        tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, x[rows]), K, order="window"))
+        z64 = oracle.swiglu(a64, c64)
+        got64 = host_f64(q4.qmm_window(pk, pb, N, K, xd[:128]))[rows]
+        assert np.all(np.abs(got64 - z64) <= Tz)
+    else:
+        check_within(host_f64(q4.qmm_window(pk, None, N, K, xd[:128]))[rows], w, x, rows=rows, label="short window w2", order="window")
