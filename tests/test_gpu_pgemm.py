@@ -261,3 +261,37 @@ def test_short_windows_match_the_whole_prompt(swiglu, out_bf16):
         assert np.all(np.abs(got64 - z64) <= Tz)
     else:
         check_within(host_f64(q4.qmm_window(pk, None, N, K, xd[:128]))[rows], w, x, rows=rows, label="short window w2", order="window")
+
+
+@pytest.mark.parametrize("N,K,M,swiglu", [(64, 64, 1, False), (64, 128, 31, True), (128, 64, 32, False), (128, 192, 33, True),
+                                          (192, 320, 63, False), (256, 64 * 17, 64, True), (1024, 576, 65, False)])
+def test_short_window_edge_shapes_against_single_rows_and_oracle(N, K, M, swiglu):
+    """Windows on the short-window workgroups at the edges of their 32-row
+    blocks (31, 32, 33, 63, 64, 65 rows), with one, two, odd and chunk-crossing
+    group counts (K = 64 .. 64 * 17), plain and SwiGLU: within the window bound
+    of the oracle, and every row bit-identical to that row alone (also a
+    short-window launch) and in bf16 to the RNE of the float32 result."""
+    say(f"short window N={N} K={K} M={M} swiglu={swiglu}")
+    rng = np.random.default_rng(N * 7 + K + M)
+    w = synthetic.draw_qweight(rng, "a", N, K)
+    w3 = synthetic.draw_qweight(rng, "b", N, K)
+    pk, pk3 = dev_weight(w), dev_weight(w3)
+    pb = pk3 if swiglu else None
+    x = synthetic.draw_bf16_rows(rng, M, K)
+    xd = dev_bf16(x)
+    y = q4.qmm_window(pk, pb, N, K, xd)
+    yb = q4.qmm_window(pk, pb, N, K, xd, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = bits32(y)
+    for r in sorted({0, M // 2, M - 1}):
+        y1 = q4.qmm_window(pk, pb, N, K, xd[r : r + 1])
+        assert np.array_equal(bits32(y1)[0], ref[r]), r
+    assert np.array_equal(bits16(yb).view(np.uint16), synthetic.bf16_bits_from_f64(y.cpu().numpy().astype(np.float64)))
+    if swiglu:
+        a64 = oracle.matmul_rows(w.wq, w.scales, w.biases, x)
+        c64 = oracle.matmul_rows(w3.wq, w3.scales, w3.biases, x)
+        Tz = tol_swiglu(a64, c64, tol(oracle.error_weight(w.wq, w.scales, w.biases, x), K, order="window"),
+                        tol(oracle.error_weight(w3.wq, w3.scales, w3.biases, x), K, order="window"))
+        assert np.all(np.abs(host_f64(y) - oracle.swiglu(a64, c64)) <= Tz)
+    else:
+        check_within(host_f64(y), w, x, label="short window edge", order="window")
