@@ -218,13 +218,16 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
           Sv[gh][v] = mfma16(ones, xa1, Sv[gh][v]);
         }
       }
-      // hand each group to the folder
+      // hand the pair to the folder. The entries of the pair R / 2 pairs
+      // back are released together (the second after the first), so the
+      // second slot's flag frees both; one wait for the writes, then both flags.
+      const int g0 = 2 * q, gl = 2 * q + 1 < G ? 2 * q + 1 : 2 * q;
+      if (gl >= R) wait_free(&done[gl % R], (uint32_t)(gl - R + 1));
 #pragma unroll
       for (int gh = 0; gh < 2; ++gh) {
-        const int g = 2 * q + gh;
+        const int g = g0 + gh;
         if (g >= G) break;
         const int slot = g % R;
-        if (g >= R) wait_free(&done[slot], (uint32_t)(g - R + 1));
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
 #pragma unroll
@@ -252,8 +255,10 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
             *dst = u32x2{bb | (bb << 16), bb};
           }
         }
-        publish(&ready[slot], (uint32_t)(g + 1));
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __hip_atomic_store(&ready[g0 % R], (uint32_t)(g0 + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (gl != g0) __hip_atomic_store(&ready[gl % R], (uint32_t)(gl + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
 
     // pairs wave, wave + NP, ...: NS private stages, pair number n of this
