@@ -289,25 +289,33 @@ void pgemm_launch_bits(bool swiglu, bool obf16, dim3 grid, dim3 block, hipStream
 // Below this many 256-column workgroups a window runs on the 64-column
 // workgroups of pgemm_narrow_kernel (4-bit codes; the same bits per row).
 constexpr int64_t kNarrowBelow = 256;
-// Among those, a window whose 32 x 32 tiles take at most two rounds of one
-// workgroup per compute unit (SwiGLU: one round) runs on pgemm_flow_kernel.
-// Measured on MI355X against the narrow kernel: 2.3x on a 128-row window of
-// w2 and 2x on o (one round), 1.1x on qkv (1.5 rounds); with SwiGLU 1.7x at
-// 16 rows (one round) but behind it at 64 rows (two rounds).
-constexpr int kFlowProducers = 3, kFlowStages = 2, kFlowRing = 8;
-
-void flow_launch(bool swiglu, bool obf16, const uint8_t* a, const uint8_t* b, int n, int k, const uint16_t* x, int64_t ldx, int m, void* y,
-                 int64_t ldy, int nb, int mb, hipStream_t s) {
+// Among those, a window whose 32 x 32 tiles fit twice on the compute units
+// runs on pgemm_flow_kernel: plain with 3 producer waves and a ring of 8
+// (74.5 KiB of LDS, two workgroups per compute unit); SwiGLU with 3 producers
+// and a ring of 8 when its tiles fit once (120 KiB), else with 2 producers and
+// a ring of 4 (72.7 KiB, two per compute unit). Measured on MI355X (us per
+// window, flow / narrow): 128-row w2 25.6 / 79.5, o 9.7 / 22.8, qkv 12.2 /
+// 23.1; SwiGLU 8192 x 2048 at 16 rows 13.1 / 23.5, at 64 rows 20.9 / 24.4.
+template <bool SW, int NP, int R>
+void flow_launch_cfg(bool obf16, const uint8_t* a, const uint8_t* b, int n, int k, const uint16_t* x, int64_t ldx, int m, void* y,
+                     int64_t ldy, int nb, int mb, hipStream_t s) {
   using namespace q4;
-  const dim3 grid((unsigned)((int64_t)nb * mb)), block(64 * (kFlowProducers + 1));
-  constexpr int NP = kFlowProducers, NS = kFlowStages, R = kFlowRing;
-  if (swiglu) {
-    if (obf16) hipLaunchKernelGGL((pgemm_flow_kernel<true, true, NP, NS, R>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mb);
-    else hipLaunchKernelGGL((pgemm_flow_kernel<true, false, NP, NS, R>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mb);
-  } else {
-    if (obf16) hipLaunchKernelGGL((pgemm_flow_kernel<false, true, NP, NS, R>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mb);
-    else hipLaunchKernelGGL((pgemm_flow_kernel<false, false, NP, NS, R>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mb);
-  }
+  const dim3 grid((unsigned)((int64_t)nb * mb)), block(64 * (NP + 1));
+  if (obf16) hipLaunchKernelGGL((pgemm_flow_kernel<SW, true, NP, R>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mb);
+  else hipLaunchKernelGGL((pgemm_flow_kernel<SW, false, NP, R>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mb);
+}
+
+// true when the window ran on pgemm_flow_kernel
+bool flow_launch(bool swiglu, bool obf16, const uint8_t* a, const uint8_t* b, int64_t N, int k, const uint16_t* x, int64_t ldx,
+                 int64_t M, void* y, int64_t ldy, hipStream_t s) {
+  using namespace q4;
+  const int64_t nb = (N + kFlowRows - 1) / kFlowRows, mb = (M + kFlowRows - 1) / kFlowRows, cus = device_cus();
+  const int n = (int)N, m = (int)M;
+  if (!swiglu && nb * mb <= 2 * cus) flow_launch_cfg<false, 3, 8>(obf16, a, b, n, k, x, ldx, m, y, ldy, (int)nb, (int)mb, s);
+  else if (swiglu && nb * mb <= cus) flow_launch_cfg<true, 3, 8>(obf16, a, b, n, k, x, ldx, m, y, ldy, (int)nb, (int)mb, s);
+  else if (swiglu && nb * mb <= 2 * cus) flow_launch_cfg<true, 2, 4>(obf16, a, b, n, k, x, ldx, m, y, ldy, (int)nb, (int)mb, s);
+  else return false;
+  return true;
 }
 
 int qmm_window_impl(const char* fn, int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x,
@@ -323,11 +331,7 @@ int qmm_window_impl(const char* fn, int bits, const void* packed_a, const void* 
   const uint8_t* b = swiglu ? (const uint8_t*)packed_b : a;
   const int n = (int)N, k = (int)K, m = (int)M;
   if (bits == 4 && blocks < kNarrowBelow) {
-    const int64_t fnb = (N + kFlowRows - 1) / kFlowRows, fmb = (M + kFlowRows - 1) / kFlowRows;
-    if (fnb * fmb <= (swiglu ? 1 : 2) * (int64_t)device_cus()) {
-      flow_launch(swiglu, obf16, a, b, n, k, x, ldx, m, y, ldy, (int)fnb, (int)fmb, s);
-      return launched(fn);
-    }
+    if (flow_launch(swiglu, obf16, a, b, N, k, x, ldx, M, y, ldy, s)) return launched(fn);
     const int cols = pgemm_narrow_cols(swiglu);
     const int nb = (n + cols - 1) / cols;
     const dim3 ngrid((unsigned)((int64_t)nb * mblk));

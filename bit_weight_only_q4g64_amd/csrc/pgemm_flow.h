@@ -10,33 +10,48 @@
 // are independent. So a workgroup here owns one tile (SwiGLU: the w1 tile and
 // the same w3 tile) with NP producer waves and one folder wave:
 //
-//   - producer p takes group pairs p, p + NP, p + 2 NP, ...: it moves the
-//     pair's 32 activation rows, code blocks and scale/bias blocks into NS
-//     private LDS stages by buffer-to-LDS DMA (NS - 1 pairs in flight while
-//     one is computed), forms P_g and the row sums S_g of both groups on the
-//     matrix cores exactly as the other window kernels do, and hands each
-//     group to the folder: P_g and the column scales through a ring of R
-//     entries in LDS, and the exact bf16 pieces of S_g and the biases b_g
-//     into its chunk's bias operands, at the lanes the bias term's matrix
-//     steps read them from;
+//   - producer p takes group pairs p, p + NP, p + 2 NP, ...: the pair's 32
+//     activation rows, code blocks and scale/bias blocks arrive in its LDS
+//     stage by buffer-to-LDS DMA; it reads them into registers and at once
+//     issues the DMA of its next pair into the same stage, so that the next
+//     pair's loads run while this one is computed. It forms P_g on the
+//     matrix cores exactly as the other window kernels do, and the row sums
+//     S_g with the same matrix steps against ones, on operands moved between
+//     lanes of the fragments it already holds (two lane swaps, no second LDS
+//     read). It hands each group to the folder: P_g and the column scales
+//     through a ring of R entries in LDS, and the exact bf16 pieces of S_g
+//     and the biases b_g into its chunk's bias operands, at the lanes the bias
+//     term's matrix steps read them from;
 //   - the folder takes the entries in ascending g and applies the order step
 //     for step: acc = fma(s_g, P_g, acc), and after the fold of the first
 //     group of each chunk of 8 the previous chunk's bias term on the matrix
-//     cores; then the epilogue.
+//     cores; then the epilogue. It reads a pair's entries one pair ahead, so
+//     the reads run under the folds of the pair before.
 //
 // Ring protocol (LDS): entry g % R holds group g once ready[g % R] = g + 1
 // (stored after the entry's writes have completed), and is free again once
-// the folder stores done[g % R] = g + 1 (after its reads have completed).
+// the folder stores done[g % R] = g + 1 (after the folds that used its values).
 // Every wait is bounded (at most 2^22 polls), so no wave can hang.
+//
+// LDS is 74.5 KiB with NP = 3, R = 8 (plain) and 72.7 KiB with NP = 2, R = 4
+// (SwiGLU), so two workgroups share a compute unit and a window of up to two
+// rounds of tiles is resident at once; SwiGLU with NP = 3, R = 8 takes 120 KiB.
+//
+// Measured on MI355X and dropped: more producers (4 to 7, two per SIMD), two
+// folders each folding half the accumulators, a ring of 16 and deeper
+// staging were all within 5% or slower. LDS writes are what waits: with
+// buffer-to-LDS DMA streaming, one wave's 128-bit LDS write took 140 to 520
+// cycles to complete against 70 idle (reads stayed near 64), so the ring's
+// hand-off writes, not the folds or the matrix work, pace a workgroup.
 //
 // Per output the arithmetic is pgemm_kernel's: the same four chained
 // 32 x 32 x 16 matrix steps per group on the same exact bf16 codes and
 // activation fragments, the same fold, the same activation sums (16 x 16 x 32
-// against ones, two per 16 rows) and the same bias term per chunk of 8
-// groups. A row's bits are the same whichever kernel computes them, and the
-// window cut stays free (TensorFold PR #1696, later revision, "What it adds",
-// prompt GEMM item: a chain per 64-wide k block; "Checks": every row alone
-// equals the row inside a window).
+// against ones, two per 16 rows, on the same operand values) and the same
+// bias term per chunk of 8 groups. A row's bits are the same whichever kernel
+// computes them, and the window cut stays free (TensorFold PR #1696, later
+// revision, "What it adds", prompt GEMM item: a chain per 64-wide k block;
+// "Checks": every row alone equals the row inside a window).
 #pragma once
 
 #include "pgemm.h"
@@ -51,15 +66,6 @@ __host__ __device__ constexpr int flow_slots(bool swiglu) { return swiglu ? 4 : 
 __host__ __device__ constexpr int flow_stage_bytes(bool swiglu) {
   return 2 * kFlowRows * kXRowBytes + flow_slots(swiglu) * (kPairCodeBytes + kPairSbBytes);
 }
-template <bool SWIGLU, int NS>
-__device__ __forceinline__ uint8_t* flow_stage_base(uint8_t* stages, int wave) {
-  return stages + wave * NS * flow_stage_bytes(SWIGLU);
-}
-// Wait until at most N of this wave's DMA loads are in flight.
-template <int N>
-__device__ __forceinline__ void flow_wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 // A buffer resource from workgroup-uniform values, pinned to scalar registers.
 __device__ __forceinline__ i32x4 flow_rsrc(const void* base, uint32_t bytes) {
   const i32x4 r = make_srsrc(base, bytes);
@@ -67,14 +73,14 @@ __device__ __forceinline__ i32x4 flow_rsrc(const void* base, uint32_t bytes) {
                __builtin_amdgcn_readfirstlane(r[3])};
 }
 
-template <bool SWIGLU, bool OUT_BF16, int NP, int NS, int R>
+template <bool SWIGLU, bool OUT_BF16, int NP, int R>
 __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t* __restrict__ pa, const uint8_t* __restrict__ pb, int N,
                                                                    int K, const uint16_t* __restrict__ x, int64_t ldx, int M,
                                                                    void* __restrict__ yv, int64_t ldy, int nblk, int mblk) {
   constexpr int kTiles = SWIGLU ? 2 : 1;
   __shared__ __align__(16) f32x4 ringP[R][kTiles][4][64];  // P_g, element quad i of lane L at [i][L]
   __shared__ float ringC[R][kTiles][64];                   // the lane's column scale s_g
-  // the bias term's matrix operands of chunks c (at c & 1), in the lanes of
+  // the bias term's matrix operands of chunk c (at c & 1), in the lanes of
   // its 32 x 32 x 16 steps m = 0, 1: A = the exact bf16 pieces of S_g of row j
   // for groups 4 m + 2 hl + e in lane j + 32 hl, B = b_g of column j likewise
   __shared__ __align__(16) u32x4 biasA[2][2][64];
@@ -83,12 +89,11 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
   constexpr int kSlots = flow_slots(SWIGLU);
   constexpr int kXBytes = 2 * kFlowRows * kXRowBytes;
   constexpr int kStageBytes = flow_stage_bytes(SWIGLU);
-  constexpr int kLoads = 8 + kSlots + kSlots / 2;  // DMA loads per pair
-  static_assert(NS >= 2 && NS <= 4 && (NS - 1) * kLoads <= 63, "stages in flight fit the load counter");
-  // at most one chunk of entries in the ring: a producer may write chunk c + 2's
-  // bias operands only after the release that follows chunk c's bias term
+  // chunk c + 2 reuses chunk c's bias operands: a producer writes group g
+  // only after the release of group g - R, and the release of group
+  // 8 (c + 1) follows chunk c's bias term, so R may not exceed a chunk
   static_assert(R >= 2 && R <= kPgemmChunk && (R & (R - 1)) == 0, "ring of 2, 4 or 8 entries");
-  __shared__ __align__(16) uint8_t smem_stages[NP * NS * kStageBytes];
+  __shared__ __align__(16) uint8_t smem_stages[NP * kStageBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -105,28 +110,12 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
   const int wtile = 2 * nb + (j >> 4);
 
   if (threadIdx.x < R) ready[threadIdx.x] = done[threadIdx.x] = 0u;
-  for (int i = threadIdx.x; i < 2 * 2 * 64; i += blockDim.x) (&biasA[0][0][0])[i] = u32x4{0u, 0u, 0u, 0u};
-  for (int i = threadIdx.x; i < 2 * kTiles * 2 * 64; i += blockDim.x) (&biasB[0][0][0][0])[i] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
   // Ring flags. Only LDS is ordered (a C++ release would also wait for the
-  // producer's loads in flight): a publisher completes its LDS accesses
-  // (lgkmcnt(0)) before it stores the flag; a waiter polls the flag and
-  // issues its reads after it has seen it. Waits are bounded (2^22 polls).
-  auto publish = [](uint32_t* f, uint32_t v) {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  };
-  // the producers' wait for a free entry polls gently, so that its LDS
-  // traffic does not slow the folder it waits for
-  auto wait_free = [](uint32_t* f, uint32_t want) {
-    for (int it = 0; it < (1 << 20); ++it) {
-      if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == want) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-    asm volatile("" ::: "memory");
-  };
-
+  // producer's loads in flight): a producer completes its entry writes
+  // (lgkmcnt(0)) before it stores the flag; the folder stores a release
+  // after the folds that consumed the entry's values. Waits are bounded.
   if (wave < NP) {
     // ---------------- producer --------------------------------------------
     // the workgroup's two weight tiles 2 nb, 2 nb + 1 (SwiGLU: of w1, then of
@@ -152,77 +141,106 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
     }
     // scale/bias DMA: lanes 0..31 the block of tile t0, lanes 32..63 of t1
     const uint32_t svo = (uint32_t)((lane >> 5) * (t1 - t0) * P * kPairSbBytes) + (uint32_t)(lane & 31) * 4u;
-    uint8_t* const stage0 = flow_stage_base<SWIGLU, NS>(smem_stages, wave);
-    const uint32_t st_lds = lds_addr(stage0);
+    uint8_t* const st = smem_stages + wave * kStageBytes;
+    const uint32_t st_lds = lds_addr(st);
     const bf16x8 ones = ones_bf16x8();
 
-    // pair q into stage b: 8 activation loads, one code block per slot, one
+    // pair q into the stage: 8 activation loads, one code block per slot, one
     // scale/bias load per two slots
-    auto issue = [&](int q, int b) {
-      const int qq = q < P ? q : P - 1;
-      const uint32_t st = st_lds + (uint32_t)b * kStageBytes;
+    auto issue = [&](int q) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        int g = 2 * qq + i / 4;
+        int g = 2 * q + i / 4;
         g = g < G ? g : G - 1;
-        dma_b128(xr, xvo[i % 4], (uint32_t)g * kXRowBytes, st + (uint32_t)((i / 4) * kFlowRows * kXRowBytes + (i % 4) * 1024));
+        dma_b128(xr, xvo[i % 4], (uint32_t)g * kXRowBytes, st_lds + (uint32_t)((i / 4) * kFlowRows * kXRowBytes + (i % 4) * 1024));
       }
 #pragma unroll
       for (int sl = 0; sl < kSlots; ++sl) {
-        const uint32_t so = (uint32_t)(((sl & 1) ? t1 - t0 : 0) * P + qq) * kPairCodeBytes;
-        if (sl >= 2) dma_b128(crb, (uint32_t)lane * 16u, so, st + kXBytes + sl * kPairCodeBytes);
-        else dma_b128(cra, (uint32_t)lane * 16u, so, st + kXBytes + sl * kPairCodeBytes);
+        const uint32_t so = (uint32_t)(((sl & 1) ? t1 - t0 : 0) * P + q) * kPairCodeBytes;
+        if (sl >= 2) dma_b128(crb, (uint32_t)lane * 16u, so, st_lds + kXBytes + sl * kPairCodeBytes);
+        else dma_b128(cra, (uint32_t)lane * 16u, so, st_lds + kXBytes + sl * kPairCodeBytes);
       }
 #pragma unroll
       for (int h = 0; h < kSlots / 2; ++h) {
-        if (h >= 1) dma_b32(srb, svo, (uint32_t)qq * kPairSbBytes, st + kXBytes + kSlots * kPairCodeBytes + 2 * h * kPairSbBytes);
-        else dma_b32(sra, svo, (uint32_t)qq * kPairSbBytes, st + kXBytes + kSlots * kPairCodeBytes + 2 * h * kPairSbBytes);
+        if (h >= 1) dma_b32(srb, svo, (uint32_t)q * kPairSbBytes, st_lds + kXBytes + kSlots * kPairCodeBytes + 2 * h * kPairSbBytes);
+        else dma_b32(sra, svo, (uint32_t)q * kPairSbBytes, st_lds + kXBytes + kSlots * kPairCodeBytes + 2 * h * kPairSbBytes);
       }
     };
 
     const int i16 = lane & 15, kc = lane >> 4;
-    auto compute = [&](int q, int b) {
-      const uint8_t* st = stage0 + b * kStageBytes;
+    const int mine = wave < P ? (P - 1 - wave) / NP + 1 : 0;  // pairs of this wave
+    if (mine > 0) issue(wave);
+    for (int n = 0; n < mine; ++n) {
+      const int q = wave + n * NP;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // pair q's DMA has landed
+      // the stage into registers: the activation fragments (row j, 16-byte
+      // chunk 2 ks + hl), the lane's code words and scale/bias words
+      u32x4 xa[2][4];
+      u32x2 c02[2][kTiles], c13[2][kTiles];
+      uint32_t w[2][kTiles];
       const uint8_t* cs = st + kXBytes;
       const uint8_t* sbs = st + kXBytes + kSlots * kPairCodeBytes;
-      f32x16 Pm[2][kTiles];
-      f32x4 Sv[2][2];
-      uint32_t w[2][kTiles];
 #pragma unroll
       for (int gh = 0; gh < 2; ++gh) {
         const uint8_t* xb = st + gh * kFlowRows * kXRowBytes;
-        bf16x8 xa[4], qb[kTiles][4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) xa[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(j, 2 * ks + hl)));
+        for (int ks = 0; ks < 4; ++ks) xa[gh][ks] = *(const u32x4*)(xb + xs_off(j, 2 * ks + hl));
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
           const int sl = 2 * t + (j >> 4);
           w[gh][t] = *(const uint32_t*)(sbs + sl * kPairSbBytes + jj * 8 + gh * 4);
           const uint8_t* cl = cs + sl * kPairCodeBytes + (jj + 16 * hl) * 16 + gh * 8;
-          const u32x2 c02 = *(const u32x2*)cl, c13 = *(const u32x2*)(cl + 512);
-          qb[t][0] = codes_to_bf16(c02[0]);
-          qb[t][2] = codes_to_bf16(c02[1]);
-          qb[t][1] = codes_to_bf16(c13[0]);
-          qb[t][3] = codes_to_bf16(c13[1]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int t = 0; t < kTiles; ++t) Pm[gh][t] = mfma32(xa[ks], qb[t][ks], ks == 0 ? f32x16{} : Pm[gh][t]);
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-          const int row = 16 * v + i16;
-          const bf16x8 xa0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc)));
-          const bf16x8 xa1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc + 4)));
-          Sv[gh][v] = mfma16(ones, xa0, f32x4{0.f, 0.f, 0.f, 0.f});
-          Sv[gh][v] = mfma16(ones, xa1, Sv[gh][v]);
+          c02[gh][t] = *(const u32x2*)cl;
+          c13[gh][t] = *(const u32x2*)(cl + 512);
         }
       }
-      // hand the pair to the folder. The entries of the pair R / 2 pairs
-      // back are released together (the second after the first), so the
-      // second slot's flag frees both; one wait for the writes, then both flags.
+      // the reads have completed: the stage takes the next pair
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (n + 1 < mine) issue(q + NP);
+
+      f32x16 Pm[2][kTiles];
+      f32x4 Sv[2][2];
+#pragma unroll
+      for (int gh = 0; gh < 2; ++gh) {
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+          Pm[gh][t] = mfma32(__builtin_bit_cast(bf16x8, xa[gh][0]), codes_to_bf16(c02[gh][t][0]), f32x16{});
+          Pm[gh][t] = mfma32(__builtin_bit_cast(bf16x8, xa[gh][1]), codes_to_bf16(c13[gh][t][0]), Pm[gh][t]);
+          Pm[gh][t] = mfma32(__builtin_bit_cast(bf16x8, xa[gh][2]), codes_to_bf16(c02[gh][t][1]), Pm[gh][t]);
+          Pm[gh][t] = mfma32(__builtin_bit_cast(bf16x8, xa[gh][3]), codes_to_bf16(c13[gh][t][1]), Pm[gh][t]);
+        }
+        // the sums' operands: lane i16 + 16 kc of row block v takes chunks
+        // kc and kc + 4 of row 16 v + i16. Lane 16 v + i16 + 32 (kc & 1) holds
+        // them in xa[kc / 2] and xa[2 + kc / 2]; a swap of lane halves (32)
+        // and then of lane quarters (16) between the two registers brings
+        // row block 0's operand to one register and row block 1's to the other
+        u32x4 X[2], Y[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const auto r = __builtin_amdgcn_permlane32_swap(xa[gh][2 * h2][d], xa[gh][2 * h2 + 1][d], false, false);
+            const auto s = __builtin_amdgcn_permlane16_swap(r[0], r[1], false, false);
+            X[h2][d] = s[0];
+            Y[h2][d] = s[1];
+          }
+        }
+        Sv[gh][0] = mfma16(ones, __builtin_bit_cast(bf16x8, X[0]), f32x4{0.f, 0.f, 0.f, 0.f});
+        Sv[gh][0] = mfma16(ones, __builtin_bit_cast(bf16x8, X[1]), Sv[gh][0]);
+        Sv[gh][1] = mfma16(ones, __builtin_bit_cast(bf16x8, Y[0]), f32x4{0.f, 0.f, 0.f, 0.f});
+        Sv[gh][1] = mfma16(ones, __builtin_bit_cast(bf16x8, Y[1]), Sv[gh][1]);
+      }
+      // hand the pair to the folder. The folder releases a pair's entries
+      // together (the second after the first), so the second slot's flag
+      // frees both; one wait for the writes, then both flags.
       const int g0 = 2 * q, gl = 2 * q + 1 < G ? 2 * q + 1 : 2 * q;
-      if (gl >= R) wait_free(&done[gl % R], (uint32_t)(gl - R + 1));
+      if (gl >= R) {
+        for (int it = 0; it < (1 << 20); ++it) {
+          if (__hip_atomic_load(&done[gl % R], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == (uint32_t)(gl - R + 1)) break;
+          __builtin_amdgcn_s_sleep(1);  // poll gently: the folder's LDS traffic comes first
+        }
+        asm volatile("" ::: "memory");
+      }
 #pragma unroll
       for (int gh = 0; gh < 2; ++gh) {
         const int g = g0 + gh;
@@ -259,27 +277,6 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __hip_atomic_store(&ready[g0 % R], (uint32_t)(g0 + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       if (gl != g0) __hip_atomic_store(&ready[gl % R], (uint32_t)(gl + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    };
-
-    // pairs wave, wave + NP, ...: NS private stages, pair number n of this
-    // wave in stage n % NS. Pair n + NS - 1 is issued into the stage of pair
-    // n - 1 (its reads complete: lgkmcnt(0)) before pair n is computed, so
-    // NS - 1 pairs are in flight during each computation.
-    const int mine = wave < P ? (P - 1 - wave) / NP + 1 : 0;  // pairs of this wave
-#pragma unroll
-    for (int n = 0; n < NS - 1; ++n)
-      if (n < mine) issue(wave + n * NP, n);
-    for (int n = 0; n < mine; ++n) {
-      if (n + NS - 1 < mine) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        issue(wave + (n + NS - 1) * NP, (n + NS - 1) % NS);
-      }
-      const int after = mine - 1 - n < NS - 1 ? mine - 1 - n : NS - 1;  // pairs issued after pair n
-      if (NS >= 4 && after >= 3) flow_wait_vm<(NS >= 4 ? 3 * kLoads : 0)>();
-      else if (NS >= 3 && after >= 2) flow_wait_vm<(NS >= 3 ? 2 * kLoads : 0)>();
-      else if (after >= 1) flow_wait_vm<kLoads>();
-      else flow_wait_vm<0>();
-      compute(wave + n * NP, n % NS);
     }
     return;
   }
@@ -291,26 +288,31 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
 
-  // chunk c's bias term on the matrix cores, added into acc; its operand
-  // area is then cleared for chunk c + 2 (no producer writes chunk c + 2
-  // before the entry of group 8 (c + 1) is released, which follows this)
+  // chunk c's bias term on the matrix cores, added into acc. The producers
+  // write every word of a whole chunk's operands; in the last chunk the
+  // positions of groups past G may hold words of chunk c - 2 and are zeroed
+  // here, in registers (lane j + 32 hl holds groups 4 m + 2 hl and + 1)
   auto bias_chunk = [&](int c) {
+    const int valid = G - c * kPgemmChunk;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const bf16x8 afr = __builtin_bit_cast(bf16x8, biasA[c & 1][m][lane]);
+      const int gb = 4 * m + 2 * hl;
+      const bool k0 = gb < valid, k1 = gb + 1 < valid;
+      u32x4 a = biasA[c & 1][m][lane];
+      if (!k0) a[0] = a[1] = 0u;
+      if (!k1) a[2] = a[3] = 0u;
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t) acc[t] = mfma32(afr, __builtin_bit_cast(bf16x8, biasB[c & 1][t][m][lane]), acc[t]);
-    }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      biasA[c & 1][m][lane] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t) biasB[c & 1][t][m][lane] = u32x4{0u, 0u, 0u, 0u};
+      for (int t = 0; t < kTiles; ++t) {
+        u32x4 b = biasB[c & 1][t][m][lane];
+        if (!k0) b[0] = b[1] = 0u;
+        if (!k1) b[2] = b[3] = 0u;
+        acc[t] = mfma32(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc[t]);
+      }
     }
   };
 
   struct Entry {
-    f32x16 P[kTiles];
+    f32x4 P[kTiles][4];
     float sc[kTiles];
   };
   auto read = [&](Entry& e, int g) {
@@ -318,13 +320,7 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 v = ringP[slot][t][i][lane];
-        e.P[t][4 * i] = v[0];
-        e.P[t][4 * i + 1] = v[1];
-        e.P[t][4 * i + 2] = v[2];
-        e.P[t][4 * i + 3] = v[3];
-      }
+      for (int i = 0; i < 4; ++i) e.P[t][i] = ringP[slot][t][i][lane];
       e.sc[t] = ringC[slot][t][lane];
     }
   };
@@ -334,37 +330,62 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
 #pragma unroll
     for (int t = 0; t < kTiles; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][r] = __builtin_fmaf(e.sc[t], e.P[t][r], acc[t][r]);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[t][4 * i + u] = __builtin_fmaf(e.sc[t], e.P[t][i][u], acc[t][4 * i + u]);
     if ((g & (kPgemmChunk - 1)) == 0 && g > 0) bias_chunk(g / kPgemmChunk - 1);
   };
-  // Pair q's entries, in one LDS round trip: the flag of its second group (a
-  // producer publishes the groups of a pair in order) and then the entries
-  // are read back to back (the LDS serves one wave's reads in order, so when
-  // the flag shows the pair, the entries read after it are the pair's); if
-  // the flag does not show it yet, all is read again.
-  auto fetch = [&](Entry& a, Entry& b, int q) {
+  // Pair q's flag (of its second group: a producer publishes a pair's groups
+  // in order) and entries, read back to back. The LDS serves one wave's
+  // accesses in order, so when the flag shows the pair, the entries read
+  // after it are the pair's.
+  auto issue_reads = [&](Entry& a, Entry& b, int q) -> uint32_t {
     const int g0 = 2 * q, g1 = g0 + 1 < G ? g0 + 1 : g0;
+    const uint32_t f = __hip_atomic_load(&ready[g1 % R], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    asm volatile("" ::: "memory");
+    read(a, g0);
+    if (g1 != g0) read(b, g1);
+    return f;
+  };
+  auto shows = [&](uint32_t f, int q) {
+    const int g1 = 2 * q + 1 < G ? 2 * q + 1 : 2 * q;
+    return __builtin_amdgcn_readfirstlane(f) == (uint32_t)(g1 + 1);
+  };
+  // read pair q until its flag shows it (bounded)
+  auto fetch = [&](Entry& a, Entry& b, int q) {
     for (int it = 0; it < (1 << 22); ++it) {
-      const uint32_t f = __hip_atomic_load(&ready[g1 % R], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      asm volatile("" ::: "memory");
-      read(a, g0);
-      if (g1 != g0) read(b, g1);
-      if (__builtin_amdgcn_readfirstlane(f) == (uint32_t)(g1 + 1)) break;
+      const uint32_t f = issue_reads(a, b, q);
+      if (shows(f, q)) break;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   };
-  // release pair q's entries after its folds (its reads have completed)
-  auto release = [&](int q) {
+  // fold pair q (in ca, cb) while pair q + 1's reads are in flight, then
+  // release pair q: every value of its entries has been consumed by then
+  auto step = [&](Entry& ca, Entry& cb, Entry& na, Entry& nb2, int q) {
+    // pair q's reads were issued a step ago: wait for them here, where the
+    // compiler sees it, so that its own wait before the folds does not also
+    // cover the reads of pair q + 1 issued below
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    uint32_t f = 0;
+    if (q + 1 < P) f = issue_reads(na, nb2, q + 1);
+    fold(ca, 2 * q);
+    if (2 * q + 1 < G) fold(cb, 2 * q + 1);
     const int g0 = 2 * q, g1 = g0 + 1 < G ? g0 + 1 : g0;
-    publish(&done[g0 % R], (uint32_t)(g0 + 1));
-    if (g1 != g0) publish(&done[g1 % R], (uint32_t)(g1 + 1));
+    asm volatile("" ::: "memory");
+    __hip_atomic_store(&done[g0 % R], (uint32_t)(g0 + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (g1 != g0) __hip_atomic_store(&done[g1 % R], (uint32_t)(g1 + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (q + 1 < P && !shows(f, q + 1)) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      fetch(na, nb2, q + 1);
+    }
   };
-  for (int q = 0; q < P; ++q) {
-    Entry ea, eb;
-    fetch(ea, eb, q);
-    fold(ea, 2 * q);
-    if (2 * q + 1 < G) fold(eb, 2 * q + 1);
-    release(q);
+  {
+    Entry a0, b0, a1, b1;
+    fetch(a0, b0, 0);
+    for (int q = 0; q < P; q += 2) {
+      step(a0, b0, a1, b1, q);
+      if (q + 1 < P) step(a1, b1, a0, b0, q + 1);
+    }
   }
   // the last chunk's producers published before the folder consumed their
   // groups, so its operands are in place
