@@ -160,9 +160,9 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_flow_kernel(const uint8_t* __
   // ended). Requested after x and the w1/w3 weights, which phase 1 waits for
   // anyway, and before the w2 weights, which it does not.
   const uint32_t tag = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-  // the first w2 item's weights, once x has landed: until then x and the
-  // w1/w3 weights have the memory system to themselves
-  issue_w2(b < items2 ? b : items2 - 1, b < items2);
+  // the first w2 item's weights are requested once this wave's w1/w3 weights
+  // have landed (after its first folds): until then x and the w1/w3 weights,
+  // which the whole step waits for, have the memory system to themselves
 
   // ---- phase 1: w1/w3 + SwiGLU, two tiles per pass -------------------------
   const int frow = i < R ? i : R - 1;
@@ -186,6 +186,7 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_flow_kernel(const uint8_t* __
 #pragma unroll
         for (int v = 0; v < NV; ++v) part1[qmv_part_index<2, 1, NV>(seg, m, 0, v, lane)] = acc[m][0][v];
     }
+    if (pr == b) issue_w2(b < items2 ? b : items2 - 1, b < items2);
     __syncthreads();
     if (wg == 0) {
       float tot[2][1][NV];
