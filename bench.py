@@ -687,9 +687,9 @@ def bench_qkv_rope(dev, K):
 
 
 def bench_wide(dev, bits, K):
-    """The decode FFN step (two calls) and the 8192-row w1/w3 window with MLX
-    6- or 8-bit codes or block-FP8 weights (bits == "fp8"): same shapes, pool
-    and timing as the 4-bit figures."""
+    """The decode FFN step (two calls), the 8192-row w1/w3 window and 128-row
+    windows of w1/w3 and w2 with MLX 6- or 8-bit codes or block-FP8 weights
+    (bits == "fp8"): same shapes, pool and timing as the 4-bit figures."""
     import torch
 
     import bit_weight_only_q4g64_amd as q4
@@ -703,6 +703,7 @@ def bench_wide(dev, bits, K):
         w13_call = lambda p1, p3, x, z: q4.qmv_w13_swiglu_fp8b(p1, p3, 8192, 2048, x, y=z)  # noqa: E731
         rows_call = lambda p2, z, y: q4.qmv_rows_fp8b(p2, 2048, 8192, z, y=y)  # noqa: E731
         win_call = lambda p1, p3, xw, zw: q4.qmm_window_fp8b(p1, p3, 8192, 2048, xw, y=zw)  # noqa: E731
+        w2win_call = lambda p2, xw, yw: q4.qmm_window_fp8b(p2, None, 2048, 8192, xw, y=yw)  # noqa: E731
         algo = lambda N, Kk: N * Kk + 4 * N * Kk // 64  # noqa: E731  (one byte per weight + the 32-bit scale words)
     else:
         draw = lambda name, N, Kk: synthetic.draw_qweight(rng, name, N, Kk, bits=bits)  # noqa: E731
@@ -710,6 +711,7 @@ def bench_wide(dev, bits, K):
         w13_call = lambda p1, p3, x, z: q4.qmv_w13_swiglu(p1, p3, 8192, 2048, x, y=z, bits=bits)  # noqa: E731
         rows_call = lambda p2, z, y: q4.qmv_rows(p2, 2048, 8192, z, y=y, bits=bits)  # noqa: E731
         win_call = lambda p1, p3, xw, zw: q4.qmm_window(p1, p3, 8192, 2048, xw, y=zw, bits=bits)  # noqa: E731
+        w2win_call = lambda p2, xw, yw: q4.qmm_window(p2, None, 2048, 8192, xw, y=yw, bits=bits)  # noqa: E731
         algo = lambda N, Kk: qbytes(N, Kk, bits)  # noqa: E731
     w1, w3, w2 = draw("w1", 8192, 2048), draw("w3", 8192, 2048), draw("w2", 2048, 8192)
     pool = rotating([pack(w1), pack(w3), pack(w2)])
@@ -728,6 +730,15 @@ def bench_wide(dev, bits, K):
     t2 = graph_us(torch, lambda i: rows_call(pool[i % nc][2], z, y), n)
     b13 = 2 * algo(8192, 2048) + 2048 * 2 + 8192 * 4
     b2 = algo(2048, 8192) + 8192 * 4 + 2048 * 4
+    # 128-row windows (the short-window kernels) on the rotating pool
+    x128 = to_dev(synthetic.draw_bf16_rows(rng, 128, 2048), np.int16, dev).view(torch.bfloat16)
+    x128w2 = to_dev(synthetic.draw_bf16_rows(rng, 128, 8192), np.int16, dev).view(torch.bfloat16)
+    z128 = torch.empty((128, 8192), dtype=torch.bfloat16, device=dev)
+    y128 = torch.empty((128, 2048), dtype=torch.float32, device=dev)
+    t128_13 = graph_us(torch, lambda i: win_call(pool[i % nc][0], pool[i % nc][1], x128, z128), n)
+    t128_2 = graph_us(torch, lambda i: w2win_call(pool[i % nc][2], x128w2, y128), n)
+    f128_13 = 2.0 * 128 * (2 * 8192) * 2048 / (t128_13 * 1e-6) / 1e12
+    f128_2 = 2.0 * 128 * 2048 * 8192 / (t128_2 * 1e-6) / 1e12
     # the prompt window over two alternating copies of weights and prompt
     xw = to_dev(synthetic.draw_bf16_rows(rng, 8192, 2048), np.int16, dev).view(torch.bfloat16)
     wins = [(pool[0][0], pool[0][1], xw), (pool[1][0], pool[1][1], xw.clone())]
@@ -741,6 +752,8 @@ def bench_wide(dev, bits, K):
         "qmv_w13_swiglu": {"us": r3(t13), "frac": round(b13 / (t13 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "qmv_rows_w2_f32x": {"us": r3(t2), "frac": round(b2 / (t2 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "pgemm_swiglu_8192": {"us": r3(tw), "TFLOP/s": round(tf, 2), "frac": round(tf / BF16_PEAK_TFLOPS, 4)},
+        "window_128": {"w1w3_swiglu": {"us": r3(t128_13), "TFLOP/s": round(f128_13, 2)},
+                       "w2": {"us": r3(t128_2), "TFLOP/s": round(f128_2, 2)}},
     }
 
 

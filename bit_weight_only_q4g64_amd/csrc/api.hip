@@ -296,26 +296,43 @@ constexpr int64_t kNarrowBelow = 256;
 // a ring of 4 (72.7 KiB, two per compute unit). Measured on MI355X (us per
 // window, flow / narrow): 128-row w2 25.6 / 79.5, o 9.7 / 22.8, qkv 12.2 /
 // 23.1; SwiGLU 8192 x 2048 at 16 rows 13.1 / 23.5, at 64 rows 20.9 / 24.4.
-template <bool SW, int NP, int R>
+template <bool SW, int NP, int R, int BITS>
 void flow_launch_cfg(bool obf16, const uint8_t* a, const uint8_t* b, int n, int k, const uint16_t* x, int64_t ldx, int m, void* y,
                      int64_t ldy, int nb, int mb, hipStream_t s) {
   using namespace q4;
   const dim3 grid((unsigned)((int64_t)nb * mb)), block(64 * (NP + 1));
-  if (obf16) hipLaunchKernelGGL((pgemm_flow_kernel<SW, true, NP, R>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mb);
-  else hipLaunchKernelGGL((pgemm_flow_kernel<SW, false, NP, R>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mb);
+  if (obf16) hipLaunchKernelGGL((pgemm_flow_kernel<SW, true, NP, R, BITS>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mb);
+  else hipLaunchKernelGGL((pgemm_flow_kernel<SW, false, NP, R, BITS>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mb);
 }
 
-// true when the window ran on pgemm_flow_kernel
-bool flow_launch(bool swiglu, bool obf16, const uint8_t* a, const uint8_t* b, int64_t N, int k, const uint16_t* x, int64_t ldx,
-                 int64_t M, void* y, int64_t ldy, hipStream_t s) {
+template <int BITS>
+bool flow_launch_bits(bool swiglu, bool obf16, const uint8_t* a, const uint8_t* b, int64_t N, int k, const uint16_t* x, int64_t ldx,
+                      int64_t M, void* y, int64_t ldy, hipStream_t s) {
   using namespace q4;
   const int64_t nb = (N + kFlowRows - 1) / kFlowRows, mb = (M + kFlowRows - 1) / kFlowRows, cus = device_cus();
   const int n = (int)N, m = (int)M;
-  if (!swiglu && nb * mb <= 2 * cus) flow_launch_cfg<false, 3, 8>(obf16, a, b, n, k, x, ldx, m, y, ldy, (int)nb, (int)mb, s);
-  else if (swiglu && nb * mb <= cus) flow_launch_cfg<true, 3, 8>(obf16, a, b, n, k, x, ldx, m, y, ldy, (int)nb, (int)mb, s);
-  else if (swiglu && nb * mb <= 2 * cus) flow_launch_cfg<true, 2, 4>(obf16, a, b, n, k, x, ldx, m, y, ldy, (int)nb, (int)mb, s);
+  // Past two rounds, 4-bit windows go to the narrow kernel. The wider codes
+  // have none: against the wide kernel this one wins up to 6 (plain) and 4
+  // (SwiGLU) tiles per CU (measured: q/k/v at 512 rows 65 -> 38 us 6-bit,
+  // w1/w3 at 128 rows 62 -> 49 us; it loses at 1024 and 256 rows)
+  const int64_t plain_max = (BITS == 4 ? 2 : 6) * cus, sw_max = (BITS == 4 ? 2 : 4) * cus;
+  if (!swiglu && nb * mb <= plain_max) flow_launch_cfg<false, 3, 8, BITS>(obf16, a, b, n, k, x, ldx, m, y, ldy, (int)nb, (int)mb, s);
+  else if (swiglu && nb * mb <= cus) flow_launch_cfg<true, 3, 8, BITS>(obf16, a, b, n, k, x, ldx, m, y, ldy, (int)nb, (int)mb, s);
+  else if (swiglu && nb * mb <= sw_max) flow_launch_cfg<true, 2, 4, BITS>(obf16, a, b, n, k, x, ldx, m, y, ldy, (int)nb, (int)mb, s);
   else return false;
   return true;
+}
+
+// true when the window ran on pgemm_flow_kernel
+bool flow_launch(int bits, bool swiglu, bool obf16, const uint8_t* a, const uint8_t* b, int64_t N, int k, const uint16_t* x, int64_t ldx,
+                 int64_t M, void* y, int64_t ldy, hipStream_t s) {
+  switch (bits) {
+    case 4: return flow_launch_bits<4>(swiglu, obf16, a, b, N, k, x, ldx, M, y, ldy, s);
+    case 6: return flow_launch_bits<6>(swiglu, obf16, a, b, N, k, x, ldx, M, y, ldy, s);
+    case 8: return flow_launch_bits<8>(swiglu, obf16, a, b, N, k, x, ldx, M, y, ldy, s);
+    case q4::kFmtFp8: return flow_launch_bits<q4::kFmtFp8>(swiglu, obf16, a, b, N, k, x, ldx, M, y, ldy, s);
+  }
+  return false;
 }
 
 int qmm_window_impl(const char* fn, int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x,
@@ -330,8 +347,10 @@ int qmm_window_impl(const char* fn, int bits, const void* packed_a, const void* 
   const uint8_t* a = (const uint8_t*)packed_a;
   const uint8_t* b = swiglu ? (const uint8_t*)packed_b : a;
   const int n = (int)N, k = (int)K, m = (int)M;
+  // short windows: the dataflow kernel (every code format) where its tiles
+  // fit twice on the CUs, else the narrow kernel (4-bit codes)
+  if (blocks < kNarrowBelow && flow_launch(bits, swiglu, obf16, a, b, N, k, x, ldx, M, y, ldy, s)) return launched(fn);
   if (bits == 4 && blocks < kNarrowBelow) {
-    if (flow_launch(swiglu, obf16, a, b, N, k, x, ldx, M, y, ldy, s)) return launched(fn);
     const int cols = pgemm_narrow_cols(swiglu);
     const int nb = (n + cols - 1) / cols;
     const dim3 ngrid((unsigned)((int64_t)nb * mblk));

@@ -1,5 +1,5 @@
-// Prompt GEMM for short windows (4-bit codes): producer waves and one folder
-// wave per 32 x 32 output tile.
+// Prompt GEMM for short windows: producer waves and one folder wave per
+// 32 x 32 output tile. Codes of 4, 6 or 8 bits (MLX affine) or block FP8.
 //
 // A window of up to a few hundred rows has few output tiles: a 128-row window
 // of w2 (2048 x 8192) is 256 tiles of 32 x 32, each a chain over 128 groups
@@ -61,10 +61,13 @@ namespace q4 {
 constexpr int kFlowRows = 32;  // window rows per workgroup
 
 // Per-producer DMA stage: a pair's activations (2 groups x 32 rows x 128
-// bytes), its code blocks (1 KiB per weight slot) and scale/bias blocks.
+// bytes), its code blocks (per weight slot 1 KiB for 4-bit codes; 2 KiB for
+// the wider ones: 8-bit and FP8 the pair's block as it is, 6-bit its 1 KiB of
+// nibble words and then its 512 bytes of high-pair words) and scale/bias blocks.
 __host__ __device__ constexpr int flow_slots(bool swiglu) { return swiglu ? 4 : 2; }
-__host__ __device__ constexpr int flow_stage_bytes(bool swiglu) {
-  return 2 * kFlowRows * kXRowBytes + flow_slots(swiglu) * (kPairCodeBytes + kPairSbBytes);
+__host__ __device__ constexpr int flow_slot_code_bytes(int bits) { return bits == 4 ? kPairCodeBytes : 2048; }
+__host__ __device__ constexpr int flow_stage_bytes(bool swiglu, int bits = 4) {
+  return 2 * kFlowRows * kXRowBytes + flow_slots(swiglu) * (flow_slot_code_bytes(bits) + kPairSbBytes);
 }
 // A buffer resource from workgroup-uniform values, pinned to scalar registers.
 __device__ __forceinline__ i32x4 flow_rsrc(const void* base, uint32_t bytes) {
@@ -73,7 +76,7 @@ __device__ __forceinline__ i32x4 flow_rsrc(const void* base, uint32_t bytes) {
                __builtin_amdgcn_readfirstlane(r[3])};
 }
 
-template <bool SWIGLU, bool OUT_BF16, int NP, int R>
+template <bool SWIGLU, bool OUT_BF16, int NP, int R, int BITS = 4>
 __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t* __restrict__ pa, const uint8_t* __restrict__ pb, int N,
                                                                    int K, const uint16_t* __restrict__ x, int64_t ldx, int M,
                                                                    void* __restrict__ yv, int64_t ldy, int nblk, int mblk) {
@@ -88,7 +91,11 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
   __shared__ uint32_t ready[R], done[R];
   constexpr int kSlots = flow_slots(SWIGLU);
   constexpr int kXBytes = 2 * kFlowRows * kXRowBytes;
-  constexpr int kStageBytes = flow_stage_bytes(SWIGLU);
+  constexpr int kStageBytes = flow_stage_bytes(SWIGLU, BITS);
+  constexpr int kPcb = pair_code_bytes(BITS);           // a pair's code block in memory
+  constexpr int kSlotCode = flow_slot_code_bytes(BITS);  // and in the stage
+  constexpr bool kBias = BITS != kFmtFp8;                // block FP8 has no bias term
+  static_assert(BITS == 4 || BITS == 6 || BITS == 8 || BITS == kFmtFp8, "4-, 6- or 8-bit codes or block FP8");
   // chunk c + 2 reuses chunk c's bias operands: a producer writes group g
   // only after the release of group g - R, and the release of group
   // 8 (c + 1) follows chunk c's bias term, so R may not exceed a chunk
@@ -122,12 +129,12 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
     // w3), clamped at N (columns past N are never stored)
     const int t0 = 2 * nb < ntiles ? 2 * nb : ntiles - 1;
     const int t1 = 2 * nb + 1 < ntiles ? 2 * nb + 1 : ntiles - 1;
-    const int64_t cb = codes_bytes(N, K, 4);
+    const int64_t cb = codes_bytes(N, K, BITS);
     const i32x4 xr = flow_rsrc(x + (int64_t)m0 * ldx, (uint32_t)((int64_t)mt * ldx * 2));
-    const i32x4 cra = flow_rsrc(pa + (int64_t)t0 * P * kPairCodeBytes, (uint32_t)((t1 - t0 + 1) * P * kPairCodeBytes));
+    const i32x4 cra = flow_rsrc(pa + (int64_t)t0 * P * kPcb, (uint32_t)((t1 - t0 + 1) * P * kPcb));
     const i32x4 sra = flow_rsrc(pa + cb + (int64_t)t0 * P * kPairSbBytes, (uint32_t)((t1 - t0 + 1) * P * kPairSbBytes));
     const uint8_t* pbm = SWIGLU ? pb : pa;
-    const i32x4 crb = flow_rsrc(pbm + (int64_t)t0 * P * kPairCodeBytes, (uint32_t)((t1 - t0 + 1) * P * kPairCodeBytes));
+    const i32x4 crb = flow_rsrc(pbm + (int64_t)t0 * P * kPcb, (uint32_t)((t1 - t0 + 1) * P * kPcb));
     const i32x4 srb = flow_rsrc(pbm + cb + (int64_t)t0 * P * kPairSbBytes, (uint32_t)((t1 - t0 + 1) * P * kPairSbBytes));
     // activation DMA: load i (0..7) of a pair is group half i / 4, rows
     // 8 (i % 4) + lane / 8, 16-byte chunk lane % 8 at its swizzled slot; rows
@@ -145,8 +152,11 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
     const uint32_t st_lds = lds_addr(st);
     const bf16x8 ones = ones_bf16x8();
 
-    // pair q into the stage: 8 activation loads, one code block per slot, one
-    // scale/bias load per two slots
+    // 6-bit high-pair words: 512 bytes, lanes 0..31 (lanes 32..63 read out of
+    // range: zeros into the rest of the slot)
+    const uint32_t hvo = lane < 32 ? 1024u + (uint32_t)lane * 16u : kOffBuffer;
+    // pair q into the stage: 8 activation loads, one or two code loads per
+    // slot, one scale/bias load per two slots
     auto issue = [&](int q) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -156,14 +166,17 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
       }
 #pragma unroll
       for (int sl = 0; sl < kSlots; ++sl) {
-        const uint32_t so = (uint32_t)(((sl & 1) ? t1 - t0 : 0) * P + q) * kPairCodeBytes;
-        if (sl >= 2) dma_b128(crb, (uint32_t)lane * 16u, so, st_lds + kXBytes + sl * kPairCodeBytes);
-        else dma_b128(cra, (uint32_t)lane * 16u, so, st_lds + kXBytes + sl * kPairCodeBytes);
+        const uint32_t so = (uint32_t)(((sl & 1) ? t1 - t0 : 0) * P + q) * kPcb;
+        const i32x4 crs = sl >= 2 ? crb : cra;
+        const uint32_t dst = st_lds + kXBytes + sl * kSlotCode;
+        dma_b128(crs, (uint32_t)lane * 16u, so, dst);
+        if constexpr (BITS == 6) dma_b128(crs, hvo, so, dst + 1024);
+        else if constexpr (BITS != 4) dma_b128(crs, (uint32_t)lane * 16u + 1024u, so, dst + 1024);
       }
 #pragma unroll
       for (int h = 0; h < kSlots / 2; ++h) {
-        if (h >= 1) dma_b32(srb, svo, (uint32_t)q * kPairSbBytes, st_lds + kXBytes + kSlots * kPairCodeBytes + 2 * h * kPairSbBytes);
-        else dma_b32(sra, svo, (uint32_t)q * kPairSbBytes, st_lds + kXBytes + kSlots * kPairCodeBytes + 2 * h * kPairSbBytes);
+        if (h >= 1) dma_b32(srb, svo, (uint32_t)q * kPairSbBytes, st_lds + kXBytes + kSlots * kSlotCode + 2 * h * kPairSbBytes);
+        else dma_b32(sra, svo, (uint32_t)q * kPairSbBytes, st_lds + kXBytes + kSlots * kSlotCode + 2 * h * kPairSbBytes);
       }
     };
 
@@ -174,12 +187,17 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
       const int q = wave + n * NP;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // pair q's DMA has landed
       // the stage into registers: the activation fragments (row j, 16-byte
-      // chunk 2 ks + hl), the lane's code words and scale/bias words
+      // chunk 2 ks + hl), the lane's code words and scale/bias words. Code
+      // words of k steps 0, 2 come from lane L = jj + 16 hl of the block,
+      // of steps 1, 3 from lane L + 32: c0 and c1 (4-bit: .xy the nibble words
+      // of steps 0, 2 | 1, 3; 8-bit and FP8: the 16 bytes; 6-bit: the two
+      // nibble words and the high-pair word)
       u32x4 xa[2][4];
-      u32x2 c02[2][kTiles], c13[2][kTiles];
+      u32x4 c0[2][kTiles], c1[2][kTiles];
       uint32_t w[2][kTiles];
       const uint8_t* cs = st + kXBytes;
-      const uint8_t* sbs = st + kXBytes + kSlots * kPairCodeBytes;
+      const uint8_t* sbs = st + kXBytes + kSlots * kSlotCode;
+      const int L = jj + 16 * hl;
 #pragma unroll
       for (int gh = 0; gh < 2; ++gh) {
         const uint8_t* xb = st + gh * kFlowRows * kXRowBytes;
@@ -189,9 +207,19 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
         for (int t = 0; t < kTiles; ++t) {
           const int sl = 2 * t + (j >> 4);
           w[gh][t] = *(const uint32_t*)(sbs + sl * kPairSbBytes + jj * 8 + gh * 4);
-          const uint8_t* cl = cs + sl * kPairCodeBytes + (jj + 16 * hl) * 16 + gh * 8;
-          c02[gh][t] = *(const u32x2*)cl;
-          c13[gh][t] = *(const u32x2*)(cl + 512);
+          const uint8_t* blk = cs + sl * kSlotCode;
+          if constexpr (BITS == 4) {
+            const u32x2 a = *(const u32x2*)(blk + L * 16 + gh * 8), b = *(const u32x2*)(blk + L * 16 + gh * 8 + 512);
+            c0[gh][t] = u32x4{a[0], a[1], 0u, 0u};
+            c1[gh][t] = u32x4{b[0], b[1], 0u, 0u};
+          } else if constexpr (BITS == 6) {
+            const u32x2 a = *(const u32x2*)(blk + L * 16 + gh * 8), b = *(const u32x2*)(blk + (L + 32) * 16 + gh * 8);
+            c0[gh][t] = u32x4{a[0], a[1], *(const uint32_t*)(blk + 1024 + L * 8 + gh * 4), 0u};
+            c1[gh][t] = u32x4{b[0], b[1], *(const uint32_t*)(blk + 1024 + (L + 32) * 8 + gh * 4), 0u};
+          } else {
+            c0[gh][t] = *(const u32x4*)(blk + gh * 1024 + L * 16);
+            c1[gh][t] = *(const u32x4*)(blk + gh * 1024 + L * 16 + 512);
+          }
         }
       }
       // the reads have completed: the stage takes the next pair
@@ -204,11 +232,36 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
       for (int gh = 0; gh < 2; ++gh) {
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
-          Pm[gh][t] = mfma32(__builtin_bit_cast(bf16x8, xa[gh][0]), codes_to_bf16(c02[gh][t][0]), f32x16{});
-          Pm[gh][t] = mfma32(__builtin_bit_cast(bf16x8, xa[gh][1]), codes_to_bf16(c13[gh][t][0]), Pm[gh][t]);
-          Pm[gh][t] = mfma32(__builtin_bit_cast(bf16x8, xa[gh][2]), codes_to_bf16(c02[gh][t][1]), Pm[gh][t]);
-          Pm[gh][t] = mfma32(__builtin_bit_cast(bf16x8, xa[gh][3]), codes_to_bf16(c13[gh][t][1]), Pm[gh][t]);
+          // the exact bf16 codes of k steps 0..3 (as the other window kernels convert them)
+          bf16x8 qk[4];
+          const u32x4 a = c0[gh][t], b = c1[gh][t];
+          if constexpr (BITS == 4) {
+            qk[0] = codes_to_bf16(a[0]);
+            qk[2] = codes_to_bf16(a[1]);
+            qk[1] = codes_to_bf16(b[0]);
+            qk[3] = codes_to_bf16(b[1]);
+          } else if constexpr (BITS == 6) {
+            qk[0] = six_to_bf16<0>(a[0], a[2]);
+            qk[2] = six_to_bf16<1>(a[1], a[2]);
+            qk[1] = six_to_bf16<0>(b[0], b[2]);
+            qk[3] = six_to_bf16<1>(b[1], b[2]);
+          } else if constexpr (BITS == kFmtFp8) {
+            qk[0] = fp8_to_bf16(a[0], a[1]);
+            qk[2] = fp8_to_bf16(a[2], a[3]);
+            qk[1] = fp8_to_bf16(b[0], b[1]);
+            qk[3] = fp8_to_bf16(b[2], b[3]);
+          } else {
+            qk[0] = bytes_to_bf16(a[0], a[1]);
+            qk[2] = bytes_to_bf16(a[2], a[3]);
+            qk[1] = bytes_to_bf16(b[0], b[1]);
+            qk[3] = bytes_to_bf16(b[2], b[3]);
+          }
+          Pm[gh][t] = mfma32(__builtin_bit_cast(bf16x8, xa[gh][0]), qk[0], f32x16{});
+          Pm[gh][t] = mfma32(__builtin_bit_cast(bf16x8, xa[gh][1]), qk[1], Pm[gh][t]);
+          Pm[gh][t] = mfma32(__builtin_bit_cast(bf16x8, xa[gh][2]), qk[2], Pm[gh][t]);
+          Pm[gh][t] = mfma32(__builtin_bit_cast(bf16x8, xa[gh][3]), qk[3], Pm[gh][t]);
         }
+        if constexpr (kBias) {
         // the sums' operands: lane i16 + 16 kc of row block v takes chunks
         // kc and kc + 4 of row 16 v + i16. Lane 16 v + i16 + 32 (kc & 1) holds
         // them in xa[kc / 2] and xa[2 + kc / 2]; a swap of lane halves (32)
@@ -229,6 +282,7 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
         Sv[gh][0] = mfma16(ones, __builtin_bit_cast(bf16x8, X[1]), Sv[gh][0]);
         Sv[gh][1] = mfma16(ones, __builtin_bit_cast(bf16x8, Y[0]), f32x4{0.f, 0.f, 0.f, 0.f});
         Sv[gh][1] = mfma16(ones, __builtin_bit_cast(bf16x8, Y[1]), Sv[gh][1]);
+        }
       }
       // hand the pair to the folder. The folder releases a pair's entries
       // together (the second after the first), so the second slot's flag
@@ -251,8 +305,9 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             ringP[slot][t][i][lane] = f32x4{Pm[gh][t][4 * i], Pm[gh][t][4 * i + 1], Pm[gh][t][4 * i + 2], Pm[gh][t][4 * i + 3]};
-          ringC[slot][t][lane] = bf16_lo(w[gh][t]);
+          ringC[slot][t][lane] = BITS == kFmtFp8 ? __uint_as_float(w[gh][t]) : bf16_lo(w[gh][t]);
         }
+        if constexpr (!kBias) continue;
         // this group's share of its chunk's bias operands: position
         // (m, hl, e) = (gg / 4, gg / 2 % 2, gg % 2) of chunk c
         const int c = g / kPgemmChunk, gg = g % kPgemmChunk, m = gg >> 2, hg = (gg >> 1) & 1, e = gg & 1;
@@ -333,7 +388,8 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[t][4 * i + u] = __builtin_fmaf(e.sc[t], e.P[t][i][u], acc[t][4 * i + u]);
-    if ((g & (kPgemmChunk - 1)) == 0 && g > 0) bias_chunk(g / kPgemmChunk - 1);
+    if constexpr (kBias)
+      if ((g & (kPgemmChunk - 1)) == 0 && g > 0) bias_chunk(g / kPgemmChunk - 1);
   };
   // Pair q's flag (of its second group: a producer publishes a pair's groups
   // in order) and entries, read back to back. The LDS serves one wave's
@@ -389,7 +445,7 @@ __global__ __launch_bounds__(64 * (NP + 1)) void pgemm_flow_kernel(const uint8_t
   }
   // the last chunk's producers published before the folder consumed their
   // groups, so its operands are in place
-  bias_chunk((G - 1) / kPgemmChunk);
+  if constexpr (kBias) bias_chunk((G - 1) / kPgemmChunk);
 
   // ---- epilogue: element r is row 8 (r / 4) + 4 hl + r % 4, column jj of the
   // lane's weight tile

@@ -263,8 +263,8 @@ def test_short_windows_match_the_whole_prompt(swiglu, out_bf16):
         check_within(host_f64(q4.qmm_window(pk, None, N, K, xd[:128]))[rows], w, x, rows=rows, label="short window w2", order="window")
 
 
-@pytest.mark.parametrize("swiglu", [False, True])
-def test_two_round_short_windows_match_the_whole_prompt(swiglu):
+@pytest.mark.parametrize("swiglu,out_bf16", [(False, False), (True, False), (True, True)])
+def test_two_round_short_windows_match_the_whole_prompt(swiglu, out_bf16):
     """Windows whose 32 x 32 tiles number between one and two per compute unit
     (N = 4096: 128 rows are 512 tiles, 65 and 96 rows 384) run with two
     short-window workgroups sharing a compute unit (SwiGLU: the 2-producer
@@ -272,17 +272,19 @@ def test_two_round_short_windows_match_the_whole_prompt(swiglu):
     N = 4096
     K = 8192 if not swiglu else 4032
     M = 2048
-    say(f"two-round short windows vs whole prompt N={N} K={K} swiglu={swiglu}")
+    say(f"two-round short windows vs whole prompt N={N} K={K} swiglu={swiglu} bf16={out_bf16}")
     rng = np.random.default_rng(N + K + 7 * swiglu)
     w = synthetic.draw_qweight(rng, "a", N, K)
     pk = dev_weight(w)
     pb = dev_weight(synthetic.draw_qweight(rng, "b", N, K)) if swiglu else None
     xd = dev_bf16(synthetic.draw_bf16_rows(rng, M, K))
-    ref = bits32(q4.qmm_window(pk, pb, N, K, xd))
+    dt = torch.bfloat16 if out_bf16 else torch.float32
+    bits = bits16 if out_bf16 else bits32
+    ref = bits(q4.qmm_window(pk, pb, N, K, xd, out_dtype=dt))
     for r0, rows in ((0, 128), (1000, 96), (300, 65), (M - 33, 33), (5, 1)):
-        y = q4.qmm_window(pk, pb, N, K, xd[r0 : r0 + rows])
+        y = q4.qmm_window(pk, pb, N, K, xd[r0 : r0 + rows], out_dtype=dt)
         torch.cuda.synchronize()
-        assert np.array_equal(bits32(y), ref[r0 : r0 + rows]), (r0, rows)
+        assert np.array_equal(bits(y), ref[r0 : r0 + rows]), (r0, rows)
 
 
 @pytest.mark.parametrize("N,K,M,swiglu", [(64, 64, 1, False), (64, 128, 31, True), (128, 64, 32, False), (128, 192, 33, True),

@@ -1,0 +1,89 @@
+"""Short windows of 6-bit, 8-bit and block-FP8 weights on the dataflow
+workgroups (one 32 x 32 tile each, products of several groups at once, folded
+in order) against the whole prompt on the wide 128 x 256 workgroups: every
+row's bits agree (TensorFold PR #1696, later revision, "Checks": a row alone
+equals the row inside a window; PR #1514, "What changes": the 4-, 6- and
+8-bit checkpoints served as stored; PR #1696, "Checks": block FP8 weights
+served weight-only). The whole prompt (8192 rows) is large enough for the
+wide kernel; the windows (1 to 1536 rows) run on the dataflow kernel, in one
+round, in its two-workgroups-per-CU SwiGLU form, and in several rounds (the
+wider codes use it up to 4 SwiGLU and 6 plain tiles per CU). One window per
+case is also checked against the float64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_only_q4g64_amd as q4
+import oracle
+import synthetic
+from tests.gpu_helpers import DEV, bits16, bits32, check_within, dev_bf16, dev_weight, host_f64, say
+from tests.tolerance import tol, tol_swiglu
+
+pytestmark = pytest.mark.gpu
+
+N, K, M = 1024, 64 * 33, 8192  # an odd group count
+# 1 to 448 rows: one or two rounds; 1024 and 1536 rows: up to 4 (SwiGLU) and 6 (plain) tiles per CU
+WINDOWS = ((0, 128), (1000, 96), (300, 65), (M - 33, 33), (5, 1), (2000, 448), (4096, 1024), (5200, 1536))
+
+
+def _pack(fmt, w):
+    if fmt == "fp8":
+        return q4.pack_fp8b(torch.from_numpy(np.ascontiguousarray(w.w8)).to(DEV), torch.from_numpy(np.ascontiguousarray(w.scales)).to(DEV))
+    return dev_weight(w)
+
+
+def _window(fmt, pa, pb, xd, dt):
+    if fmt == "fp8":
+        return q4.qmm_window_fp8b(pa, pb, N, K, xd, out_dtype=dt)
+    return q4.qmm_window(pa, pb, N, K, xd, bits=fmt, out_dtype=dt)
+
+
+@pytest.fixture(scope="module", params=[6, 8, "fp8"])
+def fmt_case(request):
+    fmt = request.param
+    rng = np.random.default_rng(901 if fmt == "fp8" else 900 + fmt)
+    if fmt == "fp8":
+        a, b = synthetic.draw_fp8_weight(rng, "a", N, K), synthetic.draw_fp8_weight(rng, "b", N, K)
+    else:
+        a, b = synthetic.draw_qweight(rng, "a", N, K, bits=fmt), synthetic.draw_qweight(rng, "b", N, K, bits=fmt)
+    x = synthetic.draw_bf16_rows(rng, M, K)
+    return {"fmt": fmt, "a": a, "b": b, "x": x, "pa": _pack(fmt, a), "pb": _pack(fmt, b), "xd": dev_bf16(x)}
+
+
+@pytest.mark.parametrize("swiglu,out_bf16", [(False, False), (True, False), (True, True)])
+def test_short_windows_of_wider_codes_match_the_whole_prompt(fmt_case, swiglu, out_bf16):
+    fmt = fmt_case["fmt"]
+    say(f"short windows fmt={fmt} swiglu={swiglu} bf16={out_bf16} vs the whole prompt")
+    pb = fmt_case["pb"] if swiglu else None
+    dt = torch.bfloat16 if out_bf16 else torch.float32
+    bits = bits16 if out_bf16 else bits32
+    ref = bits(_window(fmt, fmt_case["pa"], pb, fmt_case["xd"], dt))
+    torch.cuda.synchronize()
+    for r0, rows in WINDOWS:
+        y = _window(fmt, fmt_case["pa"], pb, fmt_case["xd"][r0 : r0 + rows], dt)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(y), ref[r0 : r0 + rows]), (r0, rows)
+
+
+def test_short_window_of_wider_codes_within_oracle_bound(fmt_case):
+    fmt = fmt_case["fmt"]
+    say(f"short window fmt={fmt} against the oracle")
+    rows = [0, 37, 95]
+    xs = fmt_case["x"][:96][rows]
+    a, b = fmt_case["a"], fmt_case["b"]
+    y = host_f64(_window(fmt, fmt_case["pa"], None, fmt_case["xd"][:96], torch.float32))[rows]
+    z = host_f64(_window(fmt, fmt_case["pa"], fmt_case["pb"], fmt_case["xd"][:96], torch.float32))[rows]
+    if fmt == "fp8":
+        a64 = oracle.matmul_rows_fp8(a.w8, a.scales, xs)
+        c64 = oracle.matmul_rows_fp8(b.w8, b.scales, xs)
+        Ta = tol(oracle.error_weight_fp8(a.w8, a.scales, xs), K, order="window", fmt="fp8")
+        Tc = tol(oracle.error_weight_fp8(b.w8, b.scales, xs), K, order="window", fmt="fp8")
+        assert np.all(np.abs(y - a64) <= Ta)
+    else:
+        check_within(y, a, fmt_case["x"][:96], rows=rows, label=f"short window {fmt}-bit", order="window")
+        a64 = oracle.matmul_rows(a.wq, a.scales, a.biases, xs, bits=fmt)
+        c64 = oracle.matmul_rows(b.wq, b.scales, b.biases, xs, bits=fmt)
+        Ta = tol(oracle.error_weight(a.wq, a.scales, a.biases, xs, bits=fmt), K, order="window")
+        Tc = tol(oracle.error_weight(b.wq, b.scales, b.biases, xs, bits=fmt), K, order="window")
+    assert np.all(np.abs(z - oracle.swiglu(a64, c64)) <= tol_swiglu(a64, c64, Ta, Tc))
