@@ -34,8 +34,9 @@
 // Every wait is bounded (at most 2^22 polls), so no wave can hang.
 //
 // LDS is 74.5 KiB with NP = 3, R = 8 (plain) and 72.7 KiB with NP = 2, R = 4
-// (SwiGLU), so two workgroups share a compute unit and a window of up to two
-// rounds of tiles is resident at once; SwiGLU with NP = 3, R = 8 takes 120 KiB.
+// (SwiGLU) for 4-bit codes, 80.7 and 80.9 KiB for the wider ones, so two
+// workgroups share a compute unit and a window of up to two rounds of tiles
+// is resident at once; SwiGLU with NP = 3, R = 8 takes 120 to 130 KiB.
 //
 // Measured on MI355X and dropped: more producers (4 to 7, two per SIMD), two
 // folders each folding half the accumulators, a ring of 16 and deeper
