@@ -288,38 +288,60 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_flow_kernel(const uint8_t* __
     __syncthreads();
     if (wave == 0) {
       const int t = it % T2, h = it / T2;
-      const int nloc = item_seg_end(it) - (it / T2) * half2;  // this item's segments
-      float tot = 0.f;
-      int j0 = 0;
+      const int nloc = item_seg_end(it) - h * half2;  // this item's segments, at most one per wave
+      // the item's segment partials, all requested at once: read one by one
+      // inside the sum, each would cost an LDS round trip on the step's
+      // critical path
+      float pv[kFfnWaves];
+#pragma unroll
+      for (int j = 0; j < kFfnWaves; ++j) pv[j] = part2[(j < nloc ? j : 0) * 64 + lane];
       if (h == 0) {
-        tot = part2[lane];
-        j0 = 1;
+        float tot = pv[0];
+#pragma unroll
+        for (int j = 1; j < kFfnWaves; ++j)
+          if (j < nloc) tot = tot + pv[j];
+        flow_st(hand + (int64_t)t * 64 + lane, tot, tag);
       } else {
-        // the lower half's running sum
+        // the lower half's running sum, polled with two loads in flight
+        // (each check waits for its own load only), so a value that lands
+        // just after one load has passed is seen by the next, not a whole
+        // round trip later
         const uint64_t* src = hand + (int64_t)t * 64 + lane;
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        uint64_t hv = flow_ld(src);
-        while (__builtin_amdgcn_ballot_w64((uint32_t)(hv >> 32) != tag) != 0) {
+        uint64_t ha = flow_ld(src), hb, hv;
+        while (true) {
+          __builtin_amdgcn_s_sleep(2);
+          hb = flow_ld(src);
+          if (__builtin_amdgcn_ballot_w64((uint32_t)(ha >> 32) != tag) == 0) {
+            hv = ha;
+            asm volatile("" ::"v"(hb));  // the load still in flight lands here, not in a register reused below
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+          ha = flow_ld(src);
+          if (__builtin_amdgcn_ballot_w64((uint32_t)(hb >> 32) != tag) == 0) {
+            hv = hb;
+            asm volatile("" ::"v"(ha));
+            break;
+          }
           if (__builtin_amdgcn_s_memrealtime() - t0 > kFfnSpinTicks) {
             ok = false;
+            hv = hb;
+            asm volatile("" ::"v"(ha));
             __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
           }
-          __builtin_amdgcn_s_sleep(1);
-          hv = flow_ld(src);
         }
-        tot = __uint_as_float((uint32_t)hv);
+        float tot = __uint_as_float((uint32_t)hv);
+#pragma unroll
+        for (int j = 0; j < kFfnWaves; ++j)
+          if (j < nloc) tot = tot + pv[j];
+        const int r = kc;
+        if (r < R) y[(int64_t)r * ldy + (int64_t)t * kTileN + i] = tot;
         // every workgroup has read the call counter by now (each produces z,
         // and this item and its partner have consumed every producer's z):
         // advance it, without waiting for the result
         if (lane == 0) (void)__hip_atomic_fetch_max(epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      for (int j = j0; j < nloc; ++j) tot = tot + part2[j * 64 + lane];
-      if (h == 0) {
-        flow_st(hand + (int64_t)t * 64 + lane, tot, tag);
-      } else {
-        const int r = kc;
-        if (r < R) y[(int64_t)r * ldy + (int64_t)t * kTileN + i] = tot;
       }
     }
     // part2 and the staged pieces are reused by the next item (LDS only)
