@@ -8,9 +8,9 @@
 // boundary), so z and y are bit-identical to the two calls. The schedule:
 //
 //   * one workgroup per CU (16 waves), all resident at once;
-//   * at the start each workgroup requests x, the weights of its w1/w3 tile
-//     pair AND the weights of its first w2 item, so the whole step's weights
-//     stream from HBM together;
+//   * at the start each workgroup requests x and the weights of its w1/w3
+//     tile pair; each wave requests its first w2 item's weights after its
+//     first w1/w3 folds, so the bytes that z waits for come first;
 //   * phase 1 (w1/w3, SwiGLU): each z value goes to the caller's z and, with
 //     a tag, to a workspace copy: one 64-bit store of {z bits, tag}, where
 //     the tag is this call's number (the workspace's call counter + 1);
