@@ -287,8 +287,22 @@ void pgemm_launch_bits(bool swiglu, bool obf16, dim3 grid, dim3 block, hipStream
 }
 
 // Below this many 256-column workgroups a window runs on the 64-column
-// workgroups of pgemm_narrow_kernel (4-bit codes; the same bits per row).
+// workgroups of pgemm_narrow_kernel (every code format; the same bits per
+// row).
 constexpr int64_t kNarrowBelow = 256;
+
+template <int BITS>
+void narrow_launch_bits(bool swiglu, bool obf16, dim3 grid, dim3 block, hipStream_t s, const uint8_t* a, const uint8_t* b, int n, int k,
+                        const uint16_t* x, int64_t ldx, int m, void* y, int64_t ldy, int nb, int mblk) {
+  using namespace q4;
+  if (swiglu) {
+    if (obf16) hipLaunchKernelGGL((pgemm_narrow_kernel<true, true, BITS>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
+    else hipLaunchKernelGGL((pgemm_narrow_kernel<true, false, BITS>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
+  } else {
+    if (obf16) hipLaunchKernelGGL((pgemm_narrow_kernel<false, true, BITS>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
+    else hipLaunchKernelGGL((pgemm_narrow_kernel<false, false, BITS>), grid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
+  }
+}
 // Among those, a window whose 32 x 32 tiles fit twice on the compute units
 // runs on pgemm_flow_kernel: plain with 3 producer waves and a ring of 8
 // (74.5 KiB of LDS, two workgroups per compute unit); SwiGLU with 3 producers
@@ -311,11 +325,13 @@ bool flow_launch_bits(bool swiglu, bool obf16, const uint8_t* a, const uint8_t* 
   using namespace q4;
   const int64_t nb = (N + kFlowRows - 1) / kFlowRows, mb = (M + kFlowRows - 1) / kFlowRows, cus = device_cus();
   const int n = (int)N, m = (int)M;
-  // Past two rounds, 4-bit windows go to the narrow kernel. The wider codes
-  // have none: against the wide kernel this one wins up to 6 (plain) and 4
-  // (SwiGLU) tiles per CU (measured: q/k/v at 512 rows 65 -> 38 us 6-bit,
-  // w1/w3 at 128 rows 62 -> 49 us; it loses at 1024 and 256 rows)
-  const int64_t plain_max = (BITS == 4 ? 2 : 6) * cus, sw_max = (BITS == 4 ? 2 : 4) * cus;
+  // Past two rounds of tiles (SwiGLU) the narrow kernel wins for every code
+  // format; past two (4-bit) or four (wider codes) rounds of plain tiles as
+  // well. Measured, us per window, this kernel / narrow: 6-bit w1/w3 at 128
+  // rows 49.6 / 32.7, FP8 37.1 / 20.0; 6-bit w2 at 384 rows (3 rounds)
+  // 69.1 / 108.6, at 768 rows (6 rounds) 125.6 / 112.9; 6-bit o at 512 rows
+  // (4 rounds) 26.9 / 30.9, q/k/v at 512 rows (6 rounds) 38.4 / 32.0.
+  const int64_t plain_max = (BITS == 4 ? 2 : 4) * cus, sw_max = 2 * cus;
   if (!swiglu && nb * mb <= plain_max) flow_launch_cfg<false, 3, 8, BITS>(obf16, a, b, n, k, x, ldx, m, y, ldy, (int)nb, (int)mb, s);
   else if (swiglu && nb * mb <= cus) flow_launch_cfg<true, 3, 8, BITS>(obf16, a, b, n, k, x, ldx, m, y, ldy, (int)nb, (int)mb, s);
   else if (swiglu && nb * mb <= sw_max) flow_launch_cfg<true, 2, 4, BITS>(obf16, a, b, n, k, x, ldx, m, y, ldy, (int)nb, (int)mb, s);
@@ -347,20 +363,21 @@ int qmm_window_impl(const char* fn, int bits, const void* packed_a, const void* 
   const uint8_t* a = (const uint8_t*)packed_a;
   const uint8_t* b = swiglu ? (const uint8_t*)packed_b : a;
   const int n = (int)N, k = (int)K, m = (int)M;
-  // short windows: the dataflow kernel (every code format) where its tiles
-  // fit twice on the CUs, else the narrow kernel (4-bit codes)
+  // short windows: the dataflow kernel where its tiles fit twice on the CUs
+  // (plain windows of the wider codes: four times), else the narrow kernel
   if (blocks < kNarrowBelow && flow_launch(bits, swiglu, obf16, a, b, N, k, x, ldx, M, y, ldy, s)) return launched(fn);
-  if (bits == 4 && blocks < kNarrowBelow) {
+  if (blocks < kNarrowBelow) {
     const int cols = pgemm_narrow_cols(swiglu);
     const int nb = (n + cols - 1) / cols;
     const dim3 ngrid((unsigned)((int64_t)nb * mblk));
-    if (swiglu) {
-      if (obf16) hipLaunchKernelGGL((pgemm_narrow_kernel<true, true>), ngrid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
-      else hipLaunchKernelGGL((pgemm_narrow_kernel<true, false>), ngrid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
-    } else {
-      if (obf16) hipLaunchKernelGGL((pgemm_narrow_kernel<false, true>), ngrid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
-      else hipLaunchKernelGGL((pgemm_narrow_kernel<false, false>), ngrid, block, 0, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
-    }
+    if (bits == 6)
+      narrow_launch_bits<6>(swiglu, obf16, ngrid, block, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
+    else if (bits == 8)
+      narrow_launch_bits<8>(swiglu, obf16, ngrid, block, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
+    else if (bits == kFmtFp8)
+      narrow_launch_bits<kFmtFp8>(swiglu, obf16, ngrid, block, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
+    else
+      narrow_launch_bits<4>(swiglu, obf16, ngrid, block, s, a, b, n, k, x, ldx, m, y, ldy, nb, mblk);
     return launched(fn);
   }
   if (bits == 6)

@@ -1,4 +1,5 @@
-// Prompt GEMM for short windows (4-bit codes).
+// Prompt GEMM for short windows. Codes of 4, 6 or 8 bits (MLX affine) or
+// block FP8.
 //
 // A window of a few hundred rows gives pgemm_kernel's 128-row x 256-column
 // workgroups too few tiles to fill the chip (a 128-row window of w1/w3 is
@@ -7,7 +8,9 @@
 // (64 weight columns; SwiGLU: 2 tiles of w1 and the same 2 of w3, 32 output
 // columns), and wave w owns rows 32w .. 32w + 31 of all of them: a quarter of
 // the work per workgroup, four times the workgroups, each wave converting the
-// codes of all 64 columns for its one row tile.
+// codes of all 64 columns for its one row tile. 4-bit codes are staged a
+// group pair at a time, the wider ones a group at a time (pgemm_kernel's
+// stages and fragment reads for each format).
 //
 // Per output the arithmetic is pgemm_kernel's, step for step: the same four
 // chained 32 x 32 x 16 matrix steps per group on the same exact bf16 codes,
@@ -25,18 +28,23 @@ namespace q4 {
 
 constexpr int kNarrowSlots = 4;     // 16-column weight tiles per workgroup
 constexpr int kNarrowSbSlot = 256;  // scale/bias stage bytes per slot (128 used, then the DMA's padding)
-constexpr int kNarrowCStage = kNarrowSlots * kPairCodeBytes;  // 4 KiB
 constexpr int kNarrowSbStage = kNarrowSlots * kNarrowSbSlot;  // 1 KiB
+// code bytes per slot and stage: a group pair of 4-bit codes, a group of the wider ones
+__host__ __device__ constexpr int narrow_slot_stage_bytes(int bits) { return bits == 4 ? kPairCodeBytes : pgemm_group_code_bytes(bits); }
 
 // Output columns covered by one workgroup.
 __host__ __device__ constexpr int pgemm_narrow_cols(bool swiglu) { return swiglu ? 2 * kTileN : kNarrowSlots * kTileN; }
 
-template <bool SWIGLU, bool OUT_BF16>
+template <bool SWIGLU, bool OUT_BF16, int BITS = 4>
 __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const uint8_t* __restrict__ pa, const uint8_t* __restrict__ pb,
                                                                          int N, int K, const uint16_t* __restrict__ x, int64_t ldx, int M,
                                                                          void* __restrict__ yv, int64_t ldy, int nblk, int mblk) {
   __shared__ __align__(16) uint8_t xs[kXStages * kXStageBytes];
-  __shared__ __align__(16) uint8_t cs[2 * kNarrowCStage];
+  constexpr int kSlotStage = narrow_slot_stage_bytes(BITS);
+  constexpr int kCSt = kNarrowSlots * kSlotStage;  // one code stage (3 or 4 KiB)
+  constexpr int kPcb = pair_code_bytes(BITS);
+  static_assert(BITS == 4 || BITS == 6 || BITS == 8 || BITS == kFmtFp8, "4-, 6- or 8-bit codes or block FP8");
+  __shared__ __align__(16) uint8_t cs[2 * kCSt];
   __shared__ __align__(16) uint8_t sbs[2 * kNarrowSbStage];
   __shared__ __align__(16) float ssum[kSumFloats];
 
@@ -49,7 +57,7 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const ui
   const int G = K / kGroup;
   const int P = (G + 1) / 2;
   const int ntiles = N / kTileN;
-  const int64_t cb = codes_bytes(N, K, 4);
+  const int64_t cb = codes_bytes(N, K, BITS);
   const bf16x8 ones = ones_bf16x8();
 
   // slot (0..3) -> weight tile (unclamped)
@@ -73,11 +81,11 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const ui
   // slot's padding with zeros.
   const uint8_t* mat = (SWIGLU && wave >= 2) ? pb : pa;
   const int tw = clamp_tile(slot_tile(wave));
-  const i32x4 cr = make_srsrc(mat + (int64_t)tw * P * kPairCodeBytes, (uint32_t)(P * kPairCodeBytes));
+  const i32x4 cr = make_srsrc(mat + (int64_t)tw * P * kPcb, (uint32_t)(P * kPcb));
   const i32x4 sr = make_srsrc(mat + cb + (int64_t)tw * P * kPairSbBytes, (uint32_t)(P * kPairSbBytes));
   const uint32_t cvo = (uint32_t)lane * 16u;
   const uint32_t svo = lane < 32 ? (uint32_t)lane * 4u : kOffBuffer;
-  const uint32_t cs_lds = lds_addr(cs) + wave * kPairCodeBytes;
+  const uint32_t cs_lds = lds_addr(cs) + wave * kSlotStage;
   const uint32_t sb_lds = lds_addr(sbs) + wave * kNarrowSbSlot;
 
   auto issue_x = [&](int g) {
@@ -85,11 +93,23 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const ui
 #pragma unroll
     for (int u = 0; u < 4; ++u) dma_b128(xr, xvo[u], (uint32_t)g * kXRowBytes, dst + u * 1024);
   };
-  // the codes and scale/bias words of pair p into stage p & 1: two loads
+  auto issue_sb = [&](int p) { dma_b32(sr, svo, (uint32_t)p * kPairSbBytes, sb_lds + (uint32_t)(p & 1) * kNarrowSbStage); };
+  // 4-bit: the codes and scale/bias words of pair p into stage p & 1: two loads
   auto issue_c = [&](int p) {
-    const uint32_t st = (uint32_t)(p & 1);
-    dma_b128(cr, cvo, (uint32_t)p * kPairCodeBytes, cs_lds + st * kNarrowCStage);
-    dma_b32(sr, svo, (uint32_t)p * kPairSbBytes, sb_lds + st * kNarrowSbStage);
+    dma_b128(cr, cvo, (uint32_t)p * kPairCodeBytes, cs_lds + (uint32_t)(p & 1) * kCSt);
+    issue_sb(p);
+  };
+  // 6- and 8-bit: the codes of group g into stage g & 1 (one or three loads)
+  auto issue_cg = [&](int g) {
+    const uint32_t dst = cs_lds + (uint32_t)(g & 1) * kCSt;
+    const uint32_t blk = (uint32_t)(g >> 1) * kPcb, gh = (uint32_t)(g & 1);
+    if constexpr (code_bits(BITS) == 8) {
+      dma_b128(cr, cvo, blk + gh * 1024u, dst);
+    } else {
+      dma_b32(cr, (uint32_t)lane * 16u + gh * 8u, blk, dst);
+      dma_b32(cr, (uint32_t)lane * 16u + gh * 8u + 4u, blk, dst + 256);
+      dma_b32(cr, 1024u + (uint32_t)lane * 8u + gh * 4u, blk, dst + 512);
+    }
   };
 
   // ---- consumer set-up ---------------------------------------------------
@@ -142,7 +162,7 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const ui
     constexpr int gh = decltype(ghc)::value;
     const int p = g >> 1, gg = g & (kPgemmChunk - 1);
     const uint8_t* xb = xs + (g % kXStages) * kXStageBytes;
-    const uint8_t* cb0 = cs + (p & 1) * kNarrowCStage;
+    const uint8_t* cb0 = cs + (BITS == 4 ? (p & 1) : (g & 1)) * kCSt;
     const uint8_t* sb0 = sbs + (p & 1) * kNarrowSbStage;
 
     uint32_t w[kPgemmNT];
@@ -150,19 +170,41 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const ui
 #pragma unroll
     for (int s = 0; s < kPgemmNT; ++s) {
       w[s] = *(const uint32_t*)(sb0 + lslot[s] * kNarrowSbSlot + jj * 8 + gh * 4);
-      sc[s] = bf16_lo(w[s]);
+      sc[s] = BITS == kFmtFp8 ? __uint_as_float(w[s]) : bf16_lo(w[s]);
     }
 
     bf16x8 q[kPgemmNT][4];
 #pragma unroll
     for (int s = 0; s < kPgemmNT; ++s) {
       const int L = jj + 16 * hl;
-      const uint8_t* cl = cb0 + lslot[s] * kPairCodeBytes + L * 16 + gh * 8;
-      const u32x2 c02 = *(const u32x2*)cl, c13 = *(const u32x2*)(cl + 512);
-      q[s][0] = codes_to_bf16(c02[0]);
-      q[s][2] = codes_to_bf16(c02[1]);
-      q[s][1] = codes_to_bf16(c13[0]);
-      q[s][3] = codes_to_bf16(c13[1]);
+      if constexpr (BITS == 4) {
+        const uint8_t* cl = cb0 + lslot[s] * kPairCodeBytes + L * 16 + gh * 8;
+        const u32x2 c02 = *(const u32x2*)cl, c13 = *(const u32x2*)(cl + 512);
+        q[s][0] = codes_to_bf16(c02[0]);
+        q[s][2] = codes_to_bf16(c02[1]);
+        q[s][1] = codes_to_bf16(c13[0]);
+        q[s][3] = codes_to_bf16(c13[1]);
+      } else if constexpr (BITS == 8) {
+        const uint8_t* cl = cb0 + lslot[s] * kSlotStage + L * 16;
+        const u32x4 c02 = *(const u32x4*)cl, c13 = *(const u32x4*)(cl + 512);
+        q[s][0] = bytes_to_bf16(c02[0], c02[1]);
+        q[s][2] = bytes_to_bf16(c02[2], c02[3]);
+        q[s][1] = bytes_to_bf16(c13[0], c13[1]);
+        q[s][3] = bytes_to_bf16(c13[2], c13[3]);
+      } else if constexpr (BITS == kFmtFp8) {
+        const uint8_t* cl = cb0 + lslot[s] * kSlotStage + L * 16;
+        const u32x4 c02 = *(const u32x4*)cl, c13 = *(const u32x4*)(cl + 512);
+        q[s][0] = fp8_to_bf16(c02[0], c02[1]);
+        q[s][2] = fp8_to_bf16(c02[2], c02[3]);
+        q[s][1] = fp8_to_bf16(c13[0], c13[1]);
+        q[s][3] = fp8_to_bf16(c13[2], c13[3]);
+      } else {
+        const uint32_t* cl = (const uint32_t*)(cb0 + lslot[s] * kSlotStage);
+        q[s][0] = six_to_bf16<0>(cl[L], cl[128 + L]);
+        q[s][2] = six_to_bf16<1>(cl[64 + L], cl[128 + L]);
+        q[s][1] = six_to_bf16<0>(cl[L + 32], cl[128 + L + 32]);
+        q[s][3] = six_to_bf16<1>(cl[64 + L + 32], cl[128 + L + 32]);
+      }
     }
     {
       const int row = rbase + j;
@@ -179,8 +221,9 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const ui
       }
     }
 
-    // activation sums of this wave's 32 rows (16 x 16 tiles)
-    {
+    // activation sums of this wave's 32 rows (16 x 16 tiles); block FP8 has
+    // no bias term and needs none
+    if constexpr (BITS != kFmtFp8) {
       const int i = lane & 15, kc = lane >> 4;
       float* sw = ssum + ((g / kPgemmChunk) & 1) * kPgemmRows * kPgemmChunk + gg;
 #pragma unroll
@@ -196,35 +239,62 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const ui
 
     // the previous chunk's bias term follows the fold of its next chunk's
     // first group; only then does this group's bias word join the new chunk
-    if constexpr (gh == 0) {
-      if (gg == 0 && g > 0) bias_chunk(g / kPgemmChunk - 1);
-    }
-    const bool take = ((gg >> 1) & 1) == hl;
+    if constexpr (BITS != kFmtFp8) {
+      if constexpr (gh == 0) {
+        if (gg == 0 && g > 0) bias_chunk(g / kPgemmChunk - 1);
+      }
+      const bool take = ((gg >> 1) & 1) == hl;
 #pragma unroll
-    for (int s = 0; s < kPgemmNT; ++s) {
-      if (take && gg < 4) bsel[s][0][gh] = w[s];
-      if (take && gg >= 4) bsel[s][1][gh] = w[s];
+      for (int s = 0; s < kPgemmNT; ++s) {
+        if (take && gg < 4) bsel[s][0][gh] = w[s];
+        if (take && gg >= 4) bsel[s][1][gh] = w[s];
+      }
     }
   };
 
-  // ---- pipeline (as pgemm_kernel's, two code loads per pair and wave) -----
-  issue_x(0);
-  issue_c(0);
-  for (int p = 0; p < P; ++p) {
-    const int g = 2 * p;
-    dma_wait_barrier<0>();
-    if (g + 1 < G) issue_x(g + 1);
-    if (p + 1 < P) issue_c(p + 1);
-    group(g, std::integral_constant<int, 0>{});
-    if (g + 1 < G) {
-      if (p + 1 < P) dma_wait_barrier<2>();
-      else dma_wait_barrier<0>();
-      if (g + 2 < G) issue_x(g + 2);
-      group(g + 1, std::integral_constant<int, 1>{});
+  // ---- pipeline (as pgemm_kernel's; 4-bit: two code loads per pair and
+  // wave, the wider codes: one group of codes in flight) ---------------------
+  if constexpr (BITS == 4) {
+    issue_x(0);
+    issue_c(0);
+    for (int p = 0; p < P; ++p) {
+      const int g = 2 * p;
+      dma_wait_barrier<0>();
+      if (g + 1 < G) issue_x(g + 1);
+      if (p + 1 < P) issue_c(p + 1);
+      group(g, std::integral_constant<int, 0>{});
+      if (g + 1 < G) {
+        if (p + 1 < P) dma_wait_barrier<2>();
+        else dma_wait_barrier<0>();
+        if (g + 2 < G) issue_x(g + 2);
+        group(g + 1, std::integral_constant<int, 1>{});
+      }
+    }
+  } else {
+    issue_x(0);
+    issue_cg(0);
+    issue_sb(0);
+    for (int p = 0; p < P; ++p) {
+      const int g = 2 * p;
+      dma_wait_barrier<0>();
+      if (g + 1 < G) {
+        issue_x(g + 1);
+        issue_cg(g + 1);
+      }
+      group(g, std::integral_constant<int, 0>{});
+      if (g + 1 < G) {
+        dma_wait_barrier<0>();
+        if (g + 2 < G) {
+          issue_x(g + 2);
+          issue_cg(g + 2);
+          issue_sb(p + 1);
+        }
+        group(g + 1, std::integral_constant<int, 1>{});
+      }
     }
   }
   dma_wait_barrier<0>();  // the last group's sums
-  bias_chunk((G - 1) / kPgemmChunk);
+  if constexpr (BITS != kFmtFp8) bias_chunk((G - 1) / kPgemmChunk);
 
   // ---- epilogue: element r of tile s is row rbase + 8 (r / 4) + 4 hl + r % 4
 #pragma unroll

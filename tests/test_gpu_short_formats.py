@@ -1,13 +1,14 @@
-"""Short windows of 6-bit, 8-bit and block-FP8 weights on the dataflow
-workgroups (one 32 x 32 tile each, products of several groups at once, folded
-in order) against the whole prompt on the wide 128 x 256 workgroups: every
-row's bits agree (TensorFold PR #1696, later revision, "Checks": a row alone
-equals the row inside a window; PR #1514, "What changes": the 4-, 6- and
-8-bit checkpoints served as stored; PR #1696, "Checks": block FP8 weights
-served weight-only). The whole prompt (8192 rows) is large enough for the
-wide kernel; the windows (1 to 1536 rows) run on the dataflow kernel, in one
-round, in its two-workgroups-per-CU SwiGLU form, and in several rounds (the
-wider codes use it up to 4 SwiGLU and 6 plain tiles per CU). One window per
+"""Short windows of 6-bit, 8-bit and block-FP8 weights against the whole
+prompt on the wide 128 x 256 workgroups: every row's bits agree (TensorFold
+PR #1696, later revision, "Checks": a row alone equals the row inside a
+window; PR #1514, "What changes": the 4-, 6- and 8-bit checkpoints served as
+stored; PR #1696, "Checks": block FP8 weights served weight-only). The whole
+prompt (8192 rows) is large enough for the wide kernel. The windows (1 to
+1536 rows) run on the two short-window kernels: on the dataflow workgroups
+(one 32 x 32 tile each, products of several groups at once, folded in order)
+in one round, in the two-workgroups-per-CU SwiGLU form and in up to four
+rounds of plain tiles; past that (1024- and 1536-row SwiGLU windows, the
+1536-row plain window) on the 64-column narrow workgroups. One window per
 case is also checked against the float64 oracle."""
 
 import numpy as np
