@@ -67,14 +67,18 @@ def test_short_windows_of_wider_codes_match_the_whole_prompt(fmt_case, swiglu, o
         assert np.array_equal(bits(y), ref[r0 : r0 + rows]), (r0, rows)
 
 
-def test_short_window_of_wider_codes_within_oracle_bound(fmt_case):
+@pytest.mark.parametrize("r0,nrows,rows", [(0, 96, [0, 37, 95]), (4096, 1024, [0, 513, 1023])])
+def test_short_window_of_wider_codes_within_oracle_bound(fmt_case, r0, nrows, rows):
+    """96 rows: dataflow workgroups for both products; 1024 rows: dataflow
+    workgroups for the plain product, narrow workgroups for SwiGLU."""
     fmt = fmt_case["fmt"]
-    say(f"short window fmt={fmt} against the oracle")
-    rows = [0, 37, 95]
-    xs = fmt_case["x"][:96][rows]
+    say(f"short window fmt={fmt} rows {r0}+{nrows} against the oracle")
+    xw = fmt_case["x"][r0 : r0 + nrows]
+    xs = xw[rows]
     a, b = fmt_case["a"], fmt_case["b"]
-    y = host_f64(_window(fmt, fmt_case["pa"], None, fmt_case["xd"][:96], torch.float32))[rows]
-    z = host_f64(_window(fmt, fmt_case["pa"], fmt_case["pb"], fmt_case["xd"][:96], torch.float32))[rows]
+    xd = fmt_case["xd"][r0 : r0 + nrows]
+    y = host_f64(_window(fmt, fmt_case["pa"], None, xd, torch.float32))[rows]
+    z = host_f64(_window(fmt, fmt_case["pa"], fmt_case["pb"], xd, torch.float32))[rows]
     if fmt == "fp8":
         a64 = oracle.matmul_rows_fp8(a.w8, a.scales, xs)
         c64 = oracle.matmul_rows_fp8(b.w8, b.scales, xs)
@@ -82,7 +86,7 @@ def test_short_window_of_wider_codes_within_oracle_bound(fmt_case):
         Tc = tol(oracle.error_weight_fp8(b.w8, b.scales, xs), K, order="window", fmt="fp8")
         assert np.all(np.abs(y - a64) <= Ta)
     else:
-        check_within(y, a, fmt_case["x"][:96], rows=rows, label=f"short window {fmt}-bit", order="window")
+        check_within(y, a, xw, rows=rows, label=f"short window {fmt}-bit", order="window")
         a64 = oracle.matmul_rows(a.wq, a.scales, a.biases, xs, bits=fmt)
         c64 = oracle.matmul_rows(b.wq, b.scales, b.biases, xs, bits=fmt)
         Ta = tol(oracle.error_weight(a.wq, a.scales, a.biases, xs, bits=fmt), K, order="window")
