@@ -598,8 +598,9 @@ def bench_c4(dev, reps=4):
 
 def bench_rows(dev, K):
     """The decode FFN step with R = 1, 2, 4, 8, 16 rows sharing it: qmv_ffn
-    (the dataflow step up to 4 rows, the barrier step beyond), and the two
-    calls with the float32 or fragment-ordered (Q4_BF16X3T) handoff."""
+    (one launch up to 2 rows, the two calls with the fragment-ordered handoff
+    beyond), and the two calls with the float32 or fragment-ordered
+    (Q4_BF16X3T) handoff."""
     import torch
 
     import bit_weight_only_q4g64_amd as q4

@@ -345,13 +345,9 @@ def qmm_cut(pa: torch.Tensor, pb: torch.Tensor | None, N: int, K: int, x: torch.
     return y
 
 
-# Barrier state in the qmv_ffn workspace (byte offsets of 32-bit words):
-# 16 arrival counters 128 bytes apart, a top counter, a generation, an error.
-FFN_COUNTER_STRIDE = 128
-FFN_TOP_OFFSET = 16 * 128
-FFN_GEN_OFFSET = 17 * 128
+# The qmv_ffn workspace (byte offsets of 32-bit words): the error word (1 once
+# a wait of the one-launch step gave up) and that step's call counter.
 FFN_ERR_OFFSET = 18 * 128
-# The dataflow step (up to 4 rows): its call counter, after the barrier state.
 FFN_FLOW_EPOCH_OFFSET = 4096
 
 
@@ -360,21 +356,21 @@ def ffn_work_bytes(N1: int, N2: int, R: int) -> int:
 
 
 def ffn_workspace(N1: int, N2: int, R: int, device="cuda") -> torch.Tensor:
-    """A zeroed workspace for qmv_ffn calls of 1..R rows (reusable by later calls on the same stream)."""
-    nbytes = max(ffn_work_bytes(N1, N2, r) for r in range(1, R + 1)) if R >= 1 else 0
+    """A zeroed workspace for qmv_ffn calls (any row count; reusable by later calls on the same stream)."""
+    nbytes = ffn_work_bytes(N1, N2, R)
     if nbytes == 0:
         raise Q4Error("q4g64_ffn_work_bytes", Q4_EINVAL, f"invalid N1={N1} N2={N2} R={R}")
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def ffn_error(work: torch.Tensor) -> int:
-    """The workspace's barrier error word (1 if a workgroup gave up waiting)."""
+    """The workspace's error word (1 if a workgroup of the one-launch step gave up waiting)."""
     return int(work[FFN_ERR_OFFSET : FFN_ERR_OFFSET + 4].view(torch.int32).item())
 
 
 def qmv_ffn(p1: torch.Tensor, p3: torch.Tensor, p2: torch.Tensor, N1: int, K1: int, N2: int, x: torch.Tensor, work: torch.Tensor,
             z: torch.Tensor | None = None, y: torch.Tensor | None = None):
-    """Decode FFN step in one launch: z = silu(W1 x) * (W3 x), y = W2 z (float32), for the 1..16 bf16 rows of x."""
+    """Decode FFN step: z = silu(W1 x) * (W3 x), y = W2 z (float32), for the 1..16 bf16 rows of x (one launch up to 2 rows, two from 3)."""
     for t, name in ((p1, "packed_w1"), (p3, "packed_w3"), (p2, "packed_w2"), (x, "x"), (work, "work")):
         _dev(t, name)
     if x.dtype != torch.bfloat16:

@@ -407,31 +407,20 @@ int check_window_args(const char* fn, const void* packed_a, const void* packed_b
   return Q4_OK;
 }
 
-template <int NV, int RTF, int SPW1, int SPW2>
-int ffn_launch_t(const uint8_t* p1, const uint8_t* p3, const uint8_t* p2, int N1, int K1, int N2, const uint16_t* x,
-                 int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, uint8_t* work, size_t lds, hipStream_t s) {
-  const int xl2 = q4::ffn_lds_bytes(K1, N1, R, true) <= q4::qmv_max_lds();
-  lds = q4::ffn_lds_bytes(K1, N1, R, xl2 != 0);
-  auto kern = q4::ffn_kernel<NV, RTF, SPW1, SPW2>;
-  static const bool lds_ok = q4::allow_max_dynamic_lds((const void*)kern);
-  (void)lds_ok;
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, q4::kFfnThreads, lds) != hipSuccess)
-    return fail(Q4_EDEVICE, "qmv_ffn: device query failed");
-  if (per_cu < 1) return fail(Q4_EUNSUPPORTED, "qmv_ffn: a %zu-byte workgroup does not fit on a CU", lds);
-  // every workgroup must be resident at once (the grid barrier waits for all)
-  const int pairs1 = (N1 / q4::kTileN + 1) / 2, items2 = 2 * (N2 / q4::kTileN);
-  int nwg = cus;
-  if (nwg > (pairs1 > items2 ? pairs1 : items2)) nwg = pairs1 > items2 ? pairs1 : items2;
-  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(q4::kFfnThreads), lds, s, p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work,
-                     xl2);
-  return launched("qmv_ffn");
-}
-
-// The dataflow step (R <= 4, whole 256-wide segments in K1 and N1): one
-// workgroup per CU, every one resident at once.
-bool ffn_flow_applies(int64_t N1, int64_t K1, int R) { return R <= q4::kFlowMaxRows && K1 % 256 == 0 && N1 % 256 == 0; }
+// The one-launch dataflow step (up to 2 rows, whole 256-wide segments in K1
+// and N1): one workgroup per CU, every one resident at once. From 3 rows the
+// two decode calls are faster (w1/w3 + SwiGLU 8192 x 2048 then w2 2048 x
+// 8192, us: 4 rows 20.1 / 15.3, 8 rows 33.1 / 16.0 for the grid-barrier
+// launch this replaced, 16 rows 53.7 / 20.0); at 1 and 2 rows the one launch
+// is (11.8 / 13.3, 13.0 / 14.1).
+constexpr int kFfnFlowRows = 2;
+bool ffn_flow_applies(int64_t N1, int64_t K1, int R) { return R <= kFfnFlowRows && K1 % 256 == 0 && N1 % 256 == 0; }
+// Workspace: the error word and the dataflow step's state (call counter,
+// tagged z, hand-overs) for up to kFfnFlowRows rows, then, 256-byte aligned,
+// the fragment-ordered planes of z for up to 16 rows, which the two-call
+// schedule hands from the first call to the second. The size does not depend
+// on R, so one workspace serves every row count.
+size_t ffn_planes_off(int64_t N1, int64_t N2) { return (q4::flow_work_bytes(N1, N2, kFfnFlowRows) + 255) / 256 * 256; }
 
 template <int NV, int SPW1>
 int flow_launch_t(const uint8_t* p1, const uint8_t* p3, const uint8_t* p2, int N1, int K1, int N2, const uint16_t* x, int64_t ldx,
@@ -458,21 +447,6 @@ int flow_launch_s1(int spw1, const uint8_t* p1, const uint8_t* p3, const uint8_t
                    int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, uint8_t* work, hipStream_t s) {
   if (spw1 <= 1) return flow_launch_t<NV, 1>(p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, s);
   return flow_launch_t<NV, 2>(p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, s);
-}
-
-template <int NV, int RTF, int SPW1>
-int ffn_launch_s2(int spw2, const uint8_t* p1, const uint8_t* p3, const uint8_t* p2, int N1, int K1, int N2, const uint16_t* x,
-                  int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, uint8_t* work, size_t lds, hipStream_t s) {
-  if (spw2 <= 1) return ffn_launch_t<NV, RTF, SPW1, 1>(p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
-  return ffn_launch_t<NV, RTF, SPW1, 2>(p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
-}
-
-template <int NV, int RTF>
-int ffn_launch_s1(int spw1, int spw2, const uint8_t* p1, const uint8_t* p3, const uint8_t* p2, int N1, int K1, int N2,
-                  const uint16_t* x, int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, uint8_t* work, size_t lds,
-                  hipStream_t s) {
-  if (spw1 <= 1) return ffn_launch_s2<NV, RTF, 1>(spw2, p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
-  return ffn_launch_s2<NV, RTF, 2>(spw2, p1, p3, p2, N1, K1, N2, x, ldx, R, z, ldz, y, ldy, work, lds, s);
 }
 
 // The rows of a window (a cut) must lie within 2^48 elements of x and of y.
@@ -744,10 +718,7 @@ int qmm_cut_qg64(int bits, const void* packed_a, const void* packed_b, int64_t N
 
 size_t q4g64_ffn_work_bytes(int64_t N1, int64_t N2, int R) {
   if (N1 <= 0 || N1 % 64 != 0 || N1 > kFfnMaxN1 || N2 <= 0 || N2 % 64 != 0 || N2 > kMaxDim || R < 1 || R > 16) return 0;
-  // the dataflow step's tagged copies exist for R <= 4 (whole segments of N1;
-  // K1 is checked at the call); the barrier state for every R
-  if (R <= q4::kFlowMaxRows && N1 % 256 == 0) return q4::flow_work_bytes(N1, N2, R);
-  return q4::kFfnWorkBytes;
+  return ffn_planes_off(N1, N2) + (size_t)q4::qmv_x3t_bytes(N1, 16);
 }
 
 int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2, int64_t N1, int64_t K1, int64_t N2,
@@ -769,29 +740,32 @@ int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2,
   if (int rc = check_ld(fn, "ldy", ldy)) return rc;
   if ((int64_t)R * ldx * 2 >= (int64_t(1) << 31))
     return fail(Q4_EUNSUPPORTED, "%s: R * ldx spans more than 2 GiB of activations", fn);
-  // 8 waves per w1/w3 tile and 16 per w2 half-tile, up to 2 segments each
-  // (a 1024-thread workgroup leaves 128 registers per lane; more segments spill)
-  if (K1 > kFfnMaxK1) return fail(Q4_EUNSUPPORTED, "%s: K1=%lld exceeds the one-launch step limit of 4096", fn, (long long)K1);
-  if (N1 > kFfnMaxN1) return fail(Q4_EUNSUPPORTED, "%s: N1=%lld exceeds the one-launch step limit of 8192", fn, (long long)N1);
-  const size_t lds = q4::ffn_lds_bytes(K1, N1, R, false);
-  if (lds > q4::qmv_max_lds()) return fail(Q4_EUNSUPPORTED, "%s: K1=%lld with R=%d needs %zu bytes of LDS", fn, (long long)K1, R, lds);
-  const int nseg1 = q4::qmv_segments(K1), nseg2 = q4::qmv_segments(N1);
-  const int spw1 = (nseg1 + q4::kFfnP1Waves - 1) / q4::kFfnP1Waves, spw2 = (nseg2 + q4::kFfnWaves - 1) / q4::kFfnWaves;
+  // the dataflow step's shape limits (8 waves per w1/w3 tile and 16 per w2
+  // half-tile, up to 2 segments each; a 1024-thread workgroup leaves 128
+  // registers per lane), kept for every row count
+  if (K1 > kFfnMaxK1) return fail(Q4_EUNSUPPORTED, "%s: K1=%lld exceeds the decode FFN step limit of 4096", fn, (long long)K1);
+  if (N1 > kFfnMaxN1) return fail(Q4_EUNSUPPORTED, "%s: N1=%lld exceeds the decode FFN step limit of 8192", fn, (long long)N1);
   const uint8_t *a = (const uint8_t*)packed_w1, *c = (const uint8_t*)packed_w3, *d = (const uint8_t*)packed_w2;
   uint8_t* w = (uint8_t*)work;
   hipStream_t s = (hipStream_t)stream;
   const int n1 = (int)N1, k1 = (int)K1, n2 = (int)N2;
-  const int nv = q4::qmv_nv(R), rtf = q4::qmv_row_tiles(1, R);
   if (ffn_flow_applies(N1, K1, R) && q4::flow_lds_bytes(K1, R) <= q4::qmv_max_lds()) {
-    if (nv == 1) return flow_launch_s1<1>(spw1, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, s);
-    if (nv == 2) return flow_launch_s1<2>(spw1, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, s);
-    return flow_launch_s1<4>(spw1, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, s);
+    const int spw1 = (q4::qmv_segments(K1) + q4::kFfnP1Waves - 1) / q4::kFfnP1Waves;
+    if (R == 1) return flow_launch_s1<1>(spw1, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, s);
+    return flow_launch_s1<2>(spw1, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, s);
   }
-  if (nv == 1) return ffn_launch_s1<1, 1>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
-  if (nv == 2) return ffn_launch_s1<2, 1>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
-  if (rtf == 1) return ffn_launch_s1<4, 1>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
-  if (rtf == 2) return ffn_launch_s1<4, 2>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
-  return ffn_launch_s1<4, 4>(spw1, spw2, a, c, d, n1, k1, n2, x, ldx, R, z, ldz, y, ldy, w, lds, s);
+  // two calls: w1/w3 + SwiGLU writing z as float32 rows and as its
+  // fragment-ordered planes in the workspace, then w2 reading the planes
+  // (the same bits as from the float32 rows)
+  if (q4::qmv_lds_bytes(K1, 0, 2, R) > kMaxLds || q4::qmv_lds_bytes(N1, 1, 1, R) > kMaxLds)
+    return fail(Q4_EUNSUPPORTED, "%s: K1=%lld, N1=%lld with R=%d exceed the decode partials' LDS", fn, (long long)K1, (long long)N1, R);
+  uint16_t* planes = (uint16_t*)(w + ffn_planes_off(N1, N2));
+  q4::QmvSplit sp{1, nullptr, nullptr};
+  sp.z32 = z;
+  sp.ldz32 = ldz;
+  q4::qmv_launch(a, c, 2, n1, k1, x, 0, ldx, R, (float*)planes, N1, s, 4, 2, sp);
+  q4::qmv_launch(d, d, 1, n2, n1, planes, 3, N1, R, y, ldy, s, 4);
+  return launched(fn);
 }
 
 size_t fp8b_packed_bytes(int64_t N, int64_t K) { return packed_bytes_impl(8, N, K); }

@@ -38,8 +38,8 @@
 
 namespace q4 {
 
-// Workspace layout (bytes). The barrier kernel's state occupies the first
-// 4096 bytes and its error word (kFfnErrOff) is shared.
+// Workspace layout (bytes): the error word at kFfnErrOff, then from byte
+// 4096 this step's state.
 constexpr size_t kFlowEpochOff = 4096;        // call counter
 constexpr size_t kFlowZOff = 4096 + 256;      // tagged z: [R][N1] of {bits, tag}
 constexpr int kFlowMaxRows = 4;

@@ -309,6 +309,10 @@ struct QmvSplit {
   int nshare;     // workgroups per column tile along z (1: no split)
   float* part;    // [tile id][segment][values per segment], tile id = x + gridDim.x * y
   uint32_t* cnt;  // [tile id] arrival counters, zero between calls
+  // fused SwiGLU writing fragment-ordered planes (Y3 = 2): when set, the
+  // same values also as float32 rows [R][ldz32]
+  float* z32 = nullptr;
+  int64_t ldz32 = 0;
 };
 
 template <int XF32, int NMAT, int SPW, int RTF, bool XLDS, int NV, int BITS, int Y3 = 0>
@@ -607,6 +611,7 @@ __global__ __launch_bounds__(kQmvMaxWaves * 64) void qmv_kernel(const uint8_t* _
         y3[qmv_x3t_offset((int)n, r, 0, tiles)] = (uint16_t)h;
         y3[qmv_x3t_offset((int)n, r, 1, tiles)] = (uint16_t)m;
         y3[qmv_x3t_offset((int)n, r, 2, tiles)] = (uint16_t)l;
+        if (sp.z32 != nullptr) sp.z32[(int64_t)r * sp.ldz32 + n] = out;
       } else {
         y[(int64_t)r * ldy + n] = out;
       }

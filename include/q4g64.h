@@ -261,32 +261,31 @@ int qmm_cut(const void* packed_a, const void* packed_b, int64_t N, int64_t K, co
 int qmm_cut_qg64(int bits, const void* packed_a, const void* packed_b, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
                  const int64_t* window_rows, int n_windows, void* y, int y_dtype, int64_t ldy, void* stream);
 
-/* Decode FFN step in one launch (PR #1696, "What it adds": w1 + w3 + SwiGLU
- * in one pass; PR #1514, "What changes": the fusion keeps every rounding
- * boundary):
+/* Decode FFN step (PR #1696, "What it adds": w1 + w3 + SwiGLU in one pass;
+ * PR #1514, "What changes": the fusion keeps every rounding boundary):
  *   z = silu(W1 x) * (W3 x)   float32 [R][ldz], bit-identical to qmv_w13_swiglu;
  *   y = W2 z                  float32 [R][ldy], bit-identical to qmv_rows on z
  *                             with x_dtype = Q4_F32.
  * W1, W3: N1 x K1 packed; W2: N2 x N1 packed. x bf16 [R][ldx], R = 1..16.
  * work: a DEVICE buffer of q4g64_ffn_work_bytes(N1, N2, R) bytes (0 means
- * the arguments are invalid), 256-byte aligned, zero-filled by the caller
- * before its first use; every completed call leaves it ready for the next,
- * and one workspace serves any later call of a shape it is large enough for
- * (calls on one workspace must not run concurrently).
- * Two schedules, both one workgroup per CU with every workgroup resident at
- * once (the call needs the whole device):
- *   - R <= 4 with K1 and N1 multiples of 256: a dataflow step. Each z value
- *     is also stored in the workspace with this call's number (a counter in
- *     the workspace that every call advances), and each w2 k segment starts
- *     as soon as its 256 z values carry that number; the two halves of K of
- *     a w2 tile hand over a running sum the same way. No workgroup waits for
- *     the whole grid. The workspace holds 4352 + 8 R N1 + 32 N2 bytes.
- *   - otherwise: z is written out, all workgroups meet at one grid barrier,
- *     then w2 runs; the workspace holds the barrier state (4096 bytes).
- * A workgroup that waits more than about 20 ms gives up, sets the 32-bit
- * word at byte 2304 of work to 1 and leaves y undefined; the workspace must
- * then be zero-filled again. Limits: K1 <= 4096, N1 <= 8192, and the staged
- * activations must fit in LDS (Q4_EUNSUPPORTED otherwise). */
+ * the arguments are invalid; the size does not depend on R), 256-byte
+ * aligned, zero-filled by the caller before its first use; every completed
+ * call leaves it ready for the next, and one workspace serves any later call
+ * with the same N1 and N2 and any R (calls on one workspace must not run
+ * concurrently). Two schedules:
+ *   - R <= 2 with K1 and N1 multiples of 256: one launch, one workgroup per
+ *     CU with every workgroup resident at once (the call needs the whole
+ *     device). Each z value is also stored in the workspace with this call's
+ *     number (a counter in the workspace that every such call advances), and
+ *     each w2 k segment starts as soon as its 256 z values carry that number;
+ *     the two halves of K of a w2 tile hand over a running sum the same way.
+ *     No workgroup waits for the whole grid. A workgroup that waits more than
+ *     about 20 ms gives up, sets the 32-bit word at byte 2304 of work to 1 and
+ *     leaves y undefined; the workspace must then be zero-filled again.
+ *   - otherwise: two launches, w1/w3 + SwiGLU writing z and its three exact
+ *     bf16 pieces in fragment order (Q4_BF16X3T) into the workspace, then w2
+ *     reading those (qmv_rows gives the same bits for them as for z).
+ * Limits: K1 <= 4096, N1 <= 8192 (Q4_EUNSUPPORTED otherwise). */
 size_t q4g64_ffn_work_bytes(int64_t N1, int64_t N2, int R);
 int qmv_ffn(const void* packed_w1, const void* packed_w3, const void* packed_w2, int64_t N1, int64_t K1, int64_t N2,
             const uint16_t* x, int64_t ldx, int R, float* z, int64_t ldz, float* y, int64_t ldy, void* work, void* stream);

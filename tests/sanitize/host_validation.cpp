@@ -116,12 +116,13 @@ void sizes() {
   SIZE(qmv_split_work_bytes(4, 128, 512, Q4_BF16, 1, 17), 0);
   SIZE(qmv_split_work_bytes(4, 128, 512, Q4_BF16, 1, IMAX), 0);
   TRUE(qmv_split_noalloc_max_bytes() >= (size_t(1) << 20));
-  // one-launch FFN workspace: the dataflow step for R <= 4 with N1 % 256 == 0
-  SIZE(q4g64_ffn_work_bytes(256, 128, 1), 4352 + 8 * 1 * 256 + 32 * 128);
-  SIZE(q4g64_ffn_work_bytes(8192, 4096, 4), 4352 + 8 * 4 * 8192 + 32 * 4096);
-  SIZE(q4g64_ffn_work_bytes(192, 128, 1), 4096);
-  SIZE(q4g64_ffn_work_bytes(256, 128, 5), 4096);
-  SIZE(q4g64_ffn_work_bytes(256, 128, 16), 4096);
+  // decode FFN workspace: the one-launch step's state for up to 2 rows, then
+  // the two-call step's fragment-ordered planes for up to 16 rows; any R
+  SIZE(q4g64_ffn_work_bytes(256, 128, 1), 4352 + 8 * 2 * 256 + 32 * 128 + 128 * 256);
+  SIZE(q4g64_ffn_work_bytes(8192, 4096, 4), 4352 + 8 * 2 * 8192 + 32 * 4096 + 128 * 8192);
+  SIZE(q4g64_ffn_work_bytes(192, 128, 1), 4352 + 8 * 2 * 192 + 32 * 128 + 128 * 192);
+  SIZE(q4g64_ffn_work_bytes(256, 128, 5), 4352 + 8 * 2 * 256 + 32 * 128 + 128 * 256);
+  SIZE(q4g64_ffn_work_bytes(256, 128, 16), 4352 + 8 * 2 * 256 + 32 * 128 + 128 * 256);
   SIZE(q4g64_ffn_work_bytes(0, 128, 1), 0);
   SIZE(q4g64_ffn_work_bytes(256, 100, 1), 0);
   SIZE(q4g64_ffn_work_bytes(8192 + 256, 128, 1), 0);

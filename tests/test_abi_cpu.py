@@ -192,14 +192,18 @@ def test_binding_refuses_host_tensors():
 
 
 def test_ffn_work_bytes():
-    # up to 4 rows with whole 256-wide segments of N1: the barrier state (4 KiB),
-    # the call counter block (256 B), the tagged z copy (8 B per value) and the
-    # lower-half sums (64 lanes x 8 B per 16-column tile of w2)
-    assert q4.ffn_work_bytes(8192, 2048, 1) == 4096 + 256 + 8192 * 8 + 128 * 512
-    assert q4.ffn_work_bytes(8192, 2048, 4) == 4096 + 256 + 4 * 8192 * 8 + 128 * 512
-    # otherwise the barrier state only
-    assert q4.ffn_work_bytes(8192, 2048, 5) == 4096
-    assert q4.ffn_work_bytes(64, 64, 1) == 4096
+    # the error word and the call counter block (4352 B), the one-launch step's
+    # tagged z copy for up to 2 rows (8 B per value) and lower-half sums (64
+    # lanes x 8 B per 16-column tile of w2); then the fragment-ordered planes
+    # the two-call step hands over, for up to 16 rows (4 piece slots of 2 B
+    # per row and k). No dependence on R.
+    def size(N1, N2):
+        head = 4352 + 2 * N1 * 8 + (N2 // 16) * 512
+        return (head + 255) // 256 * 256 + N1 * 4 * 2 * 16
+    for R in (1, 2, 3, 4, 5, 16):
+        assert q4.ffn_work_bytes(8192, 2048, R) == size(8192, 2048) == 1249536
+    assert q4.ffn_work_bytes(64, 64, 1) == size(64, 64)
+    assert q4.ffn_work_bytes(192, 128, 3) == size(192, 128)
     for bad in ((0, 64, 1), (100, 64, 1), (8192, 64, 0), (8192, 64, 17), (32768, 64, 1), (8192, 100, 1), (8192, 0, 1)):
         assert q4.ffn_work_bytes(*bad) == 0
 

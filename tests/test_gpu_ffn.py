@@ -1,10 +1,11 @@
-"""The one-launch decode FFN step (qmv_ffn) on the GPU.
+"""The decode FFN step (qmv_ffn) on the GPU: one launch up to 2 rows, two
+launches (z handed over as fragment-ordered planes in the workspace) from 3.
 
 It must return exactly the bits of the two-call composition
 qmv_w13_swiglu -> qmv_rows (float32 input), whose parity with the float64
 oracle the decode tests establish; every row must equal its one-row result;
-the workspace's barrier state must survive repeated calls and graph replays;
-and its error word must stay 0."""
+the workspace's state must survive repeated calls, changing row counts and
+graph replays; and its error word must stay 0."""
 
 import numpy as np
 import pytest
@@ -92,9 +93,9 @@ def test_rows_equal_composition_and_one_row(c1, R):
 
 @pytest.mark.parametrize("R", [1, 5])
 def test_repeated_calls_reuse_the_workspace(c1, R):
-    """Five calls on one workspace: one row runs the dataflow step (its call
-    counter advances once per call), five rows
-    the barrier step (one barrier generation per call, counters back at 0)."""
+    """Five calls on one workspace: one row runs the one-launch step (its call
+    counter advances once per call), five rows the two calls (which leave the
+    counter alone)."""
     w1, w2 = c1["w1"], c1["w2"]
     N1, K1, N2 = w1.N, w1.K, w2.N
     say(f"qmv_ffn c1 five calls on one workspace R={R}")
@@ -110,17 +111,12 @@ def test_repeated_calls_reuse_the_workspace(c1, R):
         assert np.array_equal(cur[0], ref[0]) and np.array_equal(cur[1], ref[1])
     state = work.view(torch.int32).cpu().numpy()
     assert state[q4.FFN_ERR_OFFSET // 4] == 0
-    if R == 1:
-        assert state[q4.FFN_FLOW_EPOCH_OFFSET // 4] == 5
-    else:
-        counters = state[[c * q4.FFN_COUNTER_STRIDE // 4 for c in range(16)]]
-        assert np.all(counters == 0) and state[q4.FFN_TOP_OFFSET // 4] == 0  # arrival counts back at 0
-        assert state[q4.FFN_GEN_OFFSET // 4] == 5  # one barrier generation per call
+    assert state[q4.FFN_FLOW_EPOCH_OFFSET // 4] == (5 if R == 1 else 0)
 
 
 def test_new_inputs_each_call_on_one_workspace(c1):
     """Eight calls in a row on one workspace, each with new activations and
-    row counts 1..4 and 7 (the dataflow and the barrier step in turn): every
+    row counts 1..4 and 7 (the one-launch and the two-call step in turn): every
     result equals the composition of the two decode calls, so no call reads
     values an earlier call left in the workspace."""
     w1, w2 = c1["w1"], c1["w2"]
@@ -155,14 +151,16 @@ def test_shapes_equal_composition(N1, K1, N2, R):
     assert np.array_equal(bits32(y), bits32(yc))
 
 
-def test_graph_replays_equal_eager(c1):
+@pytest.mark.parametrize("R", [1, 4])
+def test_graph_replays_equal_eager(c1, R):
+    """One row: the one-launch step; four rows: the two launches."""
     w1, w2 = c1["w1"], c1["w2"]
     N1, K1, N2 = w1.N, w1.K, w2.N
-    say("qmv_ffn c1 in a HIP graph, four replays")
-    x = dev_bf16(c1["x"])
-    work = q4.ffn_workspace(N1, N2, 1, DEV)
-    z = torch.empty((1, N1), dtype=torch.float32, device=DEV)
-    y = torch.empty((1, N2), dtype=torch.float32, device=DEV)
+    say(f"qmv_ffn c1 in a HIP graph, four replays, R={R}")
+    x = dev_bf16(c1["x"] if R == 1 else synthetic.draw_bf16_rows(np.random.default_rng(11), R, K1))
+    work = q4.ffn_workspace(N1, N2, R, DEV)
+    z = torch.empty((R, N1), dtype=torch.float32, device=DEV)
+    y = torch.empty((R, N2), dtype=torch.float32, device=DEV)
     z_ref, y_ref = q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x, work)
     torch.cuda.synchronize()
     zr, yr = bits32(z_ref), bits32(y_ref)
