@@ -157,11 +157,6 @@ __device__ __forceinline__ bf16x8 ones_bf16x8() {
   return __builtin_bit_cast(bf16x8, one);
 }
 
-__device__ __forceinline__ bf16x8 zero_bf16x8() {
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  return __builtin_bit_cast(bf16x8, z);
-}
-
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -200,9 +195,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 constexpr uint32_t kOffBuffer = 0x80000000u;
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 // The same with the non-temporal (streaming) cache policy, for data a launch
 // reads exactly once (the decode kernels' weights): measured 6% off the
