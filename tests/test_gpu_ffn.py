@@ -183,3 +183,24 @@ def test_graph_replays_equal_eager(c1, R):
         q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x, work)
         torch.cuda.synchronize()
     assert q4.ffn_error(work) == 0
+
+
+@pytest.mark.parametrize("R", [2, 6])
+def test_padded_outputs_keep_their_padding(c1, R):
+    """z and y as views of wider buffers (row strides N + 64): the rows hold
+    the composition's bits and the padding is untouched, on the one-launch
+    step (2 rows) and the two launches (6 rows)."""
+    w1, w2 = c1["w1"], c1["w2"]
+    N1, K1, N2 = w1.N, w1.K, w2.N
+    say(f"qmv_ffn c1 padded z and y, R={R}")
+    x = dev_bf16(synthetic.draw_bf16_rows(np.random.default_rng(21 + R), R, K1))
+    work = q4.ffn_workspace(N1, N2, R, DEV)
+    zbuf = torch.full((R, N1 + 64), -7.0, dtype=torch.float32, device=DEV)
+    ybuf = torch.full((R, N2 + 64), -7.0, dtype=torch.float32, device=DEV)
+    q4.qmv_ffn(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x, work, z=zbuf[:, :N1], y=ybuf[:, :N2])
+    zc, yc = _composed(c1["p1"], c1["p3"], c1["p2"], N1, K1, N2, x)
+    torch.cuda.synchronize()
+    assert q4.ffn_error(work) == 0
+    assert np.array_equal(bits32(zbuf[:, :N1]), bits32(zc))
+    assert np.array_equal(bits32(ybuf[:, :N2]), bits32(yc))
+    assert torch.all(zbuf[:, N1:] == -7.0) and torch.all(ybuf[:, N2:] == -7.0)
