@@ -92,3 +92,47 @@ def test_short_window_of_wider_codes_within_oracle_bound(fmt_case, r0, nrows, ro
         Ta = tol(oracle.error_weight(a.wq, a.scales, a.biases, xs, bits=fmt), K, order="window")
         Tc = tol(oracle.error_weight(b.wq, b.scales, b.biases, xs, bits=fmt), K, order="window")
     assert np.all(np.abs(z - oracle.swiglu(a64, c64)) <= tol_swiglu(a64, c64, Ta, Tc))
+
+
+@pytest.mark.parametrize("fmt", [6, 8, "fp8"])
+def test_narrow_workgroups_odd_shape(fmt):
+    """N = 1088 (17 narrow workgroups of 64 columns, 34 of 32 for SwiGLU; the
+    wide workgroups' last column block is partly past N) and K = 64 * 9 (the
+    last group pair half empty), on windows of 1024 and 2048 rows that take
+    the narrow workgroups. Their rows equal the whole prompt's (8192 rows,
+    wide workgroups) bit for bit, and sampled rows are within the window
+    bound of the float64 oracle."""
+    N2, K2, M2 = 1088, 64 * 9, 8192
+    say(f"narrow workgroups fmt={fmt} N={N2} K={K2}")
+    rng = np.random.default_rng(1088 + (9 if fmt == "fp8" else fmt))
+    if fmt == "fp8":
+        a, b = synthetic.draw_fp8_weight(rng, "a", N2, K2), synthetic.draw_fp8_weight(rng, "b", N2, K2)
+    else:
+        a, b = synthetic.draw_qweight(rng, "a", N2, K2, bits=fmt), synthetic.draw_qweight(rng, "b", N2, K2, bits=fmt)
+    pa, pb = _pack(fmt, a), _pack(fmt, b)
+    x = synthetic.draw_bf16_rows(rng, M2, K2)
+    xd = dev_bf16(x)
+
+    def win(p_b, xs):
+        if fmt == "fp8":
+            return q4.qmm_window_fp8b(pa, p_b, N2, K2, xs, out_dtype=torch.float32)
+        return q4.qmm_window(pa, p_b, N2, K2, xs, bits=fmt, out_dtype=torch.float32)
+
+    for p_b, r0, rows in ((None, 1000, 2048), (pb, 3000, 1024)):
+        ref = bits32(win(p_b, xd))
+        y = win(p_b, xd[r0 : r0 + rows])
+        torch.cuda.synchronize()
+        assert np.array_equal(bits32(y), ref[r0 : r0 + rows]), (p_b is None, r0, rows)
+    sample = [0, 511, 1023]
+    xs = x[3000:4024][sample]
+    z = host_f64(win(pb, xd[3000:4024]))[sample]
+    if fmt == "fp8":
+        a64, c64 = oracle.matmul_rows_fp8(a.w8, a.scales, xs), oracle.matmul_rows_fp8(b.w8, b.scales, xs)
+        Ta = tol(oracle.error_weight_fp8(a.w8, a.scales, xs), K2, order="window", fmt="fp8")
+        Tc = tol(oracle.error_weight_fp8(b.w8, b.scales, xs), K2, order="window", fmt="fp8")
+    else:
+        a64 = oracle.matmul_rows(a.wq, a.scales, a.biases, xs, bits=fmt)
+        c64 = oracle.matmul_rows(b.wq, b.scales, b.biases, xs, bits=fmt)
+        Ta = tol(oracle.error_weight(a.wq, a.scales, a.biases, xs, bits=fmt), K2, order="window")
+        Tc = tol(oracle.error_weight(b.wq, b.scales, b.biases, xs, bits=fmt), K2, order="window")
+    assert np.all(np.abs(z - oracle.swiglu(a64, c64)) <= tol_swiglu(a64, c64, Ta, Tc))
