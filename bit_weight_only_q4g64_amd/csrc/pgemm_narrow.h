@@ -157,6 +157,37 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const ui
     }
   };
 
+  // Group g's products are folded at the start of group g + 1 (the last
+  // group's after the loop), so acc still takes fold(0), fold(1), ... in
+  // ascending order, each chunk's bias term after the fold of the next
+  // chunk's first group, exactly as in pgemm_kernel.
+  f32x16 Pd[kPgemmNT];
+  float scd[kPgemmNT];
+  uint32_t wd[kPgemmNT];
+#pragma unroll
+  for (int s = 0; s < kPgemmNT; ++s) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Pd[s][r] = 0.f;
+    scd[s] = 0.f;
+    wd[s] = 0u;
+  }
+  // after the fold of group gp (half ghp of its pair): the previous chunk's
+  // bias term when gp opens a chunk (its sums are visible since the barrier
+  // of the group that follows gp), then gp's bias word joins its chunk
+  auto prev_bias = [&](int gp, auto ghpc) {
+    constexpr int ghp = decltype(ghpc)::value;
+    const int ggp = gp & (kPgemmChunk - 1);
+    if constexpr (ghp == 0) {
+      if (ggp == 0 && gp > 0) bias_chunk(gp / kPgemmChunk - 1);
+    }
+    const bool take = gp >= 0 && ((ggp >> 1) & 1) == hl;
+#pragma unroll
+    for (int s = 0; s < kPgemmNT; ++s) {
+      if (take && ggp < 4) bsel[s][0][ghp] = wd[s];
+      if (take && ggp >= 4) bsel[s][1][ghp] = wd[s];
+    }
+  };
+
   // one group; gh (compile time) is the group's half of its pair
   auto group = [&](int g, auto ghc) {
     constexpr int gh = decltype(ghc)::value;
@@ -206,6 +237,12 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const ui
         q[s][3] = six_to_bf16<1>(cl[64 + L + 32], cl[128 + L + 32]);
       }
     }
+    // keeps the previous group's fold below the DMA issue that precedes
+    // this group (the compiler would otherwise hoist it there, ahead of
+    // this group's reads, where nothing hides it)
+    static_assert(kPgemmNT == 2, "one register per column tile below");
+    asm volatile("" : "+v"(scd[0]), "+v"(scd[1]));
+    f32x16 Pn[kPgemmNT];
     {
       const int row = rbase + j;
       bf16x8 xa[4];
@@ -213,13 +250,18 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const ui
       for (int ks = 0; ks < 4; ++ks) xa[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, 2 * ks + hl)));
 #pragma unroll
       for (int s = 0; s < kPgemmNT; ++s) {
-        f32x16 Pm = mfma32(xa[0], q[s][0], f32x16{});
+        Pn[s] = mfma32(xa[0], q[s][0], f32x16{});
 #pragma unroll
-        for (int ks = 1; ks < 4; ++ks) Pm = mfma32(xa[ks], q[s][ks], Pm);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[s][r] = __builtin_fmaf(sc[s], Pm[r], acc[s][r]);
+        for (int ks = 1; ks < 4; ++ks) Pn[s] = mfma32(xa[ks], q[s][ks], Pn[s]);
       }
     }
+    // the previous group's fold: independent of this group's matrix steps,
+    // so it can issue while they run (for g = 0: fma(0, 0, +0) = +0 leaves
+    // acc as it is)
+#pragma unroll
+    for (int s = 0; s < kPgemmNT; ++s)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[s][r] = __builtin_fmaf(scd[s], Pd[s][r], acc[s][r]);
 
     // activation sums of this wave's 32 rows (16 x 16 tiles); block FP8 has
     // no bias term and needs none
@@ -233,22 +275,19 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const ui
         const bf16x8 xa1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xb + xs_off(row, kc + 4)));
         f32x4 S = mfma16(ones, xa0, f32x4{0.f, 0.f, 0.f, 0.f});
         S = mfma16(ones, xa1, S);
-        if (kc == 0) sw[row * kPgemmChunk] = S[0];
+        // every row of the ones-product holds the same sums, so all four
+        // lanes of a column store the same value (no divergent branch)
+        sw[row * kPgemmChunk] = S[0];
       }
     }
 
-    // the previous chunk's bias term follows the fold of its next chunk's
-    // first group; only then does this group's bias word join the new chunk
-    if constexpr (BITS != kFmtFp8) {
-      if constexpr (gh == 0) {
-        if (gg == 0 && g > 0) bias_chunk(g / kPgemmChunk - 1);
-      }
-      const bool take = ((gg >> 1) & 1) == hl;
+    // the previous group's bias step, now that its fold is in acc
+    if constexpr (BITS != kFmtFp8) prev_bias(g - 1, std::integral_constant<int, 1 - gh>{});
 #pragma unroll
-      for (int s = 0; s < kPgemmNT; ++s) {
-        if (take && gg < 4) bsel[s][0][gh] = w[s];
-        if (take && gg >= 4) bsel[s][1][gh] = w[s];
-      }
+    for (int s = 0; s < kPgemmNT; ++s) {
+      Pd[s] = Pn[s];
+      scd[s] = sc[s];
+      wd[s] = w[s];
     }
   };
 
@@ -294,7 +333,16 @@ __global__ __launch_bounds__(kPgemmThreads, 2) void pgemm_narrow_kernel(const ui
     }
   }
   dma_wait_barrier<0>();  // the last group's sums
-  if constexpr (BITS != kFmtFp8) bias_chunk((G - 1) / kPgemmChunk);
+  // the last group's fold and bias step, then its chunk's bias term
+#pragma unroll
+  for (int s = 0; s < kPgemmNT; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[s][r] = __builtin_fmaf(scd[s], Pd[s][r], acc[s][r]);
+  if constexpr (BITS != kFmtFp8) {
+    if ((G - 1) & 1) prev_bias(G - 1, std::integral_constant<int, 1>{});
+    else prev_bias(G - 1, std::integral_constant<int, 0>{});
+    bias_chunk((G - 1) / kPgemmChunk);
+  }
 
   // ---- epilogue: element r of tile s is row rbase + 8 (r / 4) + 4 hl + r % 4
 #pragma unroll
