@@ -136,3 +136,39 @@ def test_narrow_workgroups_odd_shape(fmt):
         Ta = tol(oracle.error_weight(a.wq, a.scales, a.biases, xs, bits=fmt), K2, order="window")
         Tc = tol(oracle.error_weight(b.wq, b.scales, b.biases, xs, bits=fmt), K2, order="window")
     assert np.all(np.abs(z - oracle.swiglu(a64, c64)) <= tol_swiglu(a64, c64, Ta, Tc))
+
+
+@pytest.mark.parametrize("fmt", [4, 6, 8, "fp8"])
+@pytest.mark.parametrize("groups", [1, 2, 9])
+def test_narrow_workgroups_group_counts(fmt, groups):
+    """K of one, two and nine groups on windows that take the 64-column narrow
+    workgroups: 128 and 100 rows of w1/w3 + SwiGLU with N = 8192 and of a
+    plain weight with N = 16384 (more 32 x 32 tiles than the dataflow kernel
+    takes, fewer than 256 wide workgroups). The narrow kernel folds each
+    group's products during the next group and the last group's after its
+    loop; every row must equal the row of a 512-row prompt on the wide
+    workgroups, which fold at once, bit for bit."""
+    K2, M2 = 64 * groups, 512
+    say(f"narrow group counts fmt={fmt} K={K2}")
+    rng = np.random.default_rng(7000 + 10 * groups + (9 if fmt == "fp8" else fmt))
+
+    def draw(name, n):
+        if fmt == "fp8":
+            return synthetic.draw_fp8_weight(rng, name, n, K2)
+        return synthetic.draw_qweight(rng, name, n, K2, bits=fmt)
+
+    xd = dev_bf16(synthetic.draw_bf16_rows(rng, M2, K2))
+    for swiglu, N2 in ((True, 8192), (False, 16384)):
+        pa = _pack(fmt, draw("a", N2))
+        pb = _pack(fmt, draw("b", N2)) if swiglu else None
+
+        def win(xs):
+            if fmt == "fp8":
+                return q4.qmm_window_fp8b(pa, pb, N2, K2, xs, out_dtype=torch.float32)
+            return q4.qmm_window(pa, pb, N2, K2, xs, bits=fmt, out_dtype=torch.float32)
+
+        ref = bits32(win(xd))
+        for r0, rows in ((0, 128), (384, 128), (200, 100)):
+            y = win(xd[r0 : r0 + rows])
+            torch.cuda.synchronize()
+            assert np.array_equal(bits32(y), ref[r0 : r0 + rows]), (swiglu, r0, rows)
